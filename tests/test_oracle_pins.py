@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each oracle function is checked against something that does not share its
+code: a library routine (numpy / torch), a closed form or a published table,
+brute-force dense evaluation of the whole layer, or an invariant of the
+mathematics.  The cases are chosen so that a dropped term, a wrong sign or
+index, or a transposed operand fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import oracle as orc
+from expert_ffn_execution_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent helpers of the checkers (not shared with the oracle)
+# ---------------------------------------------------------------------------
+def _e2m1_table():
+    """code -> value from the OCP MX v1.0 table fixture."""
+    tab = {}
+    with open(os.path.join(GOLD, "e2m1_ocp_mx_v1.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, v = line.split()
+            tab[int(c, 2)] = float(v)
+    assert len(tab) == 16
+    return tab
+
+
+def _dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Table lookup dequantisation (fp64), independent of the oracle's decode."""
+    tab = _e2m1_table()
+    lut = np.array([tab[c] for c in range(16)], np.float64)
+    lo = codes & 15
+    hi = codes >> 4
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    c = np.empty((N, K), np.uint8)
+    c[:, 0::2] = lo
+    c[:, 1::2] = hi
+    sc = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    return lut[c] * sc
+
+
+def _bf16_round_np(a: np.ndarray) -> np.ndarray:
+    """Nearest bf16 of fp64 values (ties to even) for normal-range inputs."""
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def _weights_f64(ex: dict, wdtype: str):
+    if wdtype == "mxfp4":
+        return tuple(_dequant_mxfp4(ex[n].numpy(), ex[n + "_sc"].numpy())
+                     for n in ("gate", "up", "down"))
+    return tuple(ex[n].to(torch.float64).numpy() for n in ("gate", "up", "down"))
+
+
+def _brute_force_layer(x64, logits, bias, k, experts, wdtype, shared=None):
+    """Every expert on every token, masked by the gate matrix (dense form)."""
+    T, H = x64.shape
+    E = len(experts)
+    lp = logits.astype(np.float32) + (bias.astype(np.float32) if bias is not None else 0)
+    lp = lp.astype(np.float32)
+    # gate matrix: softmax over all experts, keep the top-k, renormalise
+    order = np.argsort(-lp, axis=1, kind="stable")[:, :k]
+    p = torch.softmax(torch.from_numpy(lp.astype(np.float64)), dim=1).numpy()
+    M = np.zeros((T, E))
+    for t in range(T):
+        sel = order[t]
+        M[t, sel] = p[t, sel] / p[t, sel].sum()
+    M = M.astype(np.float32).astype(np.float64)  # gates are handed over as fp32
+    out = np.zeros((T, H))
+    rnd = wdtype != "f32"
+    allex = list(experts) + ([shared] if shared is not None else [])
+    for e, ex in enumerate(allex):
+        Wg, Wu, Wd = _weights_f64(ex, wdtype)
+        g = x64 @ Wg.T
+        u = x64 @ Wu.T
+        h = g / (1.0 + np.exp(-g)) * u
+        if rnd:
+            h = _bf16_round_np(h)
+        y = h @ Wd.T
+        out += (M[:, e:e + 1] if e < E else 1.0) * y
+    return out
+
+
+def _bits_to_f64(a):
+    return orc.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# scalar formats
+# ---------------------------------------------------------------------------
+def test_mxfp4_decode_exhaustive_against_ocp_table():
+    tab = _e2m1_table()
+    for code in range(16):
+        for X in range(256):
+            v = orc.mxfp4_value(code, X)
+            if X == 255:
+                assert math.isnan(v)
+                continue
+            ref = tab[code] * math.ldexp(1.0, X - 127)
+            assert v == ref, (code, X, v, ref)
+            if tab[code] == 0.0:
+                assert math.copysign(1.0, v) == math.copysign(1.0, tab[code])
+
+
+def test_mxfp4_quantiser_round_trip():
+    # canonical codes (no -0) with random scales survive decode -> quantise
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 16, size=(4, 64)).astype(np.uint8)
+    codes[codes == 8] = 0
+    codes[:, ::32] = 7  # every block holds its max magnitude 6 so the scale is recovered
+    scales = rng.integers(100, 140, size=(4, 2)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    vals = np.array([[orc.mxfp4_value(int(codes[r, c]), int(scales[r, c // 32]))
+                      for c in range(64)] for r in range(4)], np.float32)
+    q, s = synth.quantize_mxfp4(torch.from_numpy(vals))
+    assert np.array_equal(q.numpy(), packed)
+    assert np.array_equal(s.numpy(), scales)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(2)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),    # subnormal range
+        np.clip(rng.standard_normal(2000) * 1e38, -3.3e38, 3.3e38).astype(np.float32),  # near overflow
+        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.3895314e38, 3.4e38, 1e-45],
+                 np.float32),
+    ])
+    # exact ties between consecutive bf16 values, both parities
+    base = rng.integers(0x3F00, 0x4100, size=2000).astype(np.uint32)
+    ties = ((base << 16) | 0x8000).view(np.float32)
+    vals = np.concatenate([vals, ties])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f64_to_bf16(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, ref)
+    for b in (0x0000, 0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x8001, 0x4049):
+        f = np.array([b << 16], np.uint32).view(np.float32)[0]
+        assert orc.bf16_to_f64(b) == float(f)
+
+
+# ---------------------------------------------------------------------------
+# router logits and top-k gating
+# ---------------------------------------------------------------------------
+def test_router_logits_match_fp64_matmul():
+    sh = synth.A3B_BF16
+    x = synth.gen_x(sh, 8)
+    wr = synth.gen_router(sh)
+    got = orc.router_logits(x, wr)
+    ref = (x.double() @ wr.double().T).numpy()
+    # one fp32 rounding of an fp64 sum: within half an ulp of fp32 (plus fp64 order noise)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp + 1e-12 * np.abs(ref))
+    assert got.dtype == np.float32
+
+
+def _route_ref(logits, bias, k):
+    lp = logits.astype(np.float32)
+    if bias is not None:
+        lp = (lp + bias.astype(np.float32)).astype(np.float32)
+    ids = np.argsort(-lp, axis=1, kind="stable")[:, :k]
+    p = torch.softmax(torch.from_numpy(lp.astype(np.float64)), dim=1)
+    sel = torch.gather(p, 1, torch.from_numpy(ids.astype(np.int64)))
+    w = (sel / sel.sum(dim=1, keepdim=True)).numpy()
+    return ids.astype(np.int32), w
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (256, 6), (256, 8), (5, 5), (7, 1)])
+def test_route_matches_stable_argsort_and_torch_softmax(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    T = 64
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32) if E > 8 else None
+    ids, w = orc.route(logits, k, bias)
+    rid, rw = _route_ref(logits, bias, k)
+    assert np.array_equal(ids, rid)
+    assert np.max(np.abs(w - rw)) <= 1e-6
+    assert np.max(np.abs(w.astype(np.float64).sum(1) - 1.0)) <= 1e-6
+    if k == 1:
+        assert np.all(w == 1.0)
+    if k == E:
+        full = torch.softmax(torch.from_numpy(logits.astype(np.float64)), 1).numpy()
+        np.testing.assert_allclose(np.take_along_axis(full, ids.astype(np.int64), 1), w,
+                                   rtol=0, atol=1e-7)
+
+
+_tie_vals = st.sampled_from([0.0, -0.0, 1.0, -1.0, 0.5, 1e30, -1e30, 2.0])
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 16), st.integers(1, 40), st.data())
+def test_route_tie_heavy(T, E, data):
+    k = data.draw(st.integers(1, E))
+    vals = data.draw(st.lists(_tie_vals, min_size=T * E, max_size=T * E))
+    logits = np.array(vals, np.float32).reshape(T, E)
+    ids, w = orc.route(logits, k)
+    rid, rw = _route_ref(logits, None, k)
+    assert np.array_equal(ids, rid)
+    assert np.max(np.abs(w - rw)) <= 1e-6
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == k
+
+
+def test_route_rejects_nonfinite():
+    lg = np.zeros((2, 4), np.float32)
+    lg[1, 2] = np.inf
+    with pytest.raises(ValueError):
+        orc.route(lg, 2)
+
+
+# ---------------------------------------------------------------------------
+# alignment
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (64, 8, 2), (333, 128, 8), (1000, 256, 6)])
+def test_align_matches_bincount_and_stable_argsort(T, E, k):
+    rng = np.random.default_rng(T + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = orc.route(logits, k)
+    counts, offsets, perm, inv = orc.align(ids, E)
+    flat = ids.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert counts.sum() == T * k
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+    assert np.array_equal(inv[perm], np.arange(T * k))
+    assert np.array_equal(np.bincount(perm // k, minlength=T), np.full(T, k))
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def test_align_empty_experts_and_single_expert():
+    ids = np.zeros((5, 1), np.int32)
+    counts, offsets, perm, inv = orc.align(ids, 4)
+    assert counts.tolist() == [5, 0, 0, 0]
+    assert offsets.tolist() == [0, 5, 5, 5, 5]
+    assert perm.tolist() == [0, 1, 2, 3, 4] and inv.tolist() == [0, 1, 2, 3, 4]
+
+
+# ---------------------------------------------------------------------------
+# expert FFN and whole layer
+# ---------------------------------------------------------------------------
+def test_hand_worked_example():
+    with open(os.path.join(GOLD, "hand_layer_example.json")) as f:
+        g = json.load(f)
+    logits = np.array(g["logits"], np.float32)
+    ids, w = orc.route(logits, g["k"])
+    assert ids.tolist() == g["ids"] and w.tolist() == g["w"]
+    counts, offsets, perm, inv = orc.align(ids, g["E"])
+    assert counts.tolist() == g["counts"] and offsets.tolist() == g["offsets"]
+    assert perm.tolist() == g["perm"] and inv.tolist() == g["inv_perm"]
+    experts = [{n: torch.tensor(ex[n], dtype=torch.float32) for n in ("gate", "up", "down")}
+               for ex in g["experts"]]
+    x = np.array(g["x"], np.float32)
+    out = orc.moe_layer(x, ids, w, experts, "f32", g["I"])
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-7, atol=0)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4"])
+def test_single_expert_is_dense_swiglu(wdtype):
+    # E = 1, k = 1 reduces the layer to a dense SwiGLU MLP (torch fp64 reference)
+    H, I, T = 64, 96, 5
+    sh = synth.LayerShape("pin_dense", H=H, E=1, k=1, I=I, wdtype=wdtype,
+                          adtype="f32" if wdtype == "f32" else "bf16")
+    ex = synth.gen_expert(sh, 0)
+    x = synth.gen_x(sh, T)
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    out = _bits_to_f64(orc.moe_layer(x, ids, w, [ex], wdtype, I, out_fmt="f32"))
+    Wg, Wu, Wd = (torch.from_numpy(a) for a in _weights_f64(ex, wdtype))
+    xt = x.double()
+    h = torch.nn.functional.silu(xt @ Wg.T) * (xt @ Wu.T)
+    if wdtype != "f32":
+        h = torch.from_numpy(_bf16_round_np(h.numpy()))
+    ref = (h @ Wd.T).numpy()
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(out - ref) <= ulp)
+
+
+@pytest.mark.parametrize("wdtype,shared", [("f32", False), ("bf16", False), ("mxfp4", False),
+                                           ("mxfp4", True), ("bf16", True)])
+def test_layer_matches_brute_force_dense(wdtype, shared):
+    T, H, E, k, I = 12, 64, 6, 2, 32
+    sh = synth.LayerShape(f"pin_bf_{wdtype}_{shared}", H=H, E=E, k=k, I=I,
+                          n_shared=int(shared), wdtype=wdtype,
+                          adtype="f32" if wdtype == "f32" else "bf16", bias="normal",
+                          bias_param=0.5)
+    x = synth.gen_x(sh, T)
+    experts = [synth.gen_expert(sh, e) for e in range(E)]
+    sx = synth.gen_expert(sh, E) if shared else None
+    logits = synth.gen_logits(sh, T).numpy()
+    bias = synth.gen_bias(sh).numpy()
+    ids, w = orc.route(logits, k, bias)
+    out = _bits_to_f64(orc.moe_layer(x, ids, w, experts, wdtype, I, shared=sx, out_fmt="f32"))
+    ref = _brute_force_layer(x.double().numpy(), logits, bias, k, experts, wdtype, sx)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(out - ref) <= ulp + 1e-12)
+
+
+def test_layer_bf16_output_is_single_rounding():
+    T, H, E, k, I = 6, 64, 4, 2, 32
+    sh = synth.LayerShape("pin_bf16_out", H=H, E=E, k=k, I=I)
+    x = synth.gen_x(sh, T)
+    experts = [synth.gen_expert(sh, e) for e in range(E)]
+    ids, w = orc.route(synth.gen_logits(sh, T).numpy(), k)
+    o32 = orc.moe_layer(x, ids, w, experts, "bf16", I, out_fmt="f32")
+    o16 = orc.moe_layer(x, ids, w, experts, "bf16", I, out_fmt="bf16")
+    # fp32 output rounded to bf16 equals the direct bf16 output except where the
+    # fp32 rounding lands on a bf16 tie; the fp64 sums are the same in both
+    via32 = torch.from_numpy(o32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(via32 == o16) > 0.999
+
+
+def test_layer_invariants():
+    T, H, E, k, I = 10, 64, 8, 3, 32
+    sh = synth.LayerShape("pin_inv", H=H, E=E, k=k, I=I, wdtype="f32", adtype="f32")
+    x = synth.gen_x(sh, T)
+    experts = [synth.gen_expert(sh, e) for e in range(E)]
+    logits = synth.gen_logits(sh, T).numpy()
+    ids, w = orc.route(logits, k)
+    base = orc.moe_layer(x, ids, w, experts, "f32", I)
+    # token permutation equivariance
+    p = np.random.default_rng(3).permutation(T)
+    ids_p, w_p = orc.route(logits[p], k)
+    out_p = orc.moe_layer(x[p], ids_p, w_p, experts, "f32", I)
+    assert np.array_equal(out_p, base[p])
+    # expert relabelling (no ties in random logits)
+    q = np.random.default_rng(4).permutation(E)          # new id j holds old expert q[j]
+    ids_q, w_q = orc.route(logits[:, q], k)
+    out_q = orc.moe_layer(x, ids_q, w_q, [experts[q[j]] for j in range(E)], "f32", I)
+    np.testing.assert_array_equal(np.sort(q[ids_q], axis=1), np.sort(ids, axis=1))
+    np.testing.assert_allclose(out_q, base, rtol=0, atol=1e-6 * np.abs(base).max())
+    # scaling every down projection by 2^a scales the output by exactly 2^a
+    scaled = [{"gate": ex["gate"], "up": ex["up"], "down": ex["down"] * 8.0} for ex in experts]
+    out_s = orc.moe_layer(x, ids, w, scaled, "f32", I)
+    assert np.array_equal(out_s, base * 8.0)
+    # gate weight 1 with k = 1 on a single expert equals that expert alone
+    ids1 = np.full((T, 1), 5, np.int32)
+    out1 = orc.moe_layer(x, ids1, np.ones((T, 1), np.float32), experts, "f32", I)
+    y5 = np.stack([orc.expert_ffn(experts[5], "f32", x[t].double().numpy(), H, I, False)
+                   for t in range(T)])
+    assert np.array_equal(out1, y5.astype(np.float32))
+
+
+def test_layer_token_subset_matches_full():
+    T, H, E, k, I = 9, 64, 4, 2, 32
+    sh = synth.LayerShape("pin_subset", H=H, E=E, k=k, I=I)
+    x = synth.gen_x(sh, T)
+    experts = [synth.gen_expert(sh, e) for e in range(E)]
+    ids, w = orc.route(synth.gen_logits(sh, T).numpy(), k)
+    full = orc.moe_layer(x, ids, w, experts, "bf16", I)
+    sub = np.array([7, 0, 3], np.int32)
+    part = orc.moe_layer(x, ids, w, experts, "bf16", I, tokens=sub)
+    assert np.array_equal(part, full[sub])
