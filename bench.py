@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""MoE-layer benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: router GEMM + top-k
+(ft_moe_route), alignment (ft_moe_align), grouped expert FFN (ft_moe_ffn) and
+combine (ft_moe_combine), on inputs already resident in HBM.  Layer weight
+banks rotate between steps so that the bytes touched between two uses of the
+same weights exceed four times the 256 MB Infinity Cache.
+
+Prints one JSON line: headline = prefill tokens/s of the workload, with the
+roofline of its dominant kernel (the gate/up grouped GEMM, MFMA-bound), the
+decode points (HBM-bound FFN weight streaming) and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="35b_a3b_bf16")
+    ap.add_argument("--tokens", type=int, default=0, help="prefill tokens (default: workload's)")
+    ap.add_argument("--decode", default="", help="decode token counts, e.g. 1,16,64 "
+                                                 "(default: workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Bank:
+    """One layer's weights in device slots plus its router and bias."""
+
+    def __init__(self, sh, layer, dev):
+        import torch
+        from expert_ffn_execution_amd import ftmoe as ft
+        from expert_ffn_execution_amd import synth
+        n = synth.n_experts_total(sh)
+        self.stride = ft.slot_stride(sh.wdtype, sh.H, sh.I)
+        self.pool = torch.empty((n, self.stride), dtype=torch.uint8, device=dev)
+        for e in range(n):
+            ex = synth.gen_expert(sh, e, layer, device=dev)
+            ft.pack_expert(ex, sh.wdtype, sh.H, sh.I, self.pool[e])
+        self.wts = ft.make_weights(sh.wdtype, sh.E, sh.H, sh.I, self.pool, n_shared=sh.n_shared,
+                                   shared_slot=sh.E if sh.n_shared else 0)
+        self.wr = synth.gen_router(sh, layer, device=dev)
+        self.bias = synth.gen_bias(sh, layer, device=dev)
+        self.expert_bytes = ft.expert_layout(sh.wdtype, sh.H, sh.I)[0]
+
+
+def run_point(sh, banks, T, steps, warmup, dev, prefill):
+    """Time `steps` full steps at T tokens; returns a dict of measurements."""
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+
+    nx = 16 if T <= 64 else 2
+    xs = [synth.gen_x(sh, T, step=i, device=dev) for i in range(nx)]
+    E, k = sh.E, sh.k
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    al = (torch.empty(E, dtype=torch.int32, device=dev),
+          torch.empty(E + 1, dtype=torch.int32, device=dev),
+          torch.empty(T * k, dtype=torch.int32, device=dev),
+          torch.empty(T * k, dtype=torch.int32, device=dev))
+    aws = torch.empty(max(1, ft.align_workspace(T, k, E)), dtype=torch.uint8, device=dev)
+    fws = torch.empty(ft.ffn_workspace(banks[0].wts, T, k), dtype=torch.uint8, device=dev)
+    y = torch.empty((T * k + sh.n_shared * T, sh.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        b = banks[i % len(banks)]
+        x = xs[i % nx]
+        ft.route(T, E, k, x=x, w_router=b.wr, bias=b.bias, logits_out=logits, ids=ids, w=w)
+        ft.align(ids, E, ws=aws, out=al)
+        ft.ffn(b.wts, x, k, al[2], al[1], y=y, ws=fws)
+        ft.combine(y, al[3], w, n_shared=sh.n_shared, out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    prof = {which: [(ev(), ev()) for _ in range(steps)]
+            for which in (ft.PROF_GEMM1, ft.PROF_GEMM2, ft.PROF_FFN)}
+    active = []
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        for which, lst in prof.items():
+            ft.set_profile_events(which, *lst[i])
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    for which in prof:
+        ft.set_profile_events(which, None, None)
+    ms = t0.elapsed_time(t1) / steps
+    dur = {which: sum(a.elapsed_time(b) for a, b in lst) / steps for which, lst in prof.items()}
+    # distinct active experts of each timed step (recomputed outside the timed region)
+    for i in range(steps):
+        b = banks[(warmup + i) % len(banks)]
+        x = xs[(warmup + i) % nx]
+        ids_i, _, _ = ft.route(T, E, k, x=x, w_router=b.wr, bias=b.bias)
+        cnt = torch.bincount(ids_i.reshape(-1).long(), minlength=E)
+        active.append(int((cnt > 0).sum().item()))
+    torch.cuda.synchronize()
+    n_act = sum(active) / steps
+    eb = banks[0].expert_bytes
+    ffn_bytes = (n_act + sh.n_shared) * eb
+    rows = T * k + sh.n_shared * T
+    fl1 = 2.0 * rows * 2 * sh.I * sh.H
+    fl2 = 2.0 * rows * sh.I * sh.H
+    res = {
+        "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3),
+        "ffn_ms": dur[ft.PROF_FFN], "gemm1_ms": dur[ft.PROF_GEMM1], "gemm2_ms": dur[ft.PROF_GEMM2],
+        "active_experts": n_act, "weight_bytes": ffn_bytes,
+        "ffn_gbs": ffn_bytes / (dur[ft.PROF_FFN] * 1e-3) / 1e9,
+        "gemm1_tflops": fl1 / (dur[ft.PROF_GEMM1] * 1e-3) / 1e12,
+        "gemm2_tflops": fl2 / (dur[ft.PROF_GEMM2] * 1e-3) / 1e12,
+        "ffn_tflops": (fl1 + fl2) / (dur[ft.PROF_FFN] * 1e-3) / 1e12,
+        "gemm1_flops": fl1,
+    }
+    return res
+
+
+def cpu_baseline(sh, bank, T, dev, seconds):
+    """The CPU oracle timed on a bounded token sample of the same workload."""
+    import numpy as np
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+    from oracle import oracle as orc
+
+    x = synth.gen_x(sh, T, step=0, device=dev).cpu()
+    wr = bank.wr.cpu()
+    bias = None if bank.bias is None else bank.bias.cpu().numpy()
+    _, offs = ft.expert_layout(sh.wdtype, sh.H, sh.I)
+    H, I = sh.H, sh.I
+    raw = bank.pool.cpu()
+    experts = []
+    for e in range(synth.n_experts_total(sh)):
+        r = raw[e]
+        if sh.wdtype == "mxfp4":
+            experts.append({"gate": r[offs[0]:offs[0] + I * H // 2].view(I, H // 2),
+                            "up": r[offs[1]:offs[1] + I * H // 2].view(I, H // 2),
+                            "down": r[offs[2]:offs[2] + H * I // 2].view(H, I // 2),
+                            "gate_sc": r[offs[3]:offs[3] + I * H // 32].view(I, H // 32),
+                            "up_sc": r[offs[4]:offs[4] + I * H // 32].view(I, H // 32),
+                            "down_sc": r[offs[5]:offs[5] + H * I // 32].view(H, I // 32)})
+        else:
+            dt = torch.bfloat16 if sh.wdtype == "bf16" else torch.float32
+            es = 2 if sh.wdtype == "bf16" else 4
+            experts.append({"gate": r[offs[0]:offs[0] + I * H * es].view(dt).view(I, H),
+                            "up": r[offs[1]:offs[1] + I * H * es].view(dt).view(I, H),
+                            "down": r[offs[2]:offs[2] + H * I * es].view(dt).view(H, I)})
+    routed, shared = experts[:sh.E], (experts[sh.E] if sh.n_shared else None)
+
+    def run(n):
+        xs = x[:n]
+        t = time.perf_counter()
+        lg = orc.router_logits(xs, wr)
+        ids, w = orc.route(lg, sh.k, bias)
+        orc.align(ids, sh.E)
+        orc.moe_layer(xs, ids, w, routed, sh.wdtype, I, shared=shared)
+        return time.perf_counter() - t
+
+    n = 16
+    t = run(n)
+    n2 = int(min(T, max(n, n * seconds / max(t, 1e-3))))
+    if n2 > n:
+        n, t = n2, run(n2)
+    return {"value": n / t, "unit": "tokens/s", "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"first {n} tokens of the T={T} batch, layer 0 weights "
+                      f"(router GEMM, top-k, align, per-token expert loops, combine), "
+                      f"{t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("the MoE-layer path here is single-GPU; multi-GPU runs are not supported")
+        sys.exit(2)
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+
+    ft.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sh = synth.SHAPES[args.workload]
+    pts = synth.POINTS[sh.name]
+    T_pre = args.tokens or max(pts)
+    dec = [int(v) for v in args.decode.split(",")] if args.decode else [p for p in pts if p <= 64]
+    n_exp = synth.n_experts_total(sh)
+    bank_bytes = n_exp * ft.slot_stride(sh.wdtype, sh.H, sh.I)
+    n_banks = max(2, min(8, math.ceil(4 * MALL_BYTES * 4 / bank_bytes)))
+    log(f"workload {sh.name}: {n_banks} weight banks of {bank_bytes / 1e9:.2f} GB")
+    banks = [Bank(sh, l, dev) for l in range(n_banks)]
+    torch.cuda.synchronize()
+
+    head = run_point(sh, banks, T_pre, args.steps, args.warmup, dev, prefill=True)
+    log("prefill", json.dumps(head))
+    decode = []
+    for T in dec:
+        r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
+        decode.append({
+            "T": T, "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+            "ffn_us": r["ffn_ms"] * 1e3, "active_experts": r["active_experts"],
+            "roofline": {"bound": "hbm", "achieved": r["ffn_gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": r["ffn_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "ft_moe_ffn (both expert GEMMs)"}})
+        log("decode", json.dumps(decode[-1]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sh, banks[0], T_pre, dev, args.cpu_seconds)
+        log("cpu", json.dumps(cpu))
+
+    line = {
+        "metric": "MoE-layer tokens/s (prefill); decode HBM GB/s and prefill MFMA TFLOP/s vs peak",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": sh.wdtype, "data": "synthetic",
+        "config": {"workload": f"{sh.name} prefill T={T_pre}", "H": sh.H, "E": sh.E, "k": sh.k,
+                   "I": sh.I, "n_shared": sh.n_shared, "tokens": T_pre, "weights": sh.wdtype,
+                   "activations": "bf16", "weight_banks": n_banks},
+        "roofline": {"bound": "mfma", "achieved": head["gemm1_tflops"],
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": head["gemm1_tflops"] / MFMA_BF16_PEAK_TFS, "traffic": None,
+                     "kernel": "gate/up grouped GEMM + SwiGLU (gemm1)",
+                     "gemm1_us": head["gemm1_ms"] * 1e3, "gemm2_us": head["gemm2_ms"] * 1e3,
+                     "ffn_tflops": head["ffn_tflops"]},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+// align.hip -- token-to-expert alignment: histogram, offsets, stable permutation.
+//
+// The expert GEMMs read the tokens routed to one expert as one contiguous
+// segment (claypier.com article, "从 MoE「用不到的权重」入手的推理引擎": each
+// step touches only the experts it routes to).  perm lists the flat slots
+// f = t*k + j grouped by expert, increasing f inside a group: a stable
+// counting sort, so the result is unique and bitwise reproducible.
+//
+// Stable ranks come from wavefront ballots: a wave takes 64 consecutive
+// slots, one per lane; for each distinct expert among them, a ballot finds the
+// lanes holding it, the rank of a lane is the popcount of the matching lanes
+// below it, and a running per-expert base (kept in LDS, touched only by this
+// wave) advances by the match count.  Waves own contiguous chunks, and a
+// per-(chunk, expert) prefix scan gives each chunk its starting positions.
+#include "common.h"
+
+namespace {
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Scatter 64 consecutive slots [f0, f0 + 64) ∩ [0, n) held one per lane.
+// run[e] is this wave's next free position for expert e (LDS, wave-private).
+__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int f0, int n,
+                                             int* run, int32_t* __restrict__ perm,
+                                             int32_t* __restrict__ inv, int lane) {
+    const int f = f0 + lane;
+    const bool valid = f < n;
+    const int v = valid ? ids[f] : -1;
+    uint64_t remaining = __ballot(valid);
+    while (remaining) {
+        const int leader = __builtin_ctzll(remaining);
+        const int vl = __shfl(v, leader, 64);
+        const uint64_t peers = __ballot(v == vl);
+        const int base = run[vl];  // same address for every lane: broadcast read
+        if (v == vl) {
+            const int pos = base + __popcll(peers & lanemask_lt(lane));
+            perm[pos] = f;
+            inv[f] = pos;
+        }
+        if (lane == leader) run[vl] = base + __popcll(peers);
+        remaining &= ~peers;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small problems: one block of 8 waves does everything.
+// LDS: hist[8][E] (then running bases), tot[E].
+// ---------------------------------------------------------------------------
+constexpr int SW = 8;
+__global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __restrict__ ids,
+                                                              int n, int E,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ inv) {
+    extern __shared__ int lds[];
+    int* hist = lds;            // [SW][E]
+    int* tot = lds + SW * E;    // [E] inclusive scan scratch
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < SW * E; i += SW * 64) hist[i] = 0;
+    __syncthreads();
+    const int chunk = ((n + SW - 1) / SW + 63) & ~63;
+    const int f_lo = w * chunk, f_hi = min(n, f_lo + chunk);
+    for (int f = f_lo + lane; f < f_hi; f += 64) atomicAdd(&hist[w * E + ids[f]], 1);
+    __syncthreads();
+    // totals and exclusive offsets (Hillis-Steele over E, E <= 1024)
+    for (int e = tid; e < E; e += SW * 64) {
+        int s = 0;
+        for (int q = 0; q < SW; ++q) s += hist[q * E + e];
+        tot[e] = s;
+        counts[e] = s;
+    }
+    __syncthreads();
+    for (int o = 1; o < E; o <<= 1) {
+        int v[2] = {0, 0};
+        for (int i = 0, e = tid; e < E; e += SW * 64, ++i) v[i] = e >= o ? tot[e - o] : 0;
+        __syncthreads();
+        for (int i = 0, e = tid; e < E; e += SW * 64, ++i) tot[e] += v[i];
+        __syncthreads();
+    }
+    for (int e = tid; e < E; e += SW * 64) {
+        int base = (e ? tot[e - 1] : 0);
+        offsets[e] = base;
+        if (e == E - 1) offsets[E] = tot[e];
+        for (int q = 0; q < SW; ++q) {
+            int c = hist[q * E + e];
+            hist[q * E + e] = base;
+            base += c;
+        }
+    }
+    __syncthreads();
+    for (int f0 = f_lo; f0 < f_hi; f0 += 64)
+        wave_scatter(ids, f0, f_hi, hist + w * E, perm, inv, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Large problems: units of UNIT consecutive slots, one wave each.
+//   1) per-unit histograms hist[u][e]
+//   2) per-expert exclusive scan over units, counts[e]
+//   3) per-unit scatter from offsets[e] + hist[u][e]
+// ---------------------------------------------------------------------------
+constexpr int UNIT = 512;
+
+__global__ __launch_bounds__(256) void unit_hist_kernel(const int32_t* __restrict__ ids, int n,
+                                                        int E, int U, int* __restrict__ hist) {
+    extern __shared__ int lds[];  // [4][E]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int u = blockIdx.x * 4 + w;
+    int* h = lds + w * E;
+    for (int e = lane; e < E; e += 64) h[e] = 0;
+    __syncthreads();
+    if (u < U) {
+        const int f_lo = u * UNIT, f_hi = min(n, f_lo + UNIT);
+        for (int f = f_lo + lane; f < f_hi; f += 64) atomicAdd(&h[ids[f]], 1);
+    }
+    __syncthreads();
+    if (u < U)
+        for (int e = lane; e < E; e += 64) hist[(size_t)u * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(256) void unit_scan_kernel(int* __restrict__ hist, int E, int U,
+                                                        int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    int carry = 0;
+    for (int u0 = 0; u0 < U; u0 += 64) {
+        const int u = u0 + lane;
+        int v = u < U ? hist[(size_t)u * E + e] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        if (u < U) hist[(size_t)u * E + e] = carry + incl - v;
+        carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) counts[e] = carry;
+}
+
+__global__ __launch_bounds__(256) void unit_scatter_kernel(const int32_t* __restrict__ ids,
+                                                           int n, int E, int U,
+                                                           const int* __restrict__ hist,
+                                                           const int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ inv) {
+    extern __shared__ int lds[];  // off[E], run[4][E]
+    int* off = lds;
+    int* run = lds + E;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // exclusive scan of counts: each wave scans a quarter, then combine
+    const int per = (E + 3) / 4;
+    {
+        int carry = 0;
+        const int e_lo = w * per, e_hi = min(E, e_lo + per);
+        for (int e0 = e_lo; e0 < e_hi; e0 += 64) {
+            int e = e0 + lane;
+            int v = e < e_hi ? counts[e] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            if (e < e_hi) off[e] = carry + incl - v;
+            carry += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) run[w] = carry;  // quarter totals (run[] reused below)
+    }
+    __syncthreads();
+    int add = 0;
+    for (int q = 0; q < w; ++q) add += run[q];
+    const int grand = run[0] + run[1] + run[2] + run[3];
+    __syncthreads();
+    {
+        const int e_lo = w * per, e_hi = min(E, e_lo + per);
+        for (int e = e_lo + lane; e < e_hi; e += 64) off[e] += add;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < E; e += 256) offsets[e] = off[e];
+        if (tid == 0) offsets[E] = grand;
+    }
+    const int u = blockIdx.x * 4 + w;
+    if (u >= U) return;
+    int* r = run + w * E;
+    for (int e = lane; e < E; e += 64) r[e] = off[e] + hist[(size_t)u * E + e];
+    // wave-private from here on: no block barrier needed
+    const int f_lo = u * UNIT, f_hi = min(n, f_lo + UNIT);
+    for (int f0 = f_lo; f0 < f_hi; f0 += 64) wave_scatter(ids, f0, f_hi, r, perm, inv, lane);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, long n, int32_t v) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+namespace ft {
+
+ft_status launch_fill_i32(int32_t* p, long n, int32_t v, hipStream_t s) {
+    if (n <= 0) return FT_OK;
+    fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n, v);
+    FT_LAUNCHED("fill_i32");
+    return FT_OK;
+}
+
+constexpr long ALIGN_SMALL_MAX = 4096;
+
+size_t align_workspace(int T, int k, int E) {
+    long n = (long)T * k;
+    if (n <= ALIGN_SMALL_MAX) return 0;
+    long U = (n + UNIT - 1) / UNIT;
+    return (size_t)(U * E) * sizeof(int);
+}
+
+ft_status launch_align(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                       hipStream_t s) {
+    const long n = (long)T * k;
+    if (n <= ALIGN_SMALL_MAX) {
+        size_t lds = (size_t)(SW + 1) * E * sizeof(int);
+        align_small_kernel<<<1, SW * 64, lds, s>>>(ids, (int)n, E, counts, offsets, perm, inv);
+        FT_LAUNCHED("align_small");
+        return FT_OK;
+    }
+    const int U = (int)((n + UNIT - 1) / UNIT);
+    int* hist = (int*)ws;
+    unit_hist_kernel<<<cdiv(U, 4), 256, 4 * E * sizeof(int), s>>>(ids, (int)n, E, U, hist);
+    FT_LAUNCHED("align_hist");
+    unit_scan_kernel<<<cdiv(E, 4), 256, 0, s>>>(hist, E, U, counts);
+    FT_LAUNCHED("align_scan");
+    unit_scatter_kernel<<<cdiv(U, 4), 256, 5 * E * sizeof(int), s>>>(ids, (int)n, E, U, hist,
+                                                                       counts, offsets, perm, inv);
+    FT_LAUNCHED("align_scatter");
+    return FT_OK;
+}
+
+}  // namespace ft

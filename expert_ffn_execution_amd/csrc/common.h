@@ -1,0 +1,85 @@
+// common.h -- shared host/device helpers of libftmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/ftmoe.h"
+
+// ---------------------------------------------------------------------------
+// host-side status plumbing
+// ---------------------------------------------------------------------------
+namespace ft {
+
+ft_status set_error(ft_status st, const char* fmt, ...);
+void clear_error();
+
+#define FT_CHECK_ARG(cond, ...)                                        \
+    do {                                                               \
+        if (!(cond)) return ::ft::set_error(FT_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+#define FT_HIP(call)                                                               \
+    do {                                                                           \
+        hipError_t e_ = (call);                                                    \
+        if (e_ != hipSuccess)                                                      \
+            return ::ft::set_error(FT_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// launch-error check after <<<>>>
+#define FT_LAUNCHED(name)                                                          \
+    do {                                                                           \
+        hipError_t e_ = hipGetLastError();                                         \
+        if (e_ != hipSuccess)                                                      \
+            return ::ft::set_error(FT_ERR_HIP, "launch %s: %s", name, hipGetErrorString(e_)); \
+    } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+// profiling hooks: events recorded around selected kernels (see ft_set_profile_events)
+enum { PROF_FFN_GEMM1 = 0, PROF_FFN_GEMM2 = 1, PROF_FFN = 2, PROF_ROUTE = 3,
+       PROF_ALIGN = 4, PROF_COMBINE = 5, PROF_N = 6 };
+void prof_begin(int which, hipStream_t s);
+void prof_end(int which, hipStream_t s);
+
+}  // namespace ft
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+    return __builtin_bit_cast(bf16x2_t, u);
+}
+// sum of the two bf16 products of a and b, accumulated into c (fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + expf(-g)) * u;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}

@@ -1,0 +1,245 @@
+// slot_policy.h -- LRU expert-slot policy (host C++, no HIP).
+//
+// The device holds a fixed number of expert slots; the full pool of
+// (layer, expert) weights lives in host memory.  A request for a layer's
+// routed experts takes the resident ones (touching them as most recent) and
+// brings the others into free slots, else into the least-recently-used slots
+// that no one is reading and no copy is filling (refft.com guide, "深度解析":
+// global LRU expert caching; freelamp.com article, section 2.3: the expert
+// cache is counted in slots; claypier.com article,
+// "从 MoE「用不到的权重」入手的推理引擎": weights not used for a while are
+// evicted).  The next layer's experts can be prefetched into slots while the
+// current layer computes (FreeToken hub article, paragraph on prefill overlap).
+//
+// The policy is pure bookkeeping; an Engine performs copies and orders them
+// against the compute stream (a HIP engine in the library, a recording mock
+// in the CPU tests).  Every call visits its experts in ascending id order, so
+// timestamps and victims are deterministic.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/ftmoe.h"
+
+namespace ftp {
+
+struct Engine {
+    virtual ~Engine() {}
+    // enqueue host (layer, expert) -> device slot; must first wait for the
+    // slot's last reader (if one was recorded) and leave a completion marker.
+    virtual bool copy(int slot, int layer, int expert) = 0;
+    // has the last copy into `slot` completed?
+    virtual bool copy_done(int slot) = 0;
+    // make the compute stream wait for the last copy into `slot`
+    virtual bool compute_wait(int slot) = 0;
+    // record: work enqueued on the compute stream so far is the last reader of `slot`
+    virtual bool record_read(int slot) = 0;
+};
+
+struct Entry {
+    int layer = -1, expert = -1;   // -1: free
+    uint64_t last = 0;             // LRU timestamp
+    bool held = false;             // demanded by a map, not yet released
+    bool prefetched = false;       // brought by prefetch and not yet demanded
+    bool copying = false;          // a copy was issued and not yet seen complete
+};
+
+class Policy {
+  public:
+    Policy(int n_layers, int n_experts, int n_slots, int scope, size_t expert_bytes)
+        : L_(n_layers), E_(n_experts), S_(n_slots), scope_(scope), bytes_(expert_bytes),
+          slots_(n_slots), where_((size_t)n_layers * n_experts, -1) {
+        st_ = ft_cache_stats{};
+        st_.n_slots = n_slots;
+    }
+
+    int lookup(int layer, int expert) const {
+        if (layer < 0 || layer >= L_ || expert < 0 || expert >= E_) return -1;
+        return where_[(size_t)layer * E_ + expert];
+    }
+
+    // slot_of[i] receives the slot of experts[i].
+    ft_status map(Engine& eng, int layer, const int32_t* experts, int n, int32_t* slot_of,
+                  ft_map_stats* ms) {
+        ft_status v = check_list(layer, experts, n);
+        if (v != FT_OK) return v;
+        refresh(eng);
+        // capacity: misses must fit in free + evictable slots of the layer's range
+        int need = 0;
+        for (int i = 0; i < n; ++i)
+            if (lookup(layer, experts[i]) < 0) ++need;
+        if (need > obtainable(layer, -1)) return FT_ERR_CAPACITY;
+        ft_map_stats m{};
+        m.n_demand = n;
+        for (int i = 0; i < n; ++i) {
+            const int e = experts[i];
+            int s = lookup(layer, e);
+            if (s >= 0) {
+                Entry& en = slots_[s];
+                if (en.prefetched) ++m.n_prefetch_hit; else ++m.n_hit;
+                en.prefetched = false;
+            } else {
+                s = take_slot(eng, layer);
+                if (s < 0) return FT_ERR_CAPACITY;  // cannot happen after the check above
+                if (!start_copy(eng, s, layer, e)) return FT_ERR_HIP;
+                ++m.n_miss;
+                m.bytes_h2d += bytes_;
+            }
+            Entry& en = slots_[s];
+            en.last = ++clock_;
+            en.held = true;
+            if (en.copying && !eng.compute_wait(s)) return FT_ERR_HIP;
+            slot_of[i] = s;
+        }
+        st_.maps++;
+        st_.demand += m.n_demand;
+        st_.hits += m.n_hit;
+        st_.prefetch_hits += m.n_prefetch_hit;
+        st_.misses += m.n_miss;
+        st_.bytes_h2d += (long long)m.bytes_h2d;
+        if (ms) *ms = m;
+        return FT_OK;
+    }
+
+    ft_status release(Engine& eng, int layer) {
+        if (layer < 0 || layer >= L_) return FT_ERR_INVALID_ARG;
+        for (int s = 0; s < S_; ++s) {
+            Entry& en = slots_[s];
+            if (en.held && en.layer == layer) {
+                if (!eng.record_read(s)) return FT_ERR_HIP;
+                en.held = false;
+            }
+        }
+        return FT_OK;
+    }
+
+    ft_status prefetch(Engine& eng, int layer, const int32_t* experts, int n, int* n_issued) {
+        ft_status v = check_list(layer, experts, n);
+        if (v != FT_OK) return v;
+        refresh(eng);
+        int issued = 0;
+        bool short_of_room = false;
+        for (int i = 0; i < n; ++i) {
+            const int e = experts[i];
+            int s = lookup(layer, e);
+            if (s >= 0) {
+                slots_[s].last = ++clock_;
+                continue;
+            }
+            s = take_slot(eng, layer);
+            if (s < 0) {
+                short_of_room = true;
+                continue;  // later experts find no room either; keep scanning for residents
+            }
+            if (!start_copy(eng, s, layer, e)) return FT_ERR_HIP;
+            Entry& en = slots_[s];
+            en.prefetched = true;
+            en.last = ++clock_;
+            ++issued;
+            st_.bytes_h2d += (long long)bytes_;
+        }
+        st_.prefetch_issued += issued;
+        if (n_issued) *n_issued = issued;
+        return short_of_room ? FT_WARN_OVERLAP_DISABLED : FT_OK;
+    }
+
+    ft_status evict(Engine& eng, int layer, int expert) {
+        if (layer < 0 || layer >= L_ || expert < -1 || expert >= E_) return FT_ERR_INVALID_ARG;
+        refresh(eng);
+        const int lo = expert < 0 ? 0 : expert, hi = expert < 0 ? E_ : expert + 1;
+        for (int e = lo; e < hi; ++e) {
+            int s = lookup(layer, e);
+            if (s >= 0 && (slots_[s].held || slots_[s].copying)) return FT_ERR_BUSY;
+        }
+        for (int e = lo; e < hi; ++e) {
+            int s = lookup(layer, e);
+            if (s >= 0) drop(s);
+        }
+        return FT_OK;
+    }
+
+    ft_cache_stats stats() const {
+        ft_cache_stats o = st_;
+        o.resident = o.held = o.in_flight = 0;
+        for (const Entry& en : slots_) {
+            if (en.layer >= 0) o.resident++;
+            if (en.held) o.held++;
+            if (en.copying) o.in_flight++;
+        }
+        return o;
+    }
+
+    const Entry& entry(int s) const { return slots_[s]; }
+    int n_slots() const { return S_; }
+
+  private:
+    int L_, E_, S_, scope_;
+    size_t bytes_;
+    std::vector<Entry> slots_;
+    std::vector<int> where_;
+    uint64_t clock_ = 0;
+    ft_cache_stats st_;
+
+    int lo(int layer) const { return scope_ == FT_SCOPE_PER_LAYER ? layer * (S_ / L_) : 0; }
+    int hi(int layer) const { return scope_ == FT_SCOPE_PER_LAYER ? (layer + 1) * (S_ / L_) : S_; }
+
+    ft_status check_list(int layer, const int32_t* experts, int n) const {
+        if (layer < 0 || layer >= L_ || n < 0 || (n > 0 && !experts)) return FT_ERR_INVALID_ARG;
+        for (int i = 0; i < n; ++i) {
+            if (experts[i] < 0 || experts[i] >= E_) return FT_ERR_INVALID_ARG;
+            if (i && experts[i] <= experts[i - 1]) return FT_ERR_INVALID_ARG;
+        }
+        return FT_OK;
+    }
+
+    // mark copies seen complete
+    void refresh(Engine& eng) {
+        for (int s = 0; s < S_; ++s)
+            if (slots_[s].copying && eng.copy_done(s)) slots_[s].copying = false;
+    }
+
+    bool evictable(const Entry& en) const { return !en.held && !en.copying; }
+
+    // free + evictable slots in the layer's range
+    int obtainable(int layer, int) const {
+        int c = 0;
+        for (int s = lo(layer); s < hi(layer); ++s)
+            if (slots_[s].layer < 0 || evictable(slots_[s])) ++c;
+        return c;
+    }
+
+    // lowest free slot, else the least recently used evictable one
+    int take_slot(Engine&, int layer) {
+        for (int s = lo(layer); s < hi(layer); ++s)
+            if (slots_[s].layer < 0) return s;
+        int best = -1;
+        for (int s = lo(layer); s < hi(layer); ++s)
+            if (evictable(slots_[s]) && (best < 0 || slots_[s].last < slots_[best].last)) best = s;
+        if (best >= 0) {
+            drop(best);
+            st_.evictions++;
+        }
+        return best;
+    }
+
+    void drop(int s) {
+        Entry& en = slots_[s];
+        if (en.layer >= 0) where_[(size_t)en.layer * E_ + en.expert] = -1;
+        en = Entry{};
+    }
+
+    bool start_copy(Engine& eng, int s, int layer, int e) {
+        if (!eng.copy(s, layer, e)) return false;
+        Entry& en = slots_[s];
+        en.layer = layer;
+        en.expert = e;
+        en.copying = true;
+        en.prefetched = false;
+        where_[(size_t)layer * E_ + e] = s;
+        return true;
+    }
+};
+
+}  // namespace ftp

@@ -1,0 +1,329 @@
+"""Thin ctypes binding of libftmoe.so (the C ABI in include/ftmoe.h).
+
+Argument marshalling only: torch tensors become device pointers, the current
+torch stream becomes the hipStream_t, and a non-OK status raises FtError with
+the library's message.  Every step of the MoE layer runs in the library's HIP
+kernels; nothing here computes.  The library must have been built
+(``python -m expert_ffn_execution_amd.build``); loading fails loudly if not.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libftmoe.so")
+
+F32, BF16, MXFP4 = 0, 1, 2
+DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4}
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_NOT_PINNED, ERR_BUSY, ERR_HIP = range(7)
+WARN_OVERLAP_DISABLED = 100
+SCOPE_GLOBAL, SCOPE_PER_LAYER = 0, 1
+PROF_GEMM1, PROF_GEMM2, PROF_FFN, PROF_ROUTE, PROF_ALIGN, PROF_COMBINE = range(6)
+
+# symbols declared in include/ftmoe.h
+EXPORTS = [
+    "ft_last_error", "ft_version", "ft_moe_route", "ft_moe_align_workspace", "ft_moe_align",
+    "ft_expert_layout", "ft_moe_ffn_workspace", "ft_moe_ffn", "ft_moe_ffn_set_path",
+    "ft_set_profile_events", "ft_moe_combine", "ft_slot_cache_create", "ft_slot_cache_destroy",
+    "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
+    "ft_slot_cache_stats", "ft_slot_cache_lookup",
+]
+
+
+class FtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ftmoe status {status}: {msg}")
+        self.status = status
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [("w_dt", C.c_int), ("E", C.c_int), ("H", C.c_int), ("I", C.c_int),
+                ("n_shared", C.c_int), ("pool", C.c_void_p), ("slot_stride", C.c_size_t),
+                ("shared_slot", C.c_int)]
+
+
+class SlotCacheDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int), ("n_experts", C.c_int), ("expert_bytes", C.c_size_t),
+                ("host_pool", C.c_void_p), ("host_stride", C.c_size_t),
+                ("dev_slots", C.c_void_p), ("slot_stride", C.c_size_t), ("n_slots", C.c_int),
+                ("scope", C.c_int)]
+
+
+class MapStats(C.Structure):
+    _fields_ = [("n_demand", C.c_int), ("n_hit", C.c_int), ("n_prefetch_hit", C.c_int),
+                ("n_miss", C.c_int), ("bytes_h2d", C.c_size_t)]
+
+
+class CacheStats(C.Structure):
+    _fields_ = [("maps", C.c_longlong), ("demand", C.c_longlong), ("hits", C.c_longlong),
+                ("prefetch_hits", C.c_longlong), ("misses", C.c_longlong),
+                ("prefetch_issued", C.c_longlong), ("evictions", C.c_longlong),
+                ("bytes_h2d", C.c_longlong), ("resident", C.c_int), ("held", C.c_int),
+                ("in_flight", C.c_int), ("n_slots", C.c_int)]
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libftmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m expert_ffn_execution_amd.build` (there is no fallback)")
+    lib = C.CDLL(LIB_PATH)
+    P, I32, SZ = C.c_void_p, C.c_int, C.c_size_t
+    lib.ft_last_error.restype = C.c_char_p
+    lib.ft_version.restype = C.c_char_p
+    sig = {
+        "ft_moe_route": [P, I32, P, P, P, I32, I32, I32, I32, P, P, P, P],
+        "ft_moe_align_workspace": [I32, I32, I32],
+        "ft_moe_align": [P, I32, I32, I32, P, P, P, P, P, SZ, P],
+        "ft_expert_layout": [I32, I32, I32, P],
+        "ft_moe_ffn_workspace": [C.POINTER(MoeWeights), I32, I32],
+        "ft_moe_ffn": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P, SZ, P],
+        "ft_moe_ffn_set_path": [I32],
+        "ft_set_profile_events": [I32, P, P],
+        "ft_moe_combine": [P, I32, P, P, I32, I32, I32, I32, P, I32, P],
+        "ft_slot_cache_create": [C.POINTER(SlotCacheDesc), C.POINTER(P)],
+        "ft_slot_cache_destroy": [P],
+        "ft_slot_cache_map": [P, I32, P, I32, P, P, P, C.POINTER(MapStats)],
+        "ft_slot_cache_release": [P, I32, P],
+        "ft_slot_cache_prefetch": [P, I32, P, I32, P, C.POINTER(C.c_int)],
+        "ft_slot_cache_evict": [P, I32, I32],
+        "ft_slot_cache_stats": [P, C.POINTER(CacheStats)],
+        "ft_slot_cache_lookup": [P, I32, I32],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = C.c_int
+    lib.ft_moe_align_workspace.restype = C.c_size_t
+    lib.ft_expert_layout.restype = C.c_size_t
+    lib.ft_moe_ffn_workspace.restype = C.c_size_t
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().ft_last_error().decode()
+
+
+def _check(st: int, allow=(OK,)) -> int:
+    if st not in allow:
+        raise FtError(st, last_error())
+    return st
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    return F32 if t.dtype == torch.float32 else BF16
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA tensors"
+
+
+# ---------------------------------------------------------------------------
+# layer steps
+# ---------------------------------------------------------------------------
+def route(T: int, E: int, k: int, *, logits: Optional[torch.Tensor] = None,
+          x: Optional[torch.Tensor] = None, w_router: Optional[torch.Tensor] = None,
+          bias: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None,
+          ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None, stream=None):
+    """ft_moe_route.  Returns (ids [T,k] int32, w [T,k] fp32, logits_out or None)."""
+    dev = (logits if logits is not None else x).device
+    ids = ids if ids is not None else torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
+    H = 0
+    xdt = BF16
+    if logits is None:
+        H = x.shape[1]
+        xdt = _dt(x)
+        if logits_out is None:
+            logits_out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _dev(logits, x, w_router, bias, logits_out, ids, w)
+    _check(load().ft_moe_route(_p(x), xdt, _p(w_router), _p(logits), _p(bias), T, H, E, k,
+                               _p(logits_out), _p(ids), _p(w), _stream(stream)))
+    return ids, w, logits_out
+
+
+def align_workspace(T: int, k: int, E: int) -> int:
+    return load().ft_moe_align_workspace(T, k, E)
+
+
+def align(ids: torch.Tensor, E: int, ws: Optional[torch.Tensor] = None, out=None, stream=None):
+    """ft_moe_align.  Returns (counts [E], offsets [E+1], perm [T*k], inv_perm [T*k])."""
+    T, k = ids.shape
+    dev = ids.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    counts, offsets, perm, inv = out
+    need = align_workspace(T, k, E)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(ids, counts, offsets, perm, inv)
+    _check(load().ft_moe_align(_p(ids), T, k, E, _p(counts), _p(offsets), _p(perm), _p(inv),
+                               _p(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return counts, offsets, perm, inv
+
+
+def expert_layout(wdtype: str, H: int, I: int):
+    """(slot bytes, [offsets of gate, up, down, gate_sc, up_sc, down_sc])."""
+    offs = (C.c_size_t * 6)()
+    n = load().ft_expert_layout(DT[wdtype], H, I, offs)
+    if n == 0:
+        raise FtError(ERR_INVALID_ARG, f"unsupported layout {wdtype} H={H} I={I}")
+    return n, list(offs)
+
+
+def slot_stride(wdtype: str, H: int, I: int) -> int:
+    n, _ = expert_layout(wdtype, H, I)
+    return (n + 255) // 256 * 256
+
+
+def pack_expert(ex: dict, wdtype: str, H: int, I: int, out: torch.Tensor):
+    """Write one expert's logical tensors into a slot (uint8 view of slot_stride bytes)."""
+    n, offs = expert_layout(wdtype, H, I)
+    names = ["gate", "up", "down"] + (["gate_sc", "up_sc", "down_sc"] if wdtype == "mxfp4" else [])
+    for name, off in zip(names, offs):
+        t = ex[name].contiguous()
+        b = t.view(torch.uint8).reshape(-1)
+        out[off:off + b.numel()].copy_(b)
+
+
+def make_weights(wdtype: str, E: int, H: int, I: int, pool: torch.Tensor, n_shared: int = 0,
+                 shared_slot: int = 0) -> MoeWeights:
+    """Describe a device slot array pool [n_slots, slot_stride] (uint8)."""
+    _dev(pool)
+    return MoeWeights(DT[wdtype], E, H, I, n_shared, pool.data_ptr(), pool.shape[1], shared_slot)
+
+
+def ffn_workspace(wts: MoeWeights, T: int, k: int) -> int:
+    return load().ft_moe_ffn_workspace(C.byref(wts), T, k)
+
+
+def set_ffn_path(path: int) -> int:
+    return load().ft_moe_ffn_set_path(path)
+
+
+def ffn(wts: MoeWeights, x: torch.Tensor, k: int, perm: torch.Tensor, offsets: torch.Tensor,
+        slot_of_expert: Optional[torch.Tensor] = None, y_dtype=torch.bfloat16,
+        y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """ft_moe_ffn.  Returns y_perm [T*k + n_shared*T, H]."""
+    T = x.shape[0]
+    dev = x.device
+    rows = T * k + wts.n_shared * T
+    if y is None:
+        y = torch.empty((rows, wts.H), dtype=y_dtype, device=dev)
+    need = ffn_workspace(wts, T, k)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(x, perm, offsets, slot_of_expert, y, ws)
+    _check(load().ft_moe_ffn(C.byref(wts), _p(x), _dt(x), T, k, _p(perm), _p(offsets),
+                             _p(slot_of_expert), _p(y), _dt(y), _p(ws), ws.numel(),
+                             _stream(stream)))
+    return y
+
+
+def combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, w: torch.Tensor, n_shared: int = 0,
+            out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+    """ft_moe_combine.  Returns out [T, H]."""
+    T, k = w.shape
+    H = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
+    _dev(y_perm, inv_perm, w, out)
+    _check(load().ft_moe_combine(_p(y_perm), _dt(y_perm), _p(inv_perm), _p(w), T, k, H,
+                                 n_shared, _p(out), _dt(out), _stream(stream)))
+    return out
+
+
+def set_profile_events(which: int, start, stop):
+    """start/stop: torch.cuda.Event (created with enable_timing=True) or None."""
+    s = None if start is None else C.c_void_p(start.cuda_event)
+    e = None if stop is None else C.c_void_p(stop.cuda_event)
+    _check(load().ft_set_profile_events(which, s, e))
+
+
+# ---------------------------------------------------------------------------
+# slot cache
+# ---------------------------------------------------------------------------
+class SlotCache:
+    """ft_slot_cache_* over a pinned host pool and a device slot array."""
+
+    def __init__(self, n_layers: int, n_experts: int, expert_bytes: int,
+                 host_pool: torch.Tensor, dev_slots: torch.Tensor, scope: int = SCOPE_GLOBAL):
+        self.desc = SlotCacheDesc(n_layers, n_experts, expert_bytes, host_pool.data_ptr(),
+                                  host_pool.shape[-1], dev_slots.data_ptr(), dev_slots.shape[1],
+                                  dev_slots.shape[0], scope)
+        self._keep = (host_pool, dev_slots)
+        h = C.c_void_p()
+        _check(load().ft_slot_cache_create(C.byref(self.desc), C.byref(h)))
+        self.h = h
+        self.n_experts = n_experts
+
+    def close(self):
+        if self.h:
+            load().ft_slot_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _list(experts: Sequence[int]):
+        arr = (C.c_int32 * max(1, len(experts)))(*experts)
+        return arr, len(experts)
+
+    def map(self, layer: int, experts: Sequence[int], slot_table: torch.Tensor, compute=None,
+            copy=None) -> MapStats:
+        arr, n = self._list(experts)
+        st = MapStats()
+        _check(load().ft_slot_cache_map(self.h, layer, arr, n, _p(slot_table), _stream(compute),
+                                        _stream(copy), C.byref(st)))
+        return st
+
+    def release(self, layer: int, compute=None):
+        _check(load().ft_slot_cache_release(self.h, layer, _stream(compute)))
+
+    def prefetch(self, layer: int, experts: Sequence[int], copy=None):
+        arr, n = self._list(experts)
+        got = C.c_int(0)
+        st = _check(load().ft_slot_cache_prefetch(self.h, layer, arr, n, _stream(copy),
+                                                  C.byref(got)),
+                    allow=(OK, WARN_OVERLAP_DISABLED))
+        return st, got.value
+
+    def evict(self, layer: int, expert: int = -1):
+        _check(load().ft_slot_cache_evict(self.h, layer, expert))
+
+    def stats(self) -> CacheStats:
+        s = CacheStats()
+        _check(load().ft_slot_cache_stats(self.h, C.byref(s)))
+        return s
+
+    def lookup(self, layer: int, expert: int) -> int:
+        return load().ft_slot_cache_lookup(self.h, layer, expert)

@@ -1,0 +1,286 @@
+/*
+ * ftmoe.h -- C ABI of the MI355X (gfx950) MoE-layer FFN library (libftmoe.so).
+ *
+ * One MoE layer, T tokens of hidden size H, E routed experts, k experts per
+ * token, expert intermediate size I, optionally one always-on shared expert:
+ *
+ *   ft_moe_route    router logits (optional) -> top-k expert ids + gates
+ *   ft_moe_align    expert histogram, offsets, token->expert permutation
+ *   ft_moe_ffn      grouped gate/up GEMM + SwiGLU + down GEMM over the routed
+ *                   experts only, weights read through a slot table
+ *   ft_moe_combine  gate-weighted sum back to token order
+ *   ft_slot_cache_* LRU expert-slot cache over a pinned host expert pool, with
+ *                   the next layer's missing experts copied while this layer
+ *                   computes
+ *
+ * Sources.  The pages describe the engine around this path: a few experts per
+ * token out of hundreds, only those brought to the GPU, a global LRU expert
+ * cache sized in slots, and the next layer's weights streamed double-buffered
+ * while the current layer computes (claypier.com article,
+ * "从 MoE「用不到的权重」入手的推理引擎" and "按带宽决定分工的思路";
+ * FreeToken hub article, paragraphs on prefill overlap and on the WSL pinned
+ * memory limit; refft.com guide, "深度解析"; freelamp.com article, section 2.3).
+ * They do not spell out the routing rule or the expert FFN; the readings used
+ * (top-k on fp32 logits with ties to the lower expert id, softmax over the k
+ * picks, SwiGLU experts) are stated at each entry point.
+ *
+ * Conventions (all entry points):
+ *   - Device pointers are HIP device memory (or host-pinned memory mapped for
+ *     the device) on the current device; host pointers are ordinary memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued asynchronously; no entry point synchronises the stream
+ *     unless stated.  The caller owns every buffer; the library never
+ *     allocates device memory in these calls (workspace is passed in).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns FT_ERR_INVALID_ARG / FT_ERR_UNSUPPORTED and
+ *     enqueues nothing.  A HIP launch error returns FT_ERR_HIP.  The message
+ *     of the last failure on the calling thread is ft_last_error().
+ *   - T == 0 is a valid no-op.  T*k must be < 2^31; E <= 1024; k in [1, E].
+ *   - Results are deterministic: identical inputs give bitwise identical
+ *     outputs (no floating-point atomics anywhere).
+ */
+#ifndef FTMOE_H
+#define FTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FT_OK = 0,
+    FT_ERR_INVALID_ARG = 1,
+    FT_ERR_UNSUPPORTED = 2,
+    FT_ERR_CAPACITY = 3,
+    FT_ERR_NOT_PINNED = 4,
+    FT_ERR_BUSY = 5,
+    FT_ERR_HIP = 6,
+    FT_WARN_OVERLAP_DISABLED = 100
+} ft_status;
+
+typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2 } ft_dtype;
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* ft_last_error(void);
+/* Library version string. */
+const char* ft_version(void);
+
+/* --------------------------------------------------------------------------
+ * ft_moe_route -- router top-k gating.
+ *
+ * Logits: either supplied (`logits_in` [T][E] fp32, device; then x and
+ * w_router must be NULL) or computed here as l = x W_r^T with fp32
+ * accumulation (x [T][H], w_router [E][H], both in x_dt = FT_BF16 or FT_F32,
+ * device; then logits_out [T][E] fp32 must be given and receives l).
+ * `bias` [E] fp32 (device, may be NULL) is added to every row:
+ * l' = fl32(l + b).  The pages only imply routing (chenxutan.com article,
+ * "瓶颈为什么是带宽而不是容量": prefill tokens reach almost every expert;
+ * freelamp.com article, section 2.1: the router's choice changes with the
+ * content); the rule implemented is:
+ *   topk_ids[t][0..k-1] (int32, device) = the k largest l'[t][.] in
+ *     decreasing order, equal values ordered by increasing expert id
+ *     (-0.0 equals +0.0);
+ *   topk_w[t][j] (fp32, device) = exp(l'_j - l'_0) / sum_{i<k} exp(l'_i - l'_0),
+ *     i.e. the softmax over all experts restricted to the picks and
+ *     renormalised.
+ * Logits must be finite (not checked on the device; the result is unspecified
+ * otherwise).
+ * ------------------------------------------------------------------------ */
+ft_status ft_moe_route(const void* x, ft_dtype x_dt, const void* w_router,
+                       const float* logits_in, const float* bias, int T, int H, int E,
+                       int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+                       void* stream);
+
+/* --------------------------------------------------------------------------
+ * ft_moe_align -- token-to-expert alignment (stable counting sort).
+ *
+ * In: topk_ids [T*k] int32 device, every id in [0, E).
+ * Out (device, int32): counts[E]; offsets[E+1] exclusive prefix sums;
+ *   perm[T*k] = flat slots f = t*k + j grouped by expert, increasing f within
+ *   an expert; inv_perm[T*k] with inv_perm[perm[p]] = p.
+ * ws: device workspace of at least ft_moe_align_workspace(T, k, E) bytes
+ *   (may be NULL when that is 0); contents need not be initialised.
+ * Ids outside [0, E) give unspecified results (not checked on the device).
+ * ------------------------------------------------------------------------ */
+size_t ft_moe_align_workspace(int T, int k, int E);
+ft_status ft_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Expert weight storage ("slot" layout).  One contiguous block per expert so
+ * that one copy moves one expert (the pages' pre-merged runtime weight
+ * layout: FreeToken hub article, paragraph on the FTW format).  Within a slot:
+ *   FT_F32 / FT_BF16: gate [I][H] | up [I][H] | down [H][I], row-major,
+ *     element size 4 / 2.
+ *   FT_MXFP4: gate codes [I][H/2] | up codes [I][H/2] | down codes [H][I/2] |
+ *     gate scales [I][H/32] | up scales [I][H/32] | down scales [H][I/32].
+ *     Codes are e2m1 (bit 3 sign, bits 2..1 exponent, bit 0 mantissa), element
+ *     2j of a row in the low nibble of byte j, 2j+1 in the high nibble; scales
+ *     are e8m0 bytes 2^(X-127) for 32 consecutive elements along the
+ *     contraction dimension (OCP Microscaling Formats v1.0).
+ * All formats: H % 64 == 0 and I % 64 == 0.
+ * ft_expert_layout fills offs[6] = byte offsets of {gate, up, down,
+ * gate_sc, up_sc, down_sc} (the last three 0 unless MXFP4) and returns the
+ * slot size in bytes (0 for an unsupported combination).
+ * ------------------------------------------------------------------------ */
+size_t ft_expert_layout(ft_dtype w_dt, int H, int I, size_t offs[6]);
+
+typedef struct {
+    ft_dtype w_dt;        /* FT_F32, FT_BF16 or FT_MXFP4 */
+    int E;                /* routed experts */
+    int H;                /* hidden size */
+    int I;                /* expert intermediate size */
+    int n_shared;         /* 0 or 1 always-on shared expert */
+    const void* pool;     /* device base of the slot array */
+    size_t slot_stride;   /* bytes between slots (>= ft_expert_layout(), multiple of 256) */
+    int shared_slot;      /* slot index of the shared expert (n_shared == 1) */
+} ft_moe_weights;
+
+/* --------------------------------------------------------------------------
+ * ft_moe_ffn -- grouped expert FFN over the routed experts only.
+ *
+ * For every position p of the permutation (expert e = the segment of
+ * `offsets` holding p, token t = perm[p] / k):
+ *   g = W_gate,e x_t,  u = W_up,e x_t,  h = silu(g) * u,  y_perm[p] = W_down,e h
+ * with fp32 accumulation; h is rounded to bf16 for bf16 / MXFP4 weights.
+ * With n_shared == 1, rows T*k + t of y_perm receive the shared expert's FFN
+ * of x_t (weight 1 in the combine).  MXFP4 weights are decoded exactly to bf16
+ * on chip and multiplied with bf16 activations.
+ *   x [T][H] device, act_dt = FT_BF16 (FT_F32 only with FT_F32 weights);
+ *   perm, offsets: ft_moe_align's outputs for the same ids;
+ *   slot_of_expert [E] int32 device, or NULL for slot e = expert e: the slot
+ *     in `pool` holding expert e; -1 skips expert e (its rows of y_perm are
+ *     not written);
+ *   y_perm [T*k + n_shared*T][H] device, y_dt = FT_BF16 (bf16 weights/MXFP4)
+ *     or FT_F32 (any weights);
+ *   ws: device workspace of >= ft_moe_ffn_workspace(w, T, k) bytes.
+ * ------------------------------------------------------------------------ */
+size_t ft_moe_ffn_workspace(const ft_moe_weights* w, int T, int k);
+ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, int T, int k,
+                     const int32_t* perm, const int32_t* offsets,
+                     const int32_t* slot_of_expert, void* y_perm, ft_dtype y_dt, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Kernel family used by ft_moe_ffn: 0 = choose by size (default),
+ * 1 = weight-streaming (small token counts), 2 = MFMA tiles (large token
+ * counts).  Process-wide; a tuning and test knob.  Returns the previous value. */
+int ft_moe_ffn_set_path(int path);
+
+/* Profiling hook: HIP events (hipEvent_t as void*) recorded on the launch
+ * stream right before / after the kernels of one stage, so that a caller can
+ * time them with hipEventElapsedTime.  which: 0 = the FFN's gate/up GEMM
+ * (+SwiGLU), 1 = its down GEMM, 2 = the whole ft_moe_ffn, 3 = ft_moe_route,
+ * 4 = ft_moe_align, 5 = ft_moe_combine.  NULL events switch a stage off.
+ * Process-wide setting, not synchronised between threads. */
+ft_status ft_set_profile_events(int which, void* start, void* stop);
+
+/* --------------------------------------------------------------------------
+ * ft_moe_combine -- weighted combine back to token order.
+ *   out[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k + j]]
+ *            (+ y_perm[T*k + t] when n_shared == 1)
+ * summed in fp32 in increasing j, then the shared row, rounded once to
+ * out_dt (FT_BF16 or FT_F32).  y_perm in y_dt (FT_BF16 or FT_F32).
+ * All pointers device; out [T][H].
+ * ------------------------------------------------------------------------ */
+ft_status ft_moe_combine(const void* y_perm, ft_dtype y_dt, const int32_t* inv_perm,
+                         const float* topk_w, int T, int k, int H, int n_shared, void* out,
+                         ft_dtype out_dt, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Expert slot cache.
+ *
+ * The full expert pool sits in pinned host memory; a fixed number of device
+ * slots hold the working set under LRU replacement, counted in slots (refft.com
+ * guide, "深度解析": global LRU expert caching; freelamp.com article, section
+ * 2.3: the expert cache is sized in slots).  Missing experts are copied
+ * host->device asynchronously on a copy stream; the next layer's misses are
+ * copied while the current layer computes, which needs room for two whole
+ * layers, else the overlap is reported as disabled (FreeToken hub article,
+ * paragraph on prefill overlap and its WARNING).  Asynchronous copies need
+ * pinned host memory (FreeToken hub article, install caveat on WSL).
+ *
+ * The library owns host metadata and HIP events only; the caller owns the
+ * host pool and the device slot array.
+ * ------------------------------------------------------------------------ */
+typedef struct ft_slot_cache ft_slot_cache;
+
+typedef enum { FT_SCOPE_GLOBAL = 0, FT_SCOPE_PER_LAYER = 1 } ft_slot_scope;
+
+typedef struct {
+    int n_layers;
+    int n_experts;            /* experts per layer (routed + shared) */
+    size_t expert_bytes;      /* bytes copied per expert */
+    const void* host_pool;    /* pinned host memory, expert (l, e) at
+                                 host_pool + (l * n_experts + e) * host_stride */
+    size_t host_stride;       /* >= expert_bytes */
+    void* dev_slots;          /* device memory, slot s at dev_slots + s * slot_stride */
+    size_t slot_stride;       /* >= expert_bytes */
+    int n_slots;              /* total device slots */
+    int scope;                /* FT_SCOPE_GLOBAL: one LRU over all slots;
+                                 FT_SCOPE_PER_LAYER: n_slots / n_layers per layer */
+} ft_slot_cache_desc;
+
+typedef struct {
+    int n_demand;      /* distinct experts requested */
+    int n_hit;         /* resident before the call (demand hits) */
+    int n_prefetch_hit;/* resident or in flight because of a prefetch */
+    int n_miss;        /* copied by this call */
+    size_t bytes_h2d;  /* bytes enqueued by this call */
+} ft_map_stats;
+
+typedef struct {
+    long long maps, demand, hits, prefetch_hits, misses, prefetch_issued, evictions;
+    long long bytes_h2d;
+    int resident, held, in_flight, n_slots;
+} ft_cache_stats;
+
+/* Create / destroy.  Fails with FT_ERR_NOT_PINNED when host_pool is not
+ * pinned (page-locked) host memory, FT_ERR_INVALID_ARG on bad sizes. */
+ft_status ft_slot_cache_create(const ft_slot_cache_desc* desc, ft_slot_cache** out);
+ft_status ft_slot_cache_destroy(ft_slot_cache* c);
+
+/* ft_slot_cache_map -- make layer `layer`'s experts `experts_host[0..n-1]`
+ * (host int32, distinct, ascending) resident and write the device slot table
+ * slot_table_dev[0..n_experts-1] (int32; -1 for experts not requested).
+ * Hits are touched (most recent) and held until ft_slot_cache_release;
+ * misses take free slots, else evict least-recently-used entries that are
+ * neither held nor in flight, and are copied on `copy_stream`.  `compute`
+ * waits (on the device) for every copy the table depends on, and the table is
+ * written on `compute`.  FT_ERR_CAPACITY when the held set plus the request
+ * exceeds the slots (nothing changes).  st may be NULL. */
+ft_status ft_slot_cache_map(ft_slot_cache* c, int layer, const int32_t* experts_host, int n,
+                            int32_t* slot_table_dev, void* compute, void* copy_stream,
+                            ft_map_stats* st);
+
+/* ft_slot_cache_release -- the work enqueued on `compute` so far is the last
+ * reader of layer `layer`'s held slots: an event is recorded there and later
+ * copies into those slots wait for it.  The entries become evictable. */
+ft_status ft_slot_cache_release(ft_slot_cache* c, int layer, void* compute);
+
+/* ft_slot_cache_prefetch -- start copying layer `layer`'s experts that are not
+ * resident (host int32, distinct, ascending) on `copy_stream`, into free or
+ * evictable slots, without holding them.  Entries of the layer being computed
+ * are held and so are never victims.  When fewer than n slots can be
+ * obtained, issues what fits and returns FT_WARN_OVERLAP_DISABLED.
+ * n_issued (may be NULL) receives the number of copies started. */
+ft_status ft_slot_cache_prefetch(ft_slot_cache* c, int layer, const int32_t* experts_host,
+                                 int n, void* copy_stream, int* n_issued);
+
+/* ft_slot_cache_evict -- drop (layer, expert) from the cache, or the whole
+ * layer when expert == -1.  FT_ERR_BUSY (nothing dropped) if an entry is held
+ * or its copy is in flight. */
+ft_status ft_slot_cache_evict(ft_slot_cache* c, int layer, int expert);
+
+/* Counters since creation. */
+ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
+
+/* Slot of (layer, expert), or -1 when not cached.  Host query, no device work. */
+int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FTMOE_H */

@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from expert_ffn_execution_amd import ftmoe as ft
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ftmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ft_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_what_binding_lists():
+    assert sorted(ft.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ft.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.ft_version().startswith(b"ftmoe")
+
+
+def test_expert_layout():
+    n, offs = ft.expert_layout("bf16", 2048, 768)
+    assert n == 3 * 2048 * 768 * 2 and offs[:3] == [0, 2048 * 768 * 2, 2 * 2048 * 768 * 2]
+    n, offs = ft.expert_layout("mxfp4", 4096, 2048)
+    HI = 4096 * 2048
+    assert n == 3 * HI // 2 + 3 * HI // 32
+    assert offs == [0, HI // 2, HI, 3 * HI // 2, 3 * HI // 2 + HI // 32, 3 * HI // 2 + HI // 16]
+    with pytest.raises(ft.FtError):
+        ft.expert_layout("bf16", 100, 64)
+
+
+def _route(**kw):
+    lib = ft.load()
+    a = dict(x=None, x_dt=ft.BF16, w_router=None, logits_in=C.c_void_p(16), bias=None, T=4, H=0,
+             E=8, k=2, logits_out=None, ids=C.c_void_p(16), w=C.c_void_p(16), s=None)
+    a.update(kw)
+    return lib.ft_moe_route(a["x"], a["x_dt"], a["w_router"], a["logits_in"], a["bias"], a["T"],
+                            a["H"], a["E"], a["k"], a["logits_out"], a["ids"], a["w"], a["s"])
+
+
+def test_route_rejects_bad_arguments():
+    assert _route(k=0) == ft.ERR_INVALID_ARG
+    assert _route(k=9) == ft.ERR_INVALID_ARG
+    assert _route(E=1025, k=2) == ft.ERR_INVALID_ARG
+    assert _route(T=-1) == ft.ERR_INVALID_ARG
+    assert _route(T=1 << 30, k=2) == ft.ERR_INVALID_ARG          # T*k >= 2^31
+    assert _route(ids=None) == ft.ERR_INVALID_ARG
+    assert _route(x=C.c_void_p(16)) == ft.ERR_INVALID_ARG         # both logits and x
+    assert _route(logits_in=None) == ft.ERR_INVALID_ARG          # neither
+    assert _route(logits_in=None, x=C.c_void_p(16), w_router=C.c_void_p(16),
+                  logits_out=C.c_void_p(16), H=100) == ft.ERR_INVALID_ARG
+    assert _route(T=0) == ft.OK                                  # empty batch: no-op
+    assert "k must be" in ft.last_error() or ft.last_error() == ""
+
+
+def test_align_rejects_bad_arguments():
+    lib = ft.load()
+    p = C.c_void_p(16)
+    assert lib.ft_moe_align(p, 4, 0, 8, p, p, p, p, None, 0, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_align(p, 4, 2, 2000, p, p, p, p, None, 0, None) == ft.ERR_INVALID_ARG
+    # large problems need the workspace
+    need = lib.ft_moe_align_workspace(10000, 8, 256)
+    assert need > 0
+    assert lib.ft_moe_align(p, 10000, 8, 256, p, p, p, p, None, 0, None) == ft.ERR_INVALID_ARG
+    assert "workspace" in ft.last_error()
+
+
+def _w(**kw):
+    a = dict(w_dt=ft.BF16, E=8, H=256, I=128, n_shared=0, pool=4096,
+             slot_stride=ft.slot_stride("bf16", 256, 128), shared_slot=0)
+    a.update(kw)
+    return ft.MoeWeights(a["w_dt"], a["E"], a["H"], a["I"], a["n_shared"], a["pool"],
+                         a["slot_stride"], a["shared_slot"])
+
+
+def test_ffn_rejects_bad_arguments():
+    lib = ft.load()
+    p = C.c_void_p(4096)
+
+    def call(w, act=ft.BF16, ydt=ft.BF16, ws_bytes=1 << 30, T=4, k=2):
+        return lib.ft_moe_ffn(C.byref(w), p, act, T, k, p, p, None, p, ydt, p, ws_bytes, None)
+
+    assert call(_w(H=100)) == ft.ERR_INVALID_ARG                 # H not a multiple of 64
+    assert call(_w(I=96)) == ft.ERR_INVALID_ARG
+    assert call(_w(slot_stride=1000)) == ft.ERR_INVALID_ARG      # too small / unaligned
+    assert call(_w(pool=4097)) == ft.ERR_INVALID_ARG             # unaligned pool
+    assert call(_w(n_shared=2)) == ft.ERR_INVALID_ARG
+    assert call(_w(), act=ft.F32) == ft.ERR_INVALID_ARG          # bf16 weights, fp32 x
+    assert call(_w(w_dt=ft.F32, slot_stride=ft.slot_stride("f32", 256, 128)),
+                ydt=ft.BF16, act=ft.F32) == ft.ERR_INVALID_ARG
+    assert call(_w(), ws_bytes=16) == ft.ERR_INVALID_ARG         # workspace too small
+    assert call(_w(), k=9) == ft.ERR_INVALID_ARG
+    assert call(_w(), T=0) == ft.OK
+    w = _w()
+    assert lib.ft_moe_ffn_workspace(C.byref(w), 4, 2) > 4 * 2 * 128 * 2
+
+
+def test_combine_rejects_bad_arguments():
+    lib = ft.load()
+    p = C.c_void_p(4096)
+    assert lib.ft_moe_combine(p, ft.BF16, p, p, 4, 2, 100, 0, p, ft.BF16, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_combine(p, ft.MXFP4, p, p, 4, 2, 64, 0, p, ft.BF16, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_combine(p, ft.BF16, p, p, 4, 2, 64, 3, p, ft.BF16, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_combine(p, ft.BF16, p, p, 0, 2, 64, 0, p, ft.BF16, None) == ft.OK
+
+
+def test_slot_cache_rejects_bad_descriptors():
+    lib = ft.load()
+    h = C.c_void_p()
+    d = ft.SlotCacheDesc(0, 8, 1024, 4096, 1024, 4096, 1024, 16, 0)
+    assert lib.ft_slot_cache_create(C.byref(d), C.byref(h)) == ft.ERR_INVALID_ARG
+    d = ft.SlotCacheDesc(2, 8, 1024, 4096, 512, 4096, 1024, 16, 0)      # host stride too small
+    assert lib.ft_slot_cache_create(C.byref(d), C.byref(h)) == ft.ERR_INVALID_ARG
+    d = ft.SlotCacheDesc(3, 8, 1024, 4096, 1024, 4096, 1024, 16, 1)     # 16 % 3 per-layer
+    assert lib.ft_slot_cache_create(C.byref(d), C.byref(h)) == ft.ERR_INVALID_ARG

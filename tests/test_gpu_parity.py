@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing ids, counts, offsets, perm and inv_perm must be bit-exact (top-k runs
+on the same fp32 logits on both sides); gates within 1e-6; layer outputs
+within the tolerances in layer_harness.check_close.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from expert_ffn_execution_amd import ftmoe as ft  # noqa: E402
+from expert_ffn_execution_amd import synth  # noqa: E402
+from oracle import oracle as orc  # noqa: E402
+from tests.layer_harness import DEV, Layer, check_close, oracle_out, rel_l2, run_layer  # noqa: E402
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _reset_path():
+    ft.set_ffn_path(0)
+    yield
+    ft.set_ffn_path(0)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+ROUTE_CASES = [(1, 128, 8, False), (64, 8, 2, False), (333, 256, 6, True), (4096, 128, 8, True),
+               (77, 1024, 16, True), (5, 3, 3, False), (9, 1, 1, False), (200, 40, 40, True)]
+
+
+@pytest.mark.parametrize("T,E,k,with_bias", ROUTE_CASES)
+def test_route_bitexact(T, E, k, with_bias):
+    _say("route", T, E, k, with_bias)
+    rng = np.random.default_rng(T * 1000 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32) if with_bias else None
+    ids, w, _ = ft.route(T, E, k, logits=torch.from_numpy(logits).to(DEV),
+                         bias=None if bias is None else torch.from_numpy(bias).to(DEV))
+    rid, rw = orc.route(logits, k, bias)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (300, 128, 8), (33, 256, 6)])
+def test_route_tie_heavy_bitexact(T, E, k):
+    _say("route ties", T, E, k)
+    rng = np.random.default_rng(7 + T)
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 1e30, -1e30, 2.0], np.float32)
+    logits = vals[rng.integers(0, len(vals), size=(T, E))]
+    ids, w, _ = ft.route(T, E, k, logits=torch.from_numpy(logits).to(DEV))
+    rid, rw = orc.route(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= 1e-6
+
+
+@pytest.mark.parametrize("name,T", [("35b_a3b_bf16", 1), ("35b_a3b_bf16", 16),
+                                    ("35b_a3b_bf16", 300), ("tiny_f32", 64),
+                                    ("753b_a40b_bf16", 130)])
+def test_router_logits(name, T):
+    _say("router logits", name, T)
+    sh = synth.SHAPES[name]
+    x = synth.gen_x(sh, T)
+    wr = synth.gen_router(sh)
+    ids, w, lg = ft.route(T, sh.E, sh.k, x=x.to(DEV), w_router=wr.to(DEV))
+    ref = orc.router_logits(x, wr)
+    got = lg.cpu().numpy()
+    assert rel_l2(got, ref) <= 1e-5
+    assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------------------
+# alignment
+# ---------------------------------------------------------------------------
+ALIGN_CASES = [(1, 8, 128), (64, 2, 8), (512, 8, 128), (513, 8, 128), (16384, 8, 256),
+               (1000, 6, 1024), (4096, 8, 128), (3, 1, 1), (700, 16, 1024)]
+
+
+@pytest.mark.parametrize("T,k,E", ALIGN_CASES)
+def test_align_bitexact(T, k, E):
+    _say("align", T, k, E)
+    rng = np.random.default_rng(T + k + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (np.arange(E) % 7 == 0).astype(np.float32) * 3.0  # skewed load
+    rid, _ = orc.route(logits, k, bias)
+    counts, offsets, perm, inv = ft.align(torch.from_numpy(rid).to(DEV), E)
+    rc, ro, rp, ri = orc.align(rid, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("T,k,E", [(5000, 1, 16), (100, 4, 4)])
+def test_align_all_to_few_experts(T, k, E):
+    _say("align skew", T, k, E)
+    ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))  # every token picks experts 0..k-1
+    counts, offsets, perm, inv = ft.align(torch.from_numpy(ids).to(DEV), E)
+    rc, ro, rp, ri = orc.align(ids, E)
+    for a, b in zip((counts, offsets, perm, inv), (rc, ro, rp, ri)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+def test_empty_batch_is_noop():
+    _say("T=0")
+    E, k = 8, 2
+    ids = torch.empty((0, k), dtype=torch.int32, device=DEV)
+    counts, offsets, _, _ = ft.align(ids, E)
+    assert counts.cpu().numpy().tolist() == [0] * E
+    assert offsets.cpu().numpy().tolist() == [0] * (E + 1)
+    ids2, w2, _ = ft.route(0, E, k, logits=torch.empty((0, E), device=DEV))
+    assert ids2.shape == (0, k)
+
+
+# ---------------------------------------------------------------------------
+# whole layer, small shapes, both kernel families
+# ---------------------------------------------------------------------------
+SMALL = {
+    "bf16": synth.LayerShape("gpu_small_bf16", H=512, E=16, k=4, I=384),
+    "mxfp4": synth.LayerShape("gpu_small_mx", H=512, E=16, k=6, I=256, n_shared=1,
+                              wdtype="mxfp4"),
+    "bf16_shared": synth.LayerShape("gpu_small_bf16_sh", H=256, E=8, k=2, I=192, n_shared=1),
+}
+
+
+@pytest.mark.parametrize("kind", list(SMALL))
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("T", [1, 7, 300])
+def test_layer_small_both_paths(kind, path, T):
+    sh = SMALL[kind]
+    _say("layer small", kind, "path", path, "T", T)
+    L = Layer(sh)
+    x = synth.gen_x(sh, T)
+    logits = synth.gen_logits(sh, T)
+    ft.set_ffn_path(path)
+    r = run_layer(L, x.to(DEV), logits.to(DEV))
+    ids, w = orc.route(logits.numpy(), sh.k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    ref = oracle_out(L, x, ids, w)
+    check_close(r["out"], ref, sh.wdtype, f"{kind} path{path} T{T}")
+
+
+def test_layer_tiny_f32():
+    sh = synth.TINY_F32
+    _say("layer tiny f32")
+    L = Layer(sh)
+    x = synth.gen_x(sh, 64)
+    wr = synth.gen_router(sh)
+    logits = orc.router_logits(x, wr)
+    r = run_layer(L, x.to(DEV), torch.from_numpy(logits).to(DEV))
+    ids, w = orc.route(logits, sh.k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    ref = oracle_out(L, x, ids, w)
+    check_close(r["out"], ref, "f32", "tiny")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 300])
+def test_layer_a3b_bf16(T):
+    sh = synth.A3B_BF16
+    _say("layer 35b-a3b bf16 T", T)
+    L = _bank(sh)
+    x = synth.gen_x(sh, T)
+    logits = orc.router_logits(x, synth.gen_router(sh))
+    r = run_layer(L, x.to(DEV), torch.from_numpy(logits).to(DEV))
+    ids, w = orc.route(logits, sh.k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    ref = oracle_out(L, x, ids, w)
+    check_close(r["out"], ref, "bf16", f"a3b T{T}")
+
+
+def test_layer_a3b_prefill_sampled():
+    sh = synth.A3B_BF16
+    T = 4096
+    _say("layer 35b-a3b bf16 prefill T", T)
+    L = _bank(sh)
+    x = synth.gen_x(sh, T)
+    logits = orc.router_logits(x, synth.gen_router(sh))
+    r = run_layer(L, x.to(DEV), torch.from_numpy(logits).to(DEV))
+    ids, w = orc.route(logits, sh.k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    tok = _sample_tokens(ids, T, sh.E, 96, seed=1)
+    ref = oracle_out(L, x, ids, w, tokens=tok)
+    check_close(r["out"].cpu()[torch.from_numpy(tok).long()], ref, "bf16", "a3b prefill")
+
+
+# ---------------------------------------------------------------------------
+# invariants on the device
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", [1, 2])
+def test_deterministic_and_slot_invariant(path):
+    sh = SMALL["bf16_shared"]
+    _say("determinism / slot invariance path", path)
+    T = 200
+    x = synth.gen_x(sh, T).to(DEV)
+    logits = synth.gen_logits(sh, T).to(DEV)
+    ft.set_ffn_path(path)
+    L0 = Layer(sh)
+    a = run_layer(L0, x, logits)["out"].clone()
+    b = run_layer(L0, x, logits)["out"].clone()
+    assert torch.equal(a, b)
+    perm = np.random.default_rng(3).permutation(synth.n_experts_total(sh))
+    L1 = Layer(sh, slot_perm=perm.tolist())
+    c = run_layer(L1, x, logits)["out"]
+    assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_skipped_experts_leave_rows_untouched(path):
+    sh = SMALL["bf16"]
+    _say("skip experts path", path)
+    T = 50
+    L = Layer(sh)
+    x = synth.gen_x(sh, T).to(DEV)
+    logits = synth.gen_logits(sh, T).to(DEV)
+    ids, w, _ = ft.route(T, sh.E, sh.k, logits=logits)
+    counts, offsets, perm, inv = ft.align(ids, sh.E)
+    ft.set_ffn_path(path)
+    full = ft.ffn(L.wts, x, sh.k, perm, offsets)
+    table = torch.arange(sh.E, dtype=torch.int32, device=DEV)
+    skip = [1, 5, 6]
+    table[skip] = -1
+    y = torch.full_like(full, 7.0)
+    ft.ffn(L.wts, x, sh.k, perm, offsets, slot_of_expert=table, y=y)
+    off = offsets.cpu().numpy()
+    keep = np.ones(T * sh.k, bool)
+    for e in skip:
+        keep[off[e]:off[e + 1]] = False
+    keep_t = torch.from_numpy(keep).to(DEV)
+    assert torch.equal(y[keep_t], full[keep_t])
+    assert bool((y[~keep_t] == 7.0).all())
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads on sampled tokens
+# ---------------------------------------------------------------------------
+_BANKS = {}
+
+
+def _bank(sh):
+    if sh.name not in _BANKS:
+        _BANKS.clear()
+        torch.cuda.empty_cache()
+        _BANKS[sh.name] = Layer(sh, gen_device=DEV, keep_host=False)
+    return _BANKS[sh.name]
+
+
+def _sample_tokens(ids, T, E, n, seed):
+    """n seeded tokens plus every token routed to the most-loaded expert (capped)."""
+    rng = np.random.default_rng(seed)
+    base = rng.choice(T, size=min(n, T), replace=False)
+    cnt = np.bincount(ids.reshape(-1), minlength=E)
+    top = np.nonzero((ids == np.argmax(cnt)).any(1))[0][:32]
+    return np.unique(np.concatenate([base, top])).astype(np.int32)
+
+
+FULL = [("284b_a13b_mxfp4", 1), ("284b_a13b_mxfp4", 8), ("284b_a13b_mxfp4", 64),
+        ("284b_a13b_mxfp4", 8192), ("753b_a40b_bf16", 1), ("753b_a40b_bf16", 32),
+        ("753b_a40b_bf16", 16384), ("753b_a40b_mxfp4", 1), ("753b_a40b_mxfp4", 32),
+        ("753b_a40b_mxfp4", 16384)]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_full_size_sampled(name, T):
+    sh = synth.SHAPES[name]
+    _say("full size", name, "T", T)
+    L = _bank(sh)
+    x = synth.gen_x(sh, T, device=DEV)
+    bias = synth.gen_bias(sh, device=DEV)
+    # seeded logits with the spread a N(0, 0.02) router gives on N(0, 1) activations
+    # (std 0.02 * sqrt(H)); the router GEMM itself is checked in test_router_logits
+    lg = synth.gen_logits(sh, T, device=DEV, scale=0.02 * np.sqrt(sh.H))
+    r = run_layer(L, x, lg, bias=bias)
+    lg_np = lg.cpu().numpy()
+    ids, w = orc.route(lg_np, sh.k, None if bias is None else bias.cpu().numpy())
+    assert np.array_equal(r["ids"].cpu().numpy(), ids)
+    rc, ro, rp, ri = orc.align(ids, sh.E)
+    assert np.array_equal(r["perm"].cpu().numpy(), rp)
+    assert np.array_equal(r["counts"].cpu().numpy(), rc)
+    tok = _sample_tokens(ids, T, sh.E, 24 if T > 64 else T, seed=T)
+    ref = oracle_out(L, x, ids, w, tokens=tok)
+    got = r["out"].cpu()[torch.from_numpy(tok).long()]
+    e, m = check_close(got, ref, sh.wdtype, f"{name} T{T}")
+    _say("  rel_l2", e, "max/amax", m)
