@@ -100,11 +100,11 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    prof = {which: [(ev(), ev()) for _ in range(steps)]
+    hev = ft.HipEvents()
+    prof = {which: [(hev.create(), hev.create()) for _ in range(steps)]
             for which in (ft.PROF_GEMM1, ft.PROF_GEMM2, ft.PROF_FFN)}
     active = []
-    t0, t1 = ev(), ev()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
@@ -116,7 +116,9 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     for which in prof:
         ft.set_profile_events(which, None, None)
     ms = t0.elapsed_time(t1) / steps
-    dur = {which: sum(a.elapsed_time(b) for a, b in lst) / steps for which, lst in prof.items()}
+    dur = {which: sum(hev.elapsed_ms(a, b) for a, b in lst) / steps
+           for which, lst in prof.items()}
+    hev.close()
     # distinct active experts of each timed step (recomputed outside the timed region)
     for i in range(steps):
         b = banks[(warmup + i) % len(banks)]
@@ -128,6 +130,10 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     n_act = sum(active) / steps
     eb = banks[0].expert_bytes
     ffn_bytes = (n_act + sh.n_shared) * eb
+    # bytes of the gate/up matrices (codes + scales for MXFP4) of the experts read
+    _, offs = ft.expert_layout(sh.wdtype, sh.H, sh.I)
+    w13 = (offs[2] - offs[0]) + ((offs[5] - offs[3]) if sh.wdtype == "mxfp4" else 0)
+    w13_bytes = (n_act + sh.n_shared) * w13
     rows = T * k + sh.n_shared * T
     fl1 = 2.0 * rows * 2 * sh.I * sh.H
     fl2 = 2.0 * rows * sh.I * sh.H
@@ -136,6 +142,9 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
         "ffn_ms": dur[ft.PROF_FFN], "gemm1_ms": dur[ft.PROF_GEMM1], "gemm2_ms": dur[ft.PROF_GEMM2],
         "active_experts": n_act, "weight_bytes": ffn_bytes,
         "ffn_gbs": ffn_bytes / (dur[ft.PROF_FFN] * 1e-3) / 1e9,
+        "gemm1_gbs": w13_bytes / (dur[ft.PROF_GEMM1] * 1e-3) / 1e9,
+        "gemm2_gbs": (ffn_bytes - w13_bytes) / (dur[ft.PROF_GEMM2] * 1e-3) / 1e9,
+        "w13_bytes": w13_bytes,
         "gemm1_tflops": fl1 / (dur[ft.PROF_GEMM1] * 1e-3) / 1e12,
         "gemm2_tflops": fl2 / (dur[ft.PROF_GEMM2] * 1e-3) / 1e12,
         "ffn_tflops": (fl1 + fl2) / (dur[ft.PROF_FFN] * 1e-3) / 1e12,
@@ -227,10 +236,13 @@ def main():
         r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
         decode.append({
             "T": T, "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-            "ffn_us": r["ffn_ms"] * 1e3, "active_experts": r["active_experts"],
-            "roofline": {"bound": "hbm", "achieved": r["ffn_gbs"], "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": r["ffn_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "ft_moe_ffn (both expert GEMMs)"}})
+            "ffn_us": r["ffn_ms"] * 1e3, "gate_up_us": r["gemm1_ms"] * 1e3,
+            "down_us": r["gemm2_ms"] * 1e3, "active_experts": r["active_experts"],
+            "down_gbs": r["gemm2_gbs"],
+            "roofline": {"bound": "hbm", "achieved": r["gemm1_gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": r["gemm1_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gate/up weight streaming (ffn1_stream)",
+                         "bytes_per_launch": r["w13_bytes"]}})
         log("decode", json.dumps(decode[-1]))
 
     cpu = None

@@ -85,22 +85,66 @@ __device__ __forceinline__ const u32x4_t* row_chunks(const uint8_t* slot, size_t
     return reinterpret_cast<const u32x4_t*>(slot + moff + (size_t)row * rb);
 }
 
-// Load up to R activation rows (K elements each) into LDS.  Row r of the
-// chunk holds token rows_tok[r].  AT: bf16 (2 B) or fp32 (4 B).
-template <typename AT>
-__device__ __forceinline__ void stage_rows(AT* xs, const AT* __restrict__ src, const int* tok,
+// One pass over a weight row: this lane's chunks c = c0 + lane + 64 q, q < 4.
+// All loads of a pass are issued together so that a wavefront has 4 (or 8
+// for gate + up) 16-byte loads per lane in flight.
+template <int WT>
+struct RowPass {
+    u32x4_t v[4];
+    uint32_t s[4];
+    __device__ __forceinline__ void load(const u32x4_t* __restrict__ row,
+                                         const uint8_t* __restrict__ sc, int c0, int nch,
+                                         int lane) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = c0 + 64 * q + lane;
+            if (c < nch) {
+                v[q] = __builtin_nontemporal_load(row + c);
+                if constexpr (WT == 2) s[q] = sc[c];
+            }
+        }
+    }
+    template <typename AT>
+    __device__ __forceinline__ float dot(const AT* xrow, int c0, int nch, int lane, float acc) const {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = c0 + 64 * q + lane;
+            if (c < nch) acc = chunk_dot<WT>(v[q], WT == 2 ? s[q] : 0u, xrow + (size_t)c * W<WT>::EPC, acc);
+        }
+        return acc;
+    }
+};
+
+// Wavefront sum: DPP inside each row of 16 lanes, then two cross-row swaps.
+#define FT_DPP(v, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true))
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += FT_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+    v += FT_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+    v += FT_DPP(v, 0x141);  // row_half_mirror
+    v += FT_DPP(v, 0x140);  // row_mirror
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+#undef FT_DPP
+
+// Activation rows into LDS: row r of the chunk is source row src_row(r).
+template <typename AT, typename RowF>
+__device__ __forceinline__ void stage_rows(AT* xs, const AT* __restrict__ src, RowF src_row,
                                            int R, int K) {
     const int per_row = K * (int)sizeof(AT) / 16;
     for (int i = threadIdx.x; i < R * per_row; i += blockDim.x) {
         const int r = i / per_row, c = i % per_row;
         reinterpret_cast<u32x4_t*>(xs + (size_t)r * K)[c] =
-            reinterpret_cast<const u32x4_t*>(src + (size_t)tok[r] * K)[c];
+            reinterpret_cast<const u32x4_t*>(src + (size_t)src_row(r) * K)[c];
     }
 }
 
 // ---------------------------------------------------------------------------
 // GEMM1 + SwiGLU.  Block: RPB row pairs (gate row i, up row i); wave w takes
-// pairs w, w+4, ...  Activations: RMAX token rows at a time in LDS.
+// pairs w, w+4, ...  Activations: RMAX token rows at a time in LDS.  The
+// first pass of weight loads is issued before the activations are staged.
 // ---------------------------------------------------------------------------
 template <int WT, int RMAX>
 __global__ __launch_bounds__(256) void ffn1_stream_kernel(ft::FfnGeom g, const void* __restrict__ xv,
@@ -108,11 +152,11 @@ __global__ __launch_bounds__(256) void ffn1_stream_kernel(ft::FfnGeom g, const v
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ slot_of,
                                                           int shared_slot, int n_routed_groups,
-                                                          int RPB, void* __restrict__ hv) {
+                                                          int RPB, int RCAP,
+                                                          void* __restrict__ hv) {
     using AT = typename std::conditional<WT == 0, float, __bf16>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     AT* xs = reinterpret_cast<AT*>(smem);
-    __shared__ int tok[RMAX];
     const int NB = g.I / RPB;
     const int j = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -132,45 +176,49 @@ __global__ __launch_bounds__(256) void ffn1_stream_kernel(ft::FfnGeom g, const v
         cnt = g.T;
         hrow0 = (size_t)g.T * g.k;
     }
+    const bool shared = e == g.E;
     const uint8_t* sl = g.pool + (size_t)slot * g.slot_stride;
     const int K = g.H;
     const int nch = K / W<WT>::EPC;
     const AT* x = reinterpret_cast<const AT*>(xv);
-    for (int r0 = 0; r0 < cnt; r0 += RMAX) {
-        const int R = min(RMAX, cnt - r0);
-        __syncthreads();
-        if (threadIdx.x < R) {
-            const int p = p_lo + r0 + threadIdx.x;
-            tok[threadIdx.x] = e == g.E ? p : perm[p] / g.k;
-        }
-        __syncthreads();
-        stage_rows<AT>(xs, x, tok, R, K);
+    auto gate_row = [&](int i) { return row_chunks<WT>(sl, g.off[0], i, K); };
+    auto up_row = [&](int i) { return row_chunks<WT>(sl, g.off[1], i, K); };
+    auto gate_sc = [&](int i) { return WT == 2 ? sl + g.off[3] + (size_t)i * (K / 32) : nullptr; };
+    auto up_sc = [&](int i) { return WT == 2 ? sl + g.off[4] + (size_t)i * (K / 32) : nullptr; };
+
+    RowPass<WT> pg, pu;
+    for (int r0 = 0; r0 < cnt; r0 += RCAP) {
+        const int R = min(RCAP, cnt - r0);
+        // first pass of this wave's first row pair, in flight during staging
+        int i = nb * RPB + wave;
+        pg.load(gate_row(i), gate_sc(i), 0, nch, lane);
+        pu.load(up_row(i), up_sc(i), 0, nch, lane);
+        __syncthreads();  // previous chunk's readers are done with xs
+        stage_rows<AT>(xs, x, [&](int r) { int p = p_lo + r0 + r; return shared ? p : perm[p] / g.k; },
+                       R, K);
         __syncthreads();
         for (int ip = wave; ip < RPB; ip += 4) {
-            const int i = nb * RPB + ip;
-            const u32x4_t* wg = row_chunks<WT>(sl, g.off[0], i, K);
-            const u32x4_t* wu = row_chunks<WT>(sl, g.off[1], i, K);
-            const uint8_t* sg = WT == 2 ? sl + g.off[3] + (size_t)i * (K / 32) : nullptr;
-            const uint8_t* su = WT == 2 ? sl + g.off[4] + (size_t)i * (K / 32) : nullptr;
+            i = nb * RPB + ip;
             float ag[RMAX], au[RMAX];
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) ag[r] = au[r] = 0.f;
-            for (int c = lane; c < nch; c += 64) {
-                const u32x4_t a = wg[c], b = wu[c];
-                const uint32_t sa = WT == 2 ? sg[c] : 0u, sb = WT == 2 ? su[c] : 0u;
+            for (int c0 = 0; c0 < nch; c0 += 256) {
+                if (c0 > 0 || ip != wave) {
+                    pg.load(gate_row(i), gate_sc(i), c0, nch, lane);
+                    pu.load(up_row(i), up_sc(i), c0, nch, lane);
+                }
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r)
                     if (r < R) {
-                        const AT* xp = xs + (size_t)r * K + (size_t)c * W<WT>::EPC;
-                        ag[r] = chunk_dot<WT>(a, sa, xp, ag[r]);
-                        au[r] = chunk_dot<WT>(b, sb, xp, au[r]);
+                        ag[r] = pg.dot(xs + (size_t)r * K, c0, nch, lane, ag[r]);
+                        au[r] = pu.dot(xs + (size_t)r * K, c0, nch, lane, au[r]);
                     }
             }
 #pragma unroll
             for (int r = 0; r < RMAX; ++r)
                 if (r < R) {
-                    const float gs = wave_sum(ag[r]), us = wave_sum(au[r]);
-                    if (lane == 0) {
+                    const float gs = wave_sum_dpp(ag[r]), us = wave_sum_dpp(au[r]);
+                    if (lane == r) {
                         const float hval = silu_mul(gs, us);
                         const size_t idx = (hrow0 + r0 + r) * g.I + i;
                         if constexpr (WT == 0) reinterpret_cast<float*>(hv)[idx] = hval;
@@ -189,11 +237,11 @@ __global__ __launch_bounds__(256) void ffn2_stream_kernel(ft::FfnGeom g, const v
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ slot_of,
                                                           int shared_slot, int n_routed_groups,
-                                                          int RPB, OT* __restrict__ y) {
+                                                          int RPB, int RCAP,
+                                                          OT* __restrict__ y) {
     using AT = typename std::conditional<WT == 0, float, __bf16>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     AT* hs = reinterpret_cast<AT*>(smem);
-    __shared__ int rows[RMAX];
     const int NB = g.H / RPB;
     const int j = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -214,32 +262,33 @@ __global__ __launch_bounds__(256) void ffn2_stream_kernel(ft::FfnGeom g, const v
     const int K = g.I;
     const int nch = K / W<WT>::EPC;
     const AT* h = reinterpret_cast<const AT*>(hv);
-    for (int r0 = 0; r0 < cnt; r0 += RMAX) {
-        const int R = min(RMAX, cnt - r0);
+    auto down_row = [&](int d) { return row_chunks<WT>(sl, g.off[2], d, K); };
+    auto down_sc = [&](int d) { return WT == 2 ? sl + g.off[5] + (size_t)d * (K / 32) : nullptr; };
+
+    RowPass<WT> pd;
+    for (int r0 = 0; r0 < cnt; r0 += RCAP) {
+        const int R = min(RCAP, cnt - r0);
+        int d = nb * RPB + wave;
+        pd.load(down_row(d), down_sc(d), 0, nch, lane);
         __syncthreads();
-        if (threadIdx.x < R) rows[threadIdx.x] = (int)(hrow0 + r0 + threadIdx.x);
-        __syncthreads();
-        stage_rows<AT>(hs, h, rows, R, K);
+        stage_rows<AT>(hs, h, [&](int r) { return (int)(hrow0 + r0 + r); }, R, K);
         __syncthreads();
         for (int dp = wave; dp < RPB; dp += 4) {
-            const int d = nb * RPB + dp;
-            const u32x4_t* wd = row_chunks<WT>(sl, g.off[2], d, K);
-            const uint8_t* sd = WT == 2 ? sl + g.off[5] + (size_t)d * (K / 32) : nullptr;
+            d = nb * RPB + dp;
             float acc[RMAX];
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) acc[r] = 0.f;
-            for (int c = lane; c < nch; c += 64) {
-                const u32x4_t a = wd[c];
-                const uint32_t sa = WT == 2 ? sd[c] : 0u;
+            for (int c0 = 0; c0 < nch; c0 += 256) {
+                if (c0 > 0 || dp != wave) pd.load(down_row(d), down_sc(d), c0, nch, lane);
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r)
-                    if (r < R) acc[r] = chunk_dot<WT>(a, sa, hs + (size_t)r * K + (size_t)c * W<WT>::EPC, acc[r]);
+                    if (r < R) acc[r] = pd.dot(hs + (size_t)r * K, c0, nch, lane, acc[r]);
             }
 #pragma unroll
             for (int r = 0; r < RMAX; ++r)
                 if (r < R) {
-                    const float v = wave_sum(acc[r]);
-                    if (lane == 0) {
+                    const float v = wave_sum_dpp(acc[r]);
+                    if (lane == r) {
                         const size_t idx = (hrow0 + r0 + r) * g.H + d;
                         if constexpr (sizeof(OT) == 4) reinterpret_cast<float*>(y)[idx] = v;
                         else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
@@ -271,9 +320,10 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     const int big = g.H > 2048 || g.I > 2048;
 
     prof_begin(PROF_FFN_GEMM1, s);
+    // activation rows per pass: at most RMAX, at most T (an expert never gets more than T rows)
 #define FT_S1(WT, RM)                                                                         \
-    ffn1_stream_kernel<WT, RM><<<g1, blk, (size_t)RM * g.H * (WT == 0 ? 4 : 2), s>>>(          \
-        g, x, perm, offsets, slot_of, shared_slot, routed_groups, rpb1, h)
+    ffn1_stream_kernel<WT, RM><<<g1, blk, (size_t)min(RM, g.T) * g.H * (WT == 0 ? 4 : 2), s>>>( \
+        g, x, perm, offsets, slot_of, shared_slot, routed_groups, rpb1, min(RM, g.T), h)
     if (g.w_dt == FT_F32) FT_S1(0, 8);
     else if (g.w_dt == FT_BF16) { if (big) FT_S1(1, 4); else FT_S1(1, 8); }
     else { if (big) FT_S1(2, 4); else FT_S1(2, 8); }
@@ -283,8 +333,8 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
 
     prof_begin(PROF_FFN_GEMM2, s);
 #define FT_S2(WT, RM, OT)                                                                     \
-    ffn2_stream_kernel<WT, RM, OT><<<g2, blk, (size_t)RM * g.I * (WT == 0 ? 4 : 2), s>>>(      \
-        g, h, offsets, slot_of, shared_slot, routed_groups, rpb2, (OT*)y)
+    ffn2_stream_kernel<WT, RM, OT><<<g2, blk, (size_t)min(RM, g.T) * g.I * (WT == 0 ? 4 : 2), s>>>( \
+        g, h, offsets, slot_of, shared_slot, routed_groups, rpb2, min(RM, g.T), (OT*)y)
     if (g.w_dt == FT_F32) FT_S2(0, 8, float);
     else if (g.w_dt == FT_BF16) {
         if (y_dt == FT_F32) { if (big) FT_S2(1, 4, float); else FT_S2(1, 8, float); }

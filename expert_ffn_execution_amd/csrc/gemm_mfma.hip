@@ -23,7 +23,7 @@
 namespace {
 
 using ft::TileDesc;
-constexpr int BM = ft::GEMM_BM, BN = ft::GEMM_BN, BK = ft::GEMM_BK, NTHR = 256;
+constexpr int BK = ft::GEMM_BK;
 
 __device__ __forceinline__ int lds_idx(int r, int c) {
     return r * BK + ((c ^ ((r >> 1) & 7)) << 3);
@@ -43,240 +43,185 @@ __device__ __forceinline__ void decode_fp4x32(u32x4_t codes, uint32_t X, u32x4_t
     }
 }
 
-// Staging of one 128 x 64 B slice.  bf16: thread owns rows (tid>>3)+32i, chunk
-// tid&7.  MXFP4: thread owns row tid>>1, half tid&1 (32 codes, one scale).
-template <int BT>
-struct BStage {
-    u32x4_t v[4];
-    uint32_t sc;
-    const uint8_t* src[4];
-    const uint8_t* scp;
-
-    // rowptr(r) = byte address of B row r (codes for MXFP4), scrow(r) = its scales
-    template <typename RowF, typename ScF>
-    __device__ __forceinline__ void init(int tid, RowF rowptr, ScF scrow) {
-        if constexpr (BT == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) src[i] = rowptr((tid >> 3) + 32 * i) + (tid & 7) * 16;
-        } else {
-            src[0] = rowptr(tid >> 1) + (tid & 1) * 16;
-            scp = scrow(tid >> 1) + (tid & 1);
-        }
-    }
-    __device__ __forceinline__ void load(int kt) {
-        if constexpr (BT == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(src[i] + kt * BK * 2);
-        } else {
-            v[0] = *reinterpret_cast<const u32x4_t*>(src[0] + kt * (BK / 2));
-            sc = scp[kt * (BK / 32)];
-        }
-    }
-    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-        if constexpr (BT == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + 32 * i, tid & 7)) = v[i];
-        } else {
-            u32x4_t d[4];
-            decode_fp4x32(v[0], sc, d);
-            const int r = tid >> 1, h = (tid & 1) * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(lds + lds_idx(r, h + q)) = d[q];
-        }
-    }
-};
-
-struct AStage {
-    u32x4_t v[4];
-    const __bf16* src[4];
-    __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(src[i] + kt * BK);
-    }
-    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + 32 * i, tid & 7)) = v[i];
-    }
-};
-
 __device__ __forceinline__ bf16x8_t frag(const __bf16* lds, int r, int c) {
     return *reinterpret_cast<const bf16x8_t*>(lds + lds_idx(r, c));
 }
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// ---------------------------------------------------------------------------
-// GEMM1 + SwiGLU
-// ---------------------------------------------------------------------------
-template <int BT>
-__global__ __launch_bounds__(NTHR, 2) void gemm1_kernel(ft::FfnGeom g, const __bf16* __restrict__ x,
-                                                        const int32_t* __restrict__ perm,
-                                                        const TileDesc* __restrict__ tiles,
-                                                        const int* __restrict__ n_tiles,
-                                                        int n_ntiles, __bf16* __restrict__ h) {
-    __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN * BK];
-    const int ti = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
-    if (ti >= *n_tiles) return;
-    const TileDesc td = tiles[ti];
-    const int tid = threadIdx.x, K = g.H, I = g.I;
-    const int i0 = nt * (BN / 2);
-    const bool shared = td.e == g.E;
-    const uint8_t* slot = g.pool + (size_t)td.slot * g.slot_stride;
-
-    AStage as;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int r = min((tid >> 3) + 32 * i, td.rows - 1);
-        int p = td.p0 + r;
-        int t = shared ? p : perm[p] / g.k;
-        as.src[i] = x + (size_t)t * K + (tid & 7) * 8;
-    }
-    BStage<BT> bs;
-    if constexpr (BT == 0) {
-        bs.init(tid,
-                [&](int r) {
-                    return slot + (r < 64 ? g.off[0] : g.off[1]) + (size_t)(i0 + (r & 63)) * K * 2;
-                },
-                [&](int) { return (const uint8_t*)nullptr; });
-    } else {
-        bs.init(tid,
-                [&](int r) {
-                    return slot + (r < 64 ? g.off[0] : g.off[1]) + (size_t)(i0 + (r & 63)) * (K / 2);
-                },
-                [&](int r) {
-                    return slot + (r < 64 ? g.off[3] : g.off[4]) + (size_t)(i0 + (r & 63)) * (K / 32);
-                });
-    }
-
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    f32x4_t accg[4][2], accu[4][2];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) accg[a][b] = accu[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / BK;
-    as.load(0);
-    bs.load(0);
-    as.store(As[0], tid);
-    bs.store(Bs[0], tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            as.load(kt + 1);
-            bs.load(kt + 1);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = ks * 4 + (lane >> 4);
-            bf16x8_t a[4], bg[2], bu[2];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) a[m] = frag(As[cur], wm * 64 + m * 16 + (lane & 15), ch);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                bg[n] = frag(Bs[cur], wn * 32 + n * 16 + (lane & 15), ch);
-                bu[n] = frag(Bs[cur], 64 + wn * 32 + n * 16 + (lane & 15), ch);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    accg[m][n] = mfma16(a[m], bg[n], accg[m][n]);
-                    accu[m][n] = mfma16(a[m], bu[n], accu[m][n]);
-                }
-        }
-        if (kt + 1 < nk) {
-            as.store(As[cur ^ 1], tid);
-            bs.store(Bs[cur ^ 1], tid);
-        }
-        __syncthreads();
-    }
-
-    const size_t hbase = shared ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wm * 64 + m * 16 + 4 * (lane >> 4) + j;
-                const int col = i0 + wn * 32 + n * 16 + (lane & 15);
-                if (row < td.rows) {
-                    float hv = silu_mul(accg[m][n][j], accu[m][n][j]);
-                    reinterpret_cast<uint16_t*>(h)[(hbase + row) * I + col] =
-                        (uint16_t)f32_to_bf16_bits(hv);
-                }
-            }
+// v_mfma_f32_32x32x16_bf16 sustains about twice the rate of the 16x16x32 form
+// on gfx950 (measured), so the expert GEMMs use it
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// plain GEMM: out[row][n] = A[row] . B[n]  (GEMM2 over the tile list, or a
-// dense M x N problem for the router logits)
+// Tile shapes.  A block computes a BM x BN output tile with NW = (BM/WM) x
+// (BN/WN) wavefronts, each owning a WM x WN sub-tile of 16 x 16 MFMA tiles
+// (fp32 accumulators: WM*WN/64 registers per lane, held in AGPRs for the
+// large shape).  LDS holds two stages of BM x 64 (A) and BN x 64 (B) bf16.
 // ---------------------------------------------------------------------------
-template <int BT, typename OutT, bool DENSE>
-__global__ __launch_bounds__(NTHR, 2) void gemm_plain_kernel(
-    ft::FfnGeom g, const __bf16* __restrict__ A, const __bf16* __restrict__ Bdense, int M,
-    int N, int K, const TileDesc* __restrict__ tiles, const int* __restrict__ n_tiles,
-    int n_ntiles, OutT* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN * BK];
+template <int BM_, int BN_, int WM_, int WN_, int MINB_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MINB = MINB_;
+    static constexpr int WAVES_N = BN / WN, NW = (BM / WM) * (BN / WN), NT = NW * 64;
+    static constexpr int MT = WM / 16, NTL = WN / 16;
+    static constexpr int A_CH = BM * 8 / NT;   // 16-byte A chunks per thread per slice
+    static constexpr int B_CH = BN * 8 / NT;   // 16-byte bf16 B chunks per thread
+    static constexpr int B_MX = BN * 2 / NT;   // (row, half) MXFP4 units per thread
+    static constexpr size_t LDS = (size_t)2 * (BM + BN) * BK * 2;
+};
+using SmallTile = TileCfg<128, 128, 64, 64, 2>;
+
+enum { MODE_GATED = 0, MODE_LIST = 1, MODE_DENSE = 2 };
+
+// B staging: 32-bit byte offsets from a block-uniform base (the slot), so
+// that the per-thread state is one VGPR per chunk.
+template <class C, int BT>
+struct BSlice {
+    static constexpr int NV = BT == 0 ? C::B_CH : C::B_MX;
+    u32x4_t v[NV];
+    uint32_t sc[BT == 0 ? 1 : NV];
+    const uint8_t* base;
+    uint32_t off[NV];
+    uint32_t scoff[BT == 0 ? 1 : NV];
+
+    // rowoff(r) = byte offset of B row r (codes for MXFP4), scoff(r) = its scales
+    template <typename RowF, typename ScF>
+    __device__ __forceinline__ void init(const uint8_t* b, int tid, RowF rowoff, ScF scrow) {
+        base = b;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (BT == 0) {
+                off[i] = rowoff((tid >> 3) + (C::NT / 8) * i) + (tid & 7) * 16;
+            } else {
+                const int q = tid + C::NT * i;
+                off[i] = rowoff(q >> 1) + (q & 1) * 16;
+                scoff[i] = scrow(q >> 1) + (q & 1);
+            }
+        }
+    }
+    __device__ __forceinline__ void load(int kt) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (BT == 0) {
+                v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * BK * 2);
+            } else {
+                v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * (BK / 2));
+                sc[i] = base[scoff[i] + kt * (BK / 32)];
+            }
+        }
+    }
+    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (BT == 0) {
+                *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + (C::NT / 8) * i, tid & 7)) = v[i];
+            } else {
+                u32x4_t d[4];
+                decode_fp4x32(v[i], sc[i], d);
+                const int q = tid + C::NT * i, r = q >> 1, h = (q & 1) * 4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(lds + lds_idx(r, h + c)) = d[c];
+            }
+        }
+    }
+};
+
+// A staging: 32-bit element offsets of the (gathered) rows from the A base.
+template <class C>
+struct ASlice {
+    u32x4_t v[C::A_CH];
+    const __bf16* base;
+    uint32_t off[C::A_CH];
+    __device__ __forceinline__ void load(int kt) {
+#pragma unroll
+        for (int i = 0; i < C::A_CH; ++i)
+            v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * BK);
+    }
+    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < C::A_CH; ++i)
+            *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + (C::NT / 8) * i, tid & 7)) = v[i];
+    }
+};
+
+// One kernel for the three contractions:
+//   MODE_GATED: h[p][i] = bf16(silu(x_t . Wg_i) * (x_t . Wu_i)) (B tile = BN/2 gate rows
+//               followed by the same BN/2 up rows)
+//   MODE_LIST:  out[p][n] = A[p] . B_n over the tile list (down projection)
+//   MODE_DENSE: out[m][n] = A[m] . B_n for a dense M x N problem (router logits)
+template <class C, int MODE, int BT, typename OutT>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
+    ft::FfnGeom g, const __bf16* __restrict__ A, const int32_t* __restrict__ perm,
+    const __bf16* __restrict__ Bdense, int M, int N, int K, const TileDesc* __restrict__ tiles,
+    const int* __restrict__ n_tiles, int n_ntiles, OutT* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
+    __bf16* const A0 = smem;
+    __bf16* const B0 = smem + 2 * C::BM * BK;
     const int ti = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
     TileDesc td;
-    if constexpr (DENSE) {
-        td.e = 0;
-        td.p0 = ti * BM;
-        td.rows = min(BM, M - ti * BM);
-        td.slot = 0;
+    if constexpr (MODE == MODE_DENSE) {
+        td = TileDesc{0, ti * C::BM, min(C::BM, M - ti * C::BM), 0};
     } else {
         if (ti >= *n_tiles) return;
         td = tiles[ti];
     }
     const int tid = threadIdx.x;
-    const int n0 = nt * BN;
-    const size_t rbase =
-        DENSE ? (size_t)td.p0 : (td.e == g.E ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0);
+    const bool shared = MODE != MODE_DENSE && td.e == g.E;
+    // first output row of the tile (shared-expert rows follow the T*k routed rows)
+    const size_t obase = shared ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0;
 
-    AStage as;
+    ASlice<C> as;
+    as.base = A;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int r = min((tid >> 3) + 32 * i, td.rows - 1);
-        as.src[i] = A + (rbase + r) * K + (tid & 7) * 8;
+    for (int i = 0; i < C::A_CH; ++i) {
+        const int r = min((tid >> 3) + (C::NT / 8) * i, td.rows - 1);
+        uint32_t arow;
+        if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + r) : (uint32_t)(perm[td.p0 + r] / g.k);
+        else arow = (uint32_t)(obase + r);
+        as.off[i] = arow * (uint32_t)K + (tid & 7) * 8;
     }
-    BStage<BT> bs;
-    if constexpr (DENSE) {
-        bs.init(tid,
+    BSlice<C, BT> bs;
+    const uint8_t* slot = MODE == MODE_DENSE ? nullptr : g.pool + (size_t)td.slot * g.slot_stride;
+    const int i0 = nt * (C::BN / 2), n0 = nt * C::BN;
+    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : (uint32_t)K / 2;  // bytes per B row
+    if constexpr (MODE == MODE_GATED) {
+        bs.init(slot, tid,
                 [&](int r) {
-                    return reinterpret_cast<const uint8_t*>(Bdense + (size_t)min(n0 + r, N - 1) * K);
+                    const uint32_t row = i0 + (r % (C::BN / 2));
+                    return (uint32_t)(r < C::BN / 2 ? g.off[0] : g.off[1]) + row * rowb;
                 },
-                [&](int) { return (const uint8_t*)nullptr; });
+                [&](int r) {
+                    const uint32_t row = i0 + (r % (C::BN / 2));
+                    return (uint32_t)(r < C::BN / 2 ? g.off[3] : g.off[4]) + row * (uint32_t)(K / 32);
+                });
+    } else if constexpr (MODE == MODE_LIST) {
+        // rows past N (N not a multiple of BN) re-read row N-1; their columns are not stored
+        bs.init(slot, tid,
+                [&](int r) { return (uint32_t)g.off[2] + (uint32_t)min(n0 + r, N - 1) * rowb; },
+                [&](int r) {
+                    return (uint32_t)g.off[5] + (uint32_t)min(n0 + r, N - 1) * (uint32_t)(K / 32);
+                });
     } else {
-        const uint8_t* slot = g.pool + (size_t)td.slot * g.slot_stride;
-        // rows past N (H not a multiple of 128) re-read row N-1; their columns are not stored
-        if constexpr (BT == 0)
-            bs.init(tid, [&](int r) { return slot + g.off[2] + (size_t)min(n0 + r, N - 1) * K * 2; },
-                    [&](int) { return (const uint8_t*)nullptr; });
-        else
-            bs.init(tid, [&](int r) { return slot + g.off[2] + (size_t)min(n0 + r, N - 1) * (K / 2); },
-                    [&](int r) { return slot + g.off[5] + (size_t)min(n0 + r, N - 1) * (K / 32); });
+        bs.init(reinterpret_cast<const uint8_t*>(Bdense), tid,
+                [&](int r) { return (uint32_t)min(n0 + r, N - 1) * rowb; },
+                [&](int) { return 0u; });
     }
 
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    f32x4_t acc[4][4];
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    f32x4_t acc[C::MT][C::NTL];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < C::MT; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < C::NTL; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
     as.load(0);
     bs.load(0);
-    as.store(As[0], tid);
-    bs.store(Bs[0], tid);
+    as.store(A0, tid);
+    bs.store(B0, tid);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
@@ -284,43 +229,327 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_plain_kernel(
             as.load(kt + 1);
             bs.load(kt + 1);
         }
+        const __bf16* Ac = A0 + cur * (C::BM * BK);
+        const __bf16* Bc = B0 + cur * (C::BN * BK);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int ch = ks * 4 + (lane >> 4);
-            bf16x8_t a[4], b[4];
+            bf16x8_t a[C::MT], b[C::NTL];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) a[m] = frag(As[cur], wm * 64 + m * 16 + (lane & 15), ch);
+            for (int m = 0; m < C::MT; ++m) a[m] = frag(Ac, wm * C::WM + m * 16 + (lane & 15), ch);
 #pragma unroll
-            for (int n = 0; n < 4; ++n) b[n] = frag(Bs[cur], wn * 64 + n * 16 + (lane & 15), ch);
+            for (int n = 0; n < C::NTL; ++n) {
+                int brow;
+                if constexpr (MODE == MODE_GATED)  // first half of the wave's tiles: gate, second: up
+                    brow = (n < C::NTL / 2 ? 0 : C::BN / 2) + wn * (C::WN / 2) + (n % (C::NTL / 2)) * 16;
+                else
+                    brow = wn * C::WN + n * 16;
+                b[n] = frag(Bc, brow + (lane & 15), ch);
+            }
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-                for (int n = 0; n < 4; ++n) acc[m][n] = mfma16(a[m], b[n], acc[m][n]);
+                for (int n = 0; n < C::NTL; ++n) acc[m][n] = mfma16(a[m], b[n], acc[m][n]);
         }
         if (kt + 1 < nk) {
-            as.store(As[cur ^ 1], tid);
-            bs.store(Bs[cur ^ 1], tid);
+            as.store(A0 + (cur ^ 1) * (C::BM * BK), tid);
+            bs.store(B0 + (cur ^ 1) * (C::BN * BK), tid);
         }
         __syncthreads();
     }
 
+    // epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + j of each 16 x 16 tile
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int j = 0; j < 4; ++j) {
+            const int row = wm * C::WM + m * 16 + 4 * (lane >> 4) + j;
+            if (row >= td.rows) continue;
+            if constexpr (MODE == MODE_GATED) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wm * 64 + m * 16 + 4 * (lane >> 4) + j;
-                const int col = n0 + wn * 64 + n * 16 + (lane & 15);
-                if (row < td.rows && col < N) {
-                    float v = acc[m][n][j];
-                    if constexpr (sizeof(OutT) == 4)
-                        reinterpret_cast<float*>(out)[(rbase + row) * N + col] = v;
-                    else
-                        reinterpret_cast<uint16_t*>(out)[(rbase + row) * N + col] =
-                            (uint16_t)f32_to_bf16_bits(v);
+                for (int n = 0; n < C::NTL / 2; ++n) {
+                    const int col = i0 + wn * (C::WN / 2) + n * 16 + (lane & 15);
+                    const float hv = silu_mul(acc[m][n][j], acc[m][n + C::NTL / 2][j]);
+                    reinterpret_cast<uint16_t*>(out)[(obase + row) * g.I + col] =
+                        (uint16_t)f32_to_bf16_bits(hv);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < C::NTL; ++n) {
+                    const int col = n0 + wn * C::WN + n * 16 + (lane & 15);
+                    if (col < N) {
+                        const float v = acc[m][n][j];
+                        if constexpr (sizeof(OutT) == 4)
+                            reinterpret_cast<float*>(out)[(obase + row) * N + col] = v;
+                        else
+                            reinterpret_cast<uint16_t*>(out)[(obase + row) * N + col] =
+                                (uint16_t)f32_to_bf16_bits(v);
+                    }
                 }
             }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined tile kernel for the expert GEMMs.  256 x 256 output tile, 8
+// wavefronts (4 x 2) of 64 x 128 (2 x 4 tiles of v_mfma_f32_32x32x16_bf16),
+// K in slices of 32 through five LDS stages.
+// Slices are copied global -> LDS by the load units directly
+// (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane l
+// its 16 bytes), so four slices are in flight while the fifth feeds the
+// MFMAs and no registers hold staged data.  A wave waits for its own copies
+// of a slice with s_waitcnt vmcnt and the block barrier then publishes it.
+// The tile is as large as the 160 KB LDS allows so that every byte brought
+// into the CU feeds as many MFMAs as possible: per slice 32 KB carry 4.2
+// MFLOP.  MXFP4 weights stay packed in LDS (16 code bytes + 1 scale byte per
+// row and slice) and are decoded to bf16 when a fragment is read.
+//
+// LDS layout of a slice of rows: row r is 64 bytes = 4 chunks of 16 bytes,
+// chunk c stored at position c ^ ((r >> 2) & 3): the 16 rows a fragment read
+// touches then cover all 64 banks exactly once.
+// ---------------------------------------------------------------------------
+namespace pipe {
+constexpr int BM = 256, BN = 256, KS = 32, NT = 512, WM = 64, WN = 128, WAVES_N = 2;
+constexpr int STAGES = 5;   // 5 x 32 KB = all 160 KB of LDS (bf16)
+constexpr int MT = WM / 32, NTL = WN / 32;   // 32 x 32 MFMA tiles per wavefront
+constexpr int ROWB = KS * 2;                          // bytes of a bf16 row slice
+constexpr int A_BYTES = BM * ROWB;                    // 16 KB
+// MXFP4: codes [BN][16 B], then one 4-byte slot per row holding its scale byte
+// (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot)
+template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BN * 16 + BN * 4; }
+template <int BT> constexpr int stage_bytes() { return A_BYTES + b_bytes<BT>(); }
+template <int BT> constexpr size_t lds_bytes() { return (size_t)STAGES * stage_bytes<BT>(); }
+// global_load_lds instructions per wave per slice
+template <int BT> constexpr int loads_per_slice() { return BT == 0 ? 4 : 3; }
+__device__ __forceinline__ int sw(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+}  // namespace pipe
+
+#define FT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ bf16x8_t fp4_frag(uint32_t codes, uint32_t X) {
+    const float sc = __uint_as_float(X << 23);
+    u32x4_t d;
+    d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+    d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+    d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+    d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+    return __builtin_bit_cast(bf16x8_t, d);
+}
+
+template <int MODE, int BT, typename OutT>
+__global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
+    ft::FfnGeom g, const __bf16* __restrict__ A, const int32_t* __restrict__ perm,
+    const TileDesc* __restrict__ tiles, const int* __restrict__ n_tiles, int n_ntiles,
+    OutT* __restrict__ out) {
+    using namespace pipe;
+    static_assert(STAGES == 5, "wait schedule below assumes five stages");
+    extern __shared__ __attribute__((aligned(16))) unsigned char pipe_smem[];
+    unsigned char* const smem = pipe_smem;
+    // XCD-aware order: the dispatcher deals blocks to the 8 XCDs round-robin;
+    // give XCD x a contiguous run of the real work so that the N-tiles of one
+    // M-tile (same activation rows) share that XCD's L2.
+    const int work = *n_tiles * n_ntiles;
+    const int per_xcd = (work + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int lb = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || lb >= work) return;
+    const int ti = lb / n_ntiles, nt = lb % n_ntiles;
+    const TileDesc td = tiles[ti];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = MODE == MODE_GATED ? g.H : g.I;
+    const int NOUT = MODE == MODE_GATED ? g.I : g.H;   // output columns (h or y)
+    const bool shared = td.e == g.E;
+    const size_t obase = shared ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0;
+    const uint8_t* slot = g.pool + (size_t)td.slot * g.slot_stride;
+    // gated: B rows [0, 128) = gate rows c0.., [128, 256) = up rows c0..; plain: rows c0..
+    const int c0 = nt * (MODE == MODE_GATED ? BN / 2 : BN);
+
+    // A: lane fills LDS row r = 16 * (2 * wave + i) + lane / 4, physical chunk lane % 4
+    uint32_t aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * (2 * wave + i) + (lane >> 2);
+        const int rc = min(r, td.rows - 1);
+        uint32_t arow;
+        if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + rc) : (uint32_t)(perm[td.p0 + rc] / g.k);
+        else arow = (uint32_t)(obase + rc);
+        aoff[i] = arow * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
+    }
+    // B row r of the tile -> weight row (clamped: columns past NOUT are not stored)
+    auto wrow = [&](int r) -> uint32_t {
+        if constexpr (MODE == MODE_GATED) return (uint32_t)min(c0 + (r % (BN / 2)), NOUT - 1);
+        else return (uint32_t)min(c0 + r, NOUT - 1);
+    };
+    auto wbase = [&](int r, int which) -> uint32_t {  // which: 0 codes/values, 1 scales
+        if constexpr (MODE == MODE_GATED)
+            return (uint32_t)(r < BN / 2 ? g.off[which ? 3 : 0] : g.off[which ? 4 : 1]);
+        else
+            return (uint32_t)g.off[which ? 5 : 2];
+    };
+    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : (uint32_t)K / 2;
+    uint32_t boff[2];
+    if constexpr (BT == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 16 * (2 * wave + i) + (lane >> 2);
+            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
+        }
+    } else if (wave < 4) {  // codes: row 64 * wave + lane, 16 bytes per slice
+        const int r = 64 * wave + lane;
+        boff[0] = wbase(r, 0) + wrow(r) * rowb;
+    } else {                // scales: row 64 * (wave - 4) + lane, 1 byte per slice
+        const int r = 64 * (wave - 4) + lane;
+        boff[0] = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
+    }
+
+    auto issue = [&](int stage, int kt) {
+        unsigned char* st = smem + stage * stage_bytes<BT>();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(A + aoff[i] + kt * KS, FT_LDS(st + (2 * wave + i) * 1024), 16, 0, 0);
+        unsigned char* bst = st + A_BYTES;
+        if constexpr (BT == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * ROWB, FT_LDS(bst + (2 * wave + i) * 1024), 16, 0, 0);
+        } else if (wave < 4) {
+            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt * (KS / 2), FT_LDS(bst + wave * 1024), 16, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt, FT_LDS(bst + BN * 16 + (wave - 4) * 256), 1, 0, 0);
+        }
+    };
+
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    f32x16_t acc[MT][NTL];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int b = 0; b < NTL; ++b)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
+
+    constexpr int LPS = loads_per_slice<BT>();
+    const int nk = K / KS;
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q)
+        if (q < nk) issue(q, q);
+    const int l32 = lane & 31, hi = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        // slice kt has landed once at most `ahead` later slices are outstanding
+        const int ahead = min(STAGES - 2, nk - 1 - kt);
+        if (ahead >= 3) wait_vmcnt<3 * LPS>();
+        else if (ahead == 2) wait_vmcnt<2 * LPS>();
+        else if (ahead == 1) wait_vmcnt<LPS>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < nk) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+        const unsigned char* st = smem + (kt % STAGES) * stage_bytes<BT>();
+        const unsigned char* Bc = st + A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // 32x32x16 operands: lane holds row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7
+            const int ch = 2 * kk + hi;
+            bf16x8_t a[MT], b[NTL];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                a[m] = *reinterpret_cast<const bf16x8_t*>(st + sw(wm * WM + m * 32 + l32, ch));
+#pragma unroll
+            for (int n = 0; n < NTL; ++n) {
+                int brow;
+                if constexpr (MODE == MODE_GATED)  // wave's first NTL/2 tiles: gate, the rest: up
+                    brow = (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
+                else
+                    brow = wn * WN + n * 32;
+                const int row = brow + l32;
+                if constexpr (BT == 0) {
+                    b[n] = *reinterpret_cast<const bf16x8_t*>(Bc + sw(row, ch));
+                } else {
+                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bc + row * 16 + ch * 4);
+                    b[n] = fp4_frag(codes, Bc[BN * 16 + row * 4]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NTL; ++n) acc[m][n] = mfma32(a[m], b[n], acc[m][n]);
+        }
+    }
+
+    // epilogue: register q of a 32 x 32 tile is row 8 (q / 4) + 4 (lane / 32) + q % 4,
+    // column lane % 32
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = wm * WM + m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+            if (row >= td.rows) continue;
+            if constexpr (MODE == MODE_GATED) {
+#pragma unroll
+                for (int n = 0; n < NTL / 2; ++n) {
+                    const int col = c0 + wn * (WN / 2) + n * 32 + l32;
+                    if (col < NOUT) {
+                        const float hv = silu_mul(acc[m][n][q], acc[m][n + NTL / 2][q]);
+                        reinterpret_cast<uint16_t*>(out)[(obase + row) * NOUT + col] =
+                            (uint16_t)f32_to_bf16_bits(hv);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < NTL; ++n) {
+                    const int col = c0 + wn * WN + n * 32 + l32;
+                    if (col < NOUT) {
+                        const float v = acc[m][n][q];
+                        if constexpr (sizeof(OutT) == 4)
+                            reinterpret_cast<float*>(out)[(obase + row) * NOUT + col] = v;
+                        else
+                            reinterpret_cast<uint16_t*>(out)[(obase + row) * NOUT + col] =
+                                (uint16_t)f32_to_bf16_bits(v);
+                    }
+                }
+            }
+        }
+}
+#undef FT_LDS
+
+template <int MODE, int BT, typename OutT>
+hipError_t launch_pipe(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const __bf16* A,
+                       const int32_t* perm, const TileDesc* tiles, const int* n_tiles,
+                       int n_ntiles, OutT* out) {
+    static bool attr_set = false;
+    auto kern = gemm_pipe_kernel<MODE, BT, OutT>;
+    const size_t lds = pipe::lds_bytes<BT>();
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    kern<<<grid, pipe::NT, lds, s>>>(g, A, perm, tiles, n_tiles, n_ntiles, out);
+    return hipGetLastError();
+}
+
+// Launch one instantiation (raising its dynamic LDS limit once).
+template <class C, int MODE, int BT, typename OutT>
+hipError_t launch_tile(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const __bf16* A,
+                       const int32_t* perm, const __bf16* Bd, int M, int N, int K,
+                       const TileDesc* tiles, const int* n_tiles, int n_ntiles, OutT* out) {
+    static bool attr_set = false;
+    auto kern = gemm_tile_kernel<C, MODE, BT, OutT>;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    kern<<<grid, C::NT, C::LDS, s>>>(g, A, perm, Bd, M, N, K, tiles, n_tiles, n_ntiles, out);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -329,8 +558,9 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_plain_kernel(
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ slot_of,
                                                            int E, int T, int n_shared,
-                                                           int shared_slot, TileDesc* tiles,
-                                                           int* n_tiles, int max_tiles) {
+                                                           int shared_slot, int BMr,
+                                                           TileDesc* tiles, int* n_tiles,
+                                                           int max_tiles) {
     __shared__ int scan[1024];
     const int e = threadIdx.x;
     int cnt = 0, c = 0, off = 0, slot = -1;
@@ -338,7 +568,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
         off = offsets[e];
         c = offsets[e + 1] - off;
         slot = slot_of ? slot_of[e] : e;
-        if (slot >= 0 && c > 0) cnt = (c + BM - 1) / BM;
+        if (slot >= 0 && c > 0) cnt = (c + BMr - 1) / BMr;
     }
     scan[e] = cnt;
     __syncthreads();
@@ -351,12 +581,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     const int base = scan[e] - cnt, total = scan[1023];
     for (int m = 0; m < cnt; ++m) {
         int idx = base + m;
-        if (idx < max_tiles) tiles[idx] = TileDesc{e, off + m * BM, min(BM, c - m * BM), slot};
+        if (idx < max_tiles) tiles[idx] = TileDesc{e, off + m * BMr, min(BMr, c - m * BMr), slot};
     }
-    int ns = n_shared ? (T + BM - 1) / BM : 0;
+    int ns = n_shared ? (T + BMr - 1) / BMr : 0;
     for (int m = e; m < ns; m += 1024) {
         int idx = total + m;
-        if (idx < max_tiles) tiles[idx] = TileDesc{E, m * BM, min(BM, T - m * BM), shared_slot};
+        if (idx < max_tiles) tiles[idx] = TileDesc{E, m * BMr, min(BMr, T - m * BMr), shared_slot};
     }
     if (e == 0) *n_tiles = min(total + ns, max_tiles);
 }
@@ -365,11 +595,20 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 
 namespace ft {
 
+int max_tiles_for(const FfnGeom& g, int bm) {
+    const long tk = (long)g.T * g.k;
+    const long act = tk < g.E ? tk : g.E;
+    return (int)((tk + bm - 1) / bm + act + (g.n_shared ? (g.T + bm - 1) / bm : 0));
+}
+
+int tile_rows(const FfnGeom&) { return pipe::BM; }
+
+
 ft_status launch_build_tiles(const FfnGeom& g, const int32_t* offsets,
                              const int32_t* slot_of_expert, int shared_slot, TileDesc* tiles,
                              int* n_tiles, int max_tiles, hipStream_t s) {
     build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, slot_of_expert, g.E, g.T, g.n_shared,
-                                          shared_slot, tiles, n_tiles, max_tiles);
+                                          shared_slot, tile_rows(g), tiles, n_tiles, max_tiles);
     FT_LAUNCHED("build_tiles");
     return FT_OK;
 }
@@ -377,42 +616,41 @@ ft_status launch_build_tiles(const FfnGeom& g, const int32_t* offsets,
 ft_status launch_gemm1_mfma(const FfnGeom& g, const __bf16* x, const int32_t* perm,
                             const TileDesc* tiles, const int* n_tiles, int max_tiles,
                             __bf16* h, hipStream_t s) {
-    const int n_ntiles = g.I / (BN / 2);
-    dim3 grid((unsigned)max_tiles * n_ntiles), block(NTHR);
-    if (g.w_dt == FT_MXFP4)
-        gemm1_kernel<1><<<grid, block, 0, s>>>(g, x, perm, tiles, n_tiles, n_ntiles, h);
-    else
-        gemm1_kernel<0><<<grid, block, 0, s>>>(g, x, perm, tiles, n_tiles, n_ntiles, h);
-    FT_LAUNCHED("gemm1_mfma");
+    const int mt = min(max_tiles, max_tiles_for(g, pipe::BM));
+    const int nn = cdiv(g.I, pipe::BN / 2);
+    const unsigned grid = (unsigned)(mt * nn + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+    hipError_t e = g.w_dt == FT_MXFP4
+        ? launch_pipe<MODE_GATED, 1, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
+        : launch_pipe<MODE_GATED, 0, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h);
+    if (e != hipSuccess) return set_error(FT_ERR_HIP, "gemm1: %s", hipGetErrorString(e));
     return FT_OK;
 }
 
 ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* tiles,
                             const int* n_tiles, int max_tiles, void* y, ft_dtype y_dt,
                             hipStream_t s) {
-    const int n_ntiles = cdiv(g.H, BN);
-    dim3 grid((unsigned)max_tiles * n_ntiles), block(NTHR);
-#define FT_G2(BT, OT)                                                                    \
-    gemm_plain_kernel<BT, OT, false><<<grid, block, 0, s>>>(g, h, nullptr, 0, g.H, g.I, tiles, \
-                                                            n_tiles, n_ntiles, (OT*)y)
-    if (g.w_dt == FT_MXFP4) {
-        if (y_dt == FT_F32) FT_G2(1, float); else FT_G2(1, __bf16);
-    } else {
-        if (y_dt == FT_F32) FT_G2(0, float); else FT_G2(0, __bf16);
-    }
-#undef FT_G2
-    FT_LAUNCHED("gemm2_mfma");
+    const int mt = min(max_tiles, max_tiles_for(g, pipe::BM));
+    const int nn = cdiv(g.H, pipe::BN);
+    const unsigned grid = (unsigned)(mt * nn + 7) / 8 * 8;
+    hipError_t e;
+    if (g.w_dt == FT_MXFP4)
+        e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 1, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
+                           : launch_pipe<MODE_LIST, 1, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
+    else
+        e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 0, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
+                           : launch_pipe<MODE_LIST, 0, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
+    if (e != hipSuccess) return set_error(FT_ERR_HIP, "gemm2: %s", hipGetErrorString(e));
     return FT_OK;
 }
 
 ft_status launch_dense_gemm_f32out(const void* A, const void* B, int M, int N, int K,
                                    float* out, hipStream_t s) {
     FfnGeom g{};
-    const int n_ntiles = cdiv(N, BN);
-    dim3 grid((unsigned)cdiv(M, BM) * n_ntiles), block(NTHR);
-    gemm_plain_kernel<0, float, true><<<grid, block, 0, s>>>(
-        g, (const __bf16*)A, (const __bf16*)B, M, N, K, nullptr, nullptr, n_ntiles, out);
-    FT_LAUNCHED("dense_gemm_f32out");
+    const int n_ntiles = cdiv(N, SmallTile::BN);
+    hipError_t e = launch_tile<SmallTile, MODE_DENSE, 0, float>(
+        (unsigned)cdiv(M, SmallTile::BM) * n_ntiles, s, g, (const __bf16*)A, nullptr,
+        (const __bf16*)B, M, N, K, nullptr, nullptr, n_ntiles, out);
+    if (e != hipSuccess) return set_error(FT_ERR_HIP, "router gemm: %s", hipGetErrorString(e));
     return FT_OK;
 }
 

@@ -259,10 +259,42 @@ def combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, w: torch.Tensor, n_sha
 
 
 def set_profile_events(which: int, start, stop):
-    """start/stop: torch.cuda.Event (created with enable_timing=True) or None."""
-    s = None if start is None else C.c_void_p(start.cuda_event)
-    e = None if stop is None else C.c_void_p(stop.cuda_event)
-    _check(load().ft_set_profile_events(which, s, e))
+    """start/stop: hipEvent_t handles (int or c_void_p, see HipEvents) or None."""
+    _check(load().ft_set_profile_events(which, start, stop))
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime the process already uses (for
+    ft_set_profile_events, which records them inside the library)."""
+
+    def __init__(self):
+        self.rt = C.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.made = []
+
+    def create(self) -> C.c_void_p:
+        e = C.c_void_p()
+        rc = self.rt.hipEventCreate(C.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.made.append(e)
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        self.rt.hipEventSynchronize(b)
+        f = C.c_float()
+        rc = self.rt.hipEventElapsedTime(C.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def close(self):
+        for e in self.made:
+            self.rt.hipEventDestroy(e)
+        self.made = []
 
 
 # ---------------------------------------------------------------------------
