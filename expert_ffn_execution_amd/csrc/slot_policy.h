@@ -60,37 +60,44 @@ class Policy {
         return where_[(size_t)layer * E_ + expert];
     }
 
-    // slot_of[i] receives the slot of experts[i].
+    // slot_of[i] receives the slot of experts[i].  Resident experts are touched
+    // and held first (ascending ids), then the missing ones are brought in
+    // (ascending ids), so a request never evicts one of its own experts.
     ft_status map(Engine& eng, int layer, const int32_t* experts, int n, int32_t* slot_of,
                   ft_map_stats* ms) {
         ft_status v = check_list(layer, experts, n);
         if (v != FT_OK) return v;
         refresh(eng);
-        // capacity: misses must fit in free + evictable slots of the layer's range
+        // capacity: the misses must fit in free slots plus evictable slots that hold
+        // none of the requested experts
         int need = 0;
         for (int i = 0; i < n; ++i)
             if (lookup(layer, experts[i]) < 0) ++need;
-        if (need > obtainable(layer, -1)) return FT_ERR_CAPACITY;
+        if (need > obtainable(layer, experts, n)) return FT_ERR_CAPACITY;
         ft_map_stats m{};
         m.n_demand = n;
         for (int i = 0; i < n; ++i) {
-            const int e = experts[i];
-            int s = lookup(layer, e);
-            if (s >= 0) {
-                Entry& en = slots_[s];
-                if (en.prefetched) ++m.n_prefetch_hit; else ++m.n_hit;
-                en.prefetched = false;
-            } else {
-                s = take_slot(eng, layer);
-                if (s < 0) return FT_ERR_CAPACITY;  // cannot happen after the check above
-                if (!start_copy(eng, s, layer, e)) return FT_ERR_HIP;
-                ++m.n_miss;
-                m.bytes_h2d += bytes_;
-            }
+            const int s = lookup(layer, experts[i]);
+            if (s < 0) continue;
             Entry& en = slots_[s];
+            if (en.prefetched) ++m.n_prefetch_hit; else ++m.n_hit;
+            en.prefetched = false;
             en.last = ++clock_;
             en.held = true;
             if (en.copying && !eng.compute_wait(s)) return FT_ERR_HIP;
+            slot_of[i] = s;
+        }
+        for (int i = 0; i < n; ++i) {
+            if (lookup(layer, experts[i]) >= 0) continue;
+            const int s = take_slot(eng, layer);
+            if (s < 0) return FT_ERR_CAPACITY;  // cannot happen after the check above
+            if (!start_copy(eng, s, layer, experts[i])) return FT_ERR_HIP;
+            ++m.n_miss;
+            m.bytes_h2d += bytes_;
+            Entry& en = slots_[s];
+            en.last = ++clock_;
+            en.held = true;
+            if (!eng.compute_wait(s)) return FT_ERR_HIP;
             slot_of[i] = s;
         }
         st_.maps++;
@@ -115,25 +122,26 @@ class Policy {
         return FT_OK;
     }
 
+    // Resident experts are touched first, then the missing ones are copied into
+    // free or evictable slots while any remain; held entries are never victims.
     ft_status prefetch(Engine& eng, int layer, const int32_t* experts, int n, int* n_issued) {
         ft_status v = check_list(layer, experts, n);
         if (v != FT_OK) return v;
         refresh(eng);
+        for (int i = 0; i < n; ++i) {
+            const int s = lookup(layer, experts[i]);
+            if (s >= 0) slots_[s].last = ++clock_;
+        }
         int issued = 0;
         bool short_of_room = false;
         for (int i = 0; i < n; ++i) {
-            const int e = experts[i];
-            int s = lookup(layer, e);
-            if (s >= 0) {
-                slots_[s].last = ++clock_;
-                continue;
-            }
-            s = take_slot(eng, layer);
+            if (lookup(layer, experts[i]) >= 0) continue;
+            const int s = take_slot(eng, layer, experts, n);
             if (s < 0) {
                 short_of_room = true;
-                continue;  // later experts find no room either; keep scanning for residents
+                break;
             }
-            if (!start_copy(eng, s, layer, e)) return FT_ERR_HIP;
+            if (!start_copy(eng, s, layer, experts[i])) return FT_ERR_HIP;
             Entry& en = slots_[s];
             en.prefetched = true;
             en.last = ++clock_;
@@ -202,21 +210,34 @@ class Policy {
 
     bool evictable(const Entry& en) const { return !en.held && !en.copying; }
 
-    // free + evictable slots in the layer's range
-    int obtainable(int layer, int) const {
+    bool requested(const Entry& en, int layer, const int32_t* experts, int n) const {
+        if (en.layer != layer) return false;
+        for (int i = 0; i < n; ++i)
+            if (experts[i] == en.expert) return true;
+        return false;
+    }
+
+    // free slots plus evictable slots (not holding a requested expert) in the range
+    int obtainable(int layer, const int32_t* experts, int n) const {
         int c = 0;
-        for (int s = lo(layer); s < hi(layer); ++s)
-            if (slots_[s].layer < 0 || evictable(slots_[s])) ++c;
+        for (int s = lo(layer); s < hi(layer); ++s) {
+            const Entry& en = slots_[s];
+            if (en.layer < 0 || (evictable(en) && !requested(en, layer, experts, n))) ++c;
+        }
         return c;
     }
 
-    // lowest free slot, else the least recently used evictable one
-    int take_slot(Engine&, int layer) {
+    // lowest free slot, else the least recently used evictable slot that holds
+    // none of the experts of the current request
+    int take_slot(Engine&, int layer, const int32_t* experts = nullptr, int n = 0) {
         for (int s = lo(layer); s < hi(layer); ++s)
             if (slots_[s].layer < 0) return s;
         int best = -1;
-        for (int s = lo(layer); s < hi(layer); ++s)
-            if (evictable(slots_[s]) && (best < 0 || slots_[s].last < slots_[best].last)) best = s;
+        for (int s = lo(layer); s < hi(layer); ++s) {
+            const Entry& en = slots_[s];
+            if (!evictable(en) || requested(en, layer, experts, n)) continue;
+            if (best < 0 || en.last < slots_[best].last) best = s;
+        }
         if (best >= 0) {
             drop(best);
             st_.evictions++;

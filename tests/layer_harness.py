@@ -56,28 +56,27 @@ class Layer:
 
     def host_expert(self, e: int) -> dict:
         if self.host[e] is None:
-            s = self.slot_of[e]
-            _, offs = ft.expert_layout(self.shape.wdtype, self.shape.H, self.shape.I)
-            H, I = self.shape.H, self.shape.I
-            raw = self.pool[s].cpu()
-            if self.shape.wdtype == "mxfp4":
-                self.host[e] = {
-                    "gate": raw[offs[0]:offs[0] + I * H // 2].view(I, H // 2),
-                    "up": raw[offs[1]:offs[1] + I * H // 2].view(I, H // 2),
-                    "down": raw[offs[2]:offs[2] + H * I // 2].view(H, I // 2),
-                    "gate_sc": raw[offs[3]:offs[3] + I * H // 32].view(I, H // 32),
-                    "up_sc": raw[offs[4]:offs[4] + I * H // 32].view(I, H // 32),
-                    "down_sc": raw[offs[5]:offs[5] + H * I // 32].view(H, I // 32),
-                }
-            else:
-                dt = torch.float32 if self.shape.wdtype == "f32" else torch.bfloat16
-                es = 4 if self.shape.wdtype == "f32" else 2
-                self.host[e] = {
-                    "gate": raw[offs[0]:offs[0] + I * H * es].view(dt).view(I, H),
-                    "up": raw[offs[1]:offs[1] + I * H * es].view(dt).view(I, H),
-                    "down": raw[offs[2]:offs[2] + H * I * es].view(dt).view(H, I),
-                }
+            self.host[e] = unpack_slot(self.pool[self.slot_of[e]].cpu(), self.shape)
         return self.host[e]
+
+
+def unpack_slot(raw: torch.Tensor, shape: synth.LayerShape) -> dict:
+    """Logical tensors of one expert from the bytes of its slot (the generator's
+    output as packed for the device); views into `raw`."""
+    _, offs = ft.expert_layout(shape.wdtype, shape.H, shape.I)
+    H, I = shape.H, shape.I
+    if shape.wdtype == "mxfp4":
+        return {"gate": raw[offs[0]:offs[0] + I * H // 2].view(I, H // 2),
+                "up": raw[offs[1]:offs[1] + I * H // 2].view(I, H // 2),
+                "down": raw[offs[2]:offs[2] + H * I // 2].view(H, I // 2),
+                "gate_sc": raw[offs[3]:offs[3] + I * H // 32].view(I, H // 32),
+                "up_sc": raw[offs[4]:offs[4] + I * H // 32].view(I, H // 32),
+                "down_sc": raw[offs[5]:offs[5] + H * I // 32].view(H, I // 32)}
+    dt = torch.float32 if shape.wdtype == "f32" else torch.bfloat16
+    es = 4 if shape.wdtype == "f32" else 2
+    return {"gate": raw[offs[0]:offs[0] + I * H * es].view(dt).view(I, H),
+            "up": raw[offs[1]:offs[1] + I * H * es].view(dt).view(I, H),
+            "down": raw[offs[2]:offs[2] + H * I * es].view(dt).view(H, I)}
 
 
 def run_layer(L: Layer, x: torch.Tensor, logits: torch.Tensor, bias=None, y_dtype=None,

@@ -1,0 +1,137 @@
+"""GPU tests of the expert-slot cache: layers whose experts stream from pinned
+host memory through LRU device slots must give bitwise the same outputs as the
+same layers with every expert resident, and match the oracle."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from expert_ffn_execution_amd import ftmoe as ft  # noqa: E402
+from expert_ffn_execution_amd import synth  # noqa: E402
+from expert_ffn_execution_amd.stack import SlotStack  # noqa: E402
+from tests.layer_harness import DEV, check_close, unpack_slot  # noqa: E402
+from oracle import oracle as orc  # noqa: E402
+
+SMALL = synth.LayerShape("gpu_stack_small", H=512, E=32, k=4, I=256, bias="zipf", bias_param=1.1)
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def _resident_layer(stack: SlotStack, l: int, x: torch.Tensor):
+    """Layer l with all its experts resident (same kernels, identity slots)."""
+    sh = stack.sh
+    pool = stack.host[l].to(DEV)
+    wts = ft.make_weights(sh.wdtype, sh.E, sh.H, sh.I, pool, n_shared=sh.n_shared,
+                          shared_slot=sh.E)
+    ids, w, _ = ft.route(x.shape[0], sh.E, sh.k, x=x, w_router=stack.routers[l],
+                         bias=stack.biases[l])
+    c, off, perm, inv = ft.align(ids, sh.E)
+    y = ft.ffn(wts, x, sh.k, perm, off)
+    return ft.combine(y, inv, w, n_shared=sh.n_shared), ids, w
+
+
+def _inputs(sh, L, T, step):
+    return [synth.gen_x(sh, T, step=step, device=DEV, layer=l) for l in range(L)]
+
+
+@pytest.mark.parametrize("scope", [ft.SCOPE_GLOBAL, ft.SCOPE_PER_LAYER])
+def test_decode_steps_match_resident(scope):
+    _say("slot stack decode scope", scope)
+    L = 4
+    st = SlotStack(SMALL, L, n_slots=24, scope=scope)
+    try:
+        for step in range(6):
+            xs = _inputs(SMALL, L, 2, step)
+            outs = st.forward(xs)
+            for l in range(L):
+                ref, _, _ = _resident_layer(st, l, xs[l])
+                assert torch.equal(outs[l], ref), (step, l)
+        assert st.stats.demand > 0 and st.stats.misses > 0
+        assert st.stats.hits + st.stats.prefetch_hits + st.stats.misses == st.stats.demand
+        cs = st.cache.stats()
+        assert cs.held == 0 and cs.resident <= 24
+    finally:
+        st.close()
+
+
+def test_prefill_overlap_and_warning():
+    _say("slot stack prefill")
+    L = 3
+    # two whole layers fit: whole-layer prefetch succeeds
+    st = SlotStack(SMALL, L, n_slots=2 * SMALL.E)
+    try:
+        xs = _inputs(SMALL, L, 300, 0)
+        outs = st.forward(xs, prefill=True)
+        for l in range(L):
+            ref, _, _ = _resident_layer(st, l, xs[l])
+            assert torch.equal(outs[l], ref), l
+        assert st.stats.prefetch_warnings == 0
+        assert st.stats.prefetch_hits > 0
+    finally:
+        st.close()
+    # fewer than two layers of slots: the prefetch reports overlap disabled, results unchanged
+    st = SlotStack(SMALL, L, n_slots=SMALL.E + 8)
+    try:
+        outs = st.forward(xs, prefill=True)
+        for l in range(L):
+            ref, _, _ = _resident_layer(st, l, xs[l])
+            assert torch.equal(outs[l], ref), l
+        assert st.stats.prefetch_warnings > 0
+    finally:
+        st.close()
+
+
+def test_stack_layer_matches_oracle():
+    _say("slot stack vs oracle")
+    L = 2
+    st = SlotStack(SMALL, L, n_slots=20)
+    try:
+        xs = _inputs(SMALL, L, 16, 3)
+        # oracle router logits, supplied to both sides so routing is identical by construction
+        lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
+        outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs])
+        for l in range(L):
+            ids, w = orc.route(lgs[l], SMALL.k, st.biases[l].cpu().numpy())
+            experts = [unpack_slot(st.host[l, e], SMALL) for e in range(SMALL.E)]
+            ref = orc.moe_layer(xs[l].cpu(), ids, w, experts, "bf16", SMALL.I, out_fmt="f32")
+            check_close(outs[l], ref, "bf16", f"stack layer {l}")
+    finally:
+        st.close()
+
+
+def test_pageable_pool_is_refused():
+    _say("pageable pool")
+    host = torch.empty((2, 4, 4096), dtype=torch.uint8)          # not pinned
+    slots = torch.empty((4, 4096), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ft.FtError) as ei:
+        ft.SlotCache(2, 4, 4096, host, slots)
+    assert ei.value.status == ft.ERR_NOT_PINNED
+
+
+def test_full_size_slot_stack_sampled():
+    """8 layers of the 35B-A3B layer shape, 64 slots per layer under one global
+    LRU, Zipf(1.1)-biased routers: a few decode steps and one prefill, each
+    layer's output compared with the resident computation."""
+    sh = synth.SLOT_STACK
+    L = synth.SLOT_STACK_LAYERS
+    _say("full-size slot stack")
+    st = SlotStack(sh, L, n_slots=L * synth.SLOT_STACK_SLOTS_PER_LAYER)
+    try:
+        for step in range(3):
+            xs = _inputs(sh, L, 1, step)
+            outs = st.forward(xs)
+            l = step % L
+            ref, _, _ = _resident_layer(st, l, xs[l])
+            assert torch.equal(outs[l], ref)
+        xs = _inputs(sh, L, 2048, 100)
+        outs = st.forward(xs, prefill=True)
+        for l in (0, L - 1):
+            ref, _, _ = _resident_layer(st, l, xs[l])
+            assert torch.equal(outs[l], ref)
+        assert st.stats.prefetch_warnings == 0
+        _say("  hit rate", st.stats.hit_rate, "demand", st.stats.demand)
+    finally:
+        st.close()

@@ -1,0 +1,302 @@
+"""CPU tests of the expert-slot cache policy (LRU over (layer, expert) keys).
+
+The C++ policy (expert_ffn_execution_amd/csrc/slot_policy.h) runs behind a
+small shim with a mock copy engine; its decisions are compared with an
+independent textbook LRU model written here with an OrderedDict.
+"""
+import ctypes as C
+import os
+import subprocess
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "native", "policy_shim.cpp")
+LIB = os.path.join(HERE, "native", "_build", "libpolicy_shim.so")
+
+OK, INVALID, CAPACITY, BUSY, HIP, WARN = 0, 1, 3, 5, 6, 100
+GLOBAL, PER_LAYER = 0, 1
+
+
+def build_shim():
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-Wall",
+                    f"-I{os.path.join(ROOT, 'include')}", SRC, "-o", LIB], check=True)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(
+            os.path.getmtime(SRC),
+            os.path.getmtime(os.path.join(ROOT, "expert_ffn_execution_amd", "csrc", "slot_policy.h"))):
+        build_shim()
+    L = C.CDLL(LIB)
+    P = C.c_void_p
+    L.pol_create.restype = P
+    L.pol_create.argtypes = [C.c_int] * 4
+    for f in ("pol_destroy", "pol_complete_all", "pol_fail_next_copy"):
+        getattr(L, f).argtypes = [P]
+    L.pol_map.argtypes = [P, C.c_int, P, C.c_int, P, P]
+    L.pol_release.argtypes = [P, C.c_int]
+    L.pol_prefetch.argtypes = [P, C.c_int, P, C.c_int, P]
+    L.pol_evict.argtypes = [P, C.c_int, C.c_int]
+    L.pol_lookup.argtypes = [P, C.c_int, C.c_int]
+    L.pol_set_auto_complete.argtypes = [P, C.c_int]
+    L.pol_log.argtypes = [P, P, C.c_int]
+    L.pol_stats.argtypes = [P, P]
+    return L
+
+
+class Cache:
+    def __init__(self, lib, L, E, S, scope=GLOBAL):
+        self.lib, self.h = lib, lib.pol_create(L, E, S, scope)
+
+    def __del__(self):
+        self.lib.pol_destroy(self.h)
+
+    def map(self, layer, experts):
+        arr = (C.c_int * max(1, len(experts)))(*experts)
+        slots = (C.c_int * max(1, len(experts)))()
+        st = (C.c_int * 4)()
+        r = self.lib.pol_map(self.h, layer, arr, len(experts), slots, st)
+        return r, list(slots)[:len(experts)], list(st)
+
+    def prefetch(self, layer, experts):
+        arr = (C.c_int * max(1, len(experts)))(*experts)
+        got = C.c_int()
+        r = self.lib.pol_prefetch(self.h, layer, arr, len(experts), C.byref(got))
+        return r, got.value
+
+    def release(self, layer):
+        return self.lib.pol_release(self.h, layer)
+
+    def evict(self, layer, expert=-1):
+        return self.lib.pol_evict(self.h, layer, expert)
+
+    def lookup(self, layer, expert):
+        return self.lib.pol_lookup(self.h, layer, expert)
+
+    def log(self):
+        buf = (C.c_int * 65536)()
+        n = self.lib.pol_log(self.h, buf, 65536)
+        v = list(buf)[:n]
+        return [tuple(v[i:i + 4]) for i in range(0, n, 4)]
+
+    def stats(self):
+        out = (C.c_longlong * 12)()
+        self.lib.pol_stats(self.h, out)
+        keys = ["maps", "demand", "hits", "prefetch_hits", "misses", "prefetch_issued",
+                "evictions", "bytes_h2d", "resident", "held", "in_flight", "n_slots"]
+        return dict(zip(keys, list(out)))
+
+
+class RefLRU:
+    """Textbook LRU over (layer, expert) keys: free slots are filled lowest first;
+    otherwise the least recently used key that is neither held nor part of the
+    current request is evicted.  A request touches its resident keys first, then
+    brings in its missing keys, each in ascending expert order."""
+
+    def __init__(self, L, E, S, scope=GLOBAL):
+        self.S, self.L, self.scope = S, L, scope
+        self.slot_of = {}                 # key -> slot
+        self.key_at = [None] * S
+        self.lru = OrderedDict()          # key -> None, least recent first
+        self.held = set()
+
+    def _range(self, layer):
+        if self.scope == PER_LAYER:
+            w = self.S // self.L
+            return range(layer * w, (layer + 1) * w)
+        return range(self.S)
+
+    def _victim(self, layer, request):
+        rng = self._range(layer)
+        for s in rng:
+            if self.key_at[s] is None:
+                return s
+        for key in self.lru:
+            s = self.slot_of[key]
+            if s in rng and key not in self.held and key not in request:
+                return s
+        return None
+
+    def _place(self, key, s):
+        old = self.key_at[s]
+        if old is not None:
+            del self.slot_of[old]
+            del self.lru[old]
+        self.key_at[s] = key
+        self.slot_of[key] = s
+        self.lru[key] = None
+
+    def map(self, layer, experts):
+        req = {(layer, e) for e in experts}
+        missing = [e for e in experts if (layer, e) not in self.slot_of]
+        rng = self._range(layer)
+        room = sum(1 for s in rng if self.key_at[s] is None or
+                   (self.key_at[s] not in self.held and self.key_at[s] not in req))
+        if len(missing) > room:
+            return CAPACITY, None
+        for e in experts:
+            if (layer, e) in self.slot_of:
+                self.lru.move_to_end((layer, e))
+                self.held.add((layer, e))
+        copies = []
+        for e in missing:
+            s = self._victim(layer, req)
+            self._place((layer, e), s)
+            self.held.add((layer, e))
+            copies.append((s, layer, e))
+        return OK, ([self.slot_of[(layer, e)] for e in experts], copies)
+
+    def prefetch(self, layer, experts):
+        req = {(layer, e) for e in experts}
+        for e in experts:
+            if (layer, e) in self.slot_of:
+                self.lru.move_to_end((layer, e))
+        copies = []
+        for e in experts:
+            if (layer, e) in self.slot_of:
+                continue
+            s = self._victim(layer, req)
+            if s is None:
+                return WARN, copies
+            self._place((layer, e), s)
+            copies.append((s, layer, e))
+        return OK, copies
+
+    def release(self, layer):
+        self.held = {k for k in self.held if k[0] != layer}
+
+
+def _copies(log):
+    return [(s, l, e) for kind, s, l, e in log if kind == 0]
+
+
+@pytest.mark.parametrize("scope", [GLOBAL, PER_LAYER])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_matches_textbook_lru(lib, scope, seed):
+    L, E, S = 4, 16, 24 if scope == GLOBAL else 24
+    rng = np.random.default_rng(seed)
+    c, ref = Cache(lib, L, E, S, scope), RefLRU(L, E, S, scope)
+    skew = np.exp(-1.1 * np.log(np.arange(1, E + 1)))
+    skew /= skew.sum()
+    for step in range(200):
+        layer = step % L
+        n = int(rng.integers(1, 6))
+        experts = sorted(set(rng.choice(E, size=n, p=skew).tolist()))
+        r, slots, _ = c.map(layer, experts)
+        rr, payload = ref.map(layer, experts)
+        assert r == rr, (step, r, rr)
+        if r == OK:
+            ref_slots, ref_copies = payload
+            assert slots == ref_slots, step
+            assert _copies(c.log()) == ref_copies, step
+        nxt = (layer + 1) % L
+        pf = sorted(set(rng.choice(E, size=int(rng.integers(0, 4)), p=skew).tolist()))
+        r1, _ = c.prefetch(nxt, pf)
+        r2, ref_copies = ref.prefetch(nxt, pf)
+        assert r1 == r2 and _copies(c.log()) == ref_copies, step
+        assert c.release(layer) == OK
+        ref.release(layer)
+        for l2 in range(L):
+            for e in range(E):
+                assert c.lookup(l2, e) == ref.slot_of.get((l2, e), -1)
+
+
+def test_held_slots_are_never_evicted(lib):
+    c = Cache(lib, 2, 8, 6)
+    assert c.map(0, [0, 1, 2, 3])[0] == OK           # held until release
+    r, issued = c.prefetch(1, [0, 1, 2, 3, 4])      # only 2 free slots
+    assert r == WARN and issued == 2
+    for e in range(4):
+        assert c.lookup(0, e) >= 0
+    assert c.map(1, [0, 1, 2])[0] == CAPACITY        # 2 prefetched + 1 more > room
+    c.release(0)
+    r, slots, st = c.map(1, [0, 1, 2])
+    assert r == OK and st == [3, 0, 2, 1]             # 2 prefetch hits, 1 miss
+
+
+def test_capacity_error_changes_nothing(lib):
+    c = Cache(lib, 1, 16, 4)
+    assert c.map(0, [0, 1, 2, 3])[0] == OK
+    c.log()
+    before = [c.lookup(0, e) for e in range(16)]
+    assert c.map(0, [0, 1, 2, 3, 4])[0] == CAPACITY
+    assert [c.lookup(0, e) for e in range(16)] == before
+    assert c.log() == []
+
+
+def test_request_never_evicts_its_own_experts(lib):
+    c = Cache(lib, 1, 8, 2)
+    assert c.map(0, [1])[0] == OK
+    c.release(0)
+    assert c.map(0, [2])[0] == OK
+    c.release(0)
+    # expert 1 is the LRU entry; a request for [0, 1] must keep 1 and evict 2
+    r, slots, st = c.map(0, [0, 1])
+    assert r == OK and st == [2, 1, 0, 1]
+    assert c.lookup(0, 1) >= 0 and c.lookup(0, 2) == -1
+
+
+def test_in_flight_and_held_entries_are_busy(lib):
+    c = Cache(lib, 2, 8, 8)
+    lib.pol_set_auto_complete(c.h, 0)
+    assert c.prefetch(1, [3])[0] == OK
+    assert c.evict(1, 3) == BUSY                     # copy in flight
+    lib.pol_complete_all(c.h)
+    assert c.evict(1, 3) == OK and c.lookup(1, 3) == -1
+    lib.pol_set_auto_complete(c.h, 1)
+    assert c.map(0, [5])[0] == OK
+    assert c.evict(0, 5) == BUSY and c.evict(0) == BUSY
+    c.release(0)
+    assert c.evict(0) == OK and c.lookup(0, 5) == -1
+
+
+def test_in_flight_entries_are_not_victims(lib):
+    c = Cache(lib, 2, 8, 3)
+    lib.pol_set_auto_complete(c.h, 0)
+    assert c.prefetch(1, [0, 1, 2]) == (OK, 3)
+    assert c.prefetch(0, [4]) == (WARN, 0)           # everything in flight
+    lib.pol_complete_all(c.h)
+    assert c.prefetch(0, [4]) == (OK, 1)
+
+
+def test_map_waits_for_in_flight_copies(lib):
+    c = Cache(lib, 1, 8, 4)
+    lib.pol_set_auto_complete(c.h, 0)
+    c.prefetch(0, [2])
+    c.log()
+    r, slots, st = c.map(0, [2])
+    assert r == OK and st == [1, 0, 1, 0]
+    assert (1, slots[0], -1, -1) in c.log()          # compute waits on the fill
+
+
+def test_release_records_last_reader_and_copy_failure_retries(lib):
+    c = Cache(lib, 1, 8, 4)
+    assert c.map(0, [1, 2])[0] == OK
+    c.log()
+    c.release(0)
+    assert sorted(e[1] for e in c.log() if e[0] == 2) == sorted([c.lookup(0, 1), c.lookup(0, 2)])
+    lib.pol_fail_next_copy(c.h)
+    assert c.map(0, [5])[0] == HIP
+    assert c.lookup(0, 5) == -1                      # not marked resident
+    r, _, st = c.map(0, [5])                         # the next map copies again
+    assert r == OK and st[3] == 1
+
+
+def test_stats_and_invalid_lists(lib):
+    c = Cache(lib, 2, 8, 8)
+    assert c.map(0, [3, 1])[0] == INVALID             # not ascending
+    assert c.map(0, [1, 1])[0] == INVALID             # duplicate
+    assert c.map(2, [1])[0] == INVALID                # bad layer
+    assert c.map(0, [8])[0] == INVALID                # bad expert
+    c.map(0, [1, 2])
+    c.release(0)
+    c.map(0, [1, 3])
+    s = c.stats()
+    assert s["maps"] == 2 and s["demand"] == 4 and s["hits"] == 1 and s["misses"] == 3
+    assert s["bytes_h2d"] == 3 * 1000 and s["resident"] == 3 and s["held"] == 2
