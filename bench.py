@@ -27,10 +27,86 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
+CAL_BYTES = 1 << 30            # calibration copy
+GEMM_SRC = os.path.join(ROOT, "expert_ffn_execution_amd", "csrc", "gemm_mfma.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm1_35b_a3b_prefill_traffic.json")
+GEMM1_KERNEL = "gemm_pipe_kernelILi0ELi0E"   # gate/up GEMM, bf16 weights
+
+
+def _sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per gate/up GEMM launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != _sha(GEMM_SRC):
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark -> the
+    committed traffic summary.  Counters are KiB per dispatch; each is scaled by
+    its reading for the 1 GiB calibration copy."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        cal = [float(r["Counter_Value"]) for r in rows
+               if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
+        cal = max(cal) if cal else float("nan")
+        g1 = [float(r["Counter_Value"]) for r in rows if GEMM1_KERNEL in r["Kernel_Name"]]
+        return cal, (sum(g1) / len(g1) if g1 else float("nan")), len(g1)
+
+    fc, fg, nf = read(fetch_dir, "FETCH_SIZE")
+    wc, wg, nw = read(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = CAL_BYTES / (fc * 1024.0), CAL_BYTES / (wc * 1024.0)
+    out = {"source_sha256": _sha(GEMM_SRC), "kernel": GEMM1_KERNEL,
+           "calibration_copy_bytes": CAL_BYTES,
+           "fetch_kib_calibration": fc, "write_kib_calibration": wc,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_kib_per_launch": fg, "write_kib_per_launch": wg, "launches": [nf, nw],
+           "fetch_bytes_per_launch": fg * 1024.0 * f_scale,
+           "write_bytes_per_launch": wg * 1024.0 * w_scale}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def summarize_stats(stats_csv, command, out_md, top=16):
+    """rocprofv3 --kernel-trace --stats kernel_stats.csv -> a short markdown table."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {os.path.basename(out_md)[:-3]}", "", "Command (from the repository root):", "",
+             "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "COMMAND", "OUT_MD"),
+                    help="format a rocprofv3 kernel_stats.csv as a markdown summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -40,7 +116,8 @@ def parse():
                                                  "(default: workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs")
     return ap.parse_args()
 
 
@@ -205,6 +282,114 @@ def cpu_baseline(sh, bank, T, dev, seconds):
                       f"{t:.1f} s"}
 
 
+def h2d_peak_gbs(dev, nbytes=1 << 30):
+    """Measured pinned host -> device copy rate (the slot cache's copy path)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    best = 0.0
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            a.record()
+            dst.copy_(src, non_blocking=True)
+            b.record()
+        b.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    return best
+
+
+def run_slot_stack(args):
+    """8 layers of the 35B-A3B layer shape behind a 512-slot global LRU over a
+    pinned host pool: decode T=1 steps, then one prefill, each timed against
+    the same layers fully resident in HBM."""
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+    from expert_ffn_execution_amd.stack import SlotStack
+
+    dev = "cuda:0"
+    sh = synth.SLOT_STACK
+    L = synth.SLOT_STACK_LAYERS
+    steps = synth.SLOT_STACK_DECODE_STEPS
+    T_pre = max(synth.POINTS[sh.name])
+    peak = h2d_peak_gbs(dev)
+    log(f"pinned H2D peak {peak:.1f} GB/s")
+    st = SlotStack(sh, L, n_slots=L * synth.SLOT_STACK_SLOTS_PER_LAYER)
+    resident = [st.host[l].to(dev) for l in range(L)]
+    rwts = [ft.make_weights(sh.wdtype, sh.E, sh.H, sh.I, p) for p in resident]
+
+    def resident_pass(xs):
+        outs = []
+        for l in range(L):
+            ids, w, _ = ft.route(xs[l].shape[0], sh.E, sh.k, x=xs[l], w_router=st.routers[l],
+                                 bias=st.biases[l])
+            c, off, perm, inv = ft.align(ids, sh.E)
+            y = ft.ffn(rwts[l], xs[l], sh.k, perm, off)
+            outs.append(ft.combine(y, inv, w))
+        return outs
+
+    def timed(fn, batches):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for xs in batches:
+            fn(xs)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    dec = [[synth.gen_x(sh, 1, step=s, device=dev, layer=l) for l in range(L)]
+           for s in range(steps)]
+    warm = [[synth.gen_x(sh, 1, step=10_000 + s, device=dev, layer=l) for l in range(L)]
+            for s in range(args.warmup)]
+    timed(resident_pass, warm)
+    t_res = timed(resident_pass, dec)
+    timed(st.forward, warm)
+    s0 = dataclasses_replace(st.stats)
+    t_dec = timed(st.forward, dec)
+    d = {k: getattr(st.stats, k) - getattr(s0, k) for k in
+         ("demand", "hits", "prefetch_hits", "misses", "bytes_h2d")}
+    pre = [synth.gen_x(sh, T_pre, step=20_000, device=dev, layer=l) for l in range(L)]
+    t_res_pre = timed(resident_pass, [pre])
+    s1 = dataclasses_replace(st.stats)
+    t_pre = timed(lambda xs: st.forward(xs, prefill=True), [pre])
+    pre_bytes = st.stats.bytes_h2d - s1.bytes_h2d
+    st.close()
+    h2d_gbs = d["bytes_h2d"] / t_dec / 1e9
+    line = {
+        "metric": "MoE-layer tokens/s through a slot-cached layer stack (decode T=1)",
+        "value": steps * L / t_dec, "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": t_dec / steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": sh.wdtype, "data": "synthetic",
+        "config": {"workload": f"{sh.name}: {L} layers H{sh.H} E{sh.E} k{sh.k} I{sh.I}, "
+                               f"{L * synth.SLOT_STACK_SLOTS_PER_LAYER} slots global LRU, "
+                               f"Zipf({sh.bias_param}) router bias, pinned host pool",
+                   "decode_tokens": 1, "decode_steps": steps, "prefill_tokens": T_pre},
+        "roofline": {"bound": "h2d", "achieved": h2d_gbs, "peak": peak, "unit": "GB/s",
+                     "frac": h2d_gbs / peak, "traffic": None,
+                     "kernel": "expert copies host->device (hipMemcpyAsync, copy stream)"},
+        "slot_cache": {
+            "demand": d["demand"], "hit_rate": d["hits"] / max(1, d["demand"]),
+            "prefetch_hit_rate": d["prefetch_hits"] / max(1, d["demand"]),
+            "misses": d["misses"], "h2d_bytes_decode": d["bytes_h2d"],
+            "decode_ms_per_step": t_dec / steps * 1e3,
+            "resident_decode_ms_per_step": t_res / steps * 1e3,
+            "exposed_stall_ms_per_step": (t_dec - t_res) / steps * 1e3,
+            "prefill_ms": t_pre * 1e3, "resident_prefill_ms": t_res_pre * 1e3,
+            "prefill_h2d_bytes": pre_bytes,
+            "prefill_h2d_gbs": pre_bytes / t_pre / 1e9,
+            "prefill_tokens_per_s": T_pre / t_pre,
+            "prefetch_warnings": st.stats.prefetch_warnings,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+def dataclasses_replace(obj):
+    import dataclasses
+    return dataclasses.replace(obj)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -215,9 +400,23 @@ def main():
     from expert_ffn_execution_amd import ftmoe as ft
     from expert_ffn_execution_amd import synth
 
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
     ft.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    # a plain device copy of known size (1 GiB), outside every timed region: under
+    # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the counters
+    cal = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
+    torch.empty_like(cal).copy_(cal)
+    del cal
+    if args.workload == synth.SLOT_STACK.name:
+        run_slot_stack(args)
+        return
     sh = synth.SHAPES[args.workload]
     pts = synth.POINTS[sh.name]
     T_pre = args.tokens or max(pts)
@@ -260,7 +459,9 @@ def main():
                    "activations": "bf16", "weight_banks": n_banks},
         "roofline": {"bound": "mfma", "achieved": head["gemm1_tflops"],
                      "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": head["gemm1_tflops"] / MFMA_BF16_PEAK_TFS, "traffic": None,
+                     "frac": head["gemm1_tflops"] / MFMA_BF16_PEAK_TFS,
+                     "traffic": stored_traffic() if sh.name == "35b_a3b_bf16" and T_pre == 4096
+                     else None,
                      "kernel": "gate/up grouped GEMM + SwiGLU (gemm1)",
                      "gemm1_us": head["gemm1_ms"] * 1e3, "gemm2_us": head["gemm2_ms"] * 1e3,
                      "ffn_tflops": head["ffn_tflops"]},
