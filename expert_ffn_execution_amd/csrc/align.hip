@@ -101,7 +101,7 @@ __global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __r
 //   2) per-expert exclusive scan over units, counts[e]
 //   3) per-unit scatter from offsets[e] + hist[u][e]
 // ---------------------------------------------------------------------------
-constexpr int UNIT = 128;
+constexpr int UNIT = 64;
 
 __global__ __launch_bounds__(256) void unit_hist_kernel(const int32_t* __restrict__ ids, int n,
                                                         int E, int U, int* __restrict__ hist) {

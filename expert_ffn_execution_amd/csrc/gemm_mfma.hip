@@ -71,7 +71,8 @@ struct TileCfg {
     static constexpr int B_MX = BN * 2 / NT;   // (row, half) MXFP4 units per thread
     static constexpr size_t LDS = (size_t)2 * (BM + BN) * BK * 2;
 };
-using SmallTile = TileCfg<128, 128, 64, 64, 2>;
+// the router logits (N = E is small) use 64 x 64 tiles to spread over more CUs
+using RouterTile = TileCfg<64, 64, 32, 32, 4>;
 
 enum { MODE_GATED = 0, MODE_LIST = 1, MODE_DENSE = 2 };
 
@@ -326,11 +327,12 @@ __device__ __forceinline__ int sw(int r, int c) { return r * ROWB + ((c ^ ((r >>
 
 #define FT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8)
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vm_lgkm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 __device__ __forceinline__ bf16x8_t fp4_frag(uint32_t codes, uint32_t X) {
@@ -437,29 +439,23 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
 
     constexpr int LPS = loads_per_slice<BT>();
     const int nk = K / KS;
-#pragma unroll
-    for (int q = 0; q < STAGES - 1; ++q)
-        if (q < nk) issue(q, q);
     const int l32 = lane & 31, hi = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        // slice kt has landed once at most `ahead` later slices are outstanding
-        const int ahead = min(STAGES - 2, nk - 1 - kt);
-        if (ahead >= 3) wait_vmcnt<3 * LPS>();
-        else if (ahead == 2) wait_vmcnt<2 * LPS>();
-        else if (ahead == 1) wait_vmcnt<LPS>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + STAGES - 1 < nk) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
-        const unsigned char* st = smem + (kt % STAGES) * stage_bytes<BT>();
+
+    // Fragments of one slice (both 16-deep k-steps): the wave reads slice k+1's
+    // fragments from LDS while its MFMAs consume slice k's from registers.
+    struct Frags {
+        bf16x8_t a[2][MT], b[2][NTL];
+    };
+    auto load_frags = [&](int stage, Frags& F) {
+        const unsigned char* st = smem + stage * stage_bytes<BT>();
         const unsigned char* Bc = st + A_BYTES;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             // 32x32x16 operands: lane holds row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7
             const int ch = 2 * kk + hi;
-            bf16x8_t a[MT], b[NTL];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                a[m] = *reinterpret_cast<const bf16x8_t*>(st + sw(wm * WM + m * 32 + l32, ch));
+                F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(wm * WM + m * 32 + l32, ch));
 #pragma unroll
             for (int n = 0; n < NTL; ++n) {
                 int brow;
@@ -469,17 +465,65 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
                     brow = wn * WN + n * 32;
                 const int row = brow + l32;
                 if constexpr (BT == 0) {
-                    b[n] = *reinterpret_cast<const bf16x8_t*>(Bc + sw(row, ch));
+                    F.b[kk][n] = *reinterpret_cast<const bf16x8_t*>(Bc + sw(row, ch));
                 } else {
                     const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bc + row * 16 + ch * 4);
-                    b[n] = fp4_frag(codes, Bc[BN * 16 + row * 4]);
+                    F.b[kk][n] = fp4_frag(codes, Bc[BN * 16 + row * 4]);
                 }
             }
+        }
+    };
+    auto mfmas = [&](const Frags& F) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int n = 0; n < NTL; ++n) acc[m][n] = mfma32(a[m], b[n], acc[m][n]);
+                for (int n = 0; n < NTL; ++n) acc[m][n] = mfma32(F.a[kk][m], F.b[kk][n], acc[m][n]);
+    };
+    // wait until a slice has landed (`later` slices issued after it may stay in
+    // flight) and this wave's LDS reads are done, then meet the other waves
+    auto wait_slice = [&](int later) {
+        if (later >= 4) wait_vm_lgkm<4 * LPS>();
+        else if (later == 3) wait_vm_lgkm<3 * LPS>();
+        else if (later == 2) wait_vm_lgkm<2 * LPS>();
+        else if (later == 1) wait_vm_lgkm<LPS>();
+        else wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+    };
+    // One iteration: make slice kt+1 visible, refill the stage slice kt came from
+    // (all waves read it one iteration ago) with slice kt+STAGES, read slice kt+1's
+    // fragments into `nxt`, and run slice kt's MFMAs from `cur`.
+    // The fragment reads are unconditional so that the compiler's LDS wait lands
+    // before the next iteration's MFMAs, not before these: on the last slice they
+    // read a stage no copy targets any more (every copy has been waited for) and the
+    // values are not used.
+    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+        if (kt + 1 < nk) {
+            wait_slice(min(STAGES - 2, nk - 2 - kt));
+            if (kt + STAGES < nk) issue(kt % STAGES, kt + STAGES);
         }
+        load_frags((kt + 1) % STAGES, nxt);
+        mfmas(cur);
+        // interleave: one MFMA, one LDS read, ... so the reads hide under the MFMAs
+#pragma unroll
+        for (int i = 0; i < 2 * (MT + NTL); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * MT * NTL - 2 * (MT + NTL), 0);
+    };
+
+    // prologue: all stages in flight, slice 0 read into registers
+#pragma unroll
+    for (int q = 0; q < STAGES; ++q)
+        if (q < nk) issue(q, q);
+    Frags F0, F1;
+    wait_slice(min(STAGES - 1, nk - 1));
+    load_frags(0, F0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, F0, F1);
+        if (kt + 1 < nk) step(kt + 1, F1, F0);
     }
 
     // epilogue: register q of a 32 x 32 tile is row 8 (q / 4) + 4 (lane / 32) + q % 4,
@@ -646,9 +690,9 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
 ft_status launch_dense_gemm_f32out(const void* A, const void* B, int M, int N, int K,
                                    float* out, hipStream_t s) {
     FfnGeom g{};
-    const int n_ntiles = cdiv(N, SmallTile::BN);
-    hipError_t e = launch_tile<SmallTile, MODE_DENSE, 0, float>(
-        (unsigned)cdiv(M, SmallTile::BM) * n_ntiles, s, g, (const __bf16*)A, nullptr,
+    const int n_ntiles = cdiv(N, RouterTile::BN);
+    hipError_t e = launch_tile<RouterTile, MODE_DENSE, 0, float>(
+        (unsigned)cdiv(M, RouterTile::BM) * n_ntiles, s, g, (const __bf16*)A, nullptr,
         (const __bf16*)B, M, N, K, nullptr, nullptr, n_ntiles, out);
     if (e != hipSuccess) return set_error(FT_ERR_HIP, "router gemm: %s", hipGetErrorString(e));
     return FT_OK;
