@@ -5,21 +5,42 @@
 // read of the active experts (the pages make the same point one level up:
 // time goes to moving expert weights, not to arithmetic -- chenxutan.com
 // article, "瓶颈为什么是带宽而不是容量").  These kernels therefore stream
-// weights with 16-byte loads, every lane of a wavefront reading consecutive
-// chunks of one weight row, and keep the routed tokens' activations in LDS.
+// weights with 16-byte loads and keep the routed tokens' activations in LDS.
 // They use vector ALU dot products (v_dot2_f32_bf16 for bf16; MXFP4 codes are
 // decoded exactly to bf16 first), not MFMA: the work per byte is too small for
 // a matrix tile to pay off.
 //
-// Grid: (active expert j, block of weight rows).  A block finds the j-th
-// expert with routed tokens (and a slot) from `offsets` by wave ballots, so
-// no host round trip is needed; blocks beyond the active count exit.
+// Streaming.  HBM stays busy only if every CU keeps enough bytes in flight,
+// and the cross-lane sums at the end of each row must stay cheap.  A weight
+// row is therefore read by a segment of LPR = 8, 16, 32 or 64 lanes (the
+// fewest that cover the row in at most QMAX 16-byte loads per lane), so each
+// load instruction reads 64/LPR rows, LPR*16 contiguous bytes of each, and
+// every lane accumulates only its own row's products (one float per token
+// and matrix).  An "item" is the 64/LPR rows of one such instruction group
+// (or, for rows longer than 64*QMAX chunks, one pass over part of a row).
+// The next item's loads are issued before the current item is multiplied
+// (two register buffers), so a wave always has one item in flight while it
+// computes.  A finished item's per-token sums are reduced over the segment
+// with a butterfly that halves the token slots at each DPP exchange inside
+// a 16-lane row, so R tokens cost about R exchanges rather than R full
+// reductions.
+//
+// Grid: (group, block of weight rows), where a group is one expert and a
+// chunk of at most RCAP of its token rows (their activations fill LDS).  A
+// block finds its group from `offsets` with a wavefront scan, so no host
+// round trip is needed; the host sizes the grid for the most groups T*k
+// routed rows can make, and blocks past the last group exit.  An expert with
+// more rows than RCAP (the shared expert sees all T) is split over several
+// groups that run side by side and re-read its weights from cache.
 #include "common.h"
 #include "gemm_mfma.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace {
+
+constexpr int NWAVE = 4;  // wavefronts per block
 
 // WT: 0 = fp32 weights (fp32 activations), 1 = bf16, 2 = MXFP4 (bf16 activations)
 template <int WT> struct W;
@@ -27,282 +48,470 @@ template <> struct W<0> { static constexpr int EPC = 4; };   // elements per 16 
 template <> struct W<1> { static constexpr int EPC = 8; };
 template <> struct W<2> { static constexpr int EPC = 32; };
 
-// j-th expert (in id order) with rows and a slot; -1 if fewer than j+1.
-__device__ int find_active(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of,
-                           int E, int j, int lane) {
-    int seen = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        bool act = false;
-        if (e < E) act = offsets[e + 1] > offsets[e] && (!slot_of || slot_of[e] >= 0);
-        const uint64_t m = __ballot(act);
-        const int pc = __popcll(m);
-        if (j < seen + pc) {
-            uint64_t mm = m;
-            for (int q = 0; q < j - seen; ++q) mm &= mm - 1;
-            return e0 + __builtin_ctzll(mm);
-        }
-        seen += pc;
-    }
-    return -1;
+// How a wavefront walks one weight matrix [N][K] of 16-byte chunks.
+struct Walk {
+    int nch;  // chunks per row
+    int LPR;  // lanes per row segment: 8, 16, 32 or 64
+    int Q;    // loads per lane and matrix in one item (<= QMAX)
+    int P;    // passes per row (P > 1 only with LPR == 64 and Q == QMAX)
+    int CPP;  // chunks per pass (== nch when P == 1)
+};
+
+// Everything a streaming launch needs (passed by value).
+struct StreamArgs {
+    const uint8_t* pool;
+    size_t slot_stride;
+    size_t moff[2], soff[2];  // matrix / scale byte offsets inside a slot
+    const int32_t* offsets;
+    const int32_t* perm;  // gate/up: source token = perm[p] / k; null for down
+    const int32_t* slot_of;
+    int E, T, k, shared_slot, n_routed_groups;
+    int N, K;  // weight rows, row length in elements
+    Walk wk;
+    int RPB, NB, RCAP;
+    const void* src;  // x (gate/up) or h (down)
+    void* dst;        // h (gate/up) or y (down)
+};
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts inside each row of 16
+// lanes, then row broadcasts carry the row totals forward.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 -> rows 2, 3
+    return v;
 }
 
-// Multiply-accumulate one 16-byte weight chunk with the matching activation
-// chunk held in LDS.  xs points at the chunk's first element (bf16 or fp32).
-template <int WT>
-__device__ __forceinline__ float chunk_dot(u32x4_t wv, uint32_t sc, const void* xs, float acc) {
+// Group j of the routed experts -> (expert e, token chunk c).  Experts with
+// rows and a slot contribute ceil(rows / RCAP) groups each, in id order; the
+// loads for 256 experts are issued together, then a wavefront scan places j.
+// Returns false when j is past the last group.
+// The expert's row range [lo, hi) and slot come back from the scan's own
+// registers, so the block's first weight address needs no further load.
+struct Group { int e, c, lo, hi, slot; };
+__device__ bool find_group(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of,
+                           int E, int RCAP, int j, int lane, Group& g) {
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 256) {
+        int nc[4], lo[4], hi[4], sl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = e0 + 64 * i + lane;
+            lo[i] = hi[i] = 0;
+            sl[i] = e;
+            if (e < E) {
+                lo[i] = offsets[e];
+                hi[i] = offsets[e + 1];
+                if (slot_of) sl[i] = slot_of[e];
+            }
+            nc[i] = hi[i] > lo[i] && sl[i] >= 0 ? (hi[i] - lo[i] + RCAP - 1) / RCAP : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int incl = wave_scan_incl(nc[i]);
+            const int total = __shfl(incl, 63, 64);
+            if (j < base + total) {
+                const uint64_t m = __ballot(j < base + incl);
+                const int l = __builtin_ctzll(m);
+                g.e = e0 + 64 * i + l;
+                g.c = j - base - __shfl(incl - nc[i], l, 64);
+                g.lo = __shfl(lo[i], l, 64);
+                g.hi = __shfl(hi[i], l, 64);
+                g.slot = __shfl(sl[i], l, 64);
+                return g.e < E;
+            }
+            base += total;
+        }
+    }
+    return false;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// One butterfly exchange with the lane that DPP control CTRL pairs with this
+// one (the pair differs in lane bit BIT).  With N >= 2 slots the upper half
+// of the slots goes to the lane whose bit is 0 and the lower half to the
+// other; each lane keeps N/2 slots, summed over the pair.  With N == 1 the
+// pair's values are simply added.
+template <int CTRL, int BIT, int N, int NM, int RP>
+__device__ __forceinline__ void bstep(float (&v)[NM][RP], int lane) {
+    if constexpr (N >= 2) {
+        const bool up = (lane >> BIT) & 1;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const float lo = v[m][i], hi = v[m][i + N / 2];
+                v[m][i] = (up ? hi : lo) + dpp_f<CTRL>(up ? lo : hi);
+            }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) v[m][0] += dpp_f<CTRL>(v[m][0]);
+    }
+}
+
+// Sum v[m][r] over each LPR-lane segment.  Afterwards v[m][0] of lane l holds
+// the segment's sum for token slot seg_slot<RP, LPR>(l); RP is a power of two
+// <= 16 (<= 8 when LPR == 8).  Exchanges: row_mirror (bit 3), row_half_mirror
+// (bit 2), quad_perm [2,3,0,1] (bit 1), quad_perm [1,0,3,2] (bit 0); each
+// pairs lanes that hold the same slots so far.  Segments of 32 and 64 lanes
+// finish with cross-row swaps.
+template <int LPR, int NM, int RP>
+__device__ __forceinline__ void seg_reduce(float (&v)[NM][RP], int lane) {
+    constexpr int R1 = RP / 2 > 0 ? RP / 2 : 1, R2 = RP / 4 > 0 ? RP / 4 : 1;
+    constexpr int R3 = RP / 8 > 0 ? RP / 8 : 1;
+    if constexpr (LPR >= 16) {
+        bstep<0x140, 3, RP, NM, RP>(v, lane);
+        bstep<0x141, 2, R1, NM, RP>(v, lane);
+        bstep<0x4E, 1, R2, NM, RP>(v, lane);
+        bstep<0xB1, 0, R3, NM, RP>(v, lane);
+    } else {
+        bstep<0x141, 2, RP, NM, RP>(v, lane);
+        bstep<0x4E, 1, R1, NM, RP>(v, lane);
+        bstep<0xB1, 0, R2, NM, RP>(v, lane);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        if constexpr (LPR >= 32) v[m][0] += __shfl_xor(v[m][0], 16, 64);
+        if constexpr (LPR == 64) v[m][0] += __shfl_xor(v[m][0], 32, 64);
+    }
+}
+// token slot held by lane l after seg_reduce, and whether l writes it
+template <int RP, int LPR>
+__device__ __forceinline__ int seg_slot(int lane) {
+    constexpr int LB = LPR >= 16 ? 4 : 3;  // lane bits used by the DPP steps
+    constexpr int SB = RP == 1 ? 0 : RP == 2 ? 1 : RP == 4 ? 2 : RP == 8 ? 3 : 4;
+    return (lane & ((1 << LB) - 1)) >> (LB - SB);
+}
+template <int RP, int LPR>
+__device__ __forceinline__ bool seg_writer(int lane) {
+    constexpr int LB = LPR >= 16 ? 4 : 3;
+    constexpr int SB = RP == 1 ? 0 : RP == 2 ? 1 : RP == 4 ? 2 : RP == 8 ? 3 : 4;
+    return (lane % LPR) < (1 << LB) && (lane & ((1 << (LB - SB)) - 1)) == 0;
+}
+
+// acc += (16-byte weight chunk) . (matching activations of one token row).
+// xr points at the token row in LDS; col is the chunk column.  MXFP4 rows are
+// held in LDS sub-chunk-major (8-element unit w of chunk c at (w*nch + c)*8)
+// so that lanes reading consecutive chunks touch consecutive 16-byte words.
+template <int WT, typename AT>
+__device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* dec, const AT* xr,
+                                           int col, int nch, float acc) {
     if constexpr (WT == 0) {
-        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xs);
+        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + col * 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(wv[q]), xv[q], acc);
     } else if constexpr (WT == 1) {
-        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs);
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + col * 8);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = dot2_bf16(wv[q], xv[q], acc);
     } else {
-        const float s = __uint_as_float(sc << 23);
-        const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xs);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4_t xv = xp[q];
-            const uint32_t w = wv[q];
-            acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)), xv[0], acc);
-            acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)), xv[1], acc);
-            acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)), xv[2], acc);
-            acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3)), xv[3], acc);
+        for (int w = 0; w < 4; ++w) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + ((size_t)w * nch + col) * 8);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc = dot2_bf16(dec[4 * w + b], xv[b], acc);
         }
     }
     return acc;
 }
 
-// Weight row `row` of a [N][K] matrix at byte offset `moff` (codes) /
-// `soff` (scales) inside the slot: pointer to its 16-byte chunks and scales.
-template <int WT>
-__device__ __forceinline__ const u32x4_t* row_chunks(const uint8_t* slot, size_t moff, int row,
-                                                     int K) {
-    constexpr int bytes_per_row_num = WT == 0 ? 4 : (WT == 1 ? 2 : 1);
-    const size_t rb = WT == 2 ? (size_t)K / 2 : (size_t)K * bytes_per_row_num;
-    return reinterpret_cast<const u32x4_t*>(slot + moff + (size_t)row * rb);
-}
-
-// One pass over a weight row: this lane's chunks c = c0 + lane + 64 q, q < 4.
-// All loads of a pass are issued together so that a wavefront has 4 (or 8
-// for gate + up) 16-byte loads per lane in flight.
-template <int WT>
-struct RowPass {
-    u32x4_t v[4];
-    uint32_t s[4];
-    __device__ __forceinline__ void load(const u32x4_t* __restrict__ row,
-                                         const uint8_t* __restrict__ sc, int c0, int nch,
-                                         int lane) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = c0 + 64 * q + lane;
-            if (c < nch) {
-                v[q] = __builtin_nontemporal_load(row + c);
-                if constexpr (WT == 2) s[q] = sc[c];
-            }
-        }
-    }
-    template <typename AT>
-    __device__ __forceinline__ float dot(const AT* xrow, int c0, int nch, int lane, float acc) const {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = c0 + 64 * q + lane;
-            if (c < nch) acc = chunk_dot<WT>(v[q], WT == 2 ? s[q] : 0u, xrow + (size_t)c * W<WT>::EPC, acc);
-        }
-        return acc;
-    }
-};
-
-// Wavefront sum: DPP inside each row of 16 lanes, then two cross-row swaps.
-#define FT_DPP(v, ctrl) \
-    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true))
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    v += FT_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
-    v += FT_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
-    v += FT_DPP(v, 0x141);  // row_half_mirror
-    v += FT_DPP(v, 0x140);  // row_mirror
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-#undef FT_DPP
-
-// Activation rows into LDS: row r of the chunk is source row src_row(r).
-template <typename AT, typename RowF>
-__device__ __forceinline__ void stage_rows(AT* xs, const AT* __restrict__ src, RowF src_row,
-                                           int R, int K) {
-    const int per_row = K * (int)sizeof(AT) / 16;
-    for (int i = threadIdx.x; i < R * per_row; i += blockDim.x) {
-        const int r = i / per_row, c = i % per_row;
-        reinterpret_cast<u32x4_t*>(xs + (size_t)r * K)[c] =
-            reinterpret_cast<const u32x4_t*>(src + (size_t)src_row(r) * K)[c];
+// f(std::integral_constant<int, R>) for the runtime R in [1, N].
+template <int N, typename F>
+__device__ __forceinline__ void with_rows(int R, F&& f) {
+    if constexpr (N >= 1) {
+        if (R == N) f(std::integral_constant<int, N>{});
+        else with_rows<N - 1>(R, f);
     }
 }
 
-// ---------------------------------------------------------------------------
-// GEMM1 + SwiGLU.  Block: RPB row pairs (gate row i, up row i); wave w takes
-// pairs w, w+4, ...  Activations: RMAX token rows at a time in LDS.  The
-// first pass of weight loads is issued before the activations are staged.
-// ---------------------------------------------------------------------------
-template <int WT, int RMAX>
-__global__ __launch_bounds__(256) void ffn1_stream_kernel(ft::FfnGeom g, const void* __restrict__ xv,
-                                                          const int32_t* __restrict__ perm,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ slot_of,
-                                                          int shared_slot, int n_routed_groups,
-                                                          int RPB, int RCAP,
-                                                          void* __restrict__ hv) {
+// NM = 2: gate and up rows -> h = silu(gate) * up (row length H, N = I).
+// NM = 1: down rows -> y (row length I, N = H).
+template <int WT, int NM, int QMAX, int RMAX, typename OT>
+__global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
     using AT = typename std::conditional<WT == 0, float, __bf16>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     AT* xs = reinterpret_cast<AT*>(smem);
-    const int NB = g.I / RPB;
-    const int j = blockIdx.x / NB, nb = blockIdx.x % NB;
+    const int j = blockIdx.x / a.NB, nb = blockIdx.x % a.NB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int e, slot, p_lo, cnt;
-    size_t hrow0;
-    if (j < n_routed_groups) {
-        e = find_active(offsets, slot_of, g.E, j, lane);
-        if (e < 0) return;
-        slot = slot_of ? slot_of[e] : e;
-        p_lo = offsets[e];
-        cnt = offsets[e + 1] - p_lo;
-        hrow0 = p_lo;
+
+    // this block's group: an expert (or the shared expert) and its token chunk
+    // (all block-uniform; readfirstlane makes them scalar so the token-row
+    // loops below branch on SGPRs instead of masking lanes)
+    int slot, r0, R;
+    size_t p_lo, orow0;
+    bool shared;
+    if (j < a.n_routed_groups) {
+        Group g;
+        if (!find_group(a.offsets, a.slot_of, a.E, a.RCAP, j, lane, g)) return;
+        const int c = __builtin_amdgcn_readfirstlane(g.c);
+        slot = __builtin_amdgcn_readfirstlane(g.slot);
+        const int lo = __builtin_amdgcn_readfirstlane(g.lo);
+        const int hi = __builtin_amdgcn_readfirstlane(g.hi);
+        p_lo = lo;
+        r0 = c * a.RCAP;
+        R = min(a.RCAP, hi - lo - r0);
+        orow0 = p_lo;
+        shared = false;
     } else {
-        e = g.E;
-        slot = shared_slot;
+        slot = a.shared_slot;
         p_lo = 0;
-        cnt = g.T;
-        hrow0 = (size_t)g.T * g.k;
+        r0 = (j - a.n_routed_groups) * a.RCAP;
+        R = min(a.RCAP, a.T - r0);
+        orow0 = (size_t)a.T * a.k;
+        shared = true;
     }
-    const bool shared = e == g.E;
-    const uint8_t* sl = g.pool + (size_t)slot * g.slot_stride;
-    const int K = g.H;
-    const int nch = K / W<WT>::EPC;
-    const AT* x = reinterpret_cast<const AT*>(xv);
-    auto gate_row = [&](int i) { return row_chunks<WT>(sl, g.off[0], i, K); };
-    auto up_row = [&](int i) { return row_chunks<WT>(sl, g.off[1], i, K); };
-    auto gate_sc = [&](int i) { return WT == 2 ? sl + g.off[3] + (size_t)i * (K / 32) : nullptr; };
-    auto up_sc = [&](int i) { return WT == 2 ? sl + g.off[4] + (size_t)i * (K / 32) : nullptr; };
+    if (R <= 0) return;
+    const uint8_t* sl = a.pool + (size_t)slot * a.slot_stride;
+    const u32x4_t* mat[NM];
+    const uint8_t* scl[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        mat[m] = reinterpret_cast<const u32x4_t*>(sl + a.moff[m]);
+        scl[m] = sl + a.soff[m];
+    }
+    const Walk wk = a.wk;
+    const int K = a.K;
+    const int RS = 64 / wk.LPR;                           // rows per item
+    const int seg = lane / wk.LPR, sg = lane % wk.LPR;    // this lane's row in the item, place in it
+    const int n0 = nb * a.RPB, n1 = min(n0 + a.RPB, a.N);
+    const int ng = (n1 - n0 + RS - 1) / RS;                          // items per pass, block
+    const int gw = ng > wave ? (ng - wave + NWAVE - 1) / NWAVE : 0;  // ... of this wave
+    const int U = gw * wk.P;                                         // items of this wave
 
-    RowPass<WT> pg, pu;
-    for (int r0 = 0; r0 < cnt; r0 += RCAP) {
-        const int R = min(RCAP, cnt - r0);
-        // first pass of this wave's first row pair, in flight during staging
-        int i = nb * RPB + wave;
-        pg.load(gate_row(i), gate_sc(i), 0, nch, lane);
-        pu.load(up_row(i), up_sc(i), 0, nch, lane);
-        __syncthreads();  // previous chunk's readers are done with xs
-        stage_rows<AT>(xs, x, [&](int r) { int p = p_lo + r0 + r; return shared ? p : perm[p] / g.k; },
-                       R, K);
-        __syncthreads();
-        for (int ip = wave; ip < RPB; ip += 4) {
-            i = nb * RPB + ip;
-            float ag[RMAX], au[RMAX];
+    struct Item { int row, p, cend; };
+    auto item = [&](int u) __attribute__((always_inline)) {
+        const int gi = u / wk.P;
+        Item it;
+        it.p = u - gi * wk.P;
+        it.row = n0 + (wave + NWAVE * gi) * RS + seg;
+        it.cend = min(wk.nch, (it.p + 1) * wk.CPP);
+        return it;
+    };
+    auto col_of = [&](const Item& it, int q) __attribute__((always_inline)) {
+        return it.p * wk.CPP + sg + wk.LPR * q;
+    };
+    auto valid = [&](const Item& it, int q) __attribute__((always_inline)) {
+        return q < wk.Q && it.row < n1 && col_of(it, q) < it.cend;
+    };
+    struct Buf {
+        u32x4_t v[NM][QMAX];
+        uint32_t s[NM][QMAX];
+    };
+    // Every issue() runs all NM*QMAX loads on every lane, without branches, so
+    // that the number of loads in flight is the same on every path and the
+    // compiler's wait before consume() only covers the buffer it reads (a
+    // load under a branch makes it wait for everything).  Loads that are not
+    // part of the item (and issues past the wave's last item) point every
+    // lane at the matrix's first 16 bytes: one cache line.
+    auto issue = [&](Buf& b, int u) __attribute__((always_inline)) {
+        const bool live = u < U;  // wave-uniform
+        const Item it = item(u);
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r) ag[r] = au[r] = 0.f;
-            for (int c0 = 0; c0 < nch; c0 += 256) {
-                if (c0 > 0 || ip != wave) {
-                    pg.load(gate_row(i), gate_sc(i), c0, nch, lane);
-                    pu.load(up_row(i), up_sc(i), c0, nch, lane);
-                }
+        for (int q = 0; q < QMAX; ++q) {
+            const size_t ci = live && valid(it, q) ? (size_t)it.row * wk.nch + col_of(it, q) : 0;
 #pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    if (r < R) {
-                        ag[r] = pg.dot(xs + (size_t)r * K, c0, nch, lane, ag[r]);
-                        au[r] = pu.dot(xs + (size_t)r * K, c0, nch, lane, au[r]);
-                    }
+            for (int m = 0; m < NM; ++m) {
+                b.v[m][q] = __builtin_nontemporal_load(mat[m] + ci);
+                if constexpr (WT == 2) b.s[m][q] = scl[m][ci];
             }
+        }
+    };
+
+    float acc[NM][RMAX];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r)
-                if (r < R) {
-                    const float gs = wave_sum_dpp(ag[r]), us = wave_sum_dpp(au[r]);
-                    if (lane == r) {
-                        const float hval = silu_mul(gs, us);
-                        const size_t idx = (hrow0 + r0 + r) * g.I + i;
-                        if constexpr (WT == 0) reinterpret_cast<float*>(hv)[idx] = hval;
-                        else reinterpret_cast<uint16_t*>(hv)[idx] = (uint16_t)f32_to_bf16_bits(hval);
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) acc[m][r] = 0.f;
+    };
+
+    // consume(b, u, rows): rows is a std::integral_constant, the number of
+    // token rows of this group, so that the row loops have fixed trip counts
+    // (a runtime count makes the compiler keep every chunk's values live).
+    auto consume = [&](const Buf& b, int u, auto rows) __attribute__((always_inline)) {
+        constexpr int RR = decltype(rows)::value;
+        const Item it = item(u);
+#pragma unroll
+        for (int q = 0; q < QMAX; ++q) {
+            if (q >= wk.Q) break;  // uniform
+            const bool ok = valid(it, q);
+            const int col = ok ? col_of(it, q) : 0;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                uint32_t dec[WT == 2 ? 16 : 1];
+                u32x4_t wv = b.v[m][q];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) wv[w] = ok ? wv[w] : 0u;  // +0 codes / +0.0 weights
+                if constexpr (WT == 2) {
+                    const float sc = __uint_as_float(b.s[m][q] << 23);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t cw = wv[w];
+                        dec[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
+                        dec[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
+                        dec[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
+                        dec[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
                     }
                 }
+#pragma unroll
+                for (int r = 0; r < RR; ++r)
+                    acc[m][r] = chunk_dot<WT, AT>(wv, dec, xs + (size_t)r * K, col, wk.nch, acc[m][r]);
+            }
         }
+        if (it.p != wk.P - 1) return;
+        // item finished: reduce each token's sums over the row's segment
+        constexpr int RP = RR <= 1 ? 1 : RR <= 2 ? 2 : RR <= 4 ? 4 : RR <= 8 ? 8 : 16;
+        float v[NM][RP];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < RP; ++r) v[m][r] = r < RR ? acc[m][r] : 0.f;
+        int rs;
+        bool wr;
+        switch (wk.LPR) {
+            case 8:
+                seg_reduce<8>(v, lane);
+                rs = seg_slot<RP, 8>(lane);
+                wr = seg_writer<RP, 8>(lane);
+                break;
+            case 16:
+                seg_reduce<16>(v, lane);
+                rs = seg_slot<RP, 16>(lane);
+                wr = seg_writer<RP, 16>(lane);
+                break;
+            case 32:
+                seg_reduce<32>(v, lane);
+                rs = seg_slot<RP, 32>(lane);
+                wr = seg_writer<RP, 32>(lane);
+                break;
+            default:
+                seg_reduce<64>(v, lane);
+                rs = seg_slot<RP, 64>(lane);
+                wr = seg_writer<RP, 64>(lane);
+                break;
+        }
+        if (wr && rs < RR && it.row < n1) {
+            const size_t idx = (orow0 + r0 + rs) * (size_t)a.N + it.row;
+            float val;
+            if constexpr (NM == 2) val = silu_mul(v[0][0], v[1][0]);
+            else val = v[0][0];
+            using DT = typename std::conditional<NM == 2, AT, OT>::type;
+            if constexpr (sizeof(DT) == 4) reinterpret_cast<float*>(a.dst)[idx] = val;
+            else reinterpret_cast<uint16_t*>(a.dst)[idx] = (uint16_t)f32_to_bf16_bits(val);
+        }
+        zero_acc();
+    };
+
+    const AT* src = reinterpret_cast<const AT*>(a.src);
+    const int units = K * (int)sizeof(AT) / 16;  // 16-byte units per activation row
+    Buf A, B;
+    // the first two items are in flight while the activations are staged
+    issue(A, 0);
+    issue(B, 1);
+    for (int i = threadIdx.x; i < R * units; i += blockDim.x) {
+        const int r = i / units, uu = i - r * units;
+        const size_t srow = a.perm ? (shared ? (size_t)(r0 + r) : (size_t)(a.perm[p_lo + r0 + r] / a.k))
+                                   : orow0 + r0 + r;
+        const int du = WT == 2 ? (uu & 3) * (units >> 2) + (uu >> 2) : uu;
+        reinterpret_cast<u32x4_t*>(xs + (size_t)r * K)[du] =
+            reinterpret_cast<const u32x4_t*>(src + srow * K)[uu];
     }
+    __syncthreads();
+    zero_acc();
+    // Two items always in flight; issues past the end are single-line reads.
+    auto stream = [&](auto rows) __attribute__((always_inline)) {
+        for (int u = 0; u < U; u += 2) {
+            consume(A, u, rows);
+            issue(A, u + 2);
+            if (u + 1 < U) consume(B, u + 1, rows);
+            issue(B, u + 3);
+        }
+    };
+    with_rows<RMAX>(R, stream);
 }
 
-// ---------------------------------------------------------------------------
-// GEMM2: y[p][d] = h[p] . Wd[d].  Block: RPB rows d; h rows in LDS.
-// ---------------------------------------------------------------------------
-template <int WT, int RMAX, typename OT>
-__global__ __launch_bounds__(256) void ffn2_stream_kernel(ft::FfnGeom g, const void* __restrict__ hv,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ slot_of,
-                                                          int shared_slot, int n_routed_groups,
-                                                          int RPB, int RCAP,
-                                                          OT* __restrict__ y) {
-    using AT = typename std::conditional<WT == 0, float, __bf16>::type;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    AT* hs = reinterpret_cast<AT*>(smem);
-    const int NB = g.H / RPB;
-    const int j = blockIdx.x / NB, nb = blockIdx.x % NB;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int e, slot, cnt;
-    size_t hrow0;
-    if (j < n_routed_groups) {
-        e = find_active(offsets, slot_of, g.E, j, lane);
-        if (e < 0) return;
-        slot = slot_of ? slot_of[e] : e;
-        hrow0 = offsets[e];
-        cnt = offsets[e + 1] - offsets[e];
-    } else {
-        slot = shared_slot;
-        cnt = g.T;
-        hrow0 = (size_t)g.T * g.k;
-    }
-    const uint8_t* sl = g.pool + (size_t)slot * g.slot_stride;
-    const int K = g.I;
-    const int nch = K / W<WT>::EPC;
-    const AT* h = reinterpret_cast<const AT*>(hv);
-    auto down_row = [&](int d) { return row_chunks<WT>(sl, g.off[2], d, K); };
-    auto down_sc = [&](int d) { return WT == 2 ? sl + g.off[5] + (size_t)d * (K / 32) : nullptr; };
-
-    RowPass<WT> pd;
-    for (int r0 = 0; r0 < cnt; r0 += RCAP) {
-        const int R = min(RCAP, cnt - r0);
-        int d = nb * RPB + wave;
-        pd.load(down_row(d), down_sc(d), 0, nch, lane);
-        __syncthreads();
-        stage_rows<AT>(hs, h, [&](int r) { return (int)(hrow0 + r0 + r); }, R, K);
-        __syncthreads();
-        for (int dp = wave; dp < RPB; dp += 4) {
-            d = nb * RPB + dp;
-            float acc[RMAX];
-#pragma unroll
-            for (int r = 0; r < RMAX; ++r) acc[r] = 0.f;
-            for (int c0 = 0; c0 < nch; c0 += 256) {
-                if (c0 > 0 || dp != wave) pd.load(down_row(d), down_sc(d), c0, nch, lane);
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    if (r < R) acc[r] = pd.dot(hs + (size_t)r * K, c0, nch, lane, acc[r]);
-            }
-#pragma unroll
-            for (int r = 0; r < RMAX; ++r)
-                if (r < R) {
-                    const float v = wave_sum_dpp(acc[r]);
-                    if (lane == r) {
-                        const size_t idx = (hrow0 + r0 + r) * g.H + d;
-                        if constexpr (sizeof(OT) == 4) reinterpret_cast<float*>(y)[idx] = v;
-                        else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
-                    }
-                }
+// Segment width: the fewest lanes per row (8..64) that cover a row in at most
+// QMAX loads per lane; rows longer than 64*QMAX chunks take several passes.
+Walk make_walk(int K, int epc, int QMAX) {
+    Walk w;
+    w.nch = K / epc;
+    for (int lpr = 8; lpr <= 64; lpr *= 2) {
+        const int q = (w.nch + lpr - 1) / lpr;
+        if (q <= QMAX) {
+            w.LPR = lpr;
+            w.Q = q;
+            w.P = 1;
+            w.CPP = w.nch;
+            return w;
         }
     }
+    w.LPR = 64;
+    w.Q = QMAX;
+    w.CPP = 64 * QMAX;
+    w.P = (w.nch + w.CPP - 1) / w.CPP;
+    return w;
 }
 
-// rows per block: smallest of {4, 8, 16, 32, 64} keeping the grid <= ~4096 blocks
-int pick_rpb(long groups, int n_rows) {
-    int rpb = 4;
-    while (rpb < 64 && groups * (n_rows / rpb) > 4096 && n_rows % (rpb * 2) == 0) rpb *= 2;
+// Rows per block grow (by doubling) until the grid holds at most `target`
+// blocks.  With one token per group the whole layer is a few items per wave
+// and a grid that stays resident at once is fastest; with more tokens per
+// group a finer grid balances groups of unequal size.
+int target_blocks(int rmax) {
+    static const int forced = [] {
+        const char* s = getenv("FTMOE_STREAM_BLOCKS");
+        return s ? atoi(s) : 0;
+    }();
+    if (forced > 0) return forced;
+    return rmax == 1 ? 1024 : 4096;
+}
+int pick_rpb(long groups, int N, int rows_per_item, int target) {
+    int rpb = rows_per_item * NWAVE;
+    while (rpb < N && groups * ((N + rpb - 1) / rpb) > target) rpb *= 2;
     return rpb;
+}
+
+template <int WT, int NM, int QMAX, int RMAX, typename OT>
+ft_status launch_one(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
+    using AT = typename std::conditional<WT == 0, float, __bf16>::type;
+    const size_t row_bytes = (size_t)a.K * sizeof(AT);
+    int rcap = a.T < RMAX ? a.T : RMAX;
+    while (rcap > 1 && rcap * row_bytes > max_lds) --rcap;
+    const size_t lds = rcap * row_bytes;
+    if (lds > max_lds)
+        return ft::set_error(FT_ERR_UNSUPPORTED, "ffn stream: an activation row of %zu bytes exceeds LDS",
+                             row_bytes);
+    a.RCAP = rcap;
+    // groups: sum over experts of ceil(rows / RCAP) <= (T*k + active*(RCAP-1)) / RCAP
+    const long tk = (long)a.T * a.k;
+    const long act = tk < a.E ? tk : a.E;
+    a.n_routed_groups = (int)((tk + act * (rcap - 1)) / rcap);
+    const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
+    a.wk = make_walk(a.K, W<WT>::EPC, QMAX);
+    a.RPB = pick_rpb(groups, a.N, 64 / a.wk.LPR, target_blocks(RMAX));
+    a.NB = (a.N + a.RPB - 1) / a.RPB;
+    auto kern = stream_kernel<WT, NM, QMAX, RMAX, OT>;
+    if (lds > 65536)
+        FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+    kern<<<dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s>>>(a);
+    FT_LAUNCHED("ffn_stream");
+    return FT_OK;
+}
+
+// Token rows held per group: 1 for single-token decode (a lean kernel), else
+// up to `cap` (4 when rows are long: LDS and registers).
+template <int WT, int NM, int QMAX, typename OT>
+ft_status launch_rows(const StreamArgs& a, int n_shared, int cap, size_t max_lds, hipStream_t s) {
+    if (a.T <= 1) return launch_one<WT, NM, QMAX, 1, OT>(a, n_shared, max_lds, s);
+    if (a.T <= 4 || cap <= 4) return launch_one<WT, NM, QMAX, 4, OT>(a, n_shared, max_lds, s);
+    return launch_one<WT, NM, QMAX, 8, OT>(a, n_shared, max_lds, s);
 }
 
 }  // namespace
@@ -312,41 +521,59 @@ namespace ft {
 ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm,
                             const int32_t* offsets, const int32_t* slot_of, int shared_slot,
                             void* h, void* y, ft_dtype y_dt, hipStream_t s) {
-    const long tk = (long)g.T * g.k;
-    const int routed_groups = (int)(tk < g.E ? tk : g.E);
-    const int groups = routed_groups + (g.n_shared ? 1 : 0);
-    const int rpb1 = pick_rpb(groups, g.I), rpb2 = pick_rpb(groups, g.H);
-    dim3 g1((unsigned)groups * (g.I / rpb1)), g2((unsigned)groups * (g.H / rpb2)), blk(256);
-    const int big = g.H > 2048 || g.I > 2048;
+    const size_t max_lds = 160 * 1024;
+    const bool big = g.H > 2048 || g.I > 2048;
 
+    StreamArgs a{};
+    a.pool = g.pool;
+    a.slot_stride = g.slot_stride;
+    a.offsets = offsets;
+    a.slot_of = slot_of;
+    a.E = g.E;
+    a.T = g.T;
+    a.k = g.k;
+    a.shared_slot = shared_slot;
+
+    // gate/up + SwiGLU: rows I of length H
+    StreamArgs a1 = a;
+    a1.moff[0] = g.off[0];
+    a1.moff[1] = g.off[1];
+    a1.soff[0] = g.off[3];
+    a1.soff[1] = g.off[4];
+    a1.perm = perm;
+    a1.N = g.I;
+    a1.K = g.H;
+    a1.src = x;
+    a1.dst = h;
+    const int cap = (g.w_dt != FT_F32 && big) ? 4 : 8;
+    ft_status r;
     prof_begin(PROF_FFN_GEMM1, s);
-    // activation rows per pass: at most RMAX, at most T (an expert never gets more than T rows)
-#define FT_S1(WT, RM)                                                                         \
-    ffn1_stream_kernel<WT, RM><<<g1, blk, (size_t)min(RM, g.T) * g.H * (WT == 0 ? 4 : 2), s>>>( \
-        g, x, perm, offsets, slot_of, shared_slot, routed_groups, rpb1, min(RM, g.T), h)
-    if (g.w_dt == FT_F32) FT_S1(0, 8);
-    else if (g.w_dt == FT_BF16) { if (big) FT_S1(1, 4); else FT_S1(1, 8); }
-    else { if (big) FT_S1(2, 4); else FT_S1(2, 8); }
-#undef FT_S1
-    FT_LAUNCHED("ffn1_stream");
+    if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    else if (g.w_dt == FT_BF16) r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    else r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     prof_end(PROF_FFN_GEMM1, s);
+    if (r != FT_OK) return r;
 
+    // down: rows H of length I
+    StreamArgs a2 = a;
+    a2.moff[0] = g.off[2];
+    a2.soff[0] = g.off[5];
+    a2.perm = nullptr;
+    a2.N = g.H;
+    a2.K = g.I;
+    a2.src = h;
+    a2.dst = y;
     prof_begin(PROF_FFN_GEMM2, s);
-#define FT_S2(WT, RM, OT)                                                                     \
-    ffn2_stream_kernel<WT, RM, OT><<<g2, blk, (size_t)min(RM, g.T) * g.I * (WT == 0 ? 4 : 2), s>>>( \
-        g, h, offsets, slot_of, shared_slot, routed_groups, rpb2, min(RM, g.T), (OT*)y)
-    if (g.w_dt == FT_F32) FT_S2(0, 8, float);
+    if (g.w_dt == FT_F32) r = launch_rows<0, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) {
-        if (y_dt == FT_F32) { if (big) FT_S2(1, 4, float); else FT_S2(1, 8, float); }
-        else { if (big) FT_S2(1, 4, __bf16); else FT_S2(1, 8, __bf16); }
+        if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+        else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
     } else {
-        if (y_dt == FT_F32) { if (big) FT_S2(2, 4, float); else FT_S2(2, 8, float); }
-        else { if (big) FT_S2(2, 4, __bf16); else FT_S2(2, 8, __bf16); }
+        if (y_dt == FT_F32) r = launch_rows<2, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+        else r = launch_rows<2, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
     }
-#undef FT_S2
-    FT_LAUNCHED("ffn2_stream");
     prof_end(PROF_FFN_GEMM2, s);
-    return FT_OK;
+    return r;
 }
 
 }  // namespace ft
