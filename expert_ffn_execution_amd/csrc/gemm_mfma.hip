@@ -20,6 +20,8 @@
 // a fragment read touches fall on distinct banks.
 #include "gemm_mfma.h"
 
+#include <type_traits>
+
 namespace {
 
 using ft::TileDesc;
@@ -292,8 +294,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined tile kernel for the expert GEMMs.  256 x 256 output tile, 8
-// wavefronts (4 x 2) of 64 x 128 (2 x 4 tiles of v_mfma_f32_32x32x16_bf16),
+// Pipelined tile kernel for the expert GEMMs.  256 x 256 output tile, 4
+// wavefronts (one per SIMD), each owning all 256 rows and a 64-column strip:
+// 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane),
 // K in slices of 32 through five LDS stages.
 // Slices are copied global -> LDS by the load units directly
 // (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane l
@@ -304,24 +307,31 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
 // into the CU feeds as many MFMAs as possible: per slice 32 KB carry 4.2
 // MFLOP.  MXFP4 weights stay packed in LDS (16 code bytes + 1 scale byte per
 // row and slice) and are decoded to bf16 when a fragment is read.
+// An expert's last M-tile is usually partly filled (routing gives each
+// expert an arbitrary row count): since every wave spans all rows, all waves
+// skip the MFMAs and fragment reads of 32-row sub-tiles past the tile's rows
+// alike, and the block's time shrinks with its row count.
 //
 // LDS layout of a slice of rows: row r is 64 bytes = 4 chunks of 16 bytes,
 // chunk c stored at position c ^ ((r >> 2) & 3): the 16 rows a fragment read
 // touches then cover all 64 banks exactly once.
 // ---------------------------------------------------------------------------
 namespace pipe {
-constexpr int BM = 256, BN = 256, KS = 32, NT = 512, WM = 64, WN = 128, WAVES_N = 2;
+constexpr int BM = 256, BN = 256, KS = 32, NT = 256, NW = NT / 64, WN = BN / NW;
 constexpr int STAGES = 5;   // 5 x 32 KB = all 160 KB of LDS (bf16)
-constexpr int MT = WM / 32, NTL = WN / 32;   // 32 x 32 MFMA tiles per wavefront
+constexpr int MT = BM / 32, NTL = WN / 32;   // 32 x 32 MFMA tiles per wavefront
 constexpr int ROWB = KS * 2;                          // bytes of a bf16 row slice
 constexpr int A_BYTES = BM * ROWB;                    // 16 KB
+constexpr int AL = A_BYTES / 1024 / NW;               // A copies per wave per slice
 // MXFP4: codes [BN][16 B], then one 4-byte slot per row holding its scale byte
 // (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot)
 template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BN * 16 + BN * 4; }
 template <int BT> constexpr int stage_bytes() { return A_BYTES + b_bytes<BT>(); }
 template <int BT> constexpr size_t lds_bytes() { return (size_t)STAGES * stage_bytes<BT>(); }
-// global_load_lds instructions per wave per slice
-template <int BT> constexpr int loads_per_slice() { return BT == 0 ? 4 : 3; }
+// global_load_lds instructions per wave per slice: A, then B (bf16: 1 KB
+// pieces; MXFP4: one codes piece of 64 rows and one scale byte per lane)
+template <int BT> constexpr int b_copies() { return BT == 0 ? BN * ROWB / 1024 / NW : 1; }
+template <int BT> constexpr int loads_per_slice() { return AL + (BT == 0 ? b_copies<BT>() : 2); }
 __device__ __forceinline__ int sw(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
 }  // namespace pipe
 
@@ -343,6 +353,15 @@ __device__ __forceinline__ bf16x8_t fp4_frag(uint32_t codes, uint32_t X) {
     d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
     d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
     return __builtin_bit_cast(bf16x8_t, d);
+}
+
+// f(std::integral_constant<int, M>) for the runtime M in [1, N].
+template <int N, typename F>
+__device__ __forceinline__ void with_count(int M, F&& f) {
+    if constexpr (N >= 1) {
+        if (M >= N) f(std::integral_constant<int, N>{});
+        else with_count<N - 1>(M, f);
+    }
 }
 
 template <int MODE, int BT, typename OutT>
@@ -373,11 +392,12 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     // gated: B rows [0, 128) = gate rows c0.., [128, 256) = up rows c0..; plain: rows c0..
     const int c0 = nt * (MODE == MODE_GATED ? BN / 2 : BN);
 
-    // A: lane fills LDS row r = 16 * (2 * wave + i) + lane / 4, physical chunk lane % 4
-    uint32_t aoff[2];
+    // A: copy i of this wave fills LDS rows 16 * (AL * wave + i) + lane / 4,
+    // physical chunk lane % 4 (rows past the tile re-read its last row)
+    uint32_t aoff[AL];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 16 * (2 * wave + i) + (lane >> 2);
+    for (int i = 0; i < AL; ++i) {
+        const int r = 16 * (AL * wave + i) + (lane >> 2);
         const int rc = min(r, td.rows - 1);
         uint32_t arow;
         if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + rc) : (uint32_t)(perm[td.p0 + rc] / g.k);
@@ -385,50 +405,50 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         aoff[i] = arow * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
     }
     // B row r of the tile -> weight row (clamped: columns past NOUT are not stored)
-    auto wrow = [&](int r) -> uint32_t {
+    auto wrow = [&](int r) __attribute__((always_inline)) -> uint32_t {
         if constexpr (MODE == MODE_GATED) return (uint32_t)min(c0 + (r % (BN / 2)), NOUT - 1);
         else return (uint32_t)min(c0 + r, NOUT - 1);
     };
-    auto wbase = [&](int r, int which) -> uint32_t {  // which: 0 codes/values, 1 scales
+    auto wbase = [&](int r, int which) __attribute__((always_inline)) -> uint32_t {  // which: 0 codes/values, 1 scales
         if constexpr (MODE == MODE_GATED)
             return (uint32_t)(r < BN / 2 ? g.off[which ? 3 : 0] : g.off[which ? 4 : 1]);
         else
             return (uint32_t)g.off[which ? 5 : 2];
     };
     const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : (uint32_t)K / 2;
-    uint32_t boff[2];
+    // B value/code copies per wave: b_copies<BT>() <= 4 (a literal bound: a
+    // call in an array bound reads as a variable-length array to the host pass)
+    uint32_t boff[4], soff = 0;
+    static_assert(b_copies<BT>() <= 4, "B copies per wave");
     if constexpr (BT == 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 16 * (2 * wave + i) + (lane >> 2);
+        for (int i = 0; i < b_copies<BT>(); ++i) {
+            const int r = 16 * (b_copies<BT>() * wave + i) + (lane >> 2);
             boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
         }
-    } else if (wave < 4) {  // codes: row 64 * wave + lane, 16 bytes per slice
+    } else {  // codes: row 64 * wave + lane, 16 bytes per slice; its scale byte likewise
         const int r = 64 * wave + lane;
         boff[0] = wbase(r, 0) + wrow(r) * rowb;
-    } else {                // scales: row 64 * (wave - 4) + lane, 1 byte per slice
-        const int r = 64 * (wave - 4) + lane;
-        boff[0] = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
+        soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
     }
 
-    auto issue = [&](int stage, int kt) {
+    auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
         unsigned char* st = smem + stage * stage_bytes<BT>();
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_global_load_lds(A + aoff[i] + kt * KS, FT_LDS(st + (2 * wave + i) * 1024), 16, 0, 0);
+        for (int i = 0; i < AL; ++i)
+            __builtin_amdgcn_global_load_lds(A + aoff[i] + kt * KS, FT_LDS(st + (AL * wave + i) * 1024), 16, 0, 0);
         unsigned char* bst = st + A_BYTES;
         if constexpr (BT == 0) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * ROWB, FT_LDS(bst + (2 * wave + i) * 1024), 16, 0, 0);
-        } else if (wave < 4) {
-            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt * (KS / 2), FT_LDS(bst + wave * 1024), 16, 0, 0);
+            for (int i = 0; i < b_copies<BT>(); ++i)
+                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * ROWB, FT_LDS(bst + (b_copies<BT>() * wave + i) * 1024), 16, 0, 0);
         } else {
-            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt, FT_LDS(bst + BN * 16 + (wave - 4) * 256), 1, 0, 0);
+            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt * (KS / 2), FT_LDS(bst + wave * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(slot + soff + kt, FT_LDS(bst + BN * 16 + wave * 256), 1, 0, 0);
         }
     };
 
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wn = wave;
     f32x16_t acc[MT][NTL];
 #pragma unroll
     for (int a = 0; a < MT; ++a)
@@ -440,13 +460,15 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     constexpr int LPS = loads_per_slice<BT>();
     const int nk = K / KS;
     const int l32 = lane & 31, hi = lane >> 5;
+    const int mact = min(MT, (td.rows + 31) / 32);  // 32-row sub-tiles holding rows
 
     // Fragments of one slice (both 16-deep k-steps): the wave reads slice k+1's
     // fragments from LDS while its MFMAs consume slice k's from registers.
     struct Frags {
         bf16x8_t a[2][MT], b[2][NTL];
     };
-    auto load_frags = [&](int stage, Frags& F) {
+    auto load_frags = [&](int stage, Frags& F, auto mc) __attribute__((always_inline)) {
+        constexpr int MA = decltype(mc)::value;
         const unsigned char* st = smem + stage * stage_bytes<BT>();
         const unsigned char* Bc = st + A_BYTES;
 #pragma unroll
@@ -454,12 +476,12 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             // 32x32x16 operands: lane holds row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7
             const int ch = 2 * kk + hi;
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(wm * WM + m * 32 + l32, ch));
+            for (int m = 0; m < MA; ++m)
+                F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(m * 32 + l32, ch));
 #pragma unroll
             for (int n = 0; n < NTL; ++n) {
                 int brow;
-                if constexpr (MODE == MODE_GATED)  // wave's first NTL/2 tiles: gate, the rest: up
+                if constexpr (MODE == MODE_GATED)  // the wave's gate tile, then its up tile
                     brow = (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
                 else
                     brow = wn * WN + n * 32;
@@ -473,17 +495,18 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             }
         }
     };
-    auto mfmas = [&](const Frags& F) {
+    auto mfmas = [&](const Frags& F, auto mc) __attribute__((always_inline)) {
+        constexpr int MA = decltype(mc)::value;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MA; ++m)
 #pragma unroll
                 for (int n = 0; n < NTL; ++n) acc[m][n] = mfma32(F.a[kk][m], F.b[kk][n], acc[m][n]);
     };
     // wait until a slice has landed (`later` slices issued after it may stay in
     // flight) and this wave's LDS reads are done, then meet the other waves
-    auto wait_slice = [&](int later) {
+    auto wait_slice = [&](int later) __attribute__((always_inline)) {
         if (later >= 4) wait_vm_lgkm<4 * LPS>();
         else if (later == 3) wait_vm_lgkm<3 * LPS>();
         else if (later == 2) wait_vm_lgkm<2 * LPS>();
@@ -498,41 +521,49 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     // before the next iteration's MFMAs, not before these: on the last slice they
     // read a stage no copy targets any more (every copy has been waited for) and the
     // values are not used.
-    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+    auto step = [&](int kt, const Frags& cur, Frags& nxt, auto mc) __attribute__((always_inline)) {
+        constexpr int MA = decltype(mc)::value;
         if (kt + 1 < nk) {
             wait_slice(min(STAGES - 2, nk - 2 - kt));
             if (kt + STAGES < nk) issue(kt % STAGES, kt + STAGES);
         }
-        load_frags((kt + 1) % STAGES, nxt);
-        mfmas(cur);
+        load_frags((kt + 1) % STAGES, nxt, mc);
+        mfmas(cur, mc);
         // interleave: one MFMA, one LDS read, ... so the reads hide under the MFMAs
+        constexpr int NMF = 2 * MA * NTL, NDS = 2 * (MA + (BT == 0 ? 1 : 2) * NTL);
+        constexpr int NP = NMF < NDS ? NMF : NDS;
 #pragma unroll
-        for (int i = 0; i < 2 * (MT + NTL); ++i) {
+        for (int i = 0; i < NP; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * MT * NTL - 2 * (MT + NTL), 0);
+        if constexpr (NMF > NP) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NP, 0);
+        if constexpr (NDS > NP) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NP, 0);
     };
 
-    // prologue: all stages in flight, slice 0 read into registers
+    // prologue: all stages in flight
 #pragma unroll
     for (int q = 0; q < STAGES; ++q)
         if (q < nk) issue(q, q);
+    // the K loop, specialised on the number of 32-row sub-tiles holding rows
     Frags F0, F1;
-    wait_slice(min(STAGES - 1, nk - 1));
-    load_frags(0, F0);
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, F0, F1);
-        if (kt + 1 < nk) step(kt + 1, F1, F0);
-    }
+    with_count<MT>(mact, [&](auto mc) __attribute__((always_inline)) {
+        wait_slice(min(STAGES - 1, nk - 1));
+        load_frags(0, F0, mc);
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, F0, F1, mc);
+            if (kt + 1 < nk) step(kt + 1, F1, F0, mc);
+        }
+    });
 
     // epilogue: register q of a 32 x 32 tile is row 8 (q / 4) + 4 (lane / 32) + q % 4,
     // column lane % 32
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+        if (m >= mact) break;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int row = wm * WM + m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+            const int row = m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
             if (row >= td.rows) continue;
             if constexpr (MODE == MODE_GATED) {
 #pragma unroll
@@ -559,6 +590,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
                 }
             }
         }
+    }
 }
 #undef FT_LDS
 
