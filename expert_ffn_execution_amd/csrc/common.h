@@ -75,6 +75,12 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
+// silu(g) * u with the hardware exp2 and reciprocal (about 1 ulp each; the
+// result is rounded to bf16 by every caller): e^-g = 2^(-g log2 e)
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }

@@ -327,7 +327,10 @@ constexpr int AL = A_BYTES / 1024 / NW;               // A copies per wave per s
 // (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot)
 template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BN * 16 + BN * 4; }
 template <int BT> constexpr int stage_bytes() { return A_BYTES + b_bytes<BT>(); }
-template <int BT> constexpr size_t lds_bytes() { return (size_t)STAGES * stage_bytes<BT>(); }
+constexpr size_t EPI_BYTES = (size_t)BM * (BN + 8) * 2;   // bf16 output tile (plain GEMM)
+template <int BT> constexpr size_t lds_bytes() {
+    return (size_t)STAGES * stage_bytes<BT>() > EPI_BYTES ? (size_t)STAGES * stage_bytes<BT>() : EPI_BYTES;
+}
 // global_load_lds instructions per wave per slice: A, then B (bf16: 1 KB
 // pieces; MXFP4: one codes piece of 64 rows and one scale byte per lane)
 template <int BT> constexpr int b_copies() { return BT == 0 ? BN * ROWB / 1024 / NW : 1; }
@@ -556,37 +559,59 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         }
     });
 
-    // epilogue: register q of a 32 x 32 tile is row 8 (q / 4) + 4 (lane / 32) + q % 4,
-    // column lane % 32
+    // Epilogue.  Register q of a 32 x 32 tile is row 8 (q / 4) + 4 (lane / 32) +
+    // q % 4, column lane % 32.  bf16 results go through LDS (free once every
+    // wave has passed the K loop) so that global stores write whole rows in
+    // 16-byte pieces; fp32 results are stored directly (each store covers two
+    // 128-byte row pieces).
+    if constexpr (MODE == MODE_GATED || sizeof(OutT) == 2) {
+        constexpr int TC = MODE == MODE_GATED ? BN / 2 : BN;  // tile columns
+        constexpr int PITCH = TC + 8;                          // bf16 per LDS row (bank skew)
+        __bf16* ts = reinterpret_cast<__bf16*>(smem);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS reads are done
+        __builtin_amdgcn_s_barrier();        // ... and every other wave's
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m >= mact) break;
+        for (int m = 0; m < MT; ++m) {
+            if (m >= mact) break;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int row = m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
-            if (row >= td.rows) continue;
-            if constexpr (MODE == MODE_GATED) {
+            for (int q = 0; q < 16; ++q) {
+                const int row = m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+                if constexpr (MODE == MODE_GATED) {
 #pragma unroll
-                for (int n = 0; n < NTL / 2; ++n) {
-                    const int col = c0 + wn * (WN / 2) + n * 32 + l32;
-                    if (col < NOUT) {
-                        const float hv = silu_mul(acc[m][n][q], acc[m][n + NTL / 2][q]);
-                        reinterpret_cast<uint16_t*>(out)[(obase + row) * NOUT + col] =
-                            (uint16_t)f32_to_bf16_bits(hv);
-                    }
+                    for (int n = 0; n < NTL / 2; ++n)
+                        ts[row * PITCH + wn * (WN / 2) + n * 32 + l32] =
+                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(
+                                silu_mul_fast(acc[m][n][q], acc[m][n + NTL / 2][q])));
+                } else {
+#pragma unroll
+                    for (int n = 0; n < NTL; ++n)
+                        ts[row * PITCH + wn * WN + n * 32 + l32] =
+                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(acc[m][n][q]));
                 }
-            } else {
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = TC / 8;  // 16-byte pieces per tile row
+        const int rows = td.rows;
+        for (int c = threadIdx.x; c < rows * CPR; c += NT) {
+            const int row = c / CPR, cc = c % CPR;
+            const int col = c0 + cc * 8;
+            if (col < NOUT)
+                *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + (obase + row) * NOUT + col) =
+                    *reinterpret_cast<const u32x4_t*>(ts + row * PITCH + cc * 8);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m >= mact) break;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+                if (row >= td.rows) continue;
 #pragma unroll
                 for (int n = 0; n < NTL; ++n) {
                     const int col = c0 + wn * WN + n * 32 + l32;
-                    if (col < NOUT) {
-                        const float v = acc[m][n][q];
-                        if constexpr (sizeof(OutT) == 4)
-                            reinterpret_cast<float*>(out)[(obase + row) * NOUT + col] = v;
-                        else
-                            reinterpret_cast<uint16_t*>(out)[(obase + row) * NOUT + col] =
-                                (uint16_t)f32_to_bf16_bits(v);
-                    }
+                    if (col < NOUT) reinterpret_cast<float*>(out)[(obase + row) * NOUT + col] = acc[m][n][q];
                 }
             }
         }
