@@ -148,6 +148,24 @@ def test_layer_small_both_paths(kind, path, T):
     check_close(r["out"], ref, sh.wdtype, f"{kind} path{path} T{T}")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("T", [7, 300])
+def test_layer_fp32_expert_outputs(kind, path, T):
+    """y_perm in fp32 (the down projection's fp32 output) and an fp32 layer output."""
+    sh = SMALL[kind]
+    _say("layer fp32 y", kind, "path", path, "T", T)
+    L = Layer(sh)
+    x = synth.gen_x(sh, T)
+    logits = synth.gen_logits(sh, T)
+    ft.set_ffn_path(path)
+    r = run_layer(L, x.to(DEV), logits.to(DEV), y_dtype=torch.float32, out_dtype=torch.float32)
+    assert r["y"].dtype == torch.float32 and r["out"].dtype == torch.float32
+    ids, w = orc.route(logits.numpy(), sh.k)
+    ref = oracle_out(L, x, ids, w)
+    check_close(r["out"], ref, sh.wdtype, f"{kind} fp32 y path{path} T{T}")
+
+
 def test_layer_tiny_f32():
     sh = synth.TINY_F32
     _say("layer tiny f32")
