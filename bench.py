@@ -10,7 +10,9 @@ same weights exceed four times the 256 MB Infinity Cache.
 Prints one JSON line: headline = prefill tokens/s of the workload, with the
 roofline of its dominant kernel (the gate/up grouped GEMM, MFMA-bound), the
 decode points (HBM-bound FFN weight streaming) and the CPU oracle's rate on a
-bounded sample of the same workload.
+bounded sample of the same workload.  A decode point's tokens/s comes from
+replays of the step captured as a HIP graph (ft_moe_graph_*); the same step
+enqueued call by call is reported beside it (eager_*).
 """
 from __future__ import annotations
 
@@ -390,6 +392,33 @@ def dataclasses_replace(obj):
     return dataclasses.replace(obj)
 
 
+def run_graph_point(sh, banks, T, steps, warmup, dev):
+    """Decode step replayed as captured HIP graphs (ft_moe_graph_*), one per
+    weight bank, rotating like the eager loop; returns ms per step."""
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+
+    graphs = []
+    for i, b in enumerate(banks):
+        x = synth.gen_x(sh, T, step=i, device=dev).contiguous()
+        st = ft.LayerStep(b.wts, x, sh.k, b.wr, bias=b.bias)
+        graphs.append(st.capture())
+    for i in range(warmup):
+        graphs[i % len(graphs)].launch()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[(warmup + i) % len(graphs)].launch()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    for g in graphs:
+        g.close()
+    return ms
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -433,8 +462,10 @@ def main():
     decode = []
     for T in dec:
         r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
+        g_ms = run_graph_point(sh, banks, T, max(args.steps, 50), args.warmup, dev)
         decode.append({
-            "T": T, "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+            "T": T, "tokens_per_s": T / (g_ms / 1e3), "ms_per_step": g_ms,
+            "eager_tokens_per_s": r["tokens_per_s"], "eager_ms_per_step": r["ms_per_step"],
             "ffn_us": r["ffn_ms"] * 1e3, "gate_up_us": r["gemm1_ms"] * 1e3,
             "down_us": r["gemm2_ms"] * 1e3, "active_experts": r["active_experts"],
             "down_gbs": r["gemm2_gbs"],

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libftmoe.so")
 SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip",
-           "ffn_stream.hip", "combine.hip"]
+           "ffn_stream.hip", "combine.hip", "step.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

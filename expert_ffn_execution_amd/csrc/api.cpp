@@ -38,11 +38,15 @@ ft_status set_error(ft_status st, const char* fmt, ...) {
 void clear_error() { g_err[0] = 0; }
 
 static hipEvent_t g_prof[PROF_N][2];
+// Set while this thread captures a step into a graph: the profiling events
+// are then not recorded (they would become graph nodes).
+static thread_local bool g_capturing = false;
+void set_capturing(bool on) { g_capturing = on; }
 void prof_begin(int which, hipStream_t s) {
-    if (g_prof[which][0]) (void)hipEventRecord(g_prof[which][0], s);
+    if (g_prof[which][0] && !g_capturing) (void)hipEventRecord(g_prof[which][0], s);
 }
 void prof_end(int which, hipStream_t s) {
-    if (g_prof[which][1]) (void)hipEventRecord(g_prof[which][1], s);
+    if (g_prof[which][1] && !g_capturing) (void)hipEventRecord(g_prof[which][1], s);
 }
 
 static std::atomic<int> g_ffn_path{0};

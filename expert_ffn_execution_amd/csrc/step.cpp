@@ -1,0 +1,105 @@
+// step.cpp -- one whole MoE-layer step (route -> align -> ffn -> combine) as a
+// single call, and the same step captured once into a HIP graph.
+//
+// At decode the step is a handful of small kernels, and the host time to
+// enqueue them (argument checks, launch calls) and the gaps between them
+// exceed the FFN's own few microseconds.  The pages list graph-compatible
+// execution among the runtime's features (refft.com guide, "深度解析", the
+// runtime feature list); here a step is captured on a private stream into a
+// hipGraph whose replay enqueues every kernel with one call.  Nothing in the
+// step allocates, synchronises or writes memset nodes (empty inputs are
+// cleared by a fill kernel), so the captured graph holds kernel nodes only.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace ft {
+void set_capturing(bool on);
+}
+
+using namespace ft;
+
+struct ft_moe_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+ft_status run_step(const ft_moe_step* st, void* stream) {
+    ft_status r = ft_moe_route(st->x, st->act_dt, st->w_router, nullptr, st->bias, st->T,
+                               st->weights.H, st->weights.E, st->k, st->logits, st->topk_ids,
+                               st->topk_w, stream);
+    if (r != FT_OK) return r;
+    r = ft_moe_align(st->topk_ids, st->T, st->k, st->weights.E, st->counts, st->offsets,
+                     st->perm, st->inv_perm, st->align_ws, st->align_ws_bytes, stream);
+    if (r != FT_OK) return r;
+    r = ft_moe_ffn(&st->weights, st->x, st->act_dt, st->T, st->k, st->perm, st->offsets,
+                   st->slot_of_expert, st->y_perm, st->y_dt, st->ffn_ws, st->ffn_ws_bytes, stream);
+    if (r != FT_OK) return r;
+    return ft_moe_combine(st->y_perm, st->y_dt, st->inv_perm, st->topk_w, st->T, st->k,
+                          st->weights.H, st->weights.n_shared, st->out, st->out_dt, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+ft_status ft_moe_step_run(const ft_moe_step* st, void* stream) {
+    clear_error();
+    FT_CHECK_ARG(st, "null step");
+    return run_step(st, stream);
+}
+
+ft_status ft_moe_graph_create(const ft_moe_step* st, void* stream, ft_moe_graph** out) {
+    clear_error();
+    FT_CHECK_ARG(st && out, "null step / out");
+    *out = nullptr;
+    // one eager step first: every argument check runs, and per-kernel
+    // attributes (dynamic LDS limits) are set outside the capture
+    ft_status r = run_step(st, stream);
+    if (r != FT_OK) return r;
+    FT_HIP(hipStreamSynchronize((hipStream_t)stream));
+
+    hipStream_t cap = nullptr;
+    FT_HIP(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking));
+    ft_moe_graph* g = new ft_moe_graph;
+    hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        set_capturing(true);  // profile events stay out of the graph
+        r = run_step(st, cap);
+        set_capturing(false);
+        e = hipStreamEndCapture(cap, &g->graph);
+    }
+    if (e == hipSuccess && r == FT_OK) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cap);
+    if (r != FT_OK || e != hipSuccess) {
+        if (g->exec) (void)hipGraphExecDestroy(g->exec);
+        if (g->graph) (void)hipGraphDestroy(g->graph);
+        delete g;
+        if (r != FT_OK) return r;
+        return set_error(FT_ERR_HIP, "graph capture failed: %s", hipGetErrorString(e));
+    }
+    *out = g;
+    return FT_OK;
+}
+
+ft_status ft_moe_graph_launch(ft_moe_graph* g, void* stream) {
+    clear_error();
+    FT_CHECK_ARG(g && g->exec, "null graph");
+    FT_HIP(hipGraphLaunch(g->exec, (hipStream_t)stream));
+    return FT_OK;
+}
+
+ft_status ft_moe_graph_destroy(ft_moe_graph* g) {
+    clear_error();
+    if (!g) return FT_OK;
+    ft_status r = FT_OK;
+    if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) r = FT_ERR_HIP;
+    if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) r = FT_ERR_HIP;
+    delete g;
+    if (r != FT_OK) return set_error(r, "graph destroy failed");
+    return FT_OK;
+}
+
+}  // extern "C"

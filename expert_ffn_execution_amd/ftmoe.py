@@ -30,7 +30,8 @@ EXPORTS = [
     "ft_expert_layout", "ft_moe_ffn_workspace", "ft_moe_ffn", "ft_moe_ffn_set_path",
     "ft_set_profile_events", "ft_moe_combine", "ft_slot_cache_create", "ft_slot_cache_destroy",
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
-    "ft_slot_cache_stats", "ft_slot_cache_lookup",
+    "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_moe_step_run", "ft_moe_graph_create",
+    "ft_moe_graph_launch", "ft_moe_graph_destroy",
 ]
 
 
@@ -44,6 +45,17 @@ class MoeWeights(C.Structure):
     _fields_ = [("w_dt", C.c_int), ("E", C.c_int), ("H", C.c_int), ("I", C.c_int),
                 ("n_shared", C.c_int), ("pool", C.c_void_p), ("slot_stride", C.c_size_t),
                 ("shared_slot", C.c_int)]
+
+
+class MoeStep(C.Structure):
+    _fields_ = [("weights", MoeWeights), ("x", C.c_void_p), ("act_dt", C.c_int),
+                ("w_router", C.c_void_p), ("bias", C.c_void_p), ("T", C.c_int), ("k", C.c_int),
+                ("slot_of_expert", C.c_void_p), ("logits", C.c_void_p), ("topk_ids", C.c_void_p),
+                ("topk_w", C.c_void_p), ("counts", C.c_void_p), ("offsets", C.c_void_p),
+                ("perm", C.c_void_p), ("inv_perm", C.c_void_p), ("align_ws", C.c_void_p),
+                ("align_ws_bytes", C.c_size_t), ("y_perm", C.c_void_p), ("y_dt", C.c_int),
+                ("ffn_ws", C.c_void_p), ("ffn_ws_bytes", C.c_size_t), ("out", C.c_void_p),
+                ("out_dt", C.c_int)]
 
 
 class SlotCacheDesc(C.Structure):
@@ -99,6 +111,10 @@ def load() -> C.CDLL:
         "ft_slot_cache_evict": [P, I32, I32],
         "ft_slot_cache_stats": [P, C.POINTER(CacheStats)],
         "ft_slot_cache_lookup": [P, I32, I32],
+        "ft_moe_step_run": [C.POINTER(MoeStep), P],
+        "ft_moe_graph_create": [C.POINTER(MoeStep), P, C.POINTER(P)],
+        "ft_moe_graph_launch": [P, P],
+        "ft_moe_graph_destroy": [P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -256,6 +272,78 @@ def combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, w: torch.Tensor, n_sha
     _check(load().ft_moe_combine(_p(y_perm), _dt(y_perm), _p(inv_perm), _p(w), T, k, H,
                                  n_shared, _p(out), _dt(out), _stream(stream)))
     return out
+
+
+class LayerStep:
+    """The buffers of one whole MoE-layer step and its ft_moe_step descriptor.
+
+    x, w_router, bias and slot_of_expert are the caller's tensors (refill x in
+    place between runs); everything else is allocated here, once.
+    """
+
+    def __init__(self, wts: MoeWeights, x: torch.Tensor, k: int, w_router: torch.Tensor,
+                 bias: Optional[torch.Tensor] = None,
+                 slot_of_expert: Optional[torch.Tensor] = None, y_dtype=torch.bfloat16,
+                 out_dtype=torch.bfloat16):
+        T, H = x.shape
+        E = wts.E
+        dev = x.device
+        _dev(x, w_router, bias, slot_of_expert)
+        i32, f32 = torch.int32, torch.float32
+        self.x, self.w_router, self.bias, self.slot_of_expert = x, w_router, bias, slot_of_expert
+        self.logits = torch.empty((T, E), dtype=f32, device=dev)
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.perm = torch.empty(max(1, T * k), dtype=i32, device=dev)
+        self.inv = torch.empty(max(1, T * k), dtype=i32, device=dev)
+        self.aws = torch.empty(max(1, align_workspace(T, k, E)), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((T * k + wts.n_shared * T, H), dtype=y_dtype, device=dev)
+        self.fws = torch.empty(max(256, ffn_workspace(wts, T, k)), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, H), dtype=out_dtype, device=dev)
+        self.desc = MoeStep(wts, x.data_ptr(), _dt(x), w_router.data_ptr(),
+                            None if bias is None else bias.data_ptr(), T, k,
+                            None if slot_of_expert is None else slot_of_expert.data_ptr(),
+                            self.logits.data_ptr(), self.ids.data_ptr(), self.w.data_ptr(),
+                            self.counts.data_ptr(), self.offsets.data_ptr(), self.perm.data_ptr(),
+                            self.inv.data_ptr(), self.aws.data_ptr(), self.aws.numel(),
+                            self.y.data_ptr(), _dt(self.y), self.fws.data_ptr(),
+                            self.fws.numel(), self.out.data_ptr(), _dt(self.out))
+
+    def run(self, stream=None) -> torch.Tensor:
+        """ft_moe_step_run: route -> align -> ffn -> combine; returns out."""
+        _check(load().ft_moe_step_run(C.byref(self.desc), _stream(stream)))
+        return self.out
+
+    def capture(self, stream=None) -> "Graph":
+        """ft_moe_graph_create (runs the step once, then captures it)."""
+        return Graph(self, stream)
+
+
+class Graph:
+    """A captured LayerStep (ft_moe_graph_*); keeps the step's buffers alive."""
+
+    def __init__(self, step: LayerStep, stream=None):
+        self.step = step
+        h = C.c_void_p()
+        _check(load().ft_moe_graph_create(C.byref(step.desc), _stream(stream), C.byref(h)))
+        self.h = h
+
+    def launch(self, stream=None) -> torch.Tensor:
+        _check(load().ft_moe_graph_launch(self.h, _stream(stream)))
+        return self.step.out
+
+    def close(self):
+        if self.h:
+            _check(load().ft_moe_graph_destroy(self.h))
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def set_profile_events(which: int, start, stop):

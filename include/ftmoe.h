@@ -9,6 +9,8 @@
  *   ft_moe_ffn      grouped gate/up GEMM + SwiGLU + down GEMM over the routed
  *                   experts only, weights read through a slot table
  *   ft_moe_combine  gate-weighted sum back to token order
+ *   ft_moe_step_run / ft_moe_graph_*  the four as one step, eager or as a
+ *                   captured HIP graph
  *   ft_slot_cache_* LRU expert-slot cache over a pinned host expert pool, with
  *                   the next layer's missing experts copied while this layer
  *                   computes
@@ -188,6 +190,59 @@ ft_status ft_set_profile_events(int which, void* start, void* stop);
 ft_status ft_moe_combine(const void* y_perm, ft_dtype y_dt, const int32_t* inv_perm,
                          const float* topk_w, int T, int k, int H, int n_shared, void* out,
                          ft_dtype out_dt, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Whole-layer step and its graph.
+ *
+ * ft_moe_step_run enqueues one MoE-layer step on `stream`: ft_moe_route (from
+ * x and w_router), ft_moe_align, ft_moe_ffn, ft_moe_combine, with the buffers
+ * named in the descriptor; it returns the first failing call's status (the
+ * calls before it stay enqueued).
+ *
+ * ft_moe_graph_create runs the step once eagerly on `stream` (checking every
+ * argument), waits for it, then captures the same step on a private stream
+ * into a HIP graph.  ft_moe_graph_launch replays it on any stream: the kernels
+ * read and write the descriptor's buffers as they were at capture time, so a
+ * caller refills x (and, with a slot cache, the slot table) in place between
+ * replays.  The pages list graph-compatible execution among the runtime's
+ * features (refft.com guide, "深度解析", the runtime feature list).  The
+ * descriptor is copied; the buffers it names must outlive the graph.  Profile
+ * events (ft_set_profile_events) are not captured.  Replays of one graph must
+ * not overlap (they share every buffer).  Errors: FT_ERR_INVALID_ARG for a
+ * NULL descriptor / graph, the step's own errors, FT_ERR_HIP when capture or
+ * instantiation fails.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    ft_moe_weights weights;
+    const void* x;            /* [T][H] device, act_dt */
+    ft_dtype act_dt;          /* FT_BF16 (FT_F32 with FT_F32 weights) */
+    const void* w_router;     /* [E][H] device, act_dt */
+    const float* bias;        /* [E] device or NULL */
+    int T, k;
+    const int32_t* slot_of_expert; /* [E] device or NULL (identity) */
+    float* logits;            /* [T][E] device */
+    int32_t* topk_ids;        /* [T][k] device */
+    float* topk_w;            /* [T][k] device */
+    int32_t* counts;          /* [E] device */
+    int32_t* offsets;         /* [E+1] device */
+    int32_t* perm;            /* [T*k] device */
+    int32_t* inv_perm;        /* [T*k] device */
+    void* align_ws;           /* >= ft_moe_align_workspace(T, k, E) bytes */
+    size_t align_ws_bytes;
+    void* y_perm;             /* [T*k + n_shared*T][H] device, y_dt */
+    ft_dtype y_dt;
+    void* ffn_ws;             /* >= ft_moe_ffn_workspace(&weights, T, k) bytes */
+    size_t ffn_ws_bytes;
+    void* out;                /* [T][H] device, out_dt */
+    ft_dtype out_dt;
+} ft_moe_step;
+
+typedef struct ft_moe_graph ft_moe_graph;
+
+ft_status ft_moe_step_run(const ft_moe_step* step, void* stream);
+ft_status ft_moe_graph_create(const ft_moe_step* step, void* stream, ft_moe_graph** out);
+ft_status ft_moe_graph_launch(ft_moe_graph* graph, void* stream);
+ft_status ft_moe_graph_destroy(ft_moe_graph* graph);
 
 /* --------------------------------------------------------------------------
  * Expert slot cache.

@@ -123,3 +123,53 @@ def test_slot_cache_rejects_bad_descriptors():
     assert lib.ft_slot_cache_create(C.byref(d), C.byref(h)) == ft.ERR_INVALID_ARG
     d = ft.SlotCacheDesc(3, 8, 1024, 4096, 1024, 4096, 1024, 16, 1)     # 16 % 3 per-layer
     assert lib.ft_slot_cache_create(C.byref(d), C.byref(h)) == ft.ERR_INVALID_ARG
+
+
+def _step(k=2, T=4):
+    w = ft.MoeWeights(ft.BF16, 8, 128, 128, 0, 4096, 3 * 128 * 128 * 2, 0)
+    p = 4096
+    return ft.MoeStep(w, p, ft.BF16, p, None, T, k, None, p, p, p, p, p, p, p, p, 1 << 20, p,
+                      ft.BF16, p, 1 << 20, p, ft.BF16)
+
+
+def test_step_and_graph_reject_bad_arguments():
+    lib = ft.load()
+    h = C.c_void_p()
+    assert lib.ft_moe_step_run(None, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_graph_create(None, None, C.byref(h)) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_graph_launch(None, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_graph_destroy(None) == ft.OK
+    # the step's own checks run before anything is enqueued or captured
+    bad = _step(k=0)
+    assert lib.ft_moe_step_run(C.byref(bad), None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_graph_create(C.byref(bad), None, C.byref(h)) == ft.ERR_INVALID_ARG
+    assert not h.value
+    assert lib.ft_moe_step_run(C.byref(_step(k=9)), None) == ft.ERR_INVALID_ARG
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """ctypes mirrors of the header's structs: same size and field offsets as
+    the C compiler gives them."""
+    structs = {"ft_moe_weights": ft.MoeWeights, "ft_moe_step": ft.MoeStep,
+               "ft_slot_cache_desc": ft.SlotCacheDesc, "ft_map_stats": ft.MapStats,
+               "ft_cache_stats": ft.CacheStats}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ftmoe.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in py._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines += ['return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    r = subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    want = []
+    for cname, py in structs.items():
+        want.append(f"{cname} size {C.sizeof(py)}")
+        for f in py._fields_:
+            want.append(f"{cname} {f[0]} {getattr(py, f[0]).offset}")
+    assert [l for l in got if l] == want

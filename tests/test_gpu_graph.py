@@ -1,0 +1,99 @@
+"""GPU checks of the whole-layer step (ft_moe_step_run) and of the same step
+captured into a HIP graph (ft_moe_graph_*).
+
+The eager step is checked against the oracle (picks bit-exact on the step's
+own fp32 logits, outputs within the layer tolerance).  Each graph is then
+replayed several times, with new activations copied into x in place and an
+eager step plus synchronisations between the replays; every replay must give
+the same bits (logits, picks, gates, output) as an eager step on the same x.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from expert_ffn_execution_amd import ftmoe as ft  # noqa: E402
+from expert_ffn_execution_amd import synth  # noqa: E402
+from oracle import oracle as orc  # noqa: E402
+from tests.layer_harness import DEV, Layer, check_close, oracle_out  # noqa: E402
+
+SHAPES = {
+    "tiny_f32": synth.TINY_F32,
+    "small_bf16": synth.LayerShape("graph_small_bf16", H=512, E=16, k=4, I=384, bias="zipf"),
+    "small_mx": synth.LayerShape("graph_small_mx", H=512, E=16, k=6, I=256, n_shared=1,
+                                 wdtype="mxfp4"),
+    "35b_a3b_bf16": synth.A3B_BF16,
+    "284b_a13b_mxfp4": synth.A13B_MXFP4,
+}
+# (shape, T, permuted slots): decode sizes take the streaming kernels, T = 300
+# on the small shapes the MFMA tiles (tile list built on the device)
+CASES = [("tiny_f32", 64, False), ("small_bf16", 3, True), ("small_bf16", 300, False),
+         ("small_mx", 5, False), ("small_mx", 300, True), ("35b_a3b_bf16", 1, False),
+         ("35b_a3b_bf16", 16, False), ("284b_a13b_mxfp4", 1, False)]
+_LAYERS = {}
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def _layer(name, permuted):
+    key = (name, permuted)
+    if key not in _LAYERS:
+        _LAYERS.clear()
+        torch.cuda.empty_cache()
+        sh = SHAPES[name]
+        perm = None
+        if permuted:
+            n = synth.n_experts_total(sh)
+            perm = list(np.random.default_rng(5).permutation(n))
+        big = sh.E >= 128
+        _LAYERS[key] = Layer(sh, gen_device=DEV if big else "cpu", keep_host=not big,
+                             slot_perm=perm)
+    return _LAYERS[key]
+
+
+def _snapshot(step):
+    return [t.clone() for t in (step.logits, step.ids, step.w, step.out)]
+
+
+@pytest.mark.parametrize("name,T,permuted", CASES)
+def test_step_and_graph(name, T, permuted):
+    _say("step/graph", name, "T", T, "permuted slots" if permuted else "identity slots")
+    L = _layer(name, permuted)
+    sh = L.shape
+    act = torch.float32 if sh.adtype == "f32" else torch.bfloat16
+    y_dt = torch.float32 if sh.wdtype == "f32" else torch.bfloat16
+    wr = synth.gen_router(sh, device=DEV)
+    bias = synth.gen_bias(sh, device=DEV)
+    x = synth.gen_x(sh, T, step=3, device=DEV).contiguous()
+    step = ft.LayerStep(L.wts, x, sh.k, wr, bias=bias, slot_of_expert=L.slot_table,
+                        y_dtype=y_dt, out_dtype=act)
+
+    # eager step against the oracle
+    step.run()
+    torch.cuda.synchronize()
+    lg = step.logits.cpu().numpy()
+    ref_ids, ref_w = orc.route(lg, sh.k, None if bias is None else bias.cpu().numpy())
+    assert np.array_equal(step.ids.cpu().numpy(), ref_ids)
+    assert np.max(np.abs(step.w.cpu().numpy() - ref_w)) <= 1e-6
+    check_close(step.out, oracle_out(L, x.cpu(), ref_ids, ref_w), sh.wdtype,
+                f"step {name} T{T}")
+
+    # graph replays, each against an eager step on the same activations
+    g = step.capture()
+    try:
+        for r in range(3):
+            x.copy_(synth.gen_x(sh, T, step=10 + r, device=DEV))
+            torch.cuda.synchronize()
+            g.launch()
+            torch.cuda.synchronize()
+            got = _snapshot(step)
+            step.run()
+            torch.cuda.synchronize()
+            want = _snapshot(step)
+            for a, b, what in zip(got, want, ("logits", "ids", "w", "out")):
+                assert torch.equal(a, b), f"replay {r}: {what} differs from the eager step"
+    finally:
+        g.close()
