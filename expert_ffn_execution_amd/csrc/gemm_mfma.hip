@@ -656,6 +656,19 @@ hipError_t launch_tile(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const
 // ---------------------------------------------------------------------------
 // tile list
 // ---------------------------------------------------------------------------
+// Rows [start, start + rows) of tile m of a segment of c rows cut into
+// n = ceil(c / BM) tiles (BM a multiple of 32): the segment's s = ceil(c / 32)
+// sub-tiles of 32 rows are dealt evenly, the first s % n tiles taking one
+// more, so no tile exceeds BM rows and none is empty.  An expert just past a
+// multiple of BM rows thus gets two balanced tiles rather than a full one and
+// a nearly empty one that streams the same weight panel, for the same number
+// of MFMA sub-tiles.
+__device__ __forceinline__ void tile_span(int c, int n, int m, int& start, int& rows) {
+    const int s = (c + 31) / 32, q = s / n, r = s % n;
+    start = 32 * (m * q + min(m, r));
+    rows = min(32 * (q + (m < r ? 1 : 0)), c - start);
+}
+
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ slot_of,
                                                            int E, int T, int n_shared,
@@ -681,13 +694,15 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     }
     const int base = scan[e] - cnt, total = scan[1023];
     for (int m = 0; m < cnt; ++m) {
-        int idx = base + m;
-        if (idx < max_tiles) tiles[idx] = TileDesc{e, off + m * BMr, min(BMr, c - m * BMr), slot};
+        int idx = base + m, start, rows;
+        tile_span(c, cnt, m, start, rows);
+        if (idx < max_tiles) tiles[idx] = TileDesc{e, off + start, rows, slot};
     }
     int ns = n_shared ? (T + BMr - 1) / BMr : 0;
     for (int m = e; m < ns; m += 1024) {
-        int idx = total + m;
-        if (idx < max_tiles) tiles[idx] = TileDesc{E, m * BMr, min(BMr, T - m * BMr), shared_slot};
+        int idx = total + m, start, rows;
+        tile_span(T, ns, m, start, rows);
+        if (idx < max_tiles) tiles[idx] = TileDesc{E, start, rows, shared_slot};
     }
     if (e == 0) *n_tiles = min(total + ns, max_tiles);
 }
