@@ -68,11 +68,49 @@ struct HipEngine final : ftp::Engine {
         c->read_valid[slot] = 1;
         return true;
     }
+    bool move(int, int) override { return false; }  // only ResizeEngine moves slots
 };
 
-ft_status hip_status(const HipEngine& eng, ft_status st) {
-    if (eng.err != hipSuccess)
-        return ft::set_error(FT_ERR_HIP, "slot cache: %s", hipGetErrorString(eng.err));
+// Engine of a resize: moves copy slot src of the current array into slot dst
+// of the (possibly new) array on the copy stream, ordered after src's fill and
+// dst's last reader; dst's fill event (of the new event set) marks completion.
+struct ResizeEngine final : ftp::Engine {
+    ft_slot_cache* c;
+    hipStream_t copy_s;
+    char* dst_base;
+    std::vector<hipEvent_t>& filled_new;
+    std::vector<hipEvent_t>& read_new;
+    std::vector<char>& read_valid_new;
+    hipError_t err = hipSuccess;
+    ResizeEngine(ft_slot_cache* cc, hipStream_t cp, char* base, std::vector<hipEvent_t>& f,
+                 std::vector<hipEvent_t>& r, std::vector<char>& rv)
+        : c(cc), copy_s(cp), dst_base(base), filled_new(f), read_new(r), read_valid_new(rv) {}
+    bool ok(hipError_t e) {
+        if (e != hipSuccess && err == hipSuccess) err = e;
+        return e == hipSuccess;
+    }
+    bool copy(int, int, int) override { return false; }
+    bool copy_done(int slot) override {
+        hipError_t e = hipEventQuery(c->filled[slot]);
+        if (e == hipErrorNotReady) return false;
+        return ok(e);
+    }
+    bool compute_wait(int) override { return false; }
+    bool record_read(int) override { return false; }
+    bool move(int src, int dst) override {
+        if (!ok(hipStreamWaitEvent(copy_s, c->filled[src], 0))) return false;
+        if (read_valid_new[dst] && !ok(hipStreamWaitEvent(copy_s, read_new[dst], 0))) return false;
+        const char* from = (const char*)c->d.dev_slots + (size_t)src * c->d.slot_stride;
+        char* to = dst_base + (size_t)dst * c->d.slot_stride;
+        if (!ok(hipMemcpyAsync(to, from, c->d.expert_bytes, hipMemcpyDeviceToDevice, copy_s)))
+            return false;
+        return ok(hipEventRecord(filled_new[dst], copy_s));
+    }
+};
+
+ft_status hip_status(hipError_t err, ft_status st) {
+    if (err != hipSuccess)
+        return ft::set_error(FT_ERR_HIP, "slot cache: %s", hipGetErrorString(err));
     if (st == FT_ERR_CAPACITY)
         return ft::set_error(st, "slot cache: held slots plus this request exceed capacity");
     if (st == FT_ERR_INVALID_ARG)
@@ -83,8 +121,13 @@ ft_status hip_status(const HipEngine& eng, ft_status st) {
         return ft::set_error(st,
                              "Disabling MoE prefetch overlap: the slot cache cannot hold the "
                              "next layer's experts beside the held ones");
+    if (st == FT_ERR_UNSUPPORTED)
+        return ft::set_error(st, "slot cache: resizing needs the global scope");
     return st;
 }
+ft_status hip_status(const HipEngine& eng, ft_status st) { return hip_status(eng.err, st); }
+
+hipError_t make_event(hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); }
 
 }  // namespace
 
@@ -203,6 +246,48 @@ ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out) {
     FT_CHECK_ARG(c && out, "null cache/out");
     *out = c->policy.stats();
     return FT_OK;
+}
+
+ft_status ft_slot_cache_resize(ft_slot_cache* c, int n_slots, void* dev_slots, void* copy_stream) {
+    ft::clear_error();
+    FT_CHECK_ARG(c && n_slots > 0, "null cache or n_slots <= 0");
+    const int old_n = c->d.n_slots;
+    const bool moved = dev_slots && dev_slots != c->d.dev_slots;
+    // the event set of the new size: slots below min(old, new) keep theirs
+    std::vector<hipEvent_t> filled(n_slots, nullptr), read(n_slots, nullptr);
+    std::vector<char> read_valid(n_slots, 0);
+    for (int s = 0; s < n_slots; ++s) {
+        if (s < old_n) {
+            filled[s] = c->filled[s];
+            read[s] = c->read[s];
+            read_valid[s] = c->read_valid[s];
+        } else if (make_event(&filled[s]) != hipSuccess || make_event(&read[s]) != hipSuccess) {
+            for (int q = old_n; q <= s; ++q) {
+                if (filled[q]) (void)hipEventDestroy(filled[q]);
+                if (read[q]) (void)hipEventDestroy(read[q]);
+            }
+            return ft::set_error(FT_ERR_HIP, "hipEventCreate failed");
+        }
+    }
+    char* base = (char*)(moved ? dev_slots : c->d.dev_slots);
+    ResizeEngine eng(c, (hipStream_t)copy_stream, base, filled, read, read_valid);
+    const ft_status r = c->policy.resize(eng, n_slots, moved);
+    if (r != FT_OK && r != FT_ERR_HIP) {  // nothing changed
+        for (int s = old_n; s < n_slots; ++s) (void)hipEventDestroy(filled[s]), (void)hipEventDestroy(read[s]);
+        return hip_status(eng.err, r);
+    }
+    // the policy now has n_slots slots: retire the events of dropped slots
+    // (after the work they mark) and switch to the new set and array
+    for (int s = n_slots; s < old_n; ++s) {
+        (void)hipEventSynchronize(c->filled[s]), (void)hipEventDestroy(c->filled[s]);
+        (void)hipEventSynchronize(c->read[s]), (void)hipEventDestroy(c->read[s]);
+    }
+    c->filled.swap(filled);
+    c->read.swap(read);
+    c->read_valid.swap(read_valid);
+    c->d.n_slots = n_slots;
+    c->d.dev_slots = base;
+    return hip_status(eng.err, r);
 }
 
 int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert) {

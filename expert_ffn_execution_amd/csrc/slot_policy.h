@@ -36,6 +36,10 @@ struct Engine {
     virtual bool compute_wait(int slot) = 0;
     // record: work enqueued on the compute stream so far is the last reader of `slot`
     virtual bool record_read(int slot) = 0;
+    // resize: copy the device contents of slot `src` into slot `dst` of the
+    // (possibly new) slot array, after the last copy into `src` and the last
+    // reader of `dst`, leaving a completion marker for `dst`
+    virtual bool move(int src, int dst) = 0;
 };
 
 struct Entry {
@@ -166,6 +170,71 @@ class Policy {
             if (s >= 0) drop(s);
         }
         return FT_OK;
+    }
+
+    // Change the number of slots to n_new (global scope; the pages describe the
+    // expert cache being resized in slots at run time, without a restart or a
+    // reload of the weights: freelamp.com article, section 2.3; refft.com
+    // guide, "深度解析").  Nothing may be held.  Least-recently-used entries
+    // that no copy is filling are dropped until the residents fit; survivors
+    // keep their slot when it is below n_new, else move (ascending old slot) to
+    // the lowest free slot below n_new.  With `moved_array` (the caller gives a
+    // new slot array) every survivor is copied, else only the relocated ones;
+    // copied entries count as in flight until their move completes.
+    // FT_ERR_BUSY / FT_ERR_INVALID_ARG / FT_ERR_UNSUPPORTED change nothing.  A
+    // failed move leaves the cache empty at the new size (FT_ERR_HIP).
+    ft_status resize(Engine& eng, int n_new, bool moved_array) {
+        if (n_new <= 0) return FT_ERR_INVALID_ARG;
+        if (scope_ != FT_SCOPE_GLOBAL) return FT_ERR_UNSUPPORTED;
+        refresh(eng);
+        int inflight = 0, resident = 0;
+        for (const Entry& en : slots_) {
+            if (en.held) return FT_ERR_BUSY;
+            if (en.copying) ++inflight;
+            if (en.layer >= 0) ++resident;
+        }
+        if (inflight > n_new) return FT_ERR_BUSY;
+        while (resident > n_new) {  // an evictable entry exists: inflight <= n_new
+            int best = -1;
+            for (int s = 0; s < S_; ++s) {
+                const Entry& en = slots_[s];
+                if (en.layer < 0 || !evictable(en)) continue;
+                if (best < 0 || en.last < slots_[best].last) best = s;
+            }
+            drop(best);
+            st_.evictions++;
+            --resident;
+        }
+        std::vector<int> dst_of(S_, -1);
+        std::vector<char> taken(n_new, 0);
+        for (int s = 0; s < S_ && s < n_new; ++s)
+            if (slots_[s].layer >= 0) dst_of[s] = s, taken[s] = 1;
+        int d = 0;
+        for (int s = n_new; s < S_; ++s) {
+            if (slots_[s].layer < 0) continue;
+            while (taken[d]) ++d;  // d < n_new: resident <= n_new
+            taken[d] = 1;
+            dst_of[s] = d;
+        }
+        bool failed = false;
+        for (int s = 0; s < S_ && !failed; ++s)
+            if (dst_of[s] >= 0 && (dst_of[s] != s || moved_array)) failed = !eng.move(s, dst_of[s]);
+        std::vector<Entry> next(n_new);
+        for (int s = 0; s < S_; ++s) {
+            if (dst_of[s] < 0) continue;
+            Entry& en = slots_[s];
+            if (failed) {
+                where_[(size_t)en.layer * E_ + en.expert] = -1;
+                continue;
+            }
+            next[dst_of[s]] = en;
+            if (dst_of[s] != s || moved_array) next[dst_of[s]].copying = true;
+            where_[(size_t)en.layer * E_ + en.expert] = dst_of[s];
+        }
+        slots_.swap(next);
+        S_ = n_new;
+        st_.n_slots = n_new;
+        return failed ? FT_ERR_HIP : FT_OK;
     }
 
     ft_cache_stats stats() const {

@@ -30,8 +30,8 @@ EXPORTS = [
     "ft_expert_layout", "ft_moe_ffn_workspace", "ft_moe_ffn", "ft_moe_ffn_set_path",
     "ft_set_profile_events", "ft_moe_combine", "ft_slot_cache_create", "ft_slot_cache_destroy",
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
-    "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_moe_step_run", "ft_moe_graph_create",
-    "ft_moe_graph_launch", "ft_moe_graph_destroy",
+    "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
+    "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy",
 ]
 
 
@@ -111,6 +111,7 @@ def load() -> C.CDLL:
         "ft_slot_cache_evict": [P, I32, I32],
         "ft_slot_cache_stats": [P, C.POINTER(CacheStats)],
         "ft_slot_cache_lookup": [P, I32, I32],
+        "ft_slot_cache_resize": [P, I32, P, P],
         "ft_moe_step_run": [C.POINTER(MoeStep), P],
         "ft_moe_graph_create": [C.POINTER(MoeStep), P, C.POINTER(P)],
         "ft_moe_graph_launch": [P, P],
@@ -439,6 +440,13 @@ class SlotCache:
 
     def evict(self, layer: int, expert: int = -1):
         _check(load().ft_slot_cache_evict(self.h, layer, expert))
+
+    def resize(self, n_slots: int, dev_slots: Optional[torch.Tensor] = None, copy=None):
+        """ft_slot_cache_resize; dev_slots (a new [n_slots, slot_stride] array) is
+        kept alive here in place of the old one."""
+        _check(load().ft_slot_cache_resize(self.h, n_slots, _p(dev_slots), _stream(copy)))
+        if dev_slots is not None:
+            self._keep = (self._keep[0], dev_slots)
 
     def stats(self) -> CacheStats:
         s = CacheStats()

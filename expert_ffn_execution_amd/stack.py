@@ -143,5 +143,20 @@ class SlotStack:
         self.stats.steps += 1
         return outs
 
+    def resize(self, n_slots: int, new_array: bool = False):
+        """Grow or shrink the device slot budget between steps
+        (ft_slot_cache_resize): resident experts that fit stay resident.  A
+        budget beyond the current array, or new_array, moves the slots into a
+        fresh array of n_slots (the old one is released once the copies are done)."""
+        dev_slots = None
+        if new_array or n_slots > self.slots.shape[0]:
+            dev_slots = torch.empty((n_slots, self.stride), dtype=torch.uint8, device=self.dev)
+        self.cache.resize(n_slots, dev_slots, copy=self.copy_stream)
+        if dev_slots is not None:
+            self.copy_stream.synchronize()
+            self.slots = dev_slots
+            self.wts = ft.make_weights(self.sh.wdtype, self.sh.E, self.sh.H, self.sh.I,
+                                       self.slots, n_shared=self.sh.n_shared, shared_slot=0)
+
     def close(self):
         self.cache.close()

@@ -329,6 +329,27 @@ ft_status ft_slot_cache_prefetch(ft_slot_cache* c, int layer, const int32_t* exp
  * or its copy is in flight. */
 ft_status ft_slot_cache_evict(ft_slot_cache* c, int layer, int expert);
 
+/* ft_slot_cache_resize -- change the number of device slots at run time,
+ * keeping what fits resident (no copy from the host pool): the pages describe
+ * the expert cache being resized in slots while the engine runs, without a
+ * restart or a reload of the weights (freelamp.com article, section 2.3;
+ * refft.com guide, "深度解析").  Global scope only (FT_ERR_UNSUPPORTED for
+ * per-layer caches); nothing may be held (FT_ERR_BUSY, nothing changes; also
+ * when more than n_slots copies are in flight).
+ *   Least-recently-used entries that no copy is filling are evicted until the
+ *   residents fit.  Survivors keep their slot index when it is below n_slots;
+ *   the others move to the lowest free slots below n_slots, by device-to-device
+ *   copies on `copy_stream`.
+ *   dev_slots: NULL or the current array to keep it (it must hold n_slots
+ *   slots of slot_stride bytes), or a new device array of n_slots slots, into
+ *   which every survivor is copied; free the old array only after
+ *   `copy_stream` has passed this call's copies.
+ * Slot tables written by earlier maps are stale afterwards: map again.  The
+ * copies are ordered after each source slot's fill and each destination
+ * slot's last reader; later maps make `compute` wait for them.  A failed copy
+ * returns FT_ERR_HIP and leaves the cache empty at the new size. */
+ft_status ft_slot_cache_resize(ft_slot_cache* c, int n_slots, void* dev_slots, void* copy_stream);
+
 /* Counters since creation. */
 ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
 

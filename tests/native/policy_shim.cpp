@@ -39,6 +39,16 @@ struct Mock final : ftp::Engine {
         rec(2, slot, -1, -1);
         return true;
     }
+    bool move(int src, int dst) override {
+        if (fail_next) {
+            fail_next = false;
+            return false;
+        }
+        rec(3, src, dst, -1);
+        if ((int)pending.size() <= dst) pending.resize(dst + 1, 0);
+        pending[dst] = auto_complete ? 0 : 1;
+        return true;
+    }
 };
 
 struct Shim {
@@ -77,6 +87,12 @@ int pol_prefetch(void* h, int layer, const int* experts, int n, int* issued) {
 int pol_evict(void* h, int layer, int expert) {
     Shim* s = static_cast<Shim*>(h);
     return s->pol.evict(s->eng, layer, expert);
+}
+int pol_resize(void* h, int n_slots, int moved_array) {
+    Shim* s = static_cast<Shim*>(h);
+    int r = s->pol.resize(s->eng, n_slots, moved_array != 0);
+    if (r == FT_OK || r == FT_ERR_HIP) s->eng.pending.resize(n_slots, 0);
+    return r;
 }
 int pol_lookup(void* h, int layer, int expert) {
     return static_cast<Shim*>(h)->pol.lookup(layer, expert);

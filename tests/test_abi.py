@@ -173,3 +173,8 @@ def test_struct_layouts_match_the_header(tmp_path):
         for f in py._fields_:
             want.append(f"{cname} {f[0]} {getattr(py, f[0]).offset}")
     assert [l for l in got if l] == want
+
+
+def test_slot_cache_resize_rejects_bad_arguments():
+    lib = ft.load()
+    assert lib.ft_slot_cache_resize(None, 8, None, None) == ft.ERR_INVALID_ARG

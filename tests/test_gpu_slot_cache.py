@@ -135,3 +135,46 @@ def test_full_size_slot_stack_sampled():
         _say("  hit rate", st.stats.hit_rate, "demand", st.stats.demand)
     finally:
         st.close()
+
+
+def _slots_hold_their_experts(st):
+    """Every resident (layer, expert) slot holds that expert's bytes."""
+    torch.cuda.synchronize()
+    st.copy_stream.synchronize()
+    n = 0
+    for l in range(st.L):
+        for e in range(st.n_exp):
+            s = st.cache.lookup(l, e)
+            if s < 0:
+                continue
+            got = st.slots[s, :st.expert_bytes].cpu()
+            assert torch.equal(got, st.host[l, e, :st.expert_bytes]), (l, e, s)
+            n += 1
+    return n
+
+
+def test_resize_between_steps_matches_resident():
+    """ft_slot_cache_resize: shrink in place, grow into a new array, shrink into
+    a new array; after each, the resident slots hold their experts' bytes and
+    decode steps stay bitwise equal to the all-resident layers."""
+    _say("slot stack resize")
+    L = 4
+    st = SlotStack(SMALL, L, n_slots=24)
+    try:
+        step = 0
+        for n_slots, new_array in ((24, False), (12, False), (40, False), (20, True)):
+            if step:
+                st.resize(n_slots, new_array)
+                cs = st.cache.stats()
+                assert cs.n_slots == n_slots and cs.resident <= n_slots
+                assert _slots_hold_their_experts(st) == cs.resident
+            for _ in range(2):
+                xs = _inputs(SMALL, L, 2, step)
+                outs = st.forward(xs)
+                for l in range(L):
+                    ref, _, _ = _resident_layer(st, l, xs[l])
+                    assert torch.equal(outs[l], ref), (n_slots, step, l)
+                step += 1
+        assert st.cache.stats().held == 0
+    finally:
+        st.close()

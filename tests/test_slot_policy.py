@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "native", "policy_shim.cpp")
 LIB = os.path.join(HERE, "native", "_build", "libpolicy_shim.so")
 
-OK, INVALID, CAPACITY, BUSY, HIP, WARN = 0, 1, 3, 5, 6, 100
+OK, INVALID, UNSUPPORTED, CAPACITY, BUSY, HIP, WARN = 0, 1, 2, 3, 5, 6, 100
 GLOBAL, PER_LAYER = 0, 1
 
 
@@ -44,6 +44,7 @@ def lib():
     L.pol_prefetch.argtypes = [P, C.c_int, P, C.c_int, P]
     L.pol_evict.argtypes = [P, C.c_int, C.c_int]
     L.pol_lookup.argtypes = [P, C.c_int, C.c_int]
+    L.pol_resize.argtypes = [P, C.c_int, C.c_int]
     L.pol_set_auto_complete.argtypes = [P, C.c_int]
     L.pol_log.argtypes = [P, P, C.c_int]
     L.pol_stats.argtypes = [P, P]
@@ -300,3 +301,157 @@ def test_stats_and_invalid_lists(lib):
     s = c.stats()
     assert s["maps"] == 2 and s["demand"] == 4 and s["hits"] == 1 and s["misses"] == 3
     assert s["bytes_h2d"] == 3 * 1000 and s["resident"] == 3 and s["held"] == 2
+
+
+# ---------------------------------------------------------------------------
+# resize (elastic slot budget)
+# ---------------------------------------------------------------------------
+def _resize(lib, c, n, moved=False):
+    return lib.pol_resize(c.h, n, 1 if moved else 0)
+
+
+def _ref_resize(ref, n, moved=False):
+    """Reference resize: evict least-recently-used keys until the residents
+    fit; keys below n stay put, the others move, in ascending old slot, to the
+    lowest free slot below n.  Returns the (src, dst) copies."""
+    assert not ref.held
+    while len(ref.slot_of) > n:
+        key = next(iter(ref.lru))
+        s = ref.slot_of.pop(key)
+        ref.key_at[s] = None
+        del ref.lru[key]
+    new_at = [None] * n
+    for s in range(min(n, ref.S)):
+        new_at[s] = ref.key_at[s]
+    moves = [(s, s) for s in range(min(n, ref.S)) if moved and new_at[s] is not None]
+    d = 0
+    for s in range(n, ref.S):
+        if ref.key_at[s] is None:
+            continue
+        while new_at[d] is not None:
+            d += 1
+        new_at[d] = ref.key_at[s]
+        moves.append((s, d))
+    ref.key_at, ref.S = new_at, n
+    ref.slot_of = {k: s for s, k in enumerate(new_at) if k is not None}
+    return sorted(moves)
+
+
+def _moves(log):
+    return sorted((s, d) for kind, s, d, _ in log if kind == 3)
+
+
+def test_resize_shrink_evicts_lru_and_relocates(lib):
+    c = Cache(lib, 1, 16, 8)
+    for e in range(8):                     # LRU order: 0 (oldest) .. 7
+        assert c.map(0, [e])[0] == OK
+        c.release(0)
+    c.log()
+    assert _resize(lib, c, 5) == OK
+    assert [c.lookup(0, e) for e in range(3)] == [-1, -1, -1]     # three oldest evicted
+    # experts 3, 4 kept slots 3, 4; experts 5, 6, 7 moved to the freed slots 0, 1, 2
+    assert [c.lookup(0, e) for e in range(3, 8)] == [3, 4, 0, 1, 2]
+    assert _moves(c.log()) == [(5, 0), (6, 1), (7, 2)]
+    s = c.stats()
+    assert s["n_slots"] == 5 and s["resident"] == 5 and s["evictions"] == 3
+    r, slots, st = c.map(0, [3, 4, 5, 6, 7])                      # all hits, no copies
+    assert r == OK and st == [5, 5, 0, 0] and _copies(c.log()) == []
+
+
+def test_resize_grow_keeps_everything_in_place(lib):
+    c = Cache(lib, 1, 16, 4)
+    assert c.map(0, [1, 2, 3, 4])[0] == OK
+    c.release(0)
+    before = [c.lookup(0, e) for e in range(16)]
+    c.log()
+    assert _resize(lib, c, 8) == OK
+    assert [c.lookup(0, e) for e in range(16)] == before and _moves(c.log()) == []
+    r, slots, st = c.map(0, [5, 6, 7, 8])                         # misses fill the new slots
+    assert r == OK and sorted(slots) == [4, 5, 6, 7] and st[3] == 4
+
+
+def test_resize_into_a_new_array_copies_every_survivor(lib):
+    c = Cache(lib, 1, 16, 6)
+    assert c.map(0, [0, 2, 4, 6, 8, 10])[0] == OK
+    c.release(0)
+    c.log()
+    assert _resize(lib, c, 4, moved=True) == OK
+    mv = _moves(c.log())
+    assert len(mv) == 4 and all(d < 4 for _, d in mv)
+    assert sorted(d for _, d in mv) == [0, 1, 2, 3]
+
+
+def test_resize_busy_and_bad_arguments_change_nothing(lib):
+    c = Cache(lib, 2, 8, 6)
+    assert c.map(0, [1, 2])[0] == OK                              # held
+    before = [c.lookup(0, e) for e in range(8)]
+    assert _resize(lib, c, 3) == BUSY
+    assert [c.lookup(0, e) for e in range(8)] == before and c.stats()["n_slots"] == 6
+    c.release(0)
+    lib.pol_set_auto_complete(c.h, 0)
+    assert c.prefetch(1, [0, 1, 2, 3])[0] == OK                   # four copies in flight
+    assert _resize(lib, c, 3) == BUSY                             # cannot drop in-flight entries
+    assert _resize(lib, c, 0) == INVALID
+    lib.pol_complete_all(c.h)
+    assert _resize(lib, c, 3) == OK and c.stats()["resident"] == 3
+    p = Cache(lib, 2, 8, 6, PER_LAYER)
+    assert _resize(lib, p, 4) == UNSUPPORTED
+
+
+def test_resize_in_flight_entries_survive_and_stay_in_flight(lib):
+    c = Cache(lib, 1, 8, 4)
+    lib.pol_set_auto_complete(c.h, 0)
+    assert c.prefetch(0, [0, 1, 2, 3])[0] == OK                   # slots 0..3 in flight
+    assert _resize(lib, c, 4, moved=True) == OK
+    assert c.stats()["in_flight"] == 4                            # now the moves are in flight
+    assert c.evict(0, 3) == BUSY
+    lib.pol_complete_all(c.h)
+    assert c.evict(0, 3) == OK
+
+
+def test_resize_failed_copy_empties_the_cache(lib):
+    c = Cache(lib, 1, 8, 6)
+    assert c.map(0, [0, 1, 2, 3, 4, 5])[0] == OK
+    c.release(0)
+    lib.pol_fail_next_copy(c.h)
+    assert _resize(lib, c, 4, moved=True) == HIP
+    s = c.stats()
+    assert s["n_slots"] == 4 and s["resident"] == 0
+    assert all(c.lookup(0, e) == -1 for e in range(8))
+    assert c.map(0, [0, 1])[0] == OK                              # usable again
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_resize_matches_reference_under_traffic(lib, seed):
+    """Random maps, prefetches and resizes (between steps, nothing held)
+    against the reference LRU and the reference resize."""
+    L, E = 3, 12
+    rng = np.random.default_rng(seed)
+    S = 10
+    c, ref = Cache(lib, L, E, S), RefLRU(L, E, S)
+    skew = np.exp(-1.1 * np.log(np.arange(1, E + 1)))
+    skew /= skew.sum()
+    for step in range(150):
+        layer = step % L
+        n = int(rng.integers(1, 5))
+        experts = sorted(set(rng.choice(E, size=n, p=skew).tolist()))
+        r, slots, _ = c.map(layer, experts)
+        rr, payload = ref.map(layer, experts)
+        assert r == rr, step
+        if r == OK:
+            assert slots == payload[0] and _copies(c.log()) == payload[1], step
+        pf = sorted(set(rng.choice(E, size=int(rng.integers(0, 3)), p=skew).tolist()))
+        r1, _ = c.prefetch((layer + 1) % L, pf)
+        r2, ref_copies = ref.prefetch((layer + 1) % L, pf)
+        assert r1 == r2 and _copies(c.log()) == ref_copies, step
+        c.release(layer)
+        ref.release(layer)
+        if step % 7 == 6:
+            n_new = int(rng.integers(4, 14))
+            moved = bool(rng.integers(0, 2))
+            assert _resize(lib, c, n_new, moved) == OK, step
+            assert _moves(c.log()) == _ref_resize(ref, n_new, moved), step
+            assert c.stats()["n_slots"] == n_new
+        for l2 in range(L):
+            for e in range(E):
+                assert c.lookup(l2, e) == ref.slot_of.get((l2, e), -1), (step, l2, e)
