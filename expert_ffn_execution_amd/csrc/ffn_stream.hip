@@ -6,9 +6,11 @@
 // time goes to moving expert weights, not to arithmetic -- chenxutan.com
 // article, "瓶颈为什么是带宽而不是容量").  These kernels therefore stream
 // weights with 16-byte loads and keep the routed tokens' activations in LDS.
-// They use vector ALU dot products (v_dot2_f32_bf16 for bf16; MXFP4 codes are
-// decoded exactly to bf16 first), not MFMA: the work per byte is too small for
-// a matrix tile to pay off.
+// bf16 (and fp32) weights use vector-ALU dot products (v_dot2_f32_bf16): the
+// work per byte is too small for a matrix tile to pay off.  MXFP4 weights are
+// decoded exactly to bf16 first, which costs as much ALU again per weight
+// byte; for the down projection with more than one token they go to matrix
+// cores instead (the second kernel below).
 //
 // Streaming.  HBM stays busy only if every CU keeps enough bytes in flight,
 // and the cross-lane sums at the end of each row must stay cheap.  A weight
@@ -129,6 +131,44 @@ __device__ bool find_group(const int32_t* __restrict__ offsets, const int32_t* _
     return false;
 }
 
+// The token rows of block group j: an expert (or the shared expert) and a
+// chunk of at most RCAP of its rows.  All block-uniform; readfirstlane makes
+// them scalar so that row loops branch on SGPRs instead of masking lanes.
+struct GroupRows {
+    int slot, r0, R;     // weight slot, first row of the chunk in the group, rows
+    size_t p_lo, orow0;  // first permutation position of the expert; output row base
+    bool shared;
+};
+__device__ __forceinline__ bool resolve_group(const StreamArgs& a, int j, int lane, GroupRows& gr) {
+    if (j < a.n_routed_groups) {
+        Group g;
+        if (!find_group(a.offsets, a.slot_of, a.E, a.RCAP, j, lane, g)) return false;
+        const int c = __builtin_amdgcn_readfirstlane(g.c);
+        gr.slot = __builtin_amdgcn_readfirstlane(g.slot);
+        const int lo = __builtin_amdgcn_readfirstlane(g.lo);
+        const int hi = __builtin_amdgcn_readfirstlane(g.hi);
+        gr.p_lo = lo;
+        gr.r0 = c * a.RCAP;
+        gr.R = min(a.RCAP, hi - lo - gr.r0);
+        gr.orow0 = gr.p_lo;
+        gr.shared = false;
+    } else {
+        gr.slot = a.shared_slot;
+        gr.p_lo = 0;
+        gr.r0 = (j - a.n_routed_groups) * a.RCAP;
+        gr.R = min(a.RCAP, a.T - gr.r0);
+        gr.orow0 = (size_t)a.T * a.k;
+        gr.shared = true;
+    }
+    return gr.R > 0;
+}
+// Source row of token row r of the group: x row (gate/up) or h row (down).
+__device__ __forceinline__ size_t source_row(const StreamArgs& a, const GroupRows& gr, int r) {
+    if (!a.perm) return gr.orow0 + gr.r0 + r;
+    if (gr.shared) return (size_t)(gr.r0 + r);
+    return (size_t)(a.perm[gr.p_lo + gr.r0 + r] / a.k);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
@@ -243,7 +283,9 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
 
     // this block's group: an expert (or the shared expert) and its token chunk
     // (all block-uniform; readfirstlane makes them scalar so the token-row
-    // loops below branch on SGPRs instead of masking lanes)
+    // loops below branch on SGPRs instead of masking lanes).  Written out here
+    // rather than through resolve_group(): this kernel sits at the register
+    // limit of two wavefronts per SIMD, and the helper's struct costs 15 VGPRs.
     int slot, r0, R;
     size_t p_lo, orow0;
     bool shared;
@@ -437,6 +479,158 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
     with_rows<RMAX>(R, stream);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 down projection on matrix cores.  Decoding e2m1 codes to bf16 costs
+// one instruction per two weights, and a dot product per token row one more,
+// with the activations read from LDS four times over (32 bf16 per 16 code
+// bytes).  Here the decoded weights feed v_mfma_f32_16x16x32_bf16 instead: the group's token rows are the
+// MFMA's M (padded to 16 with zeros), 16 weight rows its N, and every token row
+// costs nothing beyond the decode.  Exact like the version above: codes decode
+// exactly to bf16 (times the block's power-of-two scale), products and sums in
+// fp32.
+//
+// Lane l loads the 16 code bytes of weight row 16 g + (l & 15) at K offset
+// 32 (l >> 4) of each 128-wide step: the 32 weights decode to four 8-wide
+// B fragments, fragment f covering k = 32 (l >> 4) + 8 f.  Every lane's k
+// positions form a permutation of the step's 128, the same for A (read from
+// LDS at those positions) and B, so the MFMA's sum over its K is the sum over
+// the step.  No cross-lane reduction is needed: the accumulator of lane l
+// holds token rows 4 (l >> 4) .. + 3 of weight row 16 g + (l & 15).
+//
+// A wavefront walks (row group of 16, K step) pairs in order with MX_D steps
+// of loads in flight (a rolling register buffer, branch-free like the kernel
+// above); the block's four wavefronts take every fourth row group of its rows.
+// Measured against the kernel above with 2 to 64 tokens (284B-A13B and
+// 753B-A40B MXFP4 layers): 11-18% faster for the down rows; for the gate/up
+// rows within 5% either way, so those stay on the kernel above.
+// Scales: one 16-byte load per lane every four steps brings a row's scale
+// bytes of those steps (byte 4 s + q is step s's for lane group q); one-byte
+// loads per step, from 16 rows at once, cost more than the codes.  The code
+// loads are ordinary (cached) loads: one instruction reads half of each of
+// 16 rows' 128-byte lines and the next step the other half, which a
+// non-temporal hint would send to memory twice (measured 10-15% slower).
+// ---------------------------------------------------------------------------
+constexpr int MX_KS = 128;  // K elements per step (64 code bytes of a row)
+constexpr int MX_D = 8;     // steps in flight per wavefront (a multiple of 4)
+static_assert(MX_D % 4 == 0, "scale words cover four steps");
+
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t codes, float sc) {
+    u32x4_t d;
+    d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+    d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+    d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+    d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+    return __builtin_bit_cast(bf16x8_t, d);
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
+    constexpr int NM = 1;  // one matrix: the down rows
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __bf16* xs = reinterpret_cast<__bf16*>(smem);
+    const int j = blockIdx.x / a.NB, nb = blockIdx.x % a.NB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    GroupRows gr;
+    if (!resolve_group(a, j, lane, gr)) return;
+    const int R = gr.R;
+    const int K = a.K, pitch = K + 8;  // bf16 per LDS row (the skew spreads rows over banks)
+    const int nks = K / MX_KS;
+    const int n0 = nb * a.RPB, n1 = min(n0 + a.RPB, a.N);
+    const int nrg = (n1 - n0) / 16;                                       // row groups of the block
+    const int rgw = nrg > wave ? (nrg - wave + NWAVE - 1) / NWAVE : 0;    // ... of this wave
+    const int U = rgw * nks;                                              // (group, step) pairs
+    const int ln = lane & 15, q = lane >> 4;
+    const uint8_t* sl = a.pool + (size_t)gr.slot * a.slot_stride;
+    const size_t rowb = (size_t)K / 2, srowb = (size_t)K / 32;
+
+    // Loads of pair u into code buffer b; pairs past the end re-read the first
+    // one.  A pair u == 0 mod 4 also loads the scales of pairs u .. u + 3 (nks
+    // is a multiple of 4: one row group) into scale slot t; the loop below
+    // runs two rounds of MX_D pairs per iteration so that slot t's readers
+    // (four pairs, MX_D pairs earlier) are done when it is refilled.
+    constexpr int NSV = 2 * MX_D / 4;  // scale slots
+    u32x4_t cb[MX_D][NM];
+    u32x4_t sv[NSV][NM];
+    auto row_of = [&](int uu) __attribute__((always_inline)) {
+        const int rgi = uu / nks;
+        // (clamped into the block: a wavefront without row groups still issues)
+        return (size_t)min(n0 + 16 * (wave + NWAVE * rgi) + ln, n1 - 1);
+    };
+    auto issue = [&](int b, int t, int u) __attribute__((always_inline)) {
+        const int uu = u < U ? u : 0;
+        const int ks = uu % nks;
+        const size_t row = row_of(uu);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+            cb[b][m] = *(reinterpret_cast<const u32x4_t*>(sl + a.moff[m] + row * rowb) + 4 * ks + q);
+        if (b % 4 == 0) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                sv[t][m] = *reinterpret_cast<const u32x4_t*>(sl + a.soff[m] + row * srowb + 4 * ks);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < MX_D; ++b) issue(b, b / 4, b);
+
+    // the group's activation rows, plain layout
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.src);
+    const int units = K / 8;
+    for (int i = threadIdx.x; i < R * units; i += blockDim.x) {
+        const int r = i / units, uu = i - r * units;
+        *reinterpret_cast<u32x4_t*>(xs + (size_t)r * pitch + 8 * uu) =
+            reinterpret_cast<const u32x4_t*>(src + source_row(a, gr, r) * K)[uu];
+    }
+    __syncthreads();
+
+    // A: this lane's token row (rows past R read row R - 1 and are zeroed)
+    const bool mrow = ln < R;
+    const __bf16* xa = xs + (size_t)min(ln, R - 1) * pitch + 32 * q;
+    f32x4_t acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u0 = 0; u0 < U; u0 += 2 * MX_D) {
+#pragma unroll
+        for (int v = 0; v < 2 * MX_D; ++v) {
+            const int u = u0 + v, b = v % MX_D, t = v / 4;
+            if (u < U) {  // wave-uniform
+                const int rgi = u / nks, ks = u - rgi * nks;
+                bf16x8_t av[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    av[f] = *reinterpret_cast<const bf16x8_t*>(xa + ks * MX_KS + 8 * f);
+                    if (!mrow) av[f] = bf16x8_t{};
+                }
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const float sc = __uint_as_float(((sv[t][m][v % 4] >> (8 * q)) & 0xFFu) << 23);
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], fp4x8_bf16(cb[b][m][f], sc),
+                                                                         acc[m], 0, 0, 0);
+                }
+                if (ks == nks - 1) {  // row group done: token rows 4 q + i of weight row
+                    const int row = n0 + 16 * (wave + NWAVE * rgi) + ln;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int mo = 4 * q + i;
+                        if (mo < R) {
+                            const size_t idx = (gr.orow0 + gr.r0 + mo) * (size_t)a.N + row;
+                            if constexpr (sizeof(OT) == 4) {
+                                reinterpret_cast<float*>(a.dst)[idx] = acc[0][i];
+                            } else {
+                                reinterpret_cast<uint16_t*>(a.dst)[idx] = (uint16_t)f32_to_bf16_bits(acc[0][i]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            issue(b, ((v + MX_D) / 4) % NSV, u + MX_D);
+        }
+    }
+}
+
 // Segment width: the fewest lanes per row (8..64) that cover a row in at most
 // QMAX loads per lane; rows longer than 64*QMAX chunks take several passes.
 Walk make_walk(int K, int epc, int QMAX) {
@@ -514,6 +708,45 @@ ft_status launch_rows(const StreamArgs& a, int n_shared, int cap, size_t max_lds
     return launch_one<WT, NM, QMAX, 8, OT>(a, n_shared, max_lds, s);
 }
 
+// MXFP4 down rows on matrix cores: rows whose length is a multiple of 4 MX_KS
+// (each 16-byte scale word then lies within its row), and more than one token
+// (single-token decode is faster on the lean one-row dot-product kernel:
+// 14.9 vs 17.0 us for the 284B-A13B layer).  Token rows per group: up to 4
+// (LDS for the rows of every resident block).
+bool mx_eligible(int K, int T) {
+    static const bool off = getenv("FTMOE_MX_DOT") != nullptr;  // keep the dot-product kernel
+    return !off && T > 1 && K % (4 * MX_KS) == 0;
+}
+template <typename OT>
+ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
+    static const int rcap_max = [] {
+        const char* e = getenv("FTMOE_MX_RCAP");
+        const int v = e ? atoi(e) : 4;
+        return v < 1 ? 1 : v > 16 ? 16 : v;
+    }();
+    const size_t row_bytes = ((size_t)a.K + 8) * 2;
+    int rcap = a.T < rcap_max ? a.T : rcap_max;
+    while (rcap > 1 && rcap * row_bytes > max_lds) --rcap;
+    const size_t lds = rcap * row_bytes;
+    if (lds > max_lds)
+        return ft::set_error(FT_ERR_UNSUPPORTED, "ffn stream: an activation row of %zu bytes exceeds LDS",
+                             row_bytes);
+    a.RCAP = rcap;
+    const long tk = (long)a.T * a.k;
+    const long act = tk < a.E ? tk : a.E;
+    a.n_routed_groups = (int)((tk + act * (rcap - 1)) / rcap);
+    const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
+    a.RPB = pick_rpb(groups, a.N, 16, target_blocks(rcap));
+    a.NB = (a.N + a.RPB - 1) / a.RPB;
+    auto kern = stream_mx_kernel<OT>;
+    if (lds > 65536)
+        FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+    kern<<<dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s>>>(a);
+    FT_LAUNCHED("ffn_stream_mx");
+    return FT_OK;
+}
+
 }  // namespace
 
 namespace ft {
@@ -568,6 +801,9 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     else if (g.w_dt == FT_BF16) {
         if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+    } else if (mx_eligible(a2.K, a2.T)) {
+        if (y_dt == FT_F32) r = launch_mx<float>(a2, g.n_shared, max_lds, s);
+        else r = launch_mx<__bf16>(a2, g.n_shared, max_lds, s);
     } else {
         if (y_dt == FT_F32) r = launch_rows<2, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<2, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
