@@ -13,6 +13,7 @@
 // wave) advances by the match count.  Waves own contiguous chunks, and a
 // per-(chunk, expert) prefix scan gives each chunk its starting positions.
 #include "common.h"
+#include "route_core.h"
 
 namespace {
 
@@ -46,16 +47,14 @@ __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, in
 
 // ---------------------------------------------------------------------------
 // Small problems: one block of 8 waves does everything.
-// LDS: hist[8][E] (then running bases), tot[E].
+// LDS: hist[8][E] (then running bases), tot[E].  `ids` may point into LDS.
 // ---------------------------------------------------------------------------
 constexpr int SW = 8;
-__global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __restrict__ ids,
-                                                              int n, int E,
-                                                              int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ perm,
-                                                              int32_t* __restrict__ inv) {
-    extern __shared__ int lds[];
+__device__ __forceinline__ void align_block(const int32_t* ids, int n, int E,
+                                            int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ perm,
+                                            int32_t* __restrict__ inv, int* lds) {
     int* hist = lds;            // [SW][E]
     int* tot = lds + SW * E;    // [E] inclusive scan scratch
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -93,6 +92,38 @@ __global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __r
     __syncthreads();
     for (int f0 = f_lo; f0 < f_hi; f0 += 64)
         wave_scatter(ids, f0, f_hi, hist + w * E, perm, inv, lane);
+}
+
+__global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __restrict__ ids,
+                                                              int n, int E,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ inv) {
+    extern __shared__ int lds[];
+    align_block(ids, n, E, counts, offsets, perm, inv, lds);
+}
+
+// Top-k of every token, then the alignment of the picks, in one block: for a
+// decode-sized batch the two steps are each a few microseconds of launch and
+// memory round trip around very little work.  Wave w picks tokens w, w + SW,
+// ... (the top-k kernel's per-token code, so the same picks and gates); the
+// picks also go to LDS, where the alignment reads them after a barrier.
+// LDS: ids[T*k], then the alignment's hist[SW][E] and tot[E].
+template <int NPL>
+__global__ __launch_bounds__(SW * 64) void topk_align_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    extern __shared__ int lds[];
+    const int n = T * k;
+    int* ids_s = lds;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += SW)
+        topk_token<NPL>(logits + (size_t)t * E, bias, E, k, ids + (size_t)t * k, w + (size_t)t * k,
+                        ids_s + t * k, lane);
+    __syncthreads();
+    align_block(ids_s, n, E, counts, offsets, perm, inv, lds + ((n + 3) & ~3));
 }
 
 // ---------------------------------------------------------------------------
@@ -238,6 +269,33 @@ ft_status launch_align(const int32_t* ids, int T, int k, int E, int32_t* counts,
     unit_scatter_kernel<<<cdiv(U, 4), 256, 5 * E * sizeof(int), s>>>(ids, (int)n, E, U, hist,
                                                                        counts, offsets, perm, inv);
     FT_LAUNCHED("align_scatter");
+    return FT_OK;
+}
+
+bool topk_align_small_ok(int T, int k) {
+    // at most one token per wavefront of the one block: with more, the tokens
+    // of a wavefront are picked in turn and the separate top-k launch (one
+    // wavefront per token) wins (35B-A3B layer, graph replays: T = 1 44.3 vs
+    // 48.5 us per step; T = 64 307 vs 277 us)
+    return T >= 1 && T <= SW && (long)T * k <= ALIGN_SMALL_MAX;
+}
+
+ft_status launch_topk_align_small(const float* logits, const float* bias, int T, int E, int k,
+                                  int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, hipStream_t s) {
+    const int n = T * k;
+    const size_t lds = (size_t)(((n + 3) & ~3) + (SW + 1) * E) * sizeof(int);
+    if (E <= 64)
+        topk_align_small_kernel<1><<<1, SW * 64, lds, s>>>(logits, bias, T, E, k, ids, w, counts, offsets, perm, inv);
+    else if (E <= 128)
+        topk_align_small_kernel<2><<<1, SW * 64, lds, s>>>(logits, bias, T, E, k, ids, w, counts, offsets, perm, inv);
+    else if (E <= 256)
+        topk_align_small_kernel<4><<<1, SW * 64, lds, s>>>(logits, bias, T, E, k, ids, w, counts, offsets, perm, inv);
+    else if (E <= 512)
+        topk_align_small_kernel<8><<<1, SW * 64, lds, s>>>(logits, bias, T, E, k, ids, w, counts, offsets, perm, inv);
+    else
+        topk_align_small_kernel<16><<<1, SW * 64, lds, s>>>(logits, bias, T, E, k, ids, w, counts, offsets, perm, inv);
+    FT_LAUNCHED("topk_align_small");
     return FT_OK;
 }
 

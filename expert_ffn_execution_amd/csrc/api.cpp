@@ -25,6 +25,9 @@ ft_status launch_ffn_stream(const FfnGeom&, const void*, const int32_t*, const i
                             const int32_t*, int, void*, void*, ft_dtype, hipStream_t);
 ft_status launch_combine(const void*, ft_dtype, const int32_t*, const float*, int, int, int, int,
                          void*, ft_dtype, hipStream_t);
+bool topk_align_small_ok(int T, int k);
+ft_status launch_topk_align_small(const float*, const float*, int, int, int, int32_t*, float*,
+                                  int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t);
 
 static thread_local char g_err[512] = "";
 
@@ -297,3 +300,37 @@ ft_status ft_moe_combine(const void* y_perm, ft_dtype y_dt, const int32_t* inv_p
 }
 
 }  // extern "C"
+
+namespace ft {
+
+// Route and align of a whole-layer step.  A decode-sized batch runs the
+// router logits, then top-k and alignment fused in one launch (same picks,
+// gates, counts, offsets and permutation as ft_moe_route + ft_moe_align, whose
+// argument checks are repeated here); larger batches call the two entry points.
+ft_status route_align(const ft_moe_step* st, hipStream_t s) {
+    const int T = st->T, E = st->weights.E, k = st->k, H = st->weights.H;
+    if (!topk_align_small_ok(T, k) || E < 1 || E > MAX_E || k < 1 || k > E) {  // (their checks reject bad E, k)
+        ft_status r = ft_moe_route(st->x, st->act_dt, st->w_router, nullptr, st->bias, T, H, E, k,
+                                   st->logits, st->topk_ids, st->topk_w, s);
+        if (r != FT_OK) return r;
+        return ft_moe_align(st->topk_ids, T, k, E, st->counts, st->offsets, st->perm, st->inv_perm,
+                            st->align_ws, st->align_ws_bytes, s);
+    }
+    clear_error();
+    FT_CHECK_ARG(st->topk_ids && st->topk_w, "null outputs");
+    FT_CHECK_ARG(st->x && st->w_router && st->logits, "x, w_router and logits_out are required");
+    FT_CHECK_ARG(valid_act(st->act_dt), "x_dt must be FT_F32 or FT_BF16");
+    FT_CHECK_ARG(H > 0 && H % 64 == 0, "H must be a positive multiple of 64");
+    FT_CHECK_ARG(aligned16(st->x) && aligned16(st->w_router), "x / w_router must be 16-byte aligned");
+    FT_CHECK_ARG(st->counts && st->offsets, "null counts/offsets");
+    FT_CHECK_ARG(st->perm && st->inv_perm, "null ids/perm/inv_perm");
+    prof_begin(PROF_ROUTE, s);
+    ft_status r = launch_router_logits(st->x, st->act_dt, st->w_router, T, H, E, st->logits, s);
+    if (r == FT_OK)
+        r = launch_topk_align_small(st->logits, st->bias, T, E, k, st->topk_ids, st->topk_w,
+                                    st->counts, st->offsets, st->perm, st->inv_perm, s);
+    prof_end(PROF_ROUTE, s);
+    return r;
+}
+
+}  // namespace ft

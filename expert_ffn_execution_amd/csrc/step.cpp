@@ -15,6 +15,7 @@
 
 namespace ft {
 void set_capturing(bool on);
+ft_status route_align(const ft_moe_step* st, hipStream_t s);
 }
 
 using namespace ft;
@@ -27,12 +28,8 @@ struct ft_moe_graph {
 namespace {
 
 ft_status run_step(const ft_moe_step* st, void* stream) {
-    ft_status r = ft_moe_route(st->x, st->act_dt, st->w_router, nullptr, st->bias, st->T,
-                               st->weights.H, st->weights.E, st->k, st->logits, st->topk_ids,
-                               st->topk_w, stream);
-    if (r != FT_OK) return r;
-    r = ft_moe_align(st->topk_ids, st->T, st->k, st->weights.E, st->counts, st->offsets,
-                     st->perm, st->inv_perm, st->align_ws, st->align_ws_bytes, stream);
+    // route + align (top-k and alignment in one launch for decode-sized batches)
+    ft_status r = route_align(st, (hipStream_t)stream);
     if (r != FT_OK) return r;
     r = ft_moe_ffn(&st->weights, st->x, st->act_dt, st->T, st->k, st->perm, st->offsets,
                    st->slot_of_expert, st->y_perm, st->y_dt, st->ffn_ws, st->ffn_ws_bytes, stream);

@@ -30,7 +30,8 @@ SHAPES = {
 # on the small shapes the MFMA tiles (tile list built on the device)
 CASES = [("tiny_f32", 64, False), ("small_bf16", 3, True), ("small_bf16", 300, False),
          ("small_mx", 5, False), ("small_mx", 300, True), ("35b_a3b_bf16", 1, False),
-         ("35b_a3b_bf16", 16, False), ("284b_a13b_mxfp4", 1, False)]
+         ("35b_a3b_bf16", 16, False), ("35b_a3b_bf16", 8, False), ("35b_a3b_bf16", 9, False),
+         ("284b_a13b_mxfp4", 1, False), ("284b_a13b_mxfp4", 8, False)]
 _LAYERS = {}
 
 
@@ -80,6 +81,18 @@ def test_step_and_graph(name, T, permuted):
     assert np.max(np.abs(step.w.cpu().numpy() - ref_w)) <= 1e-6
     check_close(step.out, oracle_out(L, x.cpu(), ref_ids, ref_w), sh.wdtype,
                 f"step {name} T{T}")
+    # the step (top-k and alignment fused for decode-sized batches) gives the
+    # same bits as the four entry points called one by one
+    ids, w, lg = ft.route(T, sh.E, sh.k, x=x, w_router=wr, bias=bias)
+    counts, offsets, perm, inv = ft.align(ids, sh.E)
+    y = ft.ffn(L.wts, x, sh.k, perm, offsets, slot_of_expert=L.slot_table, y_dtype=y_dt)
+    out = ft.combine(y, inv, w, n_shared=sh.n_shared, out_dtype=act)
+    torch.cuda.synchronize()
+    for a, b, what in ((step.logits, lg, "logits"), (step.ids, ids, "ids"), (step.w, w, "w"),
+                       (step.counts, counts, "counts"), (step.offsets, offsets, "offsets"),
+                       (step.perm[:T * sh.k], perm, "perm"), (step.inv[:T * sh.k], inv, "inv"),
+                       (step.out, out, "out")):
+        assert torch.equal(a, b), f"step vs separate calls: {what}"
 
     # graph replays, each against an eager step on the same activations
     g = step.capture()
