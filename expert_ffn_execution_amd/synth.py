@@ -42,7 +42,7 @@ class LayerShape:
     k: int              # experts per token
     I: int              # expert intermediate size
     n_shared: int = 0   # always-on shared experts (0 or 1)
-    wdtype: str = "bf16"    # expert weight storage: "f32" | "bf16" | "mxfp4"
+    wdtype: str = "bf16"    # expert weight storage: "f32" | "bf16" | "mxfp4" | "fp8"
     adtype: str = "bf16"    # activation / router storage: "f32" | "bf16"
     bias: str = "none"      # router logit bias: "none" | "zipf" | "normal"
     bias_param: float = 0.0  # zipf exponent s, or normal std
@@ -144,6 +144,20 @@ def quantize_mxfp4(w: torch.Tensor):
 
 
 # ---------------------------------------------------------------------------
+# FP8 quantiser (input recipe).  OCP 8-bit floating point, E4M3 encoding (bias
+# 7, largest finite magnitude 448, no infinities).  One fp32 scale per matrix,
+# s = amax / 448 (1 for an all-zero matrix); codes = round-to-nearest-even of
+# w / s on the e4m3 grid (torch's float8_e4m3fn cast).  Weight = value(code) * s.
+# ---------------------------------------------------------------------------
+def quantize_fp8(w: torch.Tensor):
+    """w [N, K] fp32 -> (codes uint8 [N, K], scale fp32 [1])."""
+    amax = w.abs().amax()
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    codes = (w / s).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, s.reshape(1).contiguous()
+
+
+# ---------------------------------------------------------------------------
 # Generators
 # ---------------------------------------------------------------------------
 def gen_x(shape: LayerShape, T: int, step: int = 0, device="cpu", layer: int = 0) -> torch.Tensor:
@@ -189,6 +203,8 @@ def gen_expert(shape: LayerShape, e: int, layer: int = 0, device="cpu") -> dict:
     f32/bf16: {"gate": [I,H], "up": [I,H], "down": [H,I]}.
     mxfp4:    {"gate": codes [I,H/2], "gate_sc": [I,H/32], "up", "up_sc",
                "down": codes [H,I/2], "down_sc": [H,I/32]}.
+    fp8:      {"gate": e4m3 codes [I,H], "gate_sc": fp32 [1], "up", "up_sc",
+               "down": codes [H,I], "down_sc": fp32 [1]}.
     Expert index ``e == shape.E`` is the shared expert (when n_shared == 1).
     """
     H, I = shape.H, shape.I
@@ -199,9 +215,10 @@ def gen_expert(shape: LayerShape, e: int, layer: int = 0, device="cpu") -> dict:
     if shape.wdtype in ("f32", "bf16"):
         return {"gate": to_storage(g, shape.wdtype), "up": to_storage(u, shape.wdtype),
                 "down": to_storage(d, shape.wdtype)}
+    quant = quantize_mxfp4 if shape.wdtype == "mxfp4" else quantize_fp8
     out = {}
     for name, t in (("gate", g), ("up", u), ("down", d)):
-        c, s = quantize_mxfp4(t)
+        c, s = quant(t)
         out[name], out[name + "_sc"] = c, s
     return out
 

@@ -58,11 +58,28 @@ double or_mxfp4_value(uint8_t code, uint8_t scale) {
     return s ? -v : v;
 }
 
+/* e4m3 code c (bit 7 sign, bits 6..3 exponent, bits 2..0 mantissa), the OCP
+ * 8-bit floating point "E4M3" encoding: bias 7, no infinities, exponent and
+ * mantissa fields all ones is NaN.  Exponent field 0 is the subnormal
+ * 2^-6 * m/8, otherwise 2^(E-7) * (1 + m/8).  OCP 8-bit Floating Point
+ * Specification (OFP8) v1.0. */
+double or_fp8_value(uint8_t code) {
+    int s = code >> 7, ex = (code >> 3) & 15, m = code & 7;
+    if (ex == 15 && m == 7) return NAN;
+    double mag = (ex == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, ex - 7);
+    return s ? -mag : mag;
+}
+
 /* element (row, kk) of a [rows][K] matrix stored in fmt */
 static double w_at(const void* base, const uint8_t* sc, int fmt, int row, int K, int kk) {
     size_t r = (size_t)row;
     if (fmt == OR_F32) return ((const float*)base)[r * K + kk];
     if (fmt == OR_BF16) return or_bf16_to_f64(((const uint16_t*)base)[r * K + kk]);
+    if (fmt == OR_FP8) {  /* code times the matrix's fp32 scale (sc points at it) */
+        float scale;
+        memcpy(&scale, sc, 4);
+        return or_fp8_value(((const uint8_t*)base)[r * K + kk]) * (double)scale;
+    }
     uint8_t byte = ((const uint8_t*)base)[r * (K / 2) + kk / 2];
     uint8_t c = (kk & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
     return or_mxfp4_value(c, sc[r * (K / 32) + kk / 32]);

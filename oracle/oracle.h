@@ -14,7 +14,7 @@
  *   align   counts, exclusive offsets, perm = flat slots f = t*k+j sorted stably
  *           by expert, inv_perm[perm[p]] = p
  *   expert  h = silu(x Wg^T) * (x Wu^T),  y = h Wd^T         (fp64; h rounded to bf16
- *           for bf16 / MXFP4 weights)
+ *           for bf16 / MXFP4 / FP8 weights)
  *   combine out[t] = sum_j w[t,j] * y(t,j) (+ y_shared(t)), fp64, one rounding to the
  *           output format.
  *
@@ -37,12 +37,17 @@ extern "C" {
 #endif
 
 /* storage formats of a tensor */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2, OR_FP8 = 3 };
 
 /* One expert in logical layout.
  *   OR_F32 / OR_BF16: gate [I][H], up [I][H], down [H][I] row-major.
  *   OR_MXFP4: gate/up codes [I][H/2], down codes [H][I/2] (element 2j in the
- *   low nibble of byte j), e8m0 scales gate_sc/up_sc [I][H/32], down_sc [H][I/32]. */
+ *   low nibble of byte j), e8m0 scales gate_sc/up_sc [I][H/32], down_sc [H][I/32].
+ *   OR_FP8: e4m3 codes gate/up [I][H], down [H][I], one byte each; gate_sc,
+ *   up_sc, down_sc each point at the matrix's fp32 scale (4 bytes): the weight
+ *   is the code's value times that scale.  The pages list FP8 weights without
+ *   their scaling (refft.com guide, the format list); one scale per matrix is
+ *   the plainest reading. */
 typedef struct {
     int fmt;
     const void* gate;
@@ -55,6 +60,9 @@ typedef struct {
 
 /* Exact value of one e2m1 code scaled by an e8m0 byte (OCP MX v1.0). */
 double or_mxfp4_value(uint8_t code, uint8_t scale);
+/* Exact value of one e4m3 code (OCP OFP8 v1.0, the E4M3 encoding; NaN for the
+ * two NaN codes). */
+double or_fp8_value(uint8_t code);
 /* bf16 bits -> double (exact) and double -> bf16 bits (round to nearest even). */
 double or_bf16_to_f64(uint16_t b);
 uint16_t or_f64_to_bf16(double v);

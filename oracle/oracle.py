@@ -18,8 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
-_FMT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4}
+F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
+_FMT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "fp8": FP8}
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load():
     P = C.c_void_p
     lib.or_mxfp4_value.restype = C.c_double
     lib.or_mxfp4_value.argtypes = [C.c_uint8, C.c_uint8]
+    lib.or_fp8_value.restype = C.c_double
+    lib.or_fp8_value.argtypes = [C.c_uint8]
     lib.or_bf16_to_f64.restype = C.c_double
     lib.or_bf16_to_f64.argtypes = [C.c_uint16]
     lib.or_f64_to_bf16.restype = C.c_uint16
@@ -93,6 +95,10 @@ def _ptr(a: np.ndarray):
 # ---- scalar helpers ---------------------------------------------------------
 def mxfp4_value(code: int, scale: int) -> float:
     return load().or_mxfp4_value(code, scale)
+
+
+def fp8_value(code: int) -> float:
+    return load().or_fp8_value(code)
 
 
 def bf16_to_f64(b: int) -> float:
@@ -151,7 +157,7 @@ class ExpertSet:
                 a = _np(ex[name])
                 self.keep.append(a)
                 setattr(s, name, a.ctypes.data)
-                if wdtype == "mxfp4":
+                if wdtype in ("mxfp4", "fp8"):
                     sc = _np(ex[name + "_sc"])
                     self.keep.append(sc)
                     setattr(s, name + "_sc", sc.ctypes.data)

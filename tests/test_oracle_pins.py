@@ -58,7 +58,15 @@ def _bf16_round_np(a: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
+def _dequant_fp8(codes: torch.Tensor, scale: torch.Tensor) -> np.ndarray:
+    """torch's own e4m3 decoding (float8_e4m3fn) times the matrix scale, fp64."""
+    return (codes.contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+            * scale.to(torch.float64)).numpy()
+
+
 def _weights_f64(ex: dict, wdtype: str):
+    if wdtype == "fp8":
+        return tuple(_dequant_fp8(ex[n], ex[n + "_sc"]) for n in ("gate", "up", "down"))
     if wdtype == "mxfp4":
         return tuple(_dequant_mxfp4(ex[n].numpy(), ex[n + "_sc"].numpy())
                      for n in ("gate", "up", "down"))
@@ -128,6 +136,37 @@ def test_mxfp4_quantiser_round_trip():
     q, s = synth.quantize_mxfp4(torch.from_numpy(vals))
     assert np.array_equal(q.numpy(), packed)
     assert np.array_equal(s.numpy(), scales)
+
+
+def test_fp8_decode_exhaustive_against_torch():
+    # every e4m3 code against torch's float8_e4m3fn decoding (OCP OFP8 E4M3)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).tolist()
+    for code in range(256):
+        v = orc.fp8_value(code)
+        if math.isnan(ref[code]):
+            assert math.isnan(v), code
+        else:
+            assert v == ref[code] and math.copysign(1.0, v) == math.copysign(1.0, ref[code]), code
+    # closed forms of the format
+    assert orc.fp8_value(0x7E) == 448.0 and orc.fp8_value(0x38) == 1.0
+    assert orc.fp8_value(0x01) == 2.0 ** -9 and orc.fp8_value(0x08) == 2.0 ** -6
+    assert math.isnan(orc.fp8_value(0x7F)) and math.isnan(orc.fp8_value(0xFF))
+
+
+def test_fp8_quantiser_round_trip():
+    # values on the e4m3 grid times a scale, with the largest code 448 present,
+    # quantise back to the same codes and scale
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 0x7F, size=(4, 48)).astype(np.uint8)   # finite, positive
+    codes |= (rng.integers(0, 2, size=codes.shape) << 7).astype(np.uint8)
+    codes[codes == 0x80] = 0  # no -0
+    codes[0, 0] = 0x7E
+    scale = 0.015625 * 3
+    vals = np.array([[orc.fp8_value(int(c)) * scale for c in row] for row in codes], np.float32)
+    q, s = synth.quantize_fp8(torch.from_numpy(vals))
+    assert np.array_equal(q.numpy(), codes)
+    assert float(s[0]) == np.float32(scale)
 
 
 def test_bf16_rounding_matches_torch():
@@ -268,7 +307,7 @@ def test_hand_worked_example():
     np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-7, atol=0)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4", "fp8"])
 def test_single_expert_is_dense_swiglu(wdtype):
     # E = 1, k = 1 reduces the layer to a dense SwiGLU MLP (torch fp64 reference)
     H, I, T = 64, 96, 5
@@ -290,7 +329,8 @@ def test_single_expert_is_dense_swiglu(wdtype):
 
 
 @pytest.mark.parametrize("wdtype,shared", [("f32", False), ("bf16", False), ("mxfp4", False),
-                                           ("mxfp4", True), ("bf16", True)])
+                                           ("mxfp4", True), ("bf16", True), ("fp8", False),
+                                           ("fp8", True)])
 def test_layer_matches_brute_force_dense(wdtype, shared):
     T, H, E, k, I = 12, 64, 6, 2, 32
     sh = synth.LayerShape(f"pin_bf_{wdtype}_{shared}", H=H, E=E, k=k, I=I,
