@@ -44,11 +44,13 @@ namespace {
 
 constexpr int NWAVE = 4;  // wavefronts per block
 
-// WT: 0 = fp32 weights (fp32 activations), 1 = bf16, 2 = MXFP4 (bf16 activations)
+// WT: 0 = fp32 weights (fp32 activations), 1 = bf16, 2 = MXFP4, 3 = FP8 e4m3
+// (bf16 activations)
 template <int WT> struct W;
 template <> struct W<0> { static constexpr int EPC = 4; };   // elements per 16 B chunk
 template <> struct W<1> { static constexpr int EPC = 8; };
 template <> struct W<2> { static constexpr int EPC = 32; };
+template <> struct W<3> { static constexpr int EPC = 16; };
 
 // How a wavefront walks one weight matrix [N][K] of 16-byte chunks.
 struct Walk {
@@ -240,6 +242,7 @@ __device__ __forceinline__ bool seg_writer(int lane) {
 // xr points at the token row in LDS; col is the chunk column.  MXFP4 rows are
 // held in LDS sub-chunk-major (8-element unit w of chunk c at (w*nch + c)*8)
 // so that lanes reading consecutive chunks touch consecutive 16-byte words.
+// FP8 chunks (16 codes, decoded into dec[0..7]) meet 16 plain-layout values.
 template <int WT, typename AT>
 __device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* dec, const AT* xr,
                                            int col, int nch, float acc) {
@@ -251,6 +254,13 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* de
         const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + col * 8);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = dot2_bf16(wv[q], xv[q], acc);
+    } else if constexpr (WT == 3) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + col * 16 + 8 * h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = dot2_bf16(dec[4 * h + q], xv[q], acc);
+        }
     } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -313,10 +323,13 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
     const uint8_t* sl = a.pool + (size_t)slot * a.slot_stride;
     const u32x4_t* mat[NM];
     const uint8_t* scl[NM];
+    float msc[NM];  // FP8: the matrix scales (applied to the reduced sums); else 1
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         mat[m] = reinterpret_cast<const u32x4_t*>(sl + a.moff[m]);
         scl[m] = sl + a.soff[m];
+        if constexpr (WT == 3) msc[m] = *reinterpret_cast<const float*>(scl[m]);
+        else msc[m] = 1.0f;
     }
     const Walk wk = a.wk;
     const int K = a.K;
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
             const int col = ok ? col_of(it, q) : 0;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                uint32_t dec[WT == 2 ? 16 : 1];
+                uint32_t dec[WT == 2 ? 16 : WT == 3 ? 8 : 1];
                 u32x4_t wv = b.v[m][q];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) wv[w] = ok ? wv[w] : 0u;  // +0 codes / +0.0 weights
@@ -400,6 +413,14 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
                         dec[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
                         dec[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
                         dec[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
+                    }
+                } else if constexpr (WT == 3) {
+                    // e4m3 codes to bf16 (exact; the conversion's scale operand only
+                    // takes a power of two, so the matrix scale comes later)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        dec[2 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[w], 1.0f, false));
+                        dec[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[w], 1.0f, true));
                     }
                 }
 #pragma unroll
@@ -442,8 +463,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
         if (wr && rs < RR && it.row < n1) {
             const size_t idx = (orow0 + r0 + rs) * (size_t)a.N + it.row;
             float val;
-            if constexpr (NM == 2) val = silu_mul(v[0][0], v[1][0]);
-            else val = v[0][0];
+            if constexpr (NM == 2) val = silu_mul(v[0][0] * msc[0], v[1][0] * msc[1]);
+            else val = v[0][0] * msc[0];
             using DT = typename std::conditional<NM == 2, AT, OT>::type;
             if constexpr (sizeof(DT) == 4) reinterpret_cast<float*>(a.dst)[idx] = val;
             else reinterpret_cast<uint16_t*>(a.dst)[idx] = (uint16_t)f32_to_bf16_bits(val);
@@ -783,6 +804,7 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     prof_begin(PROF_FFN_GEMM1, s);
     if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    else if (g.w_dt == FT_FP8) r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     prof_end(PROF_FFN_GEMM1, s);
     if (r != FT_OK) return r;
@@ -801,6 +823,9 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     else if (g.w_dt == FT_BF16) {
         if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+    } else if (g.w_dt == FT_FP8) {
+        if (y_dt == FT_F32) r = launch_rows<3, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+        else r = launch_rows<3, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
     } else if (mx_eligible(a2.K, a2.T)) {
         if (y_dt == FT_F32) r = launch_mx<float>(a2, g.n_shared, max_lds, s);
         else r = launch_mx<__bf16>(a2, g.n_shared, max_lds, s);

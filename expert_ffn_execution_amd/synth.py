@@ -67,8 +67,12 @@ A40B_BF16 = LayerShape("753b_a40b_bf16", H=6144, E=256, k=8, I=2048, bias="norma
 A40B_MXFP4 = LayerShape("753b_a40b_mxfp4", H=6144, E=256, k=8, I=2048, wdtype="mxfp4",
                         bias="normal", bias_param=1.0)
 
+# The 35B-A3B layer with FP8 (e4m3) weights: a weight format the pages list,
+# on the shape of the bf16 configuration (not one of the five configurations).
+A3B_FP8 = LayerShape("35b_a3b_fp8", H=2048, E=128, k=8, I=768, wdtype="fp8")
+
 SHAPES = {s.name: s for s in (TINY_F32, A3B_BF16, A13B_MXFP4, SLOT_STACK, A40B_BF16,
-                              A40B_MXFP4)}
+                              A40B_MXFP4, A3B_FP8)}
 
 # Token counts each workload is run at (decode points, then prefill).
 POINTS = {
@@ -78,6 +82,7 @@ POINTS = {
     "slot_stack_bf16": [1, 2048],
     "753b_a40b_bf16": [1, 32, 16384],
     "753b_a40b_mxfp4": [1, 32, 16384],
+    "35b_a3b_fp8": [1, 16, 64, 4096],
 }
 SLOT_STACK_LAYERS = 8
 SLOT_STACK_SLOTS_PER_LAYER = 64

@@ -62,7 +62,7 @@ typedef enum {
     FT_WARN_OVERLAP_DISABLED = 100
 } ft_status;
 
-typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2 } ft_dtype;
+typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_FP8 = 3 } ft_dtype;
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* ft_last_error(void);
@@ -123,15 +123,22 @@ ft_status ft_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* co
  *     2j of a row in the low nibble of byte j, 2j+1 in the high nibble; scales
  *     are e8m0 bytes 2^(X-127) for 32 consecutive elements along the
  *     contraction dimension (OCP Microscaling Formats v1.0).
+ *   FT_FP8: gate codes [I][H] | up codes [I][H] | down codes [H][I], one e4m3
+ *     byte each (OCP 8-bit floating point v1.0, E4M3: bias 7, no infinities,
+ *     S.1111.111 is NaN) | three fp32 scales (gate, up, down), one per matrix:
+ *     weight = value(code) * scale.  The pages list FP8 weights (refft.com
+ *     guide, the format list) without their scaling; one scale per matrix is
+ *     the plainest reading.
  * All formats: H % 64 == 0 and I % 64 == 0.
  * ft_expert_layout fills offs[6] = byte offsets of {gate, up, down,
- * gate_sc, up_sc, down_sc} (the last three 0 unless MXFP4) and returns the
+ * gate_sc, up_sc, down_sc} (scale arrays for MXFP4, the fp32 scales for
+ * FP8, 0 otherwise) and returns the
  * slot size in bytes (0 for an unsupported combination).
  * ------------------------------------------------------------------------ */
 size_t ft_expert_layout(ft_dtype w_dt, int H, int I, size_t offs[6]);
 
 typedef struct {
-    ft_dtype w_dt;        /* FT_F32, FT_BF16 or FT_MXFP4 */
+    ft_dtype w_dt;        /* FT_F32, FT_BF16, FT_MXFP4 or FT_FP8 */
     int E;                /* routed experts */
     int H;                /* hidden size */
     int I;                /* expert intermediate size */
@@ -150,7 +157,8 @@ typedef struct {
  * with fp32 accumulation; h is rounded to bf16 for bf16 / MXFP4 weights.
  * With n_shared == 1, rows T*k + t of y_perm receive the shared expert's FFN
  * of x_t (weight 1 in the combine).  MXFP4 weights are decoded exactly to bf16
- * on chip and multiplied with bf16 activations.
+ * on chip and multiplied with bf16 activations; FP8 codes likewise, the matrix
+ * scale applied to each fp32 sum.
  *   x [T][H] device, act_dt = FT_BF16 (FT_F32 only with FT_F32 weights);
  *   perm, offsets: ft_moe_align's outputs for the same ids;
  *   slot_of_expert [E] int32 device, or NULL for slot e = expert e: the slot

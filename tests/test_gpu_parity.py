@@ -128,6 +128,7 @@ SMALL = {
     "mxfp4": synth.LayerShape("gpu_small_mx", H=512, E=16, k=6, I=256, n_shared=1,
                               wdtype="mxfp4"),
     "bf16_shared": synth.LayerShape("gpu_small_bf16_sh", H=256, E=8, k=2, I=192, n_shared=1),
+    "fp8": synth.LayerShape("gpu_small_fp8", H=512, E=16, k=4, I=384, n_shared=1, wdtype="fp8"),
 }
 
 
@@ -148,7 +149,7 @@ def test_layer_small_both_paths(kind, path, T):
     check_close(r["out"], ref, sh.wdtype, f"{kind} path{path} T{T}")
 
 
-@pytest.mark.parametrize("kind", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("kind", ["bf16", "mxfp4", "fp8"])
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("T", [7, 300])
 def test_layer_fp32_expert_outputs(kind, path, T):
@@ -282,7 +283,8 @@ def _sample_tokens(ids, T, E, n, seed):
 FULL = [("284b_a13b_mxfp4", 1), ("284b_a13b_mxfp4", 8), ("284b_a13b_mxfp4", 64),
         ("284b_a13b_mxfp4", 8192), ("753b_a40b_bf16", 1), ("753b_a40b_bf16", 32),
         ("753b_a40b_bf16", 16384), ("753b_a40b_mxfp4", 1), ("753b_a40b_mxfp4", 32),
-        ("753b_a40b_mxfp4", 16384)]
+        ("753b_a40b_mxfp4", 16384), ("35b_a3b_fp8", 1), ("35b_a3b_fp8", 16),
+        ("35b_a3b_fp8", 4096)]
 
 
 @pytest.mark.parametrize("name,T", FULL)
