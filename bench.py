@@ -362,7 +362,7 @@ def run_slot_stack(args):
         "metric": "MoE-layer tokens/s through a slot-cached layer stack (decode T=1)",
         "value": steps * L / t_dec, "unit": "layer-tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": t_dec / steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": sh.wdtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if sh.wdtype == "f32" else "bf16", "data": "synthetic",
         "config": {"workload": f"{sh.name}: {L} layers H{sh.H} E{sh.E} k{sh.k} I{sh.I}, "
                                f"{L * synth.SLOT_STACK_SLOTS_PER_LAYER} slots global LRU, "
                                f"Zipf({sh.bias_param}) router bias, pinned host pool",
@@ -484,7 +484,7 @@ def main():
         "metric": "MoE-layer tokens/s (prefill); decode HBM GB/s and prefill MFMA TFLOP/s vs peak",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": sh.wdtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if sh.wdtype == "f32" else "bf16", "data": "synthetic",
         "config": {"workload": f"{sh.name} prefill T={T_pre}", "H": sh.H, "E": sh.E, "k": sh.k,
                    "I": sh.I, "n_shared": sh.n_shared, "tokens": T_pre, "weights": sh.wdtype,
                    "activations": "bf16", "weight_banks": n_banks},

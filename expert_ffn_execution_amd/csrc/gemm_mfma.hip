@@ -323,18 +323,22 @@ constexpr int MT = BM / 32, NTL = WN / 32;   // 32 x 32 MFMA tiles per wavefront
 constexpr int ROWB = KS * 2;                          // bytes of a bf16 row slice
 constexpr int A_BYTES = BM * ROWB;                    // 16 KB
 constexpr int AL = A_BYTES / 1024 / NW;               // A copies per wave per slice
+// BT: 0 bf16 weights, 1 MXFP4, 2 FP8 (e4m3, one fp32 scale per matrix).
 // MXFP4: codes [BN][16 B], then one 4-byte slot per row holding its scale byte
-// (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot)
-template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BN * 16 + BN * 4; }
+// (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot).
+// FP8: codes [BN][32 B]; the two 16-byte halves of rows 8..15 of every 16 are
+// swapped (h ^ ((r >> 3) & 1)) so that fragment reads spread over the banks.
+template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BT == 1 ? BN * 16 + BN * 4 : BN * KS; }
 template <int BT> constexpr int stage_bytes() { return A_BYTES + b_bytes<BT>(); }
 constexpr size_t EPI_BYTES = (size_t)BM * (BN + 8) * 2;   // bf16 output tile (plain GEMM)
 template <int BT> constexpr size_t lds_bytes() {
     return (size_t)STAGES * stage_bytes<BT>() > EPI_BYTES ? (size_t)STAGES * stage_bytes<BT>() : EPI_BYTES;
 }
-// global_load_lds instructions per wave per slice: A, then B (bf16: 1 KB
-// pieces; MXFP4: one codes piece of 64 rows and one scale byte per lane)
-template <int BT> constexpr int b_copies() { return BT == 0 ? BN * ROWB / 1024 / NW : 1; }
-template <int BT> constexpr int loads_per_slice() { return AL + (BT == 0 ? b_copies<BT>() : 2); }
+// global_load_lds instructions per wave per slice: A, then B (bf16 and FP8:
+// 1 KB pieces; MXFP4: one codes piece of 64 rows and one scale byte per lane)
+template <int BT> constexpr int b_copies() { return BT == 0 ? BN * ROWB / 1024 / NW : BT == 1 ? 1 : BN * KS / 1024 / NW; }
+template <int BT> constexpr int loads_per_slice() { return AL + (BT == 1 ? 2 : b_copies<BT>()); }
+__device__ __forceinline__ int fp8_half(int r, int h) { return h ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int sw(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
 }  // namespace pipe
 
@@ -346,6 +350,16 @@ template <int N>
 __device__ __forceinline__ void wait_vm_lgkm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// 8 e4m3 codes (bytes of w0, then w1) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8_t fp8_frag(uint32_t w0, uint32_t w1) {
+    u32x4_t d;
+    d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    return __builtin_bit_cast(bf16x8_t, d);
 }
 
 __device__ __forceinline__ bf16x8_t fp4_frag(uint32_t codes, uint32_t X) {
@@ -418,7 +432,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         else
             return (uint32_t)g.off[which ? 5 : 2];
     };
-    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : (uint32_t)K / 2;
+    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : BT == 1 ? (uint32_t)K / 2 : (uint32_t)K;
     // B value/code copies per wave: b_copies<BT>() <= 4 (a literal bound: a
     // call in an array bound reads as a variable-length array to the host pass)
     uint32_t boff[4], soff = 0;
@@ -429,10 +443,22 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             const int r = 16 * (b_copies<BT>() * wave + i) + (lane >> 2);
             boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
         }
-    } else {  // codes: row 64 * wave + lane, 16 bytes per slice; its scale byte likewise
+    } else if constexpr (BT == 1) {  // codes: row 64 * wave + lane, 16 bytes per slice; its scale byte likewise
         const int r = 64 * wave + lane;
         boff[0] = wbase(r, 0) + wrow(r) * rowb;
         soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
+    } else {  // FP8: copy i fills LDS 16-byte unit `lane` of rows 32 (2 wave + i) .. + 31
+#pragma unroll
+        for (int i = 0; i < b_copies<BT>(); ++i) {
+            const int r = 32 * (b_copies<BT>() * wave + i) + (lane >> 1);
+            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(fp8_half(r, lane & 1) * 16);
+        }
+    }
+    // FP8: the matrices' fp32 scales (gate / up, or down), applied in the epilogue
+    float bsc0 = 1.0f, bsc1 = 1.0f;
+    if constexpr (BT == 2) {
+        bsc0 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.off[3] : g.off[5]));
+        bsc1 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.off[4] : g.off[5]));
     }
 
     auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
@@ -441,10 +467,11 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         for (int i = 0; i < AL; ++i)
             __builtin_amdgcn_global_load_lds(A + aoff[i] + kt * KS, FT_LDS(st + (AL * wave + i) * 1024), 16, 0, 0);
         unsigned char* bst = st + A_BYTES;
-        if constexpr (BT == 0) {
+        if constexpr (BT == 0 || BT == 2) {
+            constexpr int bstep = BT == 0 ? ROWB : KS;  // bytes of a row slice
 #pragma unroll
             for (int i = 0; i < b_copies<BT>(); ++i)
-                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * ROWB, FT_LDS(bst + (b_copies<BT>() * wave + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * bstep, FT_LDS(bst + (b_copies<BT>() * wave + i) * 1024), 16, 0, 0);
         } else {
             __builtin_amdgcn_global_load_lds(slot + boff[0] + kt * (KS / 2), FT_LDS(bst + wave * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(slot + soff + kt, FT_LDS(bst + BN * 16 + wave * 256), 1, 0, 0);
@@ -474,6 +501,32 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         constexpr int MA = decltype(mc)::value;
         const unsigned char* st = smem + stage * stage_bytes<BT>();
         const unsigned char* Bc = st + A_BYTES;
+        if constexpr (BT == 2) {
+            // FP8: a lane reads its B row's 16 codes k = 16 hi .. + 15 once and
+            // fragment kk takes k = 16 hi + 8 kk .. + 7; A is read at the same
+            // positions (chunk 2 hi + kk).  Both operands use this permutation of
+            // the slice's 32 k, so the MFMA sums are those of the plain order.
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int m = 0; m < MA; ++m)
+                    F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(m * 32 + l32, 2 * hi + kk));
+            if constexpr (MA > 0) {
+#pragma unroll
+                for (int n = 0; n < NTL; ++n) {
+                    int brow;
+                    if constexpr (MODE == MODE_GATED)
+                        brow = (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
+                    else
+                        brow = wn * WN + n * 32;
+                    const int row = brow + l32;
+                    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(Bc + row * KS + fp8_half(row, hi) * 16);
+                    F.b[0][n] = fp8_frag(c[0], c[1]);
+                    F.b[1][n] = fp8_frag(c[2], c[3]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             // 32x32x16 operands: lane holds row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7
@@ -533,7 +586,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         load_frags((kt + 1) % STAGES, nxt, mc);
         mfmas(cur, mc);
         // interleave: one MFMA, one LDS read, ... so the reads hide under the MFMAs
-        constexpr int NMF = 2 * MA * NTL, NDS = 2 * (MA + (BT == 0 ? 1 : 2) * NTL);
+        constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 1 ? 4 : 1) * NTL;
         constexpr int NP = NMF < NDS ? NMF : NDS;
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
@@ -581,12 +634,12 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
                     for (int n = 0; n < NTL / 2; ++n)
                         ts[row * PITCH + wn * (WN / 2) + n * 32 + l32] =
                             __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(
-                                silu_mul_fast(acc[m][n][q], acc[m][n + NTL / 2][q])));
+                                silu_mul_fast(acc[m][n][q] * bsc0, acc[m][n + NTL / 2][q] * bsc1)));
                 } else {
 #pragma unroll
                     for (int n = 0; n < NTL; ++n)
                         ts[row * PITCH + wn * WN + n * 32 + l32] =
-                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(acc[m][n][q]));
+                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(acc[m][n][q] * bsc0));
                 }
             }
         }
@@ -611,7 +664,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
 #pragma unroll
                 for (int n = 0; n < NTL; ++n) {
                     const int col = c0 + wn * WN + n * 32 + l32;
-                    if (col < NOUT) reinterpret_cast<float*>(out)[(obase + row) * NOUT + col] = acc[m][n][q];
+                    if (col < NOUT) reinterpret_cast<float*>(out)[(obase + row) * NOUT + col] = acc[m][n][q] * bsc0;
                 }
             }
         }
@@ -735,9 +788,9 @@ ft_status launch_gemm1_mfma(const FfnGeom& g, const __bf16* x, const int32_t* pe
     const int mt = min(max_tiles, max_tiles_for(g, pipe::BM));
     const int nn = cdiv(g.I, pipe::BN / 2);
     const unsigned grid = (unsigned)(mt * nn + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-    hipError_t e = g.w_dt == FT_MXFP4
-        ? launch_pipe<MODE_GATED, 1, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
-        : launch_pipe<MODE_GATED, 0, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h);
+    hipError_t e = g.w_dt == FT_MXFP4 ? launch_pipe<MODE_GATED, 1, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
+                 : g.w_dt == FT_FP8   ? launch_pipe<MODE_GATED, 2, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
+                                      : launch_pipe<MODE_GATED, 0, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h);
     if (e != hipSuccess) return set_error(FT_ERR_HIP, "gemm1: %s", hipGetErrorString(e));
     return FT_OK;
 }
@@ -752,6 +805,9 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
     if (g.w_dt == FT_MXFP4)
         e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 1, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
                            : launch_pipe<MODE_LIST, 1, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
+    else if (g.w_dt == FT_FP8)
+        e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 2, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
+                           : launch_pipe<MODE_LIST, 2, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
     else
         e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 0, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
                            : launch_pipe<MODE_LIST, 0, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
