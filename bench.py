@@ -471,7 +471,9 @@ def main():
             "down_gbs": r["gemm2_gbs"],
             "roofline": {"bound": "hbm", "achieved": r["gemm1_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm1_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "gate/up weight streaming (stream_kernel, NM=2)",
+                         "kernel": ("gate/up weight streaming on matrix cores (stream_mx_kernel, NM=2)"
+                                    if sh.wdtype in ("mxfp4", "fp8") and T >= 2 else
+                                    "gate/up weight streaming (stream_kernel, NM=2)"),
                          "bytes_per_launch": r["w13_bytes"]}})
         log("decode", json.dumps(decode[-1]))
 

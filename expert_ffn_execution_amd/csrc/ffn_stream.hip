@@ -7,10 +7,10 @@
 // article, "瓶颈为什么是带宽而不是容量").  These kernels therefore stream
 // weights with 16-byte loads and keep the routed tokens' activations in LDS.
 // bf16 (and fp32) weights use vector-ALU dot products (v_dot2_f32_bf16): the
-// work per byte is too small for a matrix tile to pay off.  MXFP4 weights are
-// decoded exactly to bf16 first, which costs as much ALU again per weight
-// byte; for the down projection with more than one token they go to matrix
-// cores instead (the second kernel below).
+// work per byte is too small for a matrix tile to pay off.  MXFP4 and FP8
+// weights are decoded exactly to bf16 first, which costs as much ALU again
+// per weight byte; with more than one token they go to matrix cores instead
+// (the second kernel below).
 //
 // Streaming.  HBM stays busy only if every CU keeps enough bytes in flight,
 // and the cross-lane sums at the end of each row must stay cheap.  A weight
@@ -501,39 +501,40 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 down projection on matrix cores.  Decoding e2m1 codes to bf16 costs
-// one instruction per two weights, and a dot product per token row one more,
-// with the activations read from LDS four times over (32 bf16 per 16 code
-// bytes).  Here the decoded weights feed v_mfma_f32_16x16x32_bf16 instead: the group's token rows are the
-// MFMA's M (padded to 16 with zeros), 16 weight rows its N, and every token row
-// costs nothing beyond the decode.  Exact like the version above: codes decode
-// exactly to bf16 (times the block's power-of-two scale), products and sums in
-// fp32.
+// Narrow weights on matrix cores.  Decoding an e2m1 or e4m3 code to bf16
+// costs one instruction per two weights, and a dot product per token row one
+// more, with the activations read from LDS again for every token row.  Here
+// the decoded weights feed v_mfma_f32_16x16x32_bf16 instead: the group's
+// token rows are the MFMA's M (padded to 16 with zeros), 16 weight rows its
+// N, and every token row costs nothing beyond the decode.  Exact like the
+// version above: codes decode exactly to bf16 (MXFP4 times the block's
+// power-of-two scale; the FP8 matrix scale multiplies the finished sums),
+// products and sums in fp32.
 //
-// Lane l loads the 16 code bytes of weight row 16 g + (l & 15) at K offset
-// 32 (l >> 4) of each 128-wide step: the 32 weights decode to four 8-wide
-// B fragments, fragment f covering k = 32 (l >> 4) + 8 f.  Every lane's k
-// positions form a permutation of the step's 128, the same for A (read from
-// LDS at those positions) and B, so the MFMA's sum over its K is the sum over
-// the step.  No cross-lane reduction is needed: the accumulator of lane l
-// holds token rows 4 (l >> 4) .. + 3 of weight row 16 g + (l & 15).
+// Lane l takes LE weights of row 16 g + (l & 15) at K offset LE (l >> 4) of
+// each 4 LE-wide step, with two 16-byte loads: the four lane groups together
+// read a whole 128-byte line of each of the 16 rows (LE = 64 for MXFP4, 32
+// for FP8).  The weights decode to 8-wide B fragments, fragment f covering
+// k = LE (l >> 4) + 8 f.  Every lane's k positions form a permutation of the
+// step's, the same for A (read from LDS at those positions) and B, so the
+// MFMA's sum over its K is the sum over the step.  No cross-lane reduction
+// is needed: the accumulator of lane l holds token rows 4 (l >> 4) .. + 3 of
+// weight row 16 g + (l & 15).  NM = 2 runs the gate and up rows of the same
+// 16 row numbers side by side and writes silu(gate) * up.
 //
-// A wavefront walks (row group of 16, K step) pairs in order with MX_D steps
-// of loads in flight (a rolling register buffer, branch-free like the kernel
+// A wavefront walks (row group of 16, K step) pairs in order with D steps of
+// loads in flight (a rolling register buffer, branch-free like the kernel
 // above); the block's four wavefronts take every fourth row group of its rows.
-// Measured against the kernel above with 2 to 64 tokens (284B-A13B and
-// 753B-A40B MXFP4 layers): 11-18% faster for the down rows; for the gate/up
-// rows within 5% either way, so those stay on the kernel above.
-// Scales: one 16-byte load per lane every four steps brings a row's scale
-// bytes of those steps (byte 4 s + q is step s's for lane group q); one-byte
-// loads per step, from 16 rows at once, cost more than the codes.  The code
-// loads are ordinary (cached) loads: one instruction reads half of each of
-// 16 rows' 128-byte lines and the next step the other half, which a
-// non-temporal hint would send to memory twice (measured 10-15% slower).
+// MXFP4 scales: one 16-byte load per lane every two steps brings a row's
+// scale bytes of those steps; one-byte loads per step, from 16 rows at once,
+// cost more than the codes.
+// Measured (MXFP4 284B-A13B layer, 2 to 64 tokens): half a line per row and
+// step (one load per lane) was up to 20% slower than whole lines, and 8
+// steps in flight (148 VGPRs) slower than 4 (108) where blocks are short.
+// Against the kernel above: gate/up 33 vs 56 us at 2 tokens and 353 vs 418
+// us at 64; down 195 vs 223 us at 64 tokens.
 // ---------------------------------------------------------------------------
-constexpr int MX_KS = 128;  // K elements per step (64 code bytes of a row)
-constexpr int MX_D = 8;     // steps in flight per wavefront (a multiple of 4)
-static_assert(MX_D % 4 == 0, "scale words cover four steps");
+constexpr int MX_D = 4;  // steps in flight per wavefront (a multiple of 2)
 
 __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t codes, float sc) {
     u32x4_t d;
@@ -544,9 +545,33 @@ __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t codes, float sc) {
     return __builtin_bit_cast(bf16x8_t, d);
 }
 
-template <typename OT>
+// 8 e4m3 codes (two words) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8_t fp8x8_bf16(uint32_t lo, uint32_t hi) {
+    u32x4_t d;
+    d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return __builtin_bit_cast(bf16x8_t, d);
+}
+
+// Per-step shape of the matrix-core kernel (WT: 2 = MXFP4, 3 = FP8).
+template <int WT> struct MxShape {
+    static constexpr int LPS = 2;                                // 16-byte code loads per lane, step, matrix
+    static constexpr int EPL = WT == 3 ? 16 : 32;                // weights per 16-byte load
+    static constexpr int LE = LPS * EPL;                         // weights per lane and step
+    static constexpr int KS = 4 * LE;                            // K per step (128 code bytes of a row)
+    static constexpr int NF = LE / 8;                            // 8-wide B fragments per lane, step
+    static constexpr int SPW = WT == 2 ? 16 / (4 * LPS) : 1;     // MXFP4: steps per 16-byte scale word
+    static constexpr int NSV = WT == 2 ? 2 * MX_D / SPW : 1;     // MXFP4: scale-word slots
+};
+
+template <int WT, int NM, typename OT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
-    constexpr int NM = 1;  // one matrix: the down rows
+    static_assert(WT == 2 || WT == 3, "narrow weights only");
+    using S = MxShape<WT>;
+    constexpr int D = MX_D, LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
+    static_assert(D % SPW == 0, "a scale word's steps share one register round");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16* xs = reinterpret_cast<__bf16*>(smem);
     const int j = blockIdx.x / a.NB, nb = blockIdx.x % a.NB;
@@ -555,22 +580,26 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     if (!resolve_group(a, j, lane, gr)) return;
     const int R = gr.R;
     const int K = a.K, pitch = K + 8;  // bf16 per LDS row (the skew spreads rows over banks)
-    const int nks = K / MX_KS;
+    const int nks = K / KS;
     const int n0 = nb * a.RPB, n1 = min(n0 + a.RPB, a.N);
     const int nrg = (n1 - n0) / 16;                                       // row groups of the block
     const int rgw = nrg > wave ? (nrg - wave + NWAVE - 1) / NWAVE : 0;    // ... of this wave
     const int U = rgw * nks;                                              // (group, step) pairs
     const int ln = lane & 15, q = lane >> 4;
     const uint8_t* sl = a.pool + (size_t)gr.slot * a.slot_stride;
-    const size_t rowb = (size_t)K / 2, srowb = (size_t)K / 32;
+    const size_t rowb = WT == 3 ? (size_t)K : (size_t)K / 2, srowb = (size_t)K / 32;
+    float msc[NM];  // FP8: the matrix scales (applied to the finished sums)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+        msc[m] = WT == 3 ? *reinterpret_cast<const float*>(sl + a.soff[m]) : 1.0f;
 
     // Loads of pair u into code buffer b; pairs past the end re-read the first
-    // one.  A pair u == 0 mod 4 also loads the scales of pairs u .. u + 3 (nks
-    // is a multiple of 4: one row group) into scale slot t; the loop below
-    // runs two rounds of MX_D pairs per iteration so that slot t's readers
-    // (four pairs, MX_D pairs earlier) are done when it is refilled.
-    constexpr int NSV = 2 * MX_D / 4;  // scale slots
-    u32x4_t cb[MX_D][NM];
+    // one.  MXFP4: a pair u == 0 mod SPW also loads the row's 16 scale bytes of
+    // pairs u .. u + SPW - 1 (nks is a multiple of SPW: one row group) into
+    // scale slot t; the loop below runs two rounds of D pairs per iteration so
+    // that slot t's readers (SPW pairs, D pairs earlier) are done when it is
+    // refilled.
+    u32x4_t cb[D][NM][LPS];
     u32x4_t sv[NSV][NM];
     auto row_of = [&](int uu) __attribute__((always_inline)) {
         const int rgi = uu / nks;
@@ -583,15 +612,18 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
         const size_t row = row_of(uu);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-            cb[b][m] = *(reinterpret_cast<const u32x4_t*>(sl + a.moff[m] + row * rowb) + 4 * ks + q);
-        if (b % 4 == 0) {
+#pragma unroll
+            for (int h = 0; h < LPS; ++h)
+                cb[b][m][h] = *(reinterpret_cast<const u32x4_t*>(sl + a.moff[m] + row * rowb) +
+                                4 * LPS * ks + LPS * q + h);
+        if (WT == 2 && b % SPW == 0) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
-                sv[t][m] = *reinterpret_cast<const u32x4_t*>(sl + a.soff[m] + row * srowb + 4 * ks);
+                sv[t][m] = *reinterpret_cast<const u32x4_t*>(sl + a.soff[m] + row * srowb + 4 * LPS * ks);
         }
     };
 #pragma unroll
-    for (int b = 0; b < MX_D; ++b) issue(b, b / 4, b);
+    for (int b = 0; b < D; ++b) issue(b, (b / SPW) % NSV, b);
 
     // the group's activation rows, plain layout
     const __bf16* src = reinterpret_cast<const __bf16*>(a.src);
@@ -603,31 +635,42 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     }
     __syncthreads();
 
-    // A: this lane's token row (rows past R read row R - 1 and are zeroed)
+    // A: this lane's token row (rows past R read row R - 1 and are zeroed),
+    // at the lane group's K offset
     const bool mrow = ln < R;
-    const __bf16* xa = xs + (size_t)min(ln, R - 1) * pitch + 32 * q;
+    const __bf16* xa = xs + (size_t)min(ln, R - 1) * pitch + S::LE * q;
     f32x4_t acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int u0 = 0; u0 < U; u0 += 2 * MX_D) {
+    for (int u0 = 0; u0 < U; u0 += 2 * D) {
 #pragma unroll
-        for (int v = 0; v < 2 * MX_D; ++v) {
-            const int u = u0 + v, b = v % MX_D, t = v / 4;
+        for (int v = 0; v < 2 * D; ++v) {
+            const int u = u0 + v, b = v % D, t = (v / SPW) % NSV;
             if (u < U) {  // wave-uniform
                 const int rgi = u / nks, ks = u - rgi * nks;
-                bf16x8_t av[4];
+                bf16x8_t av[NF];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    av[f] = *reinterpret_cast<const bf16x8_t*>(xa + ks * MX_KS + 8 * f);
+                for (int f = 0; f < NF; ++f) {
+                    av[f] = *reinterpret_cast<const bf16x8_t*>(xa + ks * KS + 8 * f);
                     if (!mrow) av[f] = bf16x8_t{};
                 }
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
-                    const float sc = __uint_as_float(((sv[t][m][v % 4] >> (8 * q)) & 0xFFu) << 23);
 #pragma unroll
-                    for (int f = 0; f < 4; ++f)
-                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], fp4x8_bf16(cb[b][m][f], sc),
-                                                                         acc[m], 0, 0, 0);
+                    for (int f = 0; f < NF; ++f) {
+                        bf16x8_t bw;
+                        if constexpr (WT == 2) {
+                            // scale byte of this lane's 32-block: byte SPW-step s, group q, load h
+                            const int h = f / 4, by = (v % SPW) * 4 * LPS + LPS * q + h;
+                            const uint32_t word = sv[t][m][by >> 2];
+                            const float sc = __uint_as_float(((word >> (8 * (by & 3))) & 0xFFu) << 23);
+                            bw = fp4x8_bf16(cb[b][m][h][f % 4], sc);
+                        } else {
+                            const int h = f / 2, w0 = 2 * (f % 2);
+                            bw = fp8x8_bf16(cb[b][m][h][w0], cb[b][m][h][w0 + 1]);
+                        }
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], bw, acc[m], 0, 0, 0);
+                    }
                 }
                 if (ks == nks - 1) {  // row group done: token rows 4 q + i of weight row
                     const int row = n0 + 16 * (wave + NWAVE * rgi) + ln;
@@ -636,10 +679,14 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
                         const int mo = 4 * q + i;
                         if (mo < R) {
                             const size_t idx = (gr.orow0 + gr.r0 + mo) * (size_t)a.N + row;
-                            if constexpr (sizeof(OT) == 4) {
-                                reinterpret_cast<float*>(a.dst)[idx] = acc[0][i];
+                            if constexpr (NM == 2) {  // h = silu(gate) * up, bf16
+                                const float hv = silu_mul(acc[0][i] * msc[0], acc[1][i] * msc[1]);
+                                reinterpret_cast<uint16_t*>(a.dst)[idx] = (uint16_t)f32_to_bf16_bits(hv);
+                            } else if constexpr (sizeof(OT) == 4) {
+                                reinterpret_cast<float*>(a.dst)[idx] = acc[0][i] * msc[0];
                             } else {
-                                reinterpret_cast<uint16_t*>(a.dst)[idx] = (uint16_t)f32_to_bf16_bits(acc[0][i]);
+                                reinterpret_cast<uint16_t*>(a.dst)[idx] =
+                                    (uint16_t)f32_to_bf16_bits(acc[0][i] * msc[0]);
                             }
                         }
                     }
@@ -647,7 +694,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
                     for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
             }
-            issue(b, ((v + MX_D) / 4) % NSV, u + MX_D);
+            issue(b, ((v + D) / SPW) % NSV, u + D);
         }
     }
 }
@@ -729,25 +776,36 @@ ft_status launch_rows(const StreamArgs& a, int n_shared, int cap, size_t max_lds
     return launch_one<WT, NM, QMAX, 8, OT>(a, n_shared, max_lds, s);
 }
 
-// MXFP4 down rows on matrix cores: rows whose length is a multiple of 4 MX_KS
-// (each 16-byte scale word then lies within its row), and more than one token
-// (single-token decode is faster on the lean one-row dot-product kernel:
-// 14.9 vs 17.0 us for the 284B-A13B layer).  Token rows per group: up to 4
-// (LDS for the rows of every resident block).
-bool mx_eligible(int K, int T) {
+// Rows on matrix cores: MXFP4 rows whose length is a multiple of 512 (each
+// 16-byte scale word then lies within its row), FP8 rows whose length is a
+// multiple of 128.  Only with more than one token: at one token the lean
+// one-row dot-product kernel is as fast for MXFP4 and faster for FP8
+// (35B-A3B gate/up 12.8 vs 17.5 us).
+bool mx_eligible(int WT, int K, int T) {
     static const bool off = getenv("FTMOE_MX_DOT") != nullptr;  // keep the dot-product kernel
-    return !off && T > 1 && K % (4 * MX_KS) == 0;
+    static const int min_t = [] {
+        const char* e = getenv("FTMOE_MX_MIN_T");
+        return e ? atoi(e) : 2;
+    }();
+    if (off || T < min_t) return false;
+    if (WT == 2) return K % 512 == 0;
+    return WT == 3 && K % 128 == 0;
 }
-template <typename OT>
+template <int WT, int NM, typename OT>
 ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
+    // Token rows per group: up to 8, within 64 KB of LDS (two blocks or more
+    // per CU).  Fewer rows per group split busy experts into more groups that
+    // re-read the same weights (FP8 35B-A3B layer at 64 tokens: 73 -> 60 us
+    // for the down rows going from 4 to 8).
     static const int rcap_max = [] {
         const char* e = getenv("FTMOE_MX_RCAP");
-        const int v = e ? atoi(e) : 4;
+        const int v = e ? atoi(e) : 8;
         return v < 1 ? 1 : v > 16 ? 16 : v;
     }();
     const size_t row_bytes = ((size_t)a.K + 8) * 2;
+    const size_t lds_cap = max_lds < 65536 ? max_lds : 65536;
     int rcap = a.T < rcap_max ? a.T : rcap_max;
-    while (rcap > 1 && rcap * row_bytes > max_lds) --rcap;
+    while (rcap > 1 && rcap * row_bytes > lds_cap) --rcap;
     const size_t lds = rcap * row_bytes;
     if (lds > max_lds)
         return ft::set_error(FT_ERR_UNSUPPORTED, "ffn stream: an activation row of %zu bytes exceeds LDS",
@@ -757,9 +815,27 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     const long act = tk < a.E ? tk : a.E;
     a.n_routed_groups = (int)((tk + act * (rcap - 1)) / rcap);
     const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
-    a.RPB = pick_rpb(groups, a.N, 16, target_blocks(rcap));
+    // Rows per block.  A wavefront's start-up (group lookup, activation
+    // staging, the first loads' latency) is fixed, so each wavefront streams
+    // at least wave_bytes of weights (64 KB FP8, 32 KB MXFP4: measured best);
+    // then the grid is held to at most target_blocks() and, while the rows can
+    // still halve, to at least 512 blocks.  FP8 35B-A3B down rows (768 B) at
+    // 4 / 16 / 64 tokens: 29 / 66 / 60 us with one row group per wavefront,
+    // 18 / 36 / 49 us with this rule.
+    static const int wave_kb = [] {
+        const char* e = getenv("FTMOE_MX_WAVE_KB");
+        return e ? atoi(e) : 0;
+    }();
+    const size_t wave_bytes = (size_t)(wave_kb > 0 ? wave_kb : WT == 3 ? 64 : 32) * 1024;
+    const size_t row_w = (WT == 3 ? (size_t)a.K : (size_t)a.K / 2 + a.K / 32) * NM;  // weight bytes per row
+    auto nblk = [&](int rpb) { return groups * ((a.N + rpb - 1) / rpb); };
+    int rpb = 16 * NWAVE;
+    while (rpb < a.N && (size_t)(rpb / NWAVE) * row_w < wave_bytes) rpb *= 2;
+    while (rpb < a.N && nblk(rpb) > target_blocks(rcap)) rpb *= 2;
+    while (rpb > 16 * NWAVE && nblk(rpb) < 512) rpb /= 2;
+    a.RPB = rpb;
     a.NB = (a.N + a.RPB - 1) / a.RPB;
-    auto kern = stream_mx_kernel<OT>;
+    auto kern = stream_mx_kernel<WT, NM, OT>;
     if (lds > 65536)
         FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
@@ -804,8 +880,14 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     prof_begin(PROF_FFN_GEMM1, s);
     if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
-    else if (g.w_dt == FT_FP8) r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
-    else r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    else if (g.w_dt == FT_FP8) {
+        if (mx_eligible(3, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
+        else r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    } else if (mx_eligible(2, a1.K, a1.T)) {
+        r = launch_mx<2, 2, float>(a1, g.n_shared, max_lds, s);
+    } else {
+        r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    }
     prof_end(PROF_FFN_GEMM1, s);
     if (r != FT_OK) return r;
 
@@ -824,11 +906,16 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
         if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
     } else if (g.w_dt == FT_FP8) {
-        if (y_dt == FT_F32) r = launch_rows<3, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
-        else r = launch_rows<3, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
-    } else if (mx_eligible(a2.K, a2.T)) {
-        if (y_dt == FT_F32) r = launch_mx<float>(a2, g.n_shared, max_lds, s);
-        else r = launch_mx<__bf16>(a2, g.n_shared, max_lds, s);
+        if (mx_eligible(3, a2.K, a2.T)) {
+            if (y_dt == FT_F32) r = launch_mx<3, 1, float>(a2, g.n_shared, max_lds, s);
+            else r = launch_mx<3, 1, __bf16>(a2, g.n_shared, max_lds, s);
+        } else {
+            if (y_dt == FT_F32) r = launch_rows<3, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+            else r = launch_rows<3, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+        }
+    } else if (mx_eligible(2, a2.K, a2.T)) {
+        if (y_dt == FT_F32) r = launch_mx<2, 1, float>(a2, g.n_shared, max_lds, s);
+        else r = launch_mx<2, 1, __bf16>(a2, g.n_shared, max_lds, s);
     } else {
         if (y_dt == FT_F32) r = launch_rows<2, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<2, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);

@@ -25,13 +25,15 @@ SHAPES = {
                                  wdtype="mxfp4"),
     "35b_a3b_bf16": synth.A3B_BF16,
     "284b_a13b_mxfp4": synth.A13B_MXFP4,
+    "35b_a3b_fp8": synth.A3B_FP8,
 }
 # (shape, T, permuted slots): decode sizes take the streaming kernels, T = 300
 # on the small shapes the MFMA tiles (tile list built on the device)
 CASES = [("tiny_f32", 64, False), ("small_bf16", 3, True), ("small_bf16", 300, False),
          ("small_mx", 5, False), ("small_mx", 300, True), ("35b_a3b_bf16", 1, False),
          ("35b_a3b_bf16", 16, False), ("35b_a3b_bf16", 8, False), ("35b_a3b_bf16", 9, False),
-         ("284b_a13b_mxfp4", 1, False), ("284b_a13b_mxfp4", 8, False)]
+         ("284b_a13b_mxfp4", 1, False), ("284b_a13b_mxfp4", 8, False), ("35b_a3b_fp8", 1, False),
+         ("35b_a3b_fp8", 8, False), ("35b_a3b_fp8", 64, False)]
 _LAYERS = {}
 
 

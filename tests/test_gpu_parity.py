@@ -129,6 +129,9 @@ SMALL = {
                               wdtype="mxfp4"),
     "bf16_shared": synth.LayerShape("gpu_small_bf16_sh", H=256, E=8, k=2, I=192, n_shared=1),
     "fp8": synth.LayerShape("gpu_small_fp8", H=512, E=16, k=4, I=384, n_shared=1, wdtype="fp8"),
+    # rows of 512 both ways: MXFP4 gate/up and down both on the matrix-core kernel
+    "mxfp4_512": synth.LayerShape("gpu_small_mx512", H=512, E=16, k=4, I=512, n_shared=1,
+                                  wdtype="mxfp4"),
 }
 
 
