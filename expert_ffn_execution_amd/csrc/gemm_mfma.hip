@@ -296,50 +296,92 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
 // ---------------------------------------------------------------------------
 // Pipelined tile kernel for the expert GEMMs.  256 x 256 output tile, 4
 // wavefronts (one per SIMD), each owning all 256 rows and a 64-column strip:
-// 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane),
-// K in slices of 32 through five LDS stages.
-// Slices are copied global -> LDS by the load units directly
-// (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane l
-// its 16 bytes), so four slices are in flight while the fifth feeds the
-// MFMAs and no registers hold staged data.  A wave waits for its own copies
-// of a slice with s_waitcnt vmcnt and the block barrier then publishes it.
-// The tile is as large as the 160 KB LDS allows so that every byte brought
-// into the CU feeds as many MFMAs as possible: per slice 32 KB carry 4.2
-// MFLOP.  MXFP4 weights stay packed in LDS (16 code bytes + 1 scale byte per
-// row and slice) and are decoded to bf16 when a fragment is read.
+// 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+// K goes in stages of 64 through two LDS rings, one for A (the gathered
+// activation rows) and one for B (the expert's weight rows), copied global ->
+// LDS by the load units directly (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB of LDS, lane l its 16 bytes), so no registers hold
+// staged data.  A bf16 row's stage is one whole 128-byte line, and a copy
+// instruction reads 8 such lines.  With stages of 32 each instruction read
+// 16 half lines, and a probe of this copy pattern alone moved L2-resident
+// data at 15 TB/s with half lines against 32 TB/s with whole lines; the
+// copies, not the MFMAs, set the K loop's pace.  B keeps more stages in
+// flight than A: the weights stream from HBM, the activations (re-read by
+// every N-tile of an M-tile) mostly hit in L2.
+// The MFMAs take a stage in two halves of 32 (two 16-deep k-steps each), one
+// half per step: odd steps wait for the next stage (s_waitcnt vmcnt on the
+// wave's own copies, counted from the fixed issue order), meet at the block
+// barrier and copy the next A stage into the slot just freed; even steps copy
+// the next B stage.  The tile is as large as the 160 KB LDS allows so that
+// every byte brought into the CU feeds as many MFMAs as possible.  MXFP4
+// weights stay packed in LDS (32 code bytes + 2 scale bytes per row and
+// stage), FP8 likewise (64 code bytes), decoded to bf16 when a fragment is
+// read.
 // An expert's last M-tile is usually partly filled (routing gives each
 // expert an arbitrary row count): since every wave spans all rows, all waves
 // skip the MFMAs and fragment reads of 32-row sub-tiles past the tile's rows
 // alike, and the block's time shrinks with its row count.
 //
-// LDS layout of a slice of rows: row r is 64 bytes = 4 chunks of 16 bytes,
-// chunk c stored at position c ^ ((r >> 2) & 3): the 16 rows a fragment read
-// touches then cover all 64 banks exactly once.
+// LDS layout of a stage: bf16 rows are 8 chunks of 16 bytes, chunk c at
+// position c ^ ((r >> 1) & 7); FP8 rows 4 chunks at c ^ ((r >> 2) & 3); MXFP4
+// rows 2 halves at h ^ ((r >> 3) & 1).  The 16 rows one fragment read pass
+// touches then spread over the 64 banks (MXFP4: two rows per bank group).
 // ---------------------------------------------------------------------------
 namespace pipe {
-constexpr int BM = 256, BN = 256, KS = 32, NT = 256, NW = NT / 64, WN = BN / NW;
-constexpr int STAGES = 5;   // 5 x 32 KB = all 160 KB of LDS (bf16)
-constexpr int MT = BM / 32, NTL = WN / 32;   // 32 x 32 MFMA tiles per wavefront
-constexpr int ROWB = KS * 2;                          // bytes of a bf16 row slice
-constexpr int A_BYTES = BM * ROWB;                    // 16 KB
-constexpr int AL = A_BYTES / 1024 / NW;               // A copies per wave per slice
+constexpr int BM = 256, BN = 256, NT = 256, NW = NT / 64, WN = BN / NW;
+constexpr int KST = 64;                        // K per stage
+constexpr int MT = BM / 32, NTL = WN / 32;     // 32 x 32 MFMA tiles per wavefront
+constexpr int A_UNIT = BM * KST * 2;           // one A stage: 32 KB of bf16
+constexpr int LA = A_UNIT / 1024 / NW;         // A copies per wave and stage
 // BT: 0 bf16 weights, 1 MXFP4, 2 FP8 (e4m3, one fp32 scale per matrix).
-// MXFP4: codes [BN][16 B], then one 4-byte slot per row holding its scale byte
-// (a 1-byte LDS-DMA load writes each lane's byte to a 4-byte slot).
-// FP8: codes [BN][32 B]; the two 16-byte halves of rows 8..15 of every 16 are
-// swapped (h ^ ((r >> 3) & 1)) so that fragment reads spread over the banks.
-template <int BT> constexpr int b_bytes() { return BT == 0 ? BN * ROWB : BT == 1 ? BN * 16 + BN * 4 : BN * KS; }
-template <int BT> constexpr int stage_bytes() { return A_BYTES + b_bytes<BT>(); }
+template <int BT> constexpr int b_row() { return BT == 0 ? KST * 2 : BT == 1 ? KST / 2 : KST; }
+// MXFP4: codes [BN][32 B], then for each half of the stage a 4-byte slot per
+// row holding its scale byte (a 1-byte LDS-DMA load writes each lane's byte
+// to a 4-byte slot)
+template <int BT> constexpr int b_unit() { return BN * b_row<BT>() + (BT == 1 ? 2 * BN * 4 : 0); }
+template <int BT> constexpr int n_a() { return BT == 0 ? 2 : 3; }            // A ring stages
+template <int BT> constexpr int n_b() { return BT == 0 ? 3 : BT == 1 ? 6 : 4; }  // B ring stages
+template <int BT> constexpr int b_code_copies() { return BN * b_row<BT>() / 1024 / NW; }
+template <int BT> constexpr int b_copies() { return b_code_copies<BT>() + (BT == 1 ? 2 : 0); }  // per wave, stage
 constexpr size_t EPI_BYTES = (size_t)BM * (BN + 8) * 2;   // bf16 output tile (plain GEMM)
-template <int BT> constexpr size_t lds_bytes() {
-    return (size_t)STAGES * stage_bytes<BT>() > EPI_BYTES ? (size_t)STAGES * stage_bytes<BT>() : EPI_BYTES;
+template <int BT> constexpr size_t ring_bytes() {
+    return (size_t)n_a<BT>() * A_UNIT + (size_t)n_b<BT>() * b_unit<BT>();
 }
-// global_load_lds instructions per wave per slice: A, then B (bf16 and FP8:
-// 1 KB pieces; MXFP4: one codes piece of 64 rows and one scale byte per lane)
-template <int BT> constexpr int b_copies() { return BT == 0 ? BN * ROWB / 1024 / NW : BT == 1 ? 1 : BN * KS / 1024 / NW; }
-template <int BT> constexpr int loads_per_slice() { return AL + (BT == 1 ? 2 : b_copies<BT>()); }
-__device__ __forceinline__ int fp8_half(int r, int h) { return h ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int sw(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+template <int BT> constexpr size_t lds_bytes() { return ring_bytes<BT>() > EPI_BYTES ? ring_bytes<BT>() : EPI_BYTES; }
+static_assert(lds_bytes<0>() <= 160 * 1024 && lds_bytes<1>() <= 160 * 1024 && lds_bytes<2>() <= 160 * 1024,
+              "rings fit the LDS");
+__device__ __forceinline__ int swz_bf16(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int swz_fp8(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int swz_fp4(int r, int h) { return r * 32 + ((h ^ ((r >> 3) & 1)) << 4); }
+
+// Copy issue order.  Step t (t < 0: before the K loop) issues, when the stage
+// exists, A stage (t - 1) / 2 + n_a if t is odd, B stage (t - 2) / 2 + n_b if
+// even; stage x of A thus goes out at step 2 (x - n_a) + 1, of B at 2 (x - n_b) + 2.
+template <int BT> constexpr int step_of_a(int x) { return 2 * (x - n_a<BT>()) + 1; }
+template <int BT> constexpr int step_of_b(int x) { return 2 * (x - n_b<BT>()) + 2; }
+template <int BT> constexpr int first_step() {
+    return step_of_a<BT>(0) < step_of_b<BT>(0) ? step_of_a<BT>(0) : step_of_b<BT>(0);
+}
+// Copies a wave may leave in flight when it waits for stage y having issued
+// every step up to P (stages past the last, nst - 1, are never issued).
+template <int BT>
+__host__ __device__ constexpr int copies_after(int y, int P, int nst) {
+    const int la = step_of_a<BT>(y), lb = step_of_b<BT>(y);
+    int n = 0;
+    for (int t = (la > lb ? la : lb) + 1; t <= P; ++t) {
+        const int x = (t & 1) ? (t - 1) / 2 + n_a<BT>() : (t - 2) / 2 + n_b<BT>();
+        if (x >= 0 && x < nst) n += (t & 1) ? LA : b_copies<BT>();
+    }
+    return n;
+}
+// in steady state (stage y = s + 1 at odd step 2 s + 1, every stage present)
+template <int BT> constexpr int steady_in_flight() { return copies_after<BT>(1, 0, 1 << 20); }
+// the K loop's pairs of steps are straight-line once every copy of the pair exists
+template <int BT> constexpr int steady_margin() {
+    return n_b<BT>() - 1 > n_a<BT>() ? n_b<BT>() - 1 : n_a<BT>();
+}
+static_assert(steady_in_flight<0>() == 8 && steady_in_flight<1>() == 16 && steady_in_flight<2>() == 16,
+              "issue order");
 }  // namespace pipe
 
 #define FT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -350,6 +392,16 @@ template <int N>
 __device__ __forceinline__ void wait_vm_lgkm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+// the same with a run-time count, rounded down to a multiple of 4 (<= N)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_upto(int n) {
+    if constexpr (N <= 0) {
+        wait_vm_lgkm<0>();
+    } else {
+        if (n >= N) wait_vm_lgkm<N>();
+        else wait_vm_lgkm_upto<N - 4>(n);
+    }
 }
 
 // 8 e4m3 codes (bytes of w0, then w1) -> 8 bf16, exact
@@ -381,13 +433,36 @@ __device__ __forceinline__ void with_count(int M, F&& f) {
     }
 }
 
+// Scheduling groups of a steady K iteration in two phases: over the first P
+// MFMAs the NX instructions of group MX, over the remaining ones the NY of
+// group MY, each spread evenly (after MFMA i of a phase of n MFMAs, the ones
+// that bring its count to (i + 1) * N / n).
+template <int I, int NMF, int P, int MX, int NX, int MY, int NY>
+__device__ __forceinline__ void sched_two() {
+    if constexpr (I < NMF) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if constexpr (I < P) {
+            constexpr int n = ((I + 1) * NX) / P - (I * NX) / P;
+            if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(MX, n, 0);
+        } else {
+            constexpr int J = I - P, n = ((J + 1) * NY) / (NMF - P) - (J * NY) / (NMF - P);
+            if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(MY, n, 0);
+        }
+        sched_two<I + 1, NMF, P, MX, NX, MY, NY>();
+    }
+}
+template <int NX, int NY, int NMF>
+constexpr int phase_split() {
+    const int p = (NMF * NX + (NX + NY) / 2) / (NX + NY);
+    return p < 1 ? 1 : p > NMF - 1 ? NMF - 1 : p;
+}
+
 template <int MODE, int BT, typename OutT>
 __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     ft::FfnGeom g, const __bf16* __restrict__ A, const int32_t* __restrict__ perm,
     const TileDesc* __restrict__ tiles, const int* __restrict__ n_tiles, int n_ntiles,
     OutT* __restrict__ out) {
     using namespace pipe;
-    static_assert(STAGES == 5, "wait schedule below assumes five stages");
     extern __shared__ __attribute__((aligned(16))) unsigned char pipe_smem[];
     unsigned char* const smem = pipe_smem;
     // XCD-aware order: the dispatcher deals blocks to the 8 XCDs round-robin;
@@ -409,17 +484,17 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     // gated: B rows [0, 128) = gate rows c0.., [128, 256) = up rows c0..; plain: rows c0..
     const int c0 = nt * (MODE == MODE_GATED ? BN / 2 : BN);
 
-    // A: copy i of this wave fills LDS rows 16 * (AL * wave + i) + lane / 4,
-    // physical chunk lane % 4 (rows past the tile re-read its last row)
-    uint32_t aoff[AL];
+    // A: copy i of this wave fills LDS rows 8 (LA wave + i) .. + 7, lane l row
+    // + l / 8 at chunk position l % 8 (rows past the tile re-read its last row)
+    uint32_t aoff[LA];
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-        const int r = 16 * (AL * wave + i) + (lane >> 2);
+    for (int i = 0; i < LA; ++i) {
+        const int r = 8 * (LA * wave + i) + (lane >> 3);
         const int rc = min(r, td.rows - 1);
         uint32_t arow;
         if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + rc) : (uint32_t)(perm[td.p0 + rc] / g.k);
         else arow = (uint32_t)(obase + rc);
-        aoff[i] = arow * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
+        aoff[i] = arow * (uint32_t)K + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 8);
     }
     // B row r of the tile -> weight row (clamped: columns past NOUT are not stored)
     auto wrow = [&](int r) __attribute__((always_inline)) -> uint32_t {
@@ -433,25 +508,30 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             return (uint32_t)g.off[which ? 5 : 2];
     };
     const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : BT == 1 ? (uint32_t)K / 2 : (uint32_t)K;
-    // B value/code copies per wave: b_copies<BT>() <= 4 (a literal bound: a
+    // B code copies per wave: b_code_copies<BT>() <= 8 (a literal bound: a
     // call in an array bound reads as a variable-length array to the host pass)
-    uint32_t boff[4], soff = 0;
-    static_assert(b_copies<BT>() <= 4, "B copies per wave");
-    if constexpr (BT == 0) {
+    constexpr int NBC = b_code_copies<BT>();
+    static_assert(NBC <= 8, "B copies per wave");
+    uint32_t boff[8], soff = 0;
+    if constexpr (BT == 0) {  // copy i: rows 8 (NBC wave + i) .. + 7, like A
 #pragma unroll
-        for (int i = 0; i < b_copies<BT>(); ++i) {
-            const int r = 16 * (b_copies<BT>() * wave + i) + (lane >> 2);
-            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
+        for (int i = 0; i < NBC; ++i) {
+            const int r = 8 * (NBC * wave + i) + (lane >> 3);
+            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
         }
-    } else if constexpr (BT == 1) {  // codes: row 64 * wave + lane, 16 bytes per slice; its scale byte likewise
-        const int r = 64 * wave + lane;
-        boff[0] = wbase(r, 0) + wrow(r) * rowb;
-        soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
-    } else {  // FP8: copy i fills LDS 16-byte unit `lane` of rows 32 (2 wave + i) .. + 31
+    } else if constexpr (BT == 1) {  // copy i: rows 32 (NBC wave + i) .. + 31, two lanes a row; scales of row 64 wave + lane
 #pragma unroll
-        for (int i = 0; i < b_copies<BT>(); ++i) {
-            const int r = 32 * (b_copies<BT>() * wave + i) + (lane >> 1);
-            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(fp8_half(r, lane & 1) * 16);
+        for (int i = 0; i < NBC; ++i) {
+            const int r = 32 * (NBC * wave + i) + (lane >> 1);
+            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
+        }
+        const int r = 64 * wave + lane;
+        soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
+    } else {  // FP8 copy i: rows 16 (NBC wave + i) .. + 15, four lanes a row
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int r = 16 * (NBC * wave + i) + (lane >> 2);
+            boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
         }
     }
     // FP8: the matrices' fp32 scales (gate / up, or down), applied in the epilogue
@@ -461,20 +541,28 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         bsc1 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.off[4] : g.off[5]));
     }
 
-    auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
-        unsigned char* st = smem + stage * stage_bytes<BT>();
+    // (constants, not calls: a constexpr template call evaluated at run time in
+    // these lambdas keeps the host pass from emitting the kernel's launch stub)
+    constexpr int NA = n_a<BT>(), NB = n_b<BT>(), LB = b_copies<BT>();
+    constexpr int BUNIT = b_unit<BT>(), BROW = b_row<BT>();
+    unsigned char* const aring = smem;
+    unsigned char* const bring = smem + NA * A_UNIT;
+    const int nst = K / KST;
+    auto issue_a = [&](int x) __attribute__((always_inline)) {  // A stage x into its ring slot
+        unsigned char* dst = aring + (x % NA) * A_UNIT;
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            __builtin_amdgcn_global_load_lds(A + aoff[i] + kt * KS, FT_LDS(st + (AL * wave + i) * 1024), 16, 0, 0);
-        unsigned char* bst = st + A_BYTES;
-        if constexpr (BT == 0 || BT == 2) {
-            constexpr int bstep = BT == 0 ? ROWB : KS;  // bytes of a row slice
+        for (int i = 0; i < LA; ++i)
+            __builtin_amdgcn_global_load_lds(A + aoff[i] + x * KST, FT_LDS(dst + (LA * wave + i) * 1024), 16, 0, 0);
+    };
+    auto issue_b = [&](int x) __attribute__((always_inline)) {  // B stage x into its ring slot
+        unsigned char* dst = bring + (x % NB) * BUNIT;
 #pragma unroll
-            for (int i = 0; i < b_copies<BT>(); ++i)
-                __builtin_amdgcn_global_load_lds(slot + boff[i] + kt * bstep, FT_LDS(bst + (b_copies<BT>() * wave + i) * 1024), 16, 0, 0);
-        } else {
-            __builtin_amdgcn_global_load_lds(slot + boff[0] + kt * (KS / 2), FT_LDS(bst + wave * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(slot + soff + kt, FT_LDS(bst + BN * 16 + wave * 256), 1, 0, 0);
+        for (int i = 0; i < NBC; ++i)
+            __builtin_amdgcn_global_load_lds(slot + boff[i] + x * BROW, FT_LDS(dst + (NBC * wave + i) * 1024), 16, 0, 0);
+        if constexpr (BT == 1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                __builtin_amdgcn_global_load_lds(slot + soff + 2 * x + h, FT_LDS(dst + BN * 32 + h * BN * 4 + wave * 256), 1, 0, 0);
         }
     };
 
@@ -487,40 +575,40 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
 
-    constexpr int LPS = loads_per_slice<BT>();
-    const int nk = K / KS;
     const int l32 = lane & 31, hi = lane >> 5;
     const int mact = min(MT, (td.rows + 31) / 32);  // 32-row sub-tiles holding rows
 
-    // Fragments of one slice (both 16-deep k-steps): the wave reads slice k+1's
-    // fragments from LDS while its MFMAs consume slice k's from registers.
+    // Fragments of one half stage (both 16-deep k-steps): the wave reads step
+    // j+1's fragments from LDS while its MFMAs consume step j's from registers.
     struct Frags {
         bf16x8_t a[2][MT], b[2][NTL];
     };
-    auto load_frags = [&](int stage, Frags& F, auto mc) __attribute__((always_inline)) {
+    auto b_tile_row = [&](int n) __attribute__((always_inline)) {
+        if constexpr (MODE == MODE_GATED)  // the wave's gate tile, then its up tile
+            return (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
+        else
+            return wn * WN + n * 32;
+    };
+    auto load_frags = [&](int j, Frags& F, auto mc) __attribute__((always_inline)) {
         constexpr int MA = decltype(mc)::value;
-        const unsigned char* st = smem + stage * stage_bytes<BT>();
-        const unsigned char* Bc = st + A_BYTES;
+        const int x = j >> 1, h = j & 1;  // stage, half
+        const unsigned char* Au = aring + (x % NA) * A_UNIT;
+        const unsigned char* Bu = bring + (x % NB) * BUNIT;
         if constexpr (BT == 2) {
-            // FP8: a lane reads its B row's 16 codes k = 16 hi .. + 15 once and
-            // fragment kk takes k = 16 hi + 8 kk .. + 7; A is read at the same
-            // positions (chunk 2 hi + kk).  Both operands use this permutation of
-            // the slice's 32 k, so the MFMA sums are those of the plain order.
+            // FP8: a lane reads its B row's 16 codes k = 32 h + 16 hi .. + 15 once
+            // and fragment kk takes k = 32 h + 16 hi + 8 kk .. + 7; A is read at the
+            // same positions (chunk 4 h + 2 hi + kk).  Both operands use this
+            // permutation of the half's 32 k, so the MFMA sums are those of the
+            // plain order.
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int m = 0; m < MA; ++m)
-                    F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(m * 32 + l32, 2 * hi + kk));
+                    F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(Au + swz_bf16(m * 32 + l32, 4 * h + 2 * hi + kk));
             if constexpr (MA > 0) {
 #pragma unroll
                 for (int n = 0; n < NTL; ++n) {
-                    int brow;
-                    if constexpr (MODE == MODE_GATED)
-                        brow = (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
-                    else
-                        brow = wn * WN + n * 32;
-                    const int row = brow + l32;
-                    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(Bc + row * KS + fp8_half(row, hi) * 16);
+                    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(Bu + swz_fp8(b_tile_row(n) + l32, 2 * h + hi));
                     F.b[0][n] = fp8_frag(c[0], c[1]);
                     F.b[1][n] = fp8_frag(c[2], c[3]);
                 }
@@ -529,24 +617,19 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            // 32x32x16 operands: lane holds row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7
+            // 32x32x16 operands: lane holds row (lane % 32), k = 32 h + 16 kk + 8 (lane / 32) .. + 7
             const int ch = 2 * kk + hi;
 #pragma unroll
             for (int m = 0; m < MA; ++m)
-                F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(st + sw(m * 32 + l32, ch));
+                F.a[kk][m] = *reinterpret_cast<const bf16x8_t*>(Au + swz_bf16(m * 32 + l32, 4 * h + ch));
 #pragma unroll
             for (int n = 0; n < NTL; ++n) {
-                int brow;
-                if constexpr (MODE == MODE_GATED)  // the wave's gate tile, then its up tile
-                    brow = (n < NTL / 2 ? 0 : BN / 2) + wn * (WN / 2) + (n % (NTL / 2)) * 32;
-                else
-                    brow = wn * WN + n * 32;
-                const int row = brow + l32;
+                const int row = b_tile_row(n) + l32;
                 if constexpr (BT == 0) {
-                    F.b[kk][n] = *reinterpret_cast<const bf16x8_t*>(Bc + sw(row, ch));
+                    F.b[kk][n] = *reinterpret_cast<const bf16x8_t*>(Bu + swz_bf16(row, 4 * h + ch));
                 } else {
-                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bc + row * 16 + ch * 4);
-                    F.b[kk][n] = fp4_frag(codes, Bc[BN * 16 + row * 4]);
+                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bu + swz_fp4(row, h) + ch * 4);
+                    F.b[kk][n] = fp4_frag(codes, Bu[BN * 32 + h * BN * 4 + row * 4]);
                 }
             }
         }
@@ -560,55 +643,95 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
 #pragma unroll
                 for (int n = 0; n < NTL; ++n) acc[m][n] = mfma32(F.a[kk][m], F.b[kk][n], acc[m][n]);
     };
-    // wait until a slice has landed (`later` slices issued after it may stay in
-    // flight) and this wave's LDS reads are done, then meet the other waves
-    auto wait_slice = [&](int later) __attribute__((always_inline)) {
-        if (later >= 4) wait_vm_lgkm<4 * LPS>();
-        else if (later == 3) wait_vm_lgkm<3 * LPS>();
-        else if (later == 2) wait_vm_lgkm<2 * LPS>();
-        else if (later == 1) wait_vm_lgkm<LPS>();
-        else wait_vm_lgkm<0>();
-        __builtin_amdgcn_s_barrier();
-    };
-    // One iteration: make slice kt+1 visible, refill the stage slice kt came from
-    // (all waves read it one iteration ago) with slice kt+STAGES, read slice kt+1's
-    // fragments into `nxt`, and run slice kt's MFMAs from `cur`.
-    // The fragment reads are unconditional so that the compiler's LDS wait lands
-    // before the next iteration's MFMAs, not before these: on the last slice they
-    // read a stage no copy targets any more (every copy has been waited for) and the
-    // values are not used.
-    auto step = [&](int kt, const Frags& cur, Frags& nxt, auto mc) __attribute__((always_inline)) {
+    // Step j of the K loop (stage j / 2, half j % 2): odd steps wait until stage
+    // (j + 1) / 2 has landed and every wave is done with stage (j - 1) / 2, then
+    // copy A stage (j - 1) / 2 + NA into that stage's slot; even steps copy B
+    // stage j / 2 - 1 + NB (its slot freed at the barrier of step j - 1).  Then
+    // the wave reads step j+1's fragments into `nxt` and runs step j's MFMAs
+    // from `cur`.  The fragment reads are unconditional so that the compiler's
+    // LDS wait lands before the next step's MFMAs, not before these: on the last
+    // step they read a slot no copy targets any more and the values are unused.
+    // STEADY: every copy of the step exists, so the step is straight-line code
+    // and its copies and reads each get a phase of the MFMAs; copies then reads
+    // (bf16, MXFP4) or reads then copies (FP8), the order measured faster.
+    auto step = [&](int j, const Frags& cur, Frags& nxt, auto mc, auto odd, auto steady) __attribute__((always_inline)) {
         constexpr int MA = decltype(mc)::value;
-        if (kt + 1 < nk) {
-            wait_slice(min(STAGES - 2, nk - 2 - kt));
-            if (kt + STAGES < nk) issue(kt % STAGES, kt + STAGES);
-        }
-        load_frags((kt + 1) % STAGES, nxt, mc);
-        mfmas(cur, mc);
-        // interleave: one MFMA, one LDS read, ... so the reads hide under the MFMAs
+        constexpr bool ODD = decltype(odd)::value, STEADY = decltype(steady)::value;
         constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 1 ? 4 : 1) * NTL;
         constexpr int NP = NMF < NDS ? NMF : NDS;
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        constexpr int NC = ODD ? LA : LB;
+        constexpr bool COPIES_FIRST = BT != 2;
+        const int sx = ODD ? (j - 1) / 2 : j / 2;
+        auto copy = [&]() __attribute__((always_inline)) {
+            if constexpr (ODD) issue_a(sx + NA);
+            else issue_b(sx - 1 + NB);
+        };
+        if constexpr (ODD) {
+            if constexpr (STEADY) {
+                wait_vm_lgkm<steady_in_flight<BT>()>();
+                __builtin_amdgcn_s_barrier();
+            } else if (sx + 1 < nst) {
+                wait_vm_lgkm_upto<32>(copies_after<BT>(sx + 1, 2 * sx, nst));
+                __builtin_amdgcn_s_barrier();
+            }
         }
-        if constexpr (NMF > NP) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NP, 0);
-        if constexpr (NDS > NP) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NP, 0);
+        if constexpr (STEADY) {
+            if constexpr (COPIES_FIRST) {
+                copy();
+                load_frags(j + 1, nxt, mc);
+            } else {
+                load_frags(j + 1, nxt, mc);
+                copy();
+            }
+        } else {
+            if ((ODD ? sx + NA : sx - 1 + NB) < nst) copy();
+            load_frags(j + 1, nxt, mc);
+        }
+        mfmas(cur, mc);
+        if constexpr (STEADY && NMF >= 2) {
+            // The copies write LDS and the fragment reads read it, so neither may
+            // pass the other: one phase each, in program order.
+            if constexpr (COPIES_FIRST)
+                sched_two<0, NMF, phase_split<NC, NDS, NMF>(), 0x010, NC, 0x100, NDS>();
+            else
+                sched_two<0, NMF, phase_split<NDS, NC, NMF>(), 0x100, NDS, 0x010, NC>();
+        } else {
+            // interleave: one MFMA, one LDS read, ... so the reads hide under the MFMAs
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+            if constexpr (NMF > NP) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NP, 0);
+            if constexpr (NDS > NP) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NP, 0);
+        }
     };
 
-    // prologue: all stages in flight
+    // prologue: the copies of every step before the first, in issue order
 #pragma unroll
-    for (int q = 0; q < STAGES; ++q)
-        if (q < nk) issue(q, q);
+    for (int t = first_step<BT>(); t < 0; ++t) {
+        if (t & 1) {
+            const int x = (t - 1) / 2 + NA;
+            if (x >= 0 && x < nst) issue_a(x);
+        } else {
+            const int x = (t - 2) / 2 + NB;
+            if (x >= 0 && x < nst) issue_b(x);
+        }
+    }
     // the K loop, specialised on the number of 32-row sub-tiles holding rows
     Frags F0, F1;
     with_count<MT>(mact, [&](auto mc) __attribute__((always_inline)) {
-        wait_slice(min(STAGES - 1, nk - 1));
+        wait_vm_lgkm_upto<32>(copies_after<BT>(0, -1, nst));
+        __builtin_amdgcn_s_barrier();
         load_frags(0, F0, mc);
-        for (int kt = 0; kt < nk; kt += 2) {
-            step(kt, F0, F1, mc);
-            if (kt + 1 < nk) step(kt + 1, F1, F0, mc);
+        int sx = 0;
+        for (; sx < nst - steady_margin<BT>(); ++sx) {
+            step(2 * sx, F0, F1, mc, std::false_type{}, std::true_type{});
+            step(2 * sx + 1, F1, F0, mc, std::true_type{}, std::true_type{});
+        }
+        for (; sx < nst; ++sx) {
+            step(2 * sx, F0, F1, mc, std::false_type{}, std::false_type{});
+            step(2 * sx + 1, F1, F0, mc, std::true_type{}, std::false_type{});
         }
     });
 
