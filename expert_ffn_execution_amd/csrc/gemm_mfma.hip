@@ -305,9 +305,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
 // instruction reads 8 such lines.  With stages of 32 each instruction read
 // 16 half lines, and a probe of this copy pattern alone moved L2-resident
 // data at 15 TB/s with half lines against 32 TB/s with whole lines; the
-// copies, not the MFMAs, set the K loop's pace.  B keeps more stages in
-// flight than A: the weights stream from HBM, the activations (re-read by
-// every N-tile of an M-tile) mostly hit in L2.
+// copies, not the MFMAs, set the K loop's pace.  Ring depths (stages of A,
+// B): bf16 2, 3 and FP8 3, 4 -- the weights stream from HBM and need the
+// longer lead, the activations (re-read by every N-tile of an M-tile) mostly
+// hit in L2; bf16 with 3, 2 was 12% slower.  MXFP4, whose B stages are small,
+// 4, 3 (2% faster than 3, 6).
 // The MFMAs take a stage in two halves of 32 (two 16-deep k-steps each), one
 // half per step: odd steps wait for the next stage (s_waitcnt vmcnt on the
 // wave's own copies, counted from the fixed issue order), meet at the block
@@ -339,8 +341,8 @@ template <int BT> constexpr int b_row() { return BT == 0 ? KST * 2 : BT == 1 ? K
 // row holding its scale byte (a 1-byte LDS-DMA load writes each lane's byte
 // to a 4-byte slot)
 template <int BT> constexpr int b_unit() { return BN * b_row<BT>() + (BT == 1 ? 2 * BN * 4 : 0); }
-template <int BT> constexpr int n_a() { return BT == 0 ? 2 : 3; }            // A ring stages
-template <int BT> constexpr int n_b() { return BT == 0 ? 3 : BT == 1 ? 6 : 4; }  // B ring stages
+template <int BT> constexpr int n_a() { return BT == 0 ? 2 : BT == 1 ? 4 : 3; }  // A ring stages
+template <int BT> constexpr int n_b() { return BT == 0 ? 3 : BT == 1 ? 3 : 4; }  // B ring stages
 template <int BT> constexpr int b_code_copies() { return BN * b_row<BT>() / 1024 / NW; }
 template <int BT> constexpr int b_copies() { return b_code_copies<BT>() + (BT == 1 ? 2 : 0); }  // per wave, stage
 constexpr size_t EPI_BYTES = (size_t)BM * (BN + 8) * 2;   // bf16 output tile (plain GEMM)
@@ -380,7 +382,7 @@ template <int BT> constexpr int steady_in_flight() { return copies_after<BT>(1, 
 template <int BT> constexpr int steady_margin() {
     return n_b<BT>() - 1 > n_a<BT>() ? n_b<BT>() - 1 : n_a<BT>();
 }
-static_assert(steady_in_flight<0>() == 8 && steady_in_flight<1>() == 16 && steady_in_flight<2>() == 16,
+static_assert(steady_in_flight<0>() == 8 && steady_in_flight<1>() == 12 && steady_in_flight<2>() == 16,
               "issue order");
 }  // namespace pipe
 
@@ -653,14 +655,14 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     // step they read a slot no copy targets any more and the values are unused.
     // STEADY: every copy of the step exists, so the step is straight-line code
     // and its copies and reads each get a phase of the MFMAs; copies then reads
-    // (bf16, MXFP4) or reads then copies (FP8), the order measured faster.
+    // (bf16) or reads then copies (MXFP4, FP8), the order measured faster.
     auto step = [&](int j, const Frags& cur, Frags& nxt, auto mc, auto odd, auto steady) __attribute__((always_inline)) {
         constexpr int MA = decltype(mc)::value;
         constexpr bool ODD = decltype(odd)::value, STEADY = decltype(steady)::value;
         constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 1 ? 4 : 1) * NTL;
         constexpr int NP = NMF < NDS ? NMF : NDS;
         constexpr int NC = ODD ? LA : LB;
-        constexpr bool COPIES_FIRST = BT != 2;
+        constexpr bool COPIES_FIRST = BT == 0;
         const int sx = ODD ? (j - 1) / 2 : j / 2;
         auto copy = [&]() __attribute__((always_inline)) {
             if constexpr (ODD) issue_a(sx + NA);
