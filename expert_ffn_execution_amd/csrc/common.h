@@ -85,8 +85,23 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
+// Sum over the wavefront, returned uniform: DPP exchanges inside each row of
+// 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror), then the four row sums read as scalars, added as
+// (r0 + r1) + (r2 + r3).  A fixed order, like any other: the result is
+// deterministic.  (xor shuffles would go through LDS permutes.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = dpp_sum_step<0xB1>(v);
+    v = dpp_sum_step<0x4E>(v);
+    v = dpp_sum_step<0x141>(v);
+    v = dpp_sum_step<0x140>(v);
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }

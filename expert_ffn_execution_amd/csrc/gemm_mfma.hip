@@ -334,7 +334,7 @@ constexpr int BM = 256, BN = 256, NT = 256, NW = NT / 64, WN = BN / NW;
 constexpr int KST = 64;                        // K per stage
 constexpr int MT = BM / 32, NTL = WN / 32;     // 32 x 32 MFMA tiles per wavefront
 constexpr int A_UNIT = BM * KST * 2;           // one A stage: 32 KB of bf16
-constexpr int LA = A_UNIT / 1024 / NW;         // A copies per wave and stage
+constexpr int LA = A_UNIT / 1024 / NW;         // A copies per wave and stage, full tile
 // BT: 0 bf16 weights, 1 MXFP4, 2 FP8 (e4m3, one fp32 scale per matrix).
 template <int BT> constexpr int b_row() { return BT == 0 ? KST * 2 : BT == 1 ? KST / 2 : KST; }
 // MXFP4: codes [BN][32 B], then for each half of the stage a 4-byte slot per
@@ -365,24 +365,25 @@ template <int BT> constexpr int first_step() {
     return step_of_a<BT>(0) < step_of_b<BT>(0) ? step_of_a<BT>(0) : step_of_b<BT>(0);
 }
 // Copies a wave may leave in flight when it waits for stage y having issued
-// every step up to P (stages past the last, nst - 1, are never issued).
+// every step up to P (stages past the last, nst - 1, are never issued), with
+// la A copies per stage (a tile of la 32-row sub-tiles copies la per wave).
 template <int BT>
-__host__ __device__ constexpr int copies_after(int y, int P, int nst) {
-    const int la = step_of_a<BT>(y), lb = step_of_b<BT>(y);
+__host__ __device__ constexpr int copies_after(int y, int P, int nst, int la) {
+    const int sa = step_of_a<BT>(y), sb = step_of_b<BT>(y);
     int n = 0;
-    for (int t = (la > lb ? la : lb) + 1; t <= P; ++t) {
+    for (int t = (sa > sb ? sa : sb) + 1; t <= P; ++t) {
         const int x = (t & 1) ? (t - 1) / 2 + n_a<BT>() : (t - 2) / 2 + n_b<BT>();
-        if (x >= 0 && x < nst) n += (t & 1) ? LA : b_copies<BT>();
+        if (x >= 0 && x < nst) n += (t & 1) ? la : b_copies<BT>();
     }
     return n;
 }
 // in steady state (stage y = s + 1 at odd step 2 s + 1, every stage present)
-template <int BT> constexpr int steady_in_flight() { return copies_after<BT>(1, 0, 1 << 20); }
+template <int BT, int la> constexpr int steady_in_flight() { return copies_after<BT>(1, 0, 1 << 20, la); }
 // the K loop's pairs of steps are straight-line once every copy of the pair exists
 template <int BT> constexpr int steady_margin() {
     return n_b<BT>() - 1 > n_a<BT>() ? n_b<BT>() - 1 : n_a<BT>();
 }
-static_assert(steady_in_flight<0>() == 8 && steady_in_flight<1>() == 12 && steady_in_flight<2>() == 16,
+static_assert(steady_in_flight<0, LA>() == 8 && steady_in_flight<1, LA>() == 12 && steady_in_flight<2, LA>() == 16,
               "issue order");
 }  // namespace pipe
 
@@ -395,14 +396,14 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
-// the same with a run-time count, rounded down to a multiple of 4 (<= N)
+// the same with a run-time count (capped at N)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm_upto(int n) {
     if constexpr (N <= 0) {
         wait_vm_lgkm<0>();
     } else {
         if (n >= N) wait_vm_lgkm<N>();
-        else wait_vm_lgkm_upto<N - 4>(n);
+        else wait_vm_lgkm_upto<N - 1>(n);
     }
 }
 
@@ -486,12 +487,14 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     // gated: B rows [0, 128) = gate rows c0.., [128, 256) = up rows c0..; plain: rows c0..
     const int c0 = nt * (MODE == MODE_GATED ? BN / 2 : BN);
 
-    // A: copy i of this wave fills LDS rows 8 (LA wave + i) .. + 7, lane l row
-    // + l / 8 at chunk position l % 8 (rows past the tile re-read its last row)
+    // A: copy i of this wave fills LDS rows 8 (NW i + wave) .. + 7, lane l row
+    // + l / 8 at chunk position l % 8 (rows past the tile re-read its last
+    // row).  Copy i lies in 32-row sub-tile i, so a tile of MA occupied
+    // sub-tiles needs copies 0 .. MA - 1 of every wave and no others.
     uint32_t aoff[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int r = 8 * (LA * wave + i) + (lane >> 3);
+        const int r = 8 * (NW * i + wave) + (lane >> 3);
         const int rc = min(r, td.rows - 1);
         uint32_t arow;
         if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + rc) : (uint32_t)(perm[td.p0 + rc] / g.k);
@@ -550,11 +553,12 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     unsigned char* const aring = smem;
     unsigned char* const bring = smem + NA * A_UNIT;
     const int nst = K / KST;
-    auto issue_a = [&](int x) __attribute__((always_inline)) {  // A stage x into its ring slot
+    auto issue_a = [&](int x, auto mc) __attribute__((always_inline)) {  // A stage x into its ring slot
+        constexpr int MA = decltype(mc)::value;
         unsigned char* dst = aring + (x % NA) * A_UNIT;
 #pragma unroll
-        for (int i = 0; i < LA; ++i)
-            __builtin_amdgcn_global_load_lds(A + aoff[i] + x * KST, FT_LDS(dst + (LA * wave + i) * 1024), 16, 0, 0);
+        for (int i = 0; i < MA; ++i)
+            __builtin_amdgcn_global_load_lds(A + aoff[i] + x * KST, FT_LDS(dst + (NW * i + wave) * 1024), 16, 0, 0);
     };
     auto issue_b = [&](int x) __attribute__((always_inline)) {  // B stage x into its ring slot
         unsigned char* dst = bring + (x % NB) * BUNIT;
@@ -661,19 +665,19 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         constexpr bool ODD = decltype(odd)::value, STEADY = decltype(steady)::value;
         constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 1 ? 4 : 1) * NTL;
         constexpr int NP = NMF < NDS ? NMF : NDS;
-        constexpr int NC = ODD ? LA : LB;
+        constexpr int NC = ODD ? MA : LB;
         constexpr bool COPIES_FIRST = BT == 0;
         const int sx = ODD ? (j - 1) / 2 : j / 2;
         auto copy = [&]() __attribute__((always_inline)) {
-            if constexpr (ODD) issue_a(sx + NA);
+            if constexpr (ODD) issue_a(sx + NA, mc);
             else issue_b(sx - 1 + NB);
         };
         if constexpr (ODD) {
             if constexpr (STEADY) {
-                wait_vm_lgkm<steady_in_flight<BT>()>();
+                wait_vm_lgkm<steady_in_flight<BT, MA>()>();
                 __builtin_amdgcn_s_barrier();
             } else if (sx + 1 < nst) {
-                wait_vm_lgkm_upto<32>(copies_after<BT>(sx + 1, 2 * sx, nst));
+                wait_vm_lgkm_upto<32>(copies_after<BT>(sx + 1, 2 * sx, nst, MA));
                 __builtin_amdgcn_s_barrier();
             }
         }
@@ -709,21 +713,21 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         }
     };
 
-    // prologue: the copies of every step before the first, in issue order
-#pragma unroll
-    for (int t = first_step<BT>(); t < 0; ++t) {
-        if (t & 1) {
-            const int x = (t - 1) / 2 + NA;
-            if (x >= 0 && x < nst) issue_a(x);
-        } else {
-            const int x = (t - 2) / 2 + NB;
-            if (x >= 0 && x < nst) issue_b(x);
-        }
-    }
     // the K loop, specialised on the number of 32-row sub-tiles holding rows
     Frags F0, F1;
     with_count<MT>(mact, [&](auto mc) __attribute__((always_inline)) {
-        wait_vm_lgkm_upto<32>(copies_after<BT>(0, -1, nst));
+        // prologue: the copies of every step before the first, in issue order
+#pragma unroll
+        for (int t = first_step<BT>(); t < 0; ++t) {
+            if (t & 1) {
+                const int x = (t - 1) / 2 + NA;
+                if (x >= 0 && x < nst) issue_a(x, mc);
+            } else {
+                const int x = (t - 2) / 2 + NB;
+                if (x >= 0 && x < nst) issue_b(x);
+            }
+        }
+        wait_vm_lgkm_upto<32>(copies_after<BT>(0, -1, nst, decltype(mc)::value));
         __builtin_amdgcn_s_barrier();
         load_frags(0, F0, mc);
         int sx = 0;

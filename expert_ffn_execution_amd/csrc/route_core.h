@@ -27,20 +27,46 @@ __device__ __forceinline__ float key_value(uint64_t key) {
     uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
     return __uint_as_float(u);
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-        uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
+// Wave-wide max and sum, returned uniform.  DPP exchanges inside each row of
+// 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror: each pairs lanes across the next larger group), then the four
+// row results read as scalars.  (The xor-shuffle form goes through LDS
+// permutes, a round trip each: 12 per 64-bit max, and the top-k's k maxima
+// are a dependent chain.)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<0xB1>(v));
+    v = max_u64(v, dpp_u64<0x4E>(v));
+    v = max_u64(v, dpp_u64<0x141>(v));
+    v = max_u64(v, dpp_u64<0x140>(v));
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
+}
+__device__ __forceinline__ double dpp_add_f64(double v, uint64_t o) { return v + __builtin_bit_cast(double, o); }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    v = dpp_add_f64(v, dpp_u64<0xB1>(b));
+    b = __builtin_bit_cast(uint64_t, v);
+    v = dpp_add_f64(v, dpp_u64<0x4E>(b));
+    b = __builtin_bit_cast(uint64_t, v);
+    v = dpp_add_f64(v, dpp_u64<0x141>(b));
+    b = __builtin_bit_cast(uint64_t, v);
+    v = dpp_add_f64(v, dpp_u64<0x140>(b));
+    b = __builtin_bit_cast(uint64_t, v);
+    return (__builtin_bit_cast(double, lane_u64(b, 0)) + __builtin_bit_cast(double, lane_u64(b, 16))) +
+           (__builtin_bit_cast(double, lane_u64(b, 32)) + __builtin_bit_cast(double, lane_u64(b, 48)));
 }
 
 // Token t's picks and gates: row = its E logits, ids_out / w_out = its k
