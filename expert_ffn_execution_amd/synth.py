@@ -42,7 +42,7 @@ class LayerShape:
     k: int              # experts per token
     I: int              # expert intermediate size
     n_shared: int = 0   # always-on shared experts (0 or 1)
-    wdtype: str = "bf16"    # expert weight storage: "f32" | "bf16" | "mxfp4" | "fp8"
+    wdtype: str = "bf16"    # expert weight storage: "f32" | "bf16" | "mxfp4" | "fp8" | "nvfp4"
     adtype: str = "bf16"    # activation / router storage: "f32" | "bf16"
     bias: str = "none"      # router logit bias: "none" | "zipf" | "normal"
     bias_param: float = 0.0  # zipf exponent s, or normal std
@@ -70,9 +70,12 @@ A40B_MXFP4 = LayerShape("753b_a40b_mxfp4", H=6144, E=256, k=8, I=2048, wdtype="m
 # The 35B-A3B layer with FP8 (e4m3) weights: a weight format the pages list,
 # on the shape of the bf16 configuration (not one of the five configurations).
 A3B_FP8 = LayerShape("35b_a3b_fp8", H=2048, E=128, k=8, I=768, wdtype="fp8")
+# ... and with NVFP4 weights (e2m1 codes, an e4m3 scale per 16, an fp32 scale
+# per matrix), another format the pages list.
+A3B_NVFP4 = LayerShape("35b_a3b_nvfp4", H=2048, E=128, k=8, I=768, wdtype="nvfp4")
 
 SHAPES = {s.name: s for s in (TINY_F32, A3B_BF16, A13B_MXFP4, SLOT_STACK, A40B_BF16,
-                              A40B_MXFP4, A3B_FP8)}
+                              A40B_MXFP4, A3B_FP8, A3B_NVFP4)}
 
 # Token counts each workload is run at (decode points, then prefill).
 POINTS = {
@@ -83,6 +86,7 @@ POINTS = {
     "753b_a40b_bf16": [1, 32, 16384],
     "753b_a40b_mxfp4": [1, 32, 16384],
     "35b_a3b_fp8": [1, 16, 64, 4096],
+    "35b_a3b_nvfp4": [1, 16, 64, 4096],
 }
 SLOT_STACK_LAYERS = 8
 SLOT_STACK_SLOTS_PER_LAYER = 64
@@ -163,6 +167,35 @@ def quantize_fp8(w: torch.Tensor):
 
 
 # ---------------------------------------------------------------------------
+# NVFP4 quantiser (input recipe).  Blocks of 16 values along the contraction
+# dim share an e4m3 scale; the matrix has one fp32 tensor scale
+# ts = amax / (6 * 448) (1 for an all-zero matrix), so every block scale
+# bmax / 6 / ts fits e4m3; block scales are rounded to nearest even on the
+# e4m3 grid (torch's float8_e4m3fn cast), elements w / (scale * ts) to nearest
+# even on the e2m1 grid, saturating at 6 (code 0 where the block scale is 0).
+# Codes and nibble order as for MXFP4.  Weight = e2m1 * e4m3(scale) * ts.
+# ---------------------------------------------------------------------------
+def quantize_nvfp4(w: torch.Tensor):
+    """w [N, K] fp32, K % 16 == 0 -> (codes uint8 [N, K/2], block scales uint8 [N, K/16],
+    tensor scale fp32 [1])."""
+    N, K = w.shape
+    assert K % 16 == 0
+    amax = w.abs().amax()
+    ts = torch.where(amax > 0, amax / (6.0 * 448.0), torch.ones_like(amax)).to(torch.float32)
+    blk = w.reshape(N, K // 16, 16)
+    bs = (blk.abs().amax(dim=2) / 6.0 / ts).to(torch.float8_e4m3fn)
+    den = (bs.to(torch.float32) * ts).unsqueeze(2)
+    a = torch.where(den > 0, blk.abs() / torch.where(den > 0, den, torch.ones_like(den)),
+                    torch.zeros_like(blk))
+    code = ((a > 0.25).to(torch.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+            + (a > 2.5) + (a >= 3.5) + (a > 5.0)).to(torch.uint8)
+    neg = (blk < 0) & (code > 0)
+    code = (code | (neg.to(torch.uint8) << 3)).reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, bs.view(torch.uint8).contiguous(), ts.reshape(1).contiguous()
+
+
+# ---------------------------------------------------------------------------
 # Generators
 # ---------------------------------------------------------------------------
 def gen_x(shape: LayerShape, T: int, step: int = 0, device="cpu", layer: int = 0) -> torch.Tensor:
@@ -210,6 +243,9 @@ def gen_expert(shape: LayerShape, e: int, layer: int = 0, device="cpu") -> dict:
                "down": codes [H,I/2], "down_sc": [H,I/32]}.
     fp8:      {"gate": e4m3 codes [I,H], "gate_sc": fp32 [1], "up", "up_sc",
                "down": codes [H,I], "down_sc": fp32 [1]}.
+    nvfp4:    {"gate": codes [I,H/2], "gate_sc": e4m3 [I,H/16], "gate_ts": fp32 [1],
+               "up", "up_sc", "up_ts", "down": codes [H,I/2], "down_sc": [H,I/16],
+               "down_ts"}.
     Expert index ``e == shape.E`` is the shared expert (when n_shared == 1).
     """
     H, I = shape.H, shape.I
@@ -220,11 +256,13 @@ def gen_expert(shape: LayerShape, e: int, layer: int = 0, device="cpu") -> dict:
     if shape.wdtype in ("f32", "bf16"):
         return {"gate": to_storage(g, shape.wdtype), "up": to_storage(u, shape.wdtype),
                 "down": to_storage(d, shape.wdtype)}
-    quant = quantize_mxfp4 if shape.wdtype == "mxfp4" else quantize_fp8
     out = {}
     for name, t in (("gate", g), ("up", u), ("down", d)):
-        c, s = quant(t)
-        out[name], out[name + "_sc"] = c, s
+        if shape.wdtype == "nvfp4":
+            out[name], out[name + "_sc"], out[name + "_ts"] = quantize_nvfp4(t)
+        else:
+            quant = quantize_mxfp4 if shape.wdtype == "mxfp4" else quantize_fp8
+            out[name], out[name + "_sc"] = quant(t)
     return out
 
 

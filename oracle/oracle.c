@@ -70,8 +70,16 @@ double or_fp8_value(uint8_t code) {
     return s ? -mag : mag;
 }
 
-/* element (row, kk) of a [rows][K] matrix stored in fmt */
-static double w_at(const void* base, const uint8_t* sc, int fmt, int row, int K, int kk) {
+/* e2m1 code times an e4m3 block scale: the two element formats above, the
+ * code with the neutral e8m0 exponent 127 (a factor of 1). */
+double or_nvfp4_value(uint8_t code, uint8_t scale) {
+    return or_mxfp4_value(code, 127) * or_fp8_value(scale);
+}
+
+/* element (row, kk) of a [rows][K] matrix stored in fmt (ts: the tensor scale
+ * of an NVFP4 matrix) */
+static double w_at(const void* base, const uint8_t* sc, const uint8_t* ts, int fmt, int row, int K,
+                   int kk) {
     size_t r = (size_t)row;
     if (fmt == OR_F32) return ((const float*)base)[r * K + kk];
     if (fmt == OR_BF16) return or_bf16_to_f64(((const uint16_t*)base)[r * K + kk]);
@@ -82,6 +90,11 @@ static double w_at(const void* base, const uint8_t* sc, int fmt, int row, int K,
     }
     uint8_t byte = ((const uint8_t*)base)[r * (K / 2) + kk / 2];
     uint8_t c = (kk & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    if (fmt == OR_NVFP4) {
+        float tensor;
+        memcpy(&tensor, ts, 4);
+        return or_nvfp4_value(c, sc[r * (K / 16) + kk / 16]) * (double)tensor;
+    }
     return or_mxfp4_value(c, sc[r * (K / 32) + kk / 32]);
 }
 
@@ -175,15 +188,15 @@ int or_expert_ffn(const or_expert* ex, const double* x, int H, int I, int round_
     for (int i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
         for (int c = 0; c < H; ++c) {
-            g += x[c] * w_at(ex->gate, ex->gate_sc, ex->fmt, i, H, c);
-            u += x[c] * w_at(ex->up, ex->up_sc, ex->fmt, i, H, c);
+            g += x[c] * w_at(ex->gate, ex->gate_sc, ex->gate_ts, ex->fmt, i, H, c);
+            u += x[c] * w_at(ex->up, ex->up_sc, ex->up_ts, ex->fmt, i, H, c);
         }
         double a = g / (1.0 + exp(-g)) * u;
         h[i] = round_h ? or_bf16_to_f64(or_f64_to_bf16(a)) : a;
     }
     for (int d = 0; d < H; ++d) {
         double s = 0.0;
-        for (int i = 0; i < I; ++i) s += h[i] * w_at(ex->down, ex->down_sc, ex->fmt, d, I, i);
+        for (int i = 0; i < I; ++i) s += h[i] * w_at(ex->down, ex->down_sc, ex->down_ts, ex->fmt, d, I, i);
         y[d] = s;
     }
     free(h);

@@ -37,7 +37,7 @@ extern "C" {
 #endif
 
 /* storage formats of a tensor */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2, OR_FP8 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2, OR_FP8 = 3, OR_NVFP4 = 4 };
 
 /* One expert in logical layout.
  *   OR_F32 / OR_BF16: gate [I][H], up [I][H], down [H][I] row-major.
@@ -47,7 +47,13 @@ enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP4 = 2, OR_FP8 = 3 };
  *   up_sc, down_sc each point at the matrix's fp32 scale (4 bytes): the weight
  *   is the code's value times that scale.  The pages list FP8 weights without
  *   their scaling (refft.com guide, the format list); one scale per matrix is
- *   the plainest reading. */
+ *   the plainest reading.
+ *   OR_NVFP4: e2m1 codes as for OR_MXFP4; gate_sc/up_sc [I][H/16], down_sc
+ *   [H][I/16] hold one e4m3 scale byte per block of 16 consecutive elements of
+ *   a row; gate_ts, up_ts, down_ts each point at the matrix's fp32 tensor
+ *   scale.  The weight is e2m1(code) * e4m3(block scale) * tensor scale.  The
+ *   pages name NVFP4 without its layout (refft.com guide, the format list);
+ *   this is NVIDIA's published NVFP4 definition. */
 typedef struct {
     int fmt;
     const void* gate;
@@ -56,6 +62,9 @@ typedef struct {
     const uint8_t* gate_sc;
     const uint8_t* up_sc;
     const uint8_t* down_sc;
+    const uint8_t* gate_ts;
+    const uint8_t* up_ts;
+    const uint8_t* down_ts;
 } or_expert;
 
 /* Exact value of one e2m1 code scaled by an e8m0 byte (OCP MX v1.0). */
@@ -63,6 +72,9 @@ double or_mxfp4_value(uint8_t code, uint8_t scale);
 /* Exact value of one e4m3 code (OCP OFP8 v1.0, the E4M3 encoding; NaN for the
  * two NaN codes). */
 double or_fp8_value(uint8_t code);
+/* Exact value of one NVFP4 element before its tensor scale: the e2m1 code
+ * times its block's e4m3 scale byte. */
+double or_nvfp4_value(uint8_t code, uint8_t scale);
 /* bf16 bits -> double (exact) and double -> bf16 bits (round to nearest even). */
 double or_bf16_to_f64(uint16_t b);
 uint16_t or_f64_to_bf16(double v);

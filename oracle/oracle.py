@@ -18,8 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
-_FMT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "fp8": FP8}
+F32, BF16, MXFP4, FP8, NVFP4 = 0, 1, 2, 3, 4
+_FMT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "fp8": FP8, "nvfp4": NVFP4}
 
 _lib = None
 
@@ -35,7 +35,8 @@ def build() -> str:
 class _Expert(C.Structure):
     _fields_ = [("fmt", C.c_int), ("gate", C.c_void_p), ("up", C.c_void_p),
                 ("down", C.c_void_p), ("gate_sc", C.c_void_p), ("up_sc", C.c_void_p),
-                ("down_sc", C.c_void_p)]
+                ("down_sc", C.c_void_p), ("gate_ts", C.c_void_p), ("up_ts", C.c_void_p),
+                ("down_ts", C.c_void_p)]
 
 
 def load():
@@ -50,6 +51,8 @@ def load():
     lib.or_mxfp4_value.argtypes = [C.c_uint8, C.c_uint8]
     lib.or_fp8_value.restype = C.c_double
     lib.or_fp8_value.argtypes = [C.c_uint8]
+    lib.or_nvfp4_value.restype = C.c_double
+    lib.or_nvfp4_value.argtypes = [C.c_uint8, C.c_uint8]
     lib.or_bf16_to_f64.restype = C.c_double
     lib.or_bf16_to_f64.argtypes = [C.c_uint16]
     lib.or_f64_to_bf16.restype = C.c_uint16
@@ -99,6 +102,10 @@ def mxfp4_value(code: int, scale: int) -> float:
 
 def fp8_value(code: int) -> float:
     return load().or_fp8_value(code)
+
+
+def nvfp4_value(code: int, scale: int) -> float:
+    return load().or_nvfp4_value(code, scale)
 
 
 def bf16_to_f64(b: int) -> float:
@@ -157,10 +164,14 @@ class ExpertSet:
                 a = _np(ex[name])
                 self.keep.append(a)
                 setattr(s, name, a.ctypes.data)
-                if wdtype in ("mxfp4", "fp8"):
+                if wdtype in ("mxfp4", "fp8", "nvfp4"):
                     sc = _np(ex[name + "_sc"])
                     self.keep.append(sc)
                     setattr(s, name + "_sc", sc.ctypes.data)
+                if wdtype == "nvfp4":
+                    ts = np.ascontiguousarray(ex[name + "_ts"], dtype=np.float32).reshape(1)
+                    self.keep.append(ts)
+                    setattr(s, name + "_ts", ts.ctypes.data)
 
 
 def expert_ffn(expert: dict, wdtype: str, x_row, H: int, I: int, round_h: bool) -> np.ndarray:

@@ -64,7 +64,24 @@ def _dequant_fp8(codes: torch.Tensor, scale: torch.Tensor) -> np.ndarray:
             * scale.to(torch.float64)).numpy()
 
 
+def _dequant_nvfp4(codes: torch.Tensor, scales: torch.Tensor, ts: torch.Tensor) -> np.ndarray:
+    """e2m1 table value times torch's e4m3 decoding of the block scale (repeated
+    over its 16 elements) times the tensor scale, fp64; independent of the
+    oracle's decode."""
+    tab = _e2m1_table()
+    lut = np.array([tab[c] for c in range(16)], np.float64)
+    cb = codes.numpy()
+    N, K = cb.shape[0], cb.shape[1] * 2
+    c = np.empty((N, K), np.uint8)
+    c[:, 0::2] = cb & 15
+    c[:, 1::2] = cb >> 4
+    sc = scales.contiguous().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return lut[c] * np.repeat(sc, 16, axis=1) * float(ts[0])
+
+
 def _weights_f64(ex: dict, wdtype: str):
+    if wdtype == "nvfp4":
+        return tuple(_dequant_nvfp4(ex[n], ex[n + "_sc"], ex[n + "_ts"]) for n in ("gate", "up", "down"))
     if wdtype == "fp8":
         return tuple(_dequant_fp8(ex[n], ex[n + "_sc"]) for n in ("gate", "up", "down"))
     if wdtype == "mxfp4":
@@ -167,6 +184,48 @@ def test_fp8_quantiser_round_trip():
     q, s = synth.quantize_fp8(torch.from_numpy(vals))
     assert np.array_equal(q.numpy(), codes)
     assert float(s[0]) == np.float32(scale)
+
+
+def test_nvfp4_decode_exhaustive():
+    # every e2m1 code with every e4m3 block-scale byte: the OCP e2m1 table value
+    # times torch's float8_e4m3fn decoding of the scale (NaN scales give NaN)
+    tab = _e2m1_table()
+    sc = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    sc = sc.to(torch.float64).tolist()
+    for s_byte in range(256):
+        for code in range(16):
+            v = orc.nvfp4_value(code, s_byte)
+            ref = tab[code] * sc[s_byte]
+            if math.isnan(ref):
+                assert math.isnan(v), (code, s_byte)
+            else:
+                assert v == ref, (code, s_byte)
+    # closed forms: largest magnitude 6 * 448, smallest nonzero 0.5 * 2^-9
+    assert orc.nvfp4_value(0x7, 0x7E) == 2688.0 and orc.nvfp4_value(0xF, 0x7E) == -2688.0
+    assert orc.nvfp4_value(0x1, 0x01) == 2.0 ** -10
+
+
+def test_nvfp4_quantiser_round_trip():
+    # values e2m1 * e4m3 * ts with a power-of-two ts (all products exact), every
+    # block holding a magnitude-6 element, and 6 * 448 * ts the largest
+    # magnitude, quantise back to the same codes, block scales and ts
+    rng = np.random.default_rng(4)
+    N, K = 4, 64
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    codes[codes == 8] = 0                                  # no -0
+    codes[:, 0::16] = 0x7 | (rng.integers(0, 2, size=(N, K // 16)) << 3).astype(np.uint8)
+    scales = rng.integers(0x01, 0x7E, size=(N, K // 16)).astype(np.uint8)
+    scales[0, 0] = 0x7E
+    ts = 2.0 ** -10
+    tab = _e2m1_table()
+    sdec = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    vals = np.array([[tab[codes[r, c]] * sdec[r, c // 16] * ts for c in range(K)] for r in range(N)],
+                    np.float32)
+    q, s, t = synth.quantize_nvfp4(torch.from_numpy(vals))
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    assert np.array_equal(q.numpy(), packed)
+    assert np.array_equal(s.numpy(), scales)
+    assert float(t[0]) == ts
 
 
 def test_bf16_rounding_matches_torch():
@@ -307,7 +366,7 @@ def test_hand_worked_example():
     np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-7, atol=0)
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4", "fp8"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4", "fp8", "nvfp4"])
 def test_single_expert_is_dense_swiglu(wdtype):
     # E = 1, k = 1 reduces the layer to a dense SwiGLU MLP (torch fp64 reference)
     H, I, T = 64, 96, 5
@@ -330,7 +389,7 @@ def test_single_expert_is_dense_swiglu(wdtype):
 
 @pytest.mark.parametrize("wdtype,shared", [("f32", False), ("bf16", False), ("mxfp4", False),
                                            ("mxfp4", True), ("bf16", True), ("fp8", False),
-                                           ("fp8", True)])
+                                           ("fp8", True), ("nvfp4", False), ("nvfp4", True)])
 def test_layer_matches_brute_force_dense(wdtype, shared):
     T, H, E, k, I = 12, 64, 6, 2, 32
     sh = synth.LayerShape(f"pin_bf_{wdtype}_{shared}", H=H, E=E, k=k, I=I,
