@@ -209,9 +209,9 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     n_act = sum(active) / steps
     eb = banks[0].expert_bytes
     ffn_bytes = (n_act + sh.n_shared) * eb
-    # bytes of the gate/up matrices (codes + scales for MXFP4) of the experts read
+    # bytes of the gate/up matrices (codes + block scales for MXFP4 and NVFP4) of the experts read
     _, offs = ft.expert_layout(sh.wdtype, sh.H, sh.I)
-    w13 = (offs[2] - offs[0]) + ((offs[5] - offs[3]) if sh.wdtype == "mxfp4" else 0)
+    w13 = (offs[2] - offs[0]) + ((offs[5] - offs[3]) if sh.wdtype in ("mxfp4", "nvfp4") else 0)
     w13_bytes = (n_act + sh.n_shared) * w13
     rows = T * k + sh.n_shared * T
     fl1 = 2.0 * rows * 2 * sh.I * sh.H
@@ -249,19 +249,25 @@ def cpu_baseline(sh, bank, T, dev, seconds):
     experts = []
     for e in range(synth.n_experts_total(sh)):
         r = raw[e]
-        if sh.wdtype == "mxfp4":
-            experts.append({"gate": r[offs[0]:offs[0] + I * H // 2].view(I, H // 2),
-                            "up": r[offs[1]:offs[1] + I * H // 2].view(I, H // 2),
-                            "down": r[offs[2]:offs[2] + H * I // 2].view(H, I // 2),
-                            "gate_sc": r[offs[3]:offs[3] + I * H // 32].view(I, H // 32),
-                            "up_sc": r[offs[4]:offs[4] + I * H // 32].view(I, H // 32),
-                            "down_sc": r[offs[5]:offs[5] + H * I // 32].view(H, I // 32)})
-        else:
-            dt = torch.bfloat16 if sh.wdtype == "bf16" else torch.float32
-            es = 2 if sh.wdtype == "bf16" else 4
-            experts.append({"gate": r[offs[0]:offs[0] + I * H * es].view(dt).view(I, H),
-                            "up": r[offs[1]:offs[1] + I * H * es].view(dt).view(I, H),
-                            "down": r[offs[2]:offs[2] + H * I * es].view(dt).view(H, I)})
+        shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+        ex = {}
+        for m, name in enumerate(("gate", "up", "down")):
+            rows, K = shapes[name]
+            if sh.wdtype in ("mxfp4", "nvfp4"):
+                nb = 32 if sh.wdtype == "mxfp4" else 16
+                ex[name] = r[offs[m]:offs[m] + rows * K // 2].view(rows, K // 2)
+                ex[name + "_sc"] = r[offs[3 + m]:offs[3 + m] + rows * K // nb].view(rows, K // nb)
+                if sh.wdtype == "nvfp4":
+                    t0 = offs[5] + H * I // 16 + 4 * m
+                    ex[name + "_ts"] = r[t0:t0 + 4].view(torch.float32)
+            elif sh.wdtype == "fp8":
+                ex[name] = r[offs[m]:offs[m] + rows * K].view(rows, K)
+                ex[name + "_sc"] = r[offs[3 + m]:offs[3 + m] + 4].view(torch.float32)
+            else:
+                dt = torch.bfloat16 if sh.wdtype == "bf16" else torch.float32
+                es = 2 if sh.wdtype == "bf16" else 4
+                ex[name] = r[offs[m]:offs[m] + rows * K * es].view(dt).view(rows, K)
+        experts.append(ex)
     routed, shared = experts[:sh.E], (experts[sh.E] if sh.n_shared else None)
 
     def run(n):
@@ -472,7 +478,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": r["gemm1_gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": r["gemm1_gbs"] / HBM_PEAK_GBS, "traffic": None,
                          "kernel": ("gate/up weight streaming on matrix cores (stream_mx_kernel, NM=2)"
-                                    if sh.wdtype in ("mxfp4", "fp8") and T >= 2 else
+                                    if sh.wdtype in ("mxfp4", "fp8", "nvfp4") and T >= 2 else
                                     "gate/up weight streaming (stream_kernel, NM=2)"),
                          "bytes_per_launch": r["w13_bytes"]}})
         log("decode", json.dumps(decode[-1]))

@@ -83,6 +83,14 @@ size_t layout(ft_dtype w, int H, int I, size_t offs[6]) {
         offs[5] = offs[3] + 8;
         return offs[3] + 16;
     }
+    if (w == FT_NVFP4) {  // codes, e4m3 block scales, then the three fp32 tensor scales
+        offs[1] = HI / 2;
+        offs[2] = HI;
+        offs[3] = 3 * HI / 2;
+        offs[4] = offs[3] + HI / 16;
+        offs[5] = offs[4] + HI / 16;
+        return offs[5] + HI / 16 + 16;
+    }
     if (w == FT_MXFP4) {
         offs[1] = HI / 2;
         offs[2] = HI;
@@ -117,7 +125,8 @@ FfnPlan plan_ffn(const ft_moe_weights& w, int T, int k) {
 
 ft_status check_weights(const ft_moe_weights* w) {
     FT_CHECK_ARG(w, "null weights");
-    FT_CHECK_ARG(w->w_dt == FT_F32 || w->w_dt == FT_BF16 || w->w_dt == FT_MXFP4 || w->w_dt == FT_FP8,
+    FT_CHECK_ARG(w->w_dt == FT_F32 || w->w_dt == FT_BF16 || w->w_dt == FT_MXFP4 || w->w_dt == FT_FP8 ||
+                     w->w_dt == FT_NVFP4,
                  "bad w_dt");
     FT_CHECK_ARG(w->E >= 1 && w->E <= MAX_E, "E must be in [1, %d]", MAX_E);
     FT_CHECK_ARG(w->H > 0 && w->I > 0 && w->H % 64 == 0 && w->I % 64 == 0,
@@ -237,7 +246,7 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
     if (w->w_dt == FT_F32) {
         FT_CHECK_ARG(act_dt == FT_F32 && y_dt == FT_F32, "fp32 weights take fp32 x and y");
     } else {
-        FT_CHECK_ARG(act_dt == FT_BF16, "bf16/MXFP4/FP8 weights take bf16 activations");
+        FT_CHECK_ARG(act_dt == FT_BF16, "bf16/MXFP4/FP8/NVFP4 weights take bf16 activations");
         FT_CHECK_ARG(y_dt == FT_BF16 || y_dt == FT_F32, "y_dt must be FT_BF16 or FT_F32");
     }
     const FfnPlan p = plan_ffn(*w, T, k);
@@ -256,12 +265,15 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
     g.pool = (const uint8_t*)w->pool;
     g.slot_stride = w->slot_stride;
     layout(w->w_dt, w->H, w->I, g.off);
+    for (int m = 0; m < 3; ++m)  // NVFP4 tensor scales follow the down block scales
+        g.toff[m] = g.off[5] + (size_t)w->H * w->I / 16 + 4 * (size_t)m;
 
     const long tk = (long)T * k;
     const long act = tk < w->E ? tk : w->E;
     int path = g_ffn_path.load();
     if (path == 0) path = (w->w_dt != FT_F32 && tk >= (long)MFMA_MIN_ROWS * act) ? 2 : 1;
     if (path == 2 && w->w_dt == FT_F32) path = 1;  // no fp32 MFMA tiles: fp32 is the tiny case
+    if (path == 2 && w->w_dt == FT_NVFP4) path = 1;  // NVFP4 has no MFMA tiles yet: weight streaming
 
     char* wsb = (char*)ws;
     void* h = wsb;

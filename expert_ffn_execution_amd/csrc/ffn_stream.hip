@@ -44,13 +44,14 @@ namespace {
 
 constexpr int NWAVE = 4;  // wavefronts per block
 
-// WT: 0 = fp32 weights (fp32 activations), 1 = bf16, 2 = MXFP4, 3 = FP8 e4m3
-// (bf16 activations)
+// WT: 0 = fp32 weights (fp32 activations), 1 = bf16, 2 = MXFP4, 3 = FP8 e4m3,
+// 4 = NVFP4 (bf16 activations)
 template <int WT> struct W;
 template <> struct W<0> { static constexpr int EPC = 4; };   // elements per 16 B chunk
 template <> struct W<1> { static constexpr int EPC = 8; };
 template <> struct W<2> { static constexpr int EPC = 32; };
 template <> struct W<3> { static constexpr int EPC = 16; };
+template <> struct W<4> { static constexpr int EPC = 32; };
 
 // How a wavefront walks one weight matrix [N][K] of 16-byte chunks.
 struct Walk {
@@ -66,6 +67,7 @@ struct StreamArgs {
     const uint8_t* pool;
     size_t slot_stride;
     size_t moff[2], soff[2];  // matrix / scale byte offsets inside a slot
+    size_t toff[2];           // NVFP4: the matrices' fp32 tensor scales
     const int32_t* offsets;
     const int32_t* perm;  // gate/up: source token = perm[p] / k; null for down
     const int32_t* slot_of;
@@ -243,9 +245,12 @@ __device__ __forceinline__ bool seg_writer(int lane) {
 // held in LDS sub-chunk-major (8-element unit w of chunk c at (w*nch + c)*8)
 // so that lanes reading consecutive chunks touch consecutive 16-byte words.
 // FP8 chunks (16 codes, decoded into dec[0..7]) meet 16 plain-layout values.
+// NVFP4 chunks (two blocks of 16 codes, laid out like MXFP4) sum each block
+// in fp32 and add it times the block's scale (bs0, bs1).
 template <int WT, typename AT>
 __device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* dec, const AT* xr,
-                                           int col, int nch, float acc) {
+                                           int col, int nch, float acc, float bs0 = 0.f,
+                                           float bs1 = 0.f) {
     if constexpr (WT == 0) {
         const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(xr + col * 4);
 #pragma unroll
@@ -261,6 +266,18 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* de
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc = dot2_bf16(dec[4 * h + q], xv[q], acc);
         }
+    } else if constexpr (WT == 4) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float p = 0.f;
+#pragma unroll
+            for (int w = 2 * blk; w < 2 * blk + 2; ++w) {
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + ((size_t)w * nch + col) * 8);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) p = dot2_bf16(dec[4 * w + b], xv[b], p);
+            }
+            acc = fmaf(p, blk ? bs1 : bs0, acc);
+        }
     } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -270,6 +287,13 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t& wv, const uint32_t* de
         }
     }
     return acc;
+}
+
+// two e4m3 bytes (the low half of w) -> floats, exact
+__device__ __forceinline__ void e4m3x2_f32(uint32_t w, float& lo, float& hi) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    lo = __uint_as_float(b << 16);
+    hi = __uint_as_float(b & 0xFFFF0000u);
 }
 
 // f(std::integral_constant<int, R>) for the runtime R in [1, N].
@@ -329,6 +353,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
         mat[m] = reinterpret_cast<const u32x4_t*>(sl + a.moff[m]);
         scl[m] = sl + a.soff[m];
         if constexpr (WT == 3) msc[m] = *reinterpret_cast<const float*>(scl[m]);
+        else if constexpr (WT == 4) msc[m] = *reinterpret_cast<const float*>(sl + a.toff[m]);
         else msc[m] = 1.0f;
     }
     const Walk wk = a.wk;
@@ -375,6 +400,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
             for (int m = 0; m < NM; ++m) {
                 b.v[m][q] = __builtin_nontemporal_load(mat[m] + ci);
                 if constexpr (WT == 2) b.s[m][q] = scl[m][ci];
+                if constexpr (WT == 4) b.s[m][q] = reinterpret_cast<const uint16_t*>(scl[m])[ci];
             }
         }
     };
@@ -400,7 +426,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
             const int col = ok ? col_of(it, q) : 0;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                uint32_t dec[WT == 2 ? 16 : WT == 3 ? 8 : 1];
+                uint32_t dec[WT == 2 || WT == 4 ? 16 : WT == 3 ? 8 : 1];
+                float bs0 = 0.f, bs1 = 0.f;  // NVFP4 block scales of the chunk
                 u32x4_t wv = b.v[m][q];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) wv[w] = ok ? wv[w] : 0u;  // +0 codes / +0.0 weights
@@ -414,6 +441,17 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
                         dec[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
                         dec[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
                     }
+                } else if constexpr (WT == 4) {
+                    // e2m1 codes to bf16 (exact); each block's sum is scaled later
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t cw = wv[w];
+                        dec[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 0));
+                        dec[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 1));
+                        dec[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 2));
+                        dec[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 3));
+                    }
+                    e4m3x2_f32(ok ? b.s[m][q] : 0u, bs0, bs1);
                 } else if constexpr (WT == 3) {
                     // e4m3 codes to bf16 (exact; the conversion's scale operand only
                     // takes a power of two, so the matrix scale comes later)
@@ -425,7 +463,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
                 }
 #pragma unroll
                 for (int r = 0; r < RR; ++r)
-                    acc[m][r] = chunk_dot<WT, AT>(wv, dec, xs + (size_t)r * K, col, wk.nch, acc[m][r]);
+                    acc[m][r] = chunk_dot<WT, AT>(wv, dec, xs + (size_t)r * K, col, wk.nch, acc[m][r], bs0, bs1);
             }
         }
         if (it.p != wk.P - 1) return;
@@ -482,7 +520,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
         const int r = i / units, uu = i - r * units;
         const size_t srow = a.perm ? (shared ? (size_t)(r0 + r) : (size_t)(a.perm[p_lo + r0 + r] / a.k))
                                    : orow0 + r0 + r;
-        const int du = WT == 2 ? (uu & 3) * (units >> 2) + (uu >> 2) : uu;
+        const int du = (WT == 2 || WT == 4) ? (uu & 3) * (units >> 2) + (uu >> 2) : uu;
         reinterpret_cast<u32x4_t*>(xs + (size_t)r * K)[du] =
             reinterpret_cast<const u32x4_t*>(src + srow * K)[uu];
     }
@@ -555,7 +593,26 @@ __device__ __forceinline__ bf16x8_t fp8x8_bf16(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(bf16x8_t, d);
 }
 
-// Per-step shape of the matrix-core kernel (WT: 2 = MXFP4, 3 = FP8).
+// NVFP4: 8 codes times their block scale -> 8 bf16.  e2m1 times e4m3 has at
+// most 6 significant bits, so the product (in fp32) converts to bf16 exactly.
+__device__ __forceinline__ bf16x8_t nvfp4x8_bf16(uint32_t codes, float bs) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    f32x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3)};
+    u32x4_t d;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b].x *= bs;
+        v[b].y *= bs;
+        d[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[b], bf16x2));
+    }
+    return __builtin_bit_cast(bf16x8_t, d);
+}
+
+// Per-step shape of the matrix-core kernel (WT: 2 = MXFP4, 3 = FP8, 4 = NVFP4).
 template <int WT> struct MxShape {
     static constexpr int LPS = 2;                                // 16-byte code loads per lane, step, matrix
     static constexpr int EPL = WT == 3 ? 16 : 32;                // weights per 16-byte load
@@ -568,7 +625,7 @@ template <int WT> struct MxShape {
 
 template <int WT, int NM, typename OT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
-    static_assert(WT == 2 || WT == 3, "narrow weights only");
+    static_assert(WT == 2 || WT == 3 || WT == 4, "narrow weights only");
     using S = MxShape<WT>;
     constexpr int D = MX_D, LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
     static_assert(D % SPW == 0, "a scale word's steps share one register round");
@@ -587,11 +644,12 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     const int U = rgw * nks;                                              // (group, step) pairs
     const int ln = lane & 15, q = lane >> 4;
     const uint8_t* sl = a.pool + (size_t)gr.slot * a.slot_stride;
-    const size_t rowb = WT == 3 ? (size_t)K : (size_t)K / 2, srowb = (size_t)K / 32;
-    float msc[NM];  // FP8: the matrix scales (applied to the finished sums)
+    const size_t rowb = WT == 3 ? (size_t)K : (size_t)K / 2, srowb = (size_t)K / (WT == 4 ? 16 : 32);
+    float msc[NM];  // FP8 matrix / NVFP4 tensor scales (applied to the finished sums)
 #pragma unroll
     for (int m = 0; m < NM; ++m)
-        msc[m] = WT == 3 ? *reinterpret_cast<const float*>(sl + a.soff[m]) : 1.0f;
+        msc[m] = WT == 3 ? *reinterpret_cast<const float*>(sl + a.soff[m])
+               : WT == 4 ? *reinterpret_cast<const float*>(sl + a.toff[m]) : 1.0f;
 
     // Loads of pair u into code buffer b; pairs past the end re-read the first
     // one.  MXFP4: a pair u == 0 mod SPW also loads the row's 16 scale bytes of
@@ -601,6 +659,8 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     // refilled.
     u32x4_t cb[D][NM][LPS];
     u32x4_t sv[NSV][NM];
+    // NVFP4: the 4 block-scale bytes of this lane's 64 weights of each step
+    uint32_t s4[WT == 4 ? D : 1][NM];
     auto row_of = [&](int uu) __attribute__((always_inline)) {
         const int rgi = uu / nks;
         // (clamped into the block: a wavefront without row groups still issues)
@@ -620,6 +680,11 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 sv[t][m] = *reinterpret_cast<const u32x4_t*>(sl + a.soff[m] + row * srowb + 4 * LPS * ks);
+        }
+        if constexpr (WT == 4) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                s4[b][m] = *reinterpret_cast<const uint32_t*>(sl + a.soff[m] + row * srowb + 16 * ks + 4 * q);
         }
     };
 #pragma unroll
@@ -665,6 +730,11 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
                             const uint32_t word = sv[t][m][by >> 2];
                             const float sc = __uint_as_float(((word >> (8 * (by & 3))) & 0xFFu) << 23);
                             bw = fp4x8_bf16(cb[b][m][h][f % 4], sc);
+                        } else if constexpr (WT == 4) {
+                            // fragment f lies in this lane's block f / 2 (16 weights)
+                            float bs0, bs1;
+                            e4m3x2_f32(s4[b][m] >> (16 * (f / 4)), bs0, bs1);
+                            bw = nvfp4x8_bf16(cb[b][m][f / 4][f % 4], (f / 2) % 2 ? bs1 : bs0);
                         } else {
                             const int h = f / 2, w0 = 2 * (f % 2);
                             bw = fp8x8_bf16(cb[b][m][h][w0], cb[b][m][h][w0 + 1]);
@@ -789,6 +859,7 @@ bool mx_eligible(int WT, int K, int T) {
     }();
     if (off || T < min_t) return false;
     if (WT == 2) return K % 512 == 0;
+    if (WT == 4) return K % 256 == 0;
     return WT == 3 && K % 128 == 0;
 }
 template <int WT, int NM, typename OT>
@@ -827,7 +898,7 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
         return e ? atoi(e) : 0;
     }();
     const size_t wave_bytes = (size_t)(wave_kb > 0 ? wave_kb : WT == 3 ? 64 : 32) * 1024;
-    const size_t row_w = (WT == 3 ? (size_t)a.K : (size_t)a.K / 2 + a.K / 32) * NM;  // weight bytes per row
+    const size_t row_w = (WT == 3 ? (size_t)a.K : (size_t)a.K / 2 + a.K / (WT == 4 ? 16 : 32)) * NM;  // weight bytes per row
     auto nblk = [&](int rpb) { return groups * ((a.N + rpb - 1) / rpb); };
     int rpb = 16 * NWAVE;
     while (rpb < a.N && (size_t)(rpb / NWAVE) * row_w < wave_bytes) rpb *= 2;
@@ -870,6 +941,8 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a1.moff[1] = g.off[1];
     a1.soff[0] = g.off[3];
     a1.soff[1] = g.off[4];
+    a1.toff[0] = g.toff[0];
+    a1.toff[1] = g.toff[1];
     a1.perm = perm;
     a1.N = g.I;
     a1.K = g.H;
@@ -883,6 +956,9 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     else if (g.w_dt == FT_FP8) {
         if (mx_eligible(3, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
         else r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    } else if (g.w_dt == FT_NVFP4) {
+        if (mx_eligible(4, a1.K, a1.T)) r = launch_mx<4, 2, float>(a1, g.n_shared, max_lds, s);
+        else r = launch_rows<4, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     } else if (mx_eligible(2, a1.K, a1.T)) {
         r = launch_mx<2, 2, float>(a1, g.n_shared, max_lds, s);
     } else {
@@ -895,6 +971,7 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     StreamArgs a2 = a;
     a2.moff[0] = g.off[2];
     a2.soff[0] = g.off[5];
+    a2.toff[0] = g.toff[2];
     a2.perm = nullptr;
     a2.N = g.H;
     a2.K = g.I;
@@ -912,6 +989,14 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
         } else {
             if (y_dt == FT_F32) r = launch_rows<3, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
             else r = launch_rows<3, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+        }
+    } else if (g.w_dt == FT_NVFP4) {
+        if (mx_eligible(4, a2.K, a2.T)) {
+            if (y_dt == FT_F32) r = launch_mx<4, 1, float>(a2, g.n_shared, max_lds, s);
+            else r = launch_mx<4, 1, __bf16>(a2, g.n_shared, max_lds, s);
+        } else {
+            if (y_dt == FT_F32) r = launch_rows<4, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+            else r = launch_rows<4, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
         }
     } else if (mx_eligible(2, a2.K, a2.T)) {
         if (y_dt == FT_F32) r = launch_mx<2, 1, float>(a2, g.n_shared, max_lds, s);

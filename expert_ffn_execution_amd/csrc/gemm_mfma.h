@@ -25,6 +25,7 @@ struct FfnGeom {
     const uint8_t* pool;
     size_t slot_stride;
     size_t off[6];  // gate, up, down, gate_sc, up_sc, down_sc (bytes within a slot)
+    size_t toff[3];  // NVFP4: the fp32 tensor scales of gate, up, down
 };
 
 // Build the M-tile list from offsets (one block).  tiles[0..max_tiles),

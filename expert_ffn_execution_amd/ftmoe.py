@@ -17,8 +17,8 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libftmoe.so")
 
-F32, BF16, MXFP4, FP8 = 0, 1, 2, 3
-DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "fp8": FP8}
+F32, BF16, MXFP4, FP8, NVFP4 = 0, 1, 2, 3, 4
+DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "fp8": FP8, "nvfp4": NVFP4}
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_NOT_PINNED, ERR_BUSY, ERR_HIP = range(7)
 WARN_OVERLAP_DISABLED = 100
 SCOPE_GLOBAL, SCOPE_PER_LAYER = 0, 1
@@ -222,7 +222,11 @@ def pack_expert(ex: dict, wdtype: str, H: int, I: int, out: torch.Tensor):
     """Write one expert's logical tensors into a slot (uint8 view of slot_stride bytes)."""
     n, offs = expert_layout(wdtype, H, I)
     names = ["gate", "up", "down"] + (["gate_sc", "up_sc", "down_sc"]
-                                      if wdtype in ("mxfp4", "fp8") else [])
+                                      if wdtype in ("mxfp4", "fp8", "nvfp4") else [])
+    offs = list(offs)
+    if wdtype == "nvfp4":  # the fp32 tensor scales follow the down block scales
+        names += ["gate_ts", "up_ts", "down_ts"]
+        offs += [offs[5] + H * I // 16 + 4 * m for m in range(3)]
     for name, off in zip(names, offs):
         t = ex[name].contiguous()
         b = t.view(torch.uint8).reshape(-1)

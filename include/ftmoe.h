@@ -62,7 +62,7 @@ typedef enum {
     FT_WARN_OVERLAP_DISABLED = 100
 } ft_status;
 
-typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_FP8 = 3 } ft_dtype;
+typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_FP8 = 3, FT_NVFP4 = 4 } ft_dtype;
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* ft_last_error(void);
@@ -129,16 +129,24 @@ ft_status ft_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* co
  *     weight = value(code) * scale.  The pages list FP8 weights (refft.com
  *     guide, the format list) without their scaling; one scale per matrix is
  *     the plainest reading.
+ *   FT_NVFP4: gate codes [I][H/2] | up codes [I][H/2] | down codes [H][I/2]
+ *     (e2m1 nibbles as for MXFP4) | gate scales [I][H/16] | up scales [I][H/16]
+ *     | down scales [H][I/16] (one e4m3 byte per 16 consecutive elements along
+ *     the contraction dimension) | three fp32 tensor scales (gate, up, down) at
+ *     byte offsets offs[5] + H*I/16 + 0, 4, 8: weight = e2m1(code) *
+ *     e4m3(block scale) * tensor scale.  The pages list NVFP4 (refft.com
+ *     guide, the format list) without its layout; this is NVIDIA's published
+ *     NVFP4 definition.
  * All formats: H % 64 == 0 and I % 64 == 0.
  * ft_expert_layout fills offs[6] = byte offsets of {gate, up, down,
- * gate_sc, up_sc, down_sc} (scale arrays for MXFP4, the fp32 scales for
- * FP8, 0 otherwise) and returns the
+ * gate_sc, up_sc, down_sc} (scale arrays for MXFP4 and NVFP4, the fp32 scales
+ * for FP8, 0 otherwise) and returns the
  * slot size in bytes (0 for an unsupported combination).
  * ------------------------------------------------------------------------ */
 size_t ft_expert_layout(ft_dtype w_dt, int H, int I, size_t offs[6]);
 
 typedef struct {
-    ft_dtype w_dt;        /* FT_F32, FT_BF16, FT_MXFP4 or FT_FP8 */
+    ft_dtype w_dt;        /* FT_F32, FT_BF16, FT_MXFP4, FT_FP8 or FT_NVFP4 */
     int E;                /* routed experts */
     int H;                /* hidden size */
     int I;                /* expert intermediate size */
@@ -158,7 +166,9 @@ typedef struct {
  * With n_shared == 1, rows T*k + t of y_perm receive the shared expert's FFN
  * of x_t (weight 1 in the combine).  MXFP4 weights are decoded exactly to bf16
  * on chip and multiplied with bf16 activations; FP8 codes likewise, the matrix
- * scale applied to each fp32 sum.
+ * scale applied to each fp32 sum; NVFP4 codes times their block scales
+ * likewise (exactly representable in bf16), the tensor scale applied to each
+ * fp32 sum.
  *   x [T][H] device, act_dt = FT_BF16 (FT_F32 only with FT_F32 weights);
  *   perm, offsets: ft_moe_align's outputs for the same ids;
  *   slot_of_expert [E] int32 device, or NULL for slot e = expert e: the slot

@@ -72,6 +72,17 @@ def unpack_slot(raw: torch.Tensor, shape: synth.LayerShape) -> dict:
                 "gate_sc": raw[offs[3]:offs[3] + I * H // 32].view(I, H // 32),
                 "up_sc": raw[offs[4]:offs[4] + I * H // 32].view(I, H // 32),
                 "down_sc": raw[offs[5]:offs[5] + H * I // 32].view(H, I // 32)}
+    if shape.wdtype == "nvfp4":
+        ts = offs[5] + H * I // 16
+        return {"gate": raw[offs[0]:offs[0] + I * H // 2].view(I, H // 2),
+                "up": raw[offs[1]:offs[1] + I * H // 2].view(I, H // 2),
+                "down": raw[offs[2]:offs[2] + H * I // 2].view(H, I // 2),
+                "gate_sc": raw[offs[3]:offs[3] + I * H // 16].view(I, H // 16),
+                "up_sc": raw[offs[4]:offs[4] + I * H // 16].view(I, H // 16),
+                "down_sc": raw[offs[5]:offs[5] + H * I // 16].view(H, I // 16),
+                "gate_ts": raw[ts:ts + 4].view(torch.float32),
+                "up_ts": raw[ts + 4:ts + 8].view(torch.float32),
+                "down_ts": raw[ts + 8:ts + 12].view(torch.float32)}
     if shape.wdtype == "fp8":
         return {"gate": raw[offs[0]:offs[0] + I * H].view(I, H),
                 "up": raw[offs[1]:offs[1] + I * H].view(I, H),
@@ -126,7 +137,9 @@ def check_close(got, ref, wdtype: str, what: str = ""):
     """The pass criteria: fp32 rel L2 <= 1e-5 and max abs <= 1e-4 max|ref|; bf16
     rel L2 <= 5e-3 and max abs <= 2e-2 max|ref|; MXFP4 rel L2 <= 1e-2.  FP8
     weights take the bf16 bar: their codes decode exactly to bf16 and the
-    arithmetic is the bf16 weights' (bf16 products, fp32 sums, bf16 h)."""
+    arithmetic is the bf16 weights' (bf16 products, fp32 sums, bf16 h).  NVFP4
+    weights likewise: code times block scale is exact in bf16 (matrix cores),
+    or each block's fp32 sum is scaled (dot products)."""
     g = to_np_f64(got)
     r = np.asarray(ref, np.float64)
     e = rel_l2(g, r)
@@ -134,7 +147,7 @@ def check_close(got, ref, wdtype: str, what: str = ""):
     amax = float(np.max(np.abs(r))) if r.size else 0.0
     if wdtype == "f32":
         assert e <= 1e-5 and mx <= 1e-4 * amax, (what, e, mx, amax)
-    elif wdtype in ("bf16", "fp8"):
+    elif wdtype in ("bf16", "fp8", "nvfp4"):
         assert e <= 5e-3 and mx <= 2e-2 * amax, (what, e, mx, amax)
     else:
         assert e <= 1e-2, (what, e, mx, amax)

@@ -38,6 +38,9 @@ def test_expert_layout():
     n, offs = ft.expert_layout("fp8", 2048, 768)
     HI = 2048 * 768
     assert n == 3 * HI + 16 and offs == [0, HI, 2 * HI, 3 * HI, 3 * HI + 4, 3 * HI + 8]
+    n, offs = ft.expert_layout("nvfp4", 2048, 768)
+    assert n == 3 * HI // 2 + 3 * HI // 16 + 16
+    assert offs == [0, HI // 2, HI, 3 * HI // 2, 3 * HI // 2 + HI // 16, 3 * HI // 2 + HI // 8]
     with pytest.raises(ft.FtError):
         ft.expert_layout("bf16", 100, 64)
 

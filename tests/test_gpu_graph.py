@@ -26,6 +26,7 @@ SHAPES = {
     "35b_a3b_bf16": synth.A3B_BF16,
     "284b_a13b_mxfp4": synth.A13B_MXFP4,
     "35b_a3b_fp8": synth.A3B_FP8,
+    "35b_a3b_nvfp4": synth.A3B_NVFP4,
 }
 # (shape, T, permuted slots): decode sizes take the streaming kernels, T = 300
 # on the small shapes the MFMA tiles (tile list built on the device)
@@ -33,7 +34,8 @@ CASES = [("tiny_f32", 64, False), ("small_bf16", 3, True), ("small_bf16", 300, F
          ("small_mx", 5, False), ("small_mx", 300, True), ("35b_a3b_bf16", 1, False),
          ("35b_a3b_bf16", 16, False), ("35b_a3b_bf16", 8, False), ("35b_a3b_bf16", 9, False),
          ("284b_a13b_mxfp4", 1, False), ("284b_a13b_mxfp4", 8, False), ("35b_a3b_fp8", 1, False),
-         ("35b_a3b_fp8", 8, False), ("35b_a3b_fp8", 64, False)]
+         ("35b_a3b_fp8", 8, False), ("35b_a3b_fp8", 64, False), ("35b_a3b_nvfp4", 1, False),
+         ("35b_a3b_nvfp4", 8, False)]
 _LAYERS = {}
 
 

@@ -132,6 +132,11 @@ SMALL = {
     # rows of 512 both ways: MXFP4 gate/up and down both on the matrix-core kernel
     "mxfp4_512": synth.LayerShape("gpu_small_mx512", H=512, E=16, k=4, I=512, n_shared=1,
                                   wdtype="mxfp4"),
+    # NVFP4: gate/up rows (512) on matrix cores from two tokens on, down rows
+    # (384, not a multiple of 256) on the dot-product kernel
+    "nvfp4": synth.LayerShape("gpu_small_nvfp4", H=512, E=16, k=4, I=384, n_shared=1,
+                              wdtype="nvfp4"),
+    "nvfp4_512": synth.LayerShape("gpu_small_nvfp4_512", H=512, E=16, k=6, I=512, wdtype="nvfp4"),
 }
 
 
@@ -152,7 +157,7 @@ def test_layer_small_both_paths(kind, path, T):
     check_close(r["out"], ref, sh.wdtype, f"{kind} path{path} T{T}")
 
 
-@pytest.mark.parametrize("kind", ["bf16", "mxfp4", "fp8"])
+@pytest.mark.parametrize("kind", ["bf16", "mxfp4", "fp8", "nvfp4"])
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("T", [7, 300])
 def test_layer_fp32_expert_outputs(kind, path, T):
@@ -287,7 +292,8 @@ FULL = [("284b_a13b_mxfp4", 1), ("284b_a13b_mxfp4", 8), ("284b_a13b_mxfp4", 64),
         ("284b_a13b_mxfp4", 8192), ("753b_a40b_bf16", 1), ("753b_a40b_bf16", 32),
         ("753b_a40b_bf16", 16384), ("753b_a40b_mxfp4", 1), ("753b_a40b_mxfp4", 32),
         ("753b_a40b_mxfp4", 16384), ("35b_a3b_fp8", 1), ("35b_a3b_fp8", 16),
-        ("35b_a3b_fp8", 4096)]
+        ("35b_a3b_fp8", 4096), ("35b_a3b_nvfp4", 1), ("35b_a3b_nvfp4", 16),
+        ("35b_a3b_nvfp4", 64), ("35b_a3b_nvfp4", 4096)]
 
 
 @pytest.mark.parametrize("name,T", FULL)
