@@ -273,7 +273,6 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
     int path = g_ffn_path.load();
     if (path == 0) path = (w->w_dt != FT_F32 && tk >= (long)MFMA_MIN_ROWS * act) ? 2 : 1;
     if (path == 2 && w->w_dt == FT_F32) path = 1;  // no fp32 MFMA tiles: fp32 is the tiny case
-    if (path == 2 && w->w_dt == FT_NVFP4) path = 1;  // NVFP4 has no MFMA tiles yet: weight streaming
 
     char* wsb = (char*)ws;
     void* h = wsb;

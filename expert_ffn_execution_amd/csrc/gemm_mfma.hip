@@ -335,22 +335,29 @@ constexpr int KST = 64;                        // K per stage
 constexpr int MT = BM / 32, NTL = WN / 32;     // 32 x 32 MFMA tiles per wavefront
 constexpr int A_UNIT = BM * KST * 2;           // one A stage: 32 KB of bf16
 constexpr int LA = A_UNIT / 1024 / NW;         // A copies per wave and stage, full tile
-// BT: 0 bf16 weights, 1 MXFP4, 2 FP8 (e4m3, one fp32 scale per matrix).
-template <int BT> constexpr int b_row() { return BT == 0 ? KST * 2 : BT == 1 ? KST / 2 : KST; }
+// BT: 0 bf16 weights, 1 MXFP4, 2 FP8 (e4m3, one fp32 scale per matrix), 3 NVFP4
+// (e2m1 with an e4m3 scale per 16 and an fp32 scale per matrix).
+template <int BT> constexpr int b_row() { return BT == 0 ? KST * 2 : BT == 2 ? KST : KST / 2; }
 // MXFP4: codes [BN][32 B], then for each half of the stage a 4-byte slot per
 // row holding its scale byte (a 1-byte LDS-DMA load writes each lane's byte
-// to a 4-byte slot)
-template <int BT> constexpr int b_unit() { return BN * b_row<BT>() + (BT == 1 ? 2 * BN * 4 : 0); }
-template <int BT> constexpr int n_a() { return BT == 0 ? 2 : BT == 1 ? 4 : 3; }  // A ring stages
-template <int BT> constexpr int n_b() { return BT == 0 ? 3 : BT == 1 ? 3 : 4; }  // B ring stages
+// to a 4-byte slot).  NVFP4: codes [BN][32 B], then the row's 4 block-scale
+// bytes of the stage [BN][4 B].
+template <int BT> constexpr int b_unit() {
+    return BN * b_row<BT>() + (BT == 1 ? 2 * BN * 4 : BT == 3 ? BN * 4 : 0);
+}
+template <int BT> constexpr int n_a() { return BT == 0 ? 2 : BT == 2 ? 3 : 4; }  // A ring stages
+template <int BT> constexpr int n_b() { return BT == 0 ? 3 : BT == 2 ? 4 : 3; }  // B ring stages
 template <int BT> constexpr int b_code_copies() { return BN * b_row<BT>() / 1024 / NW; }
-template <int BT> constexpr int b_copies() { return b_code_copies<BT>() + (BT == 1 ? 2 : 0); }  // per wave, stage
+template <int BT> constexpr int b_copies() {  // per wave, stage
+    return b_code_copies<BT>() + (BT == 1 ? 2 : BT == 3 ? 1 : 0);
+}
 constexpr size_t EPI_BYTES = (size_t)BM * (BN + 8) * 2;   // bf16 output tile (plain GEMM)
 template <int BT> constexpr size_t ring_bytes() {
     return (size_t)n_a<BT>() * A_UNIT + (size_t)n_b<BT>() * b_unit<BT>();
 }
 template <int BT> constexpr size_t lds_bytes() { return ring_bytes<BT>() > EPI_BYTES ? ring_bytes<BT>() : EPI_BYTES; }
-static_assert(lds_bytes<0>() <= 160 * 1024 && lds_bytes<1>() <= 160 * 1024 && lds_bytes<2>() <= 160 * 1024,
+static_assert(lds_bytes<0>() <= 160 * 1024 && lds_bytes<1>() <= 160 * 1024 && lds_bytes<2>() <= 160 * 1024 &&
+                  lds_bytes<3>() <= 160 * 1024,
               "rings fit the LDS");
 __device__ __forceinline__ int swz_bf16(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 __device__ __forceinline__ int swz_fp8(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
@@ -424,6 +431,28 @@ __device__ __forceinline__ bf16x8_t fp4_frag(uint32_t codes, uint32_t X) {
     d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
     d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
     d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+    return __builtin_bit_cast(bf16x8_t, d);
+}
+
+// NVFP4: 8 e2m1 codes times their block's e4m3 scale byte -> 8 bf16.  The
+// product of an e2m1 and an e4m3 value has at most 6 significant bits, so the
+// fp32 product converts to bf16 exactly.
+__device__ __forceinline__ bf16x8_t nvfp4_frag(uint32_t codes, uint32_t scale_byte) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const float bs = __uint_as_float(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(scale_byte, 1.0f, false)) << 16);
+    f32x2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2),
+                  __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3)};
+    u32x4_t d;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b].x *= bs;
+        v[b].y *= bs;
+        d[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[b], bf16x2));
+    }
     return __builtin_bit_cast(bf16x8_t, d);
 }
 
@@ -512,7 +541,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         else
             return (uint32_t)g.off[which ? 5 : 2];
     };
-    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : BT == 1 ? (uint32_t)K / 2 : (uint32_t)K;
+    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : BT == 2 ? (uint32_t)K : (uint32_t)K / 2;
     // B code copies per wave: b_code_copies<BT>() <= 8 (a literal bound: a
     // call in an array bound reads as a variable-length array to the host pass)
     constexpr int NBC = b_code_copies<BT>();
@@ -524,14 +553,14 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             const int r = 8 * (NBC * wave + i) + (lane >> 3);
             boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
         }
-    } else if constexpr (BT == 1) {  // copy i: rows 32 (NBC wave + i) .. + 31, two lanes a row; scales of row 64 wave + lane
+    } else if constexpr (BT == 1 || BT == 3) {  // copy i: rows 32 (NBC wave + i) .. + 31, two lanes a row; scales of row 64 wave + lane
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
             const int r = 32 * (NBC * wave + i) + (lane >> 1);
             boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
         }
         const int r = 64 * wave + lane;
-        soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / 32);
+        soff = wbase(r, 1) + wrow(r) * (uint32_t)(K / (BT == 1 ? 32 : 16));
     } else {  // FP8 copy i: rows 16 (NBC wave + i) .. + 15, four lanes a row
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
@@ -539,11 +568,14 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
             boff[i] = wbase(r, 0) + wrow(r) * rowb + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
         }
     }
-    // FP8: the matrices' fp32 scales (gate / up, or down), applied in the epilogue
+    // FP8 matrix / NVFP4 tensor scales (gate / up, or down), applied in the epilogue
     float bsc0 = 1.0f, bsc1 = 1.0f;
     if constexpr (BT == 2) {
         bsc0 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.off[3] : g.off[5]));
         bsc1 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.off[4] : g.off[5]));
+    } else if constexpr (BT == 3) {
+        bsc0 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.toff[0] : g.toff[2]));
+        bsc1 = *reinterpret_cast<const float*>(slot + (MODE == MODE_GATED ? g.toff[1] : g.toff[2]));
     }
 
     // (constants, not calls: a constexpr template call evaluated at run time in
@@ -569,6 +601,8 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 __builtin_amdgcn_global_load_lds(slot + soff + 2 * x + h, FT_LDS(dst + BN * 32 + h * BN * 4 + wave * 256), 1, 0, 0);
+        } else if constexpr (BT == 3) {  // the row's 4 block scales of the stage
+            __builtin_amdgcn_global_load_lds(slot + soff + 4 * x, FT_LDS(dst + BN * 32 + wave * 256), 4, 0, 0);
         }
     };
 
@@ -633,9 +667,12 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
                 const int row = b_tile_row(n) + l32;
                 if constexpr (BT == 0) {
                     F.b[kk][n] = *reinterpret_cast<const bf16x8_t*>(Bu + swz_bf16(row, 4 * h + ch));
-                } else {
+                } else if constexpr (BT == 1) {
                     const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bu + swz_fp4(row, h) + ch * 4);
                     F.b[kk][n] = fp4_frag(codes, Bu[BN * 32 + h * BN * 4 + row * 4]);
+                } else {  // NVFP4: these 8 codes (k = 32 h + 8 ch ..) lie in block 2 h + ch / 2
+                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(Bu + swz_fp4(row, h) + ch * 4);
+                    F.b[kk][n] = nvfp4_frag(codes, Bu[BN * 32 + row * 4 + 2 * h + ch / 2]);
                 }
             }
         }
@@ -663,7 +700,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     auto step = [&](int j, const Frags& cur, Frags& nxt, auto mc, auto odd, auto steady) __attribute__((always_inline)) {
         constexpr int MA = decltype(mc)::value;
         constexpr bool ODD = decltype(odd)::value, STEADY = decltype(steady)::value;
-        constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 1 ? 4 : 1) * NTL;
+        constexpr int NMF = 2 * MA * NTL, NDS = 2 * MA + (BT == 0 ? 2 : BT == 2 ? 1 : 4) * NTL;
         constexpr int NP = NMF < NDS ? NMF : NDS;
         constexpr int NC = ODD ? MA : LB;
         constexpr bool COPIES_FIRST = BT == 0;
@@ -919,6 +956,7 @@ ft_status launch_gemm1_mfma(const FfnGeom& g, const __bf16* x, const int32_t* pe
     const unsigned grid = (unsigned)(mt * nn + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     hipError_t e = g.w_dt == FT_MXFP4 ? launch_pipe<MODE_GATED, 1, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
                  : g.w_dt == FT_FP8   ? launch_pipe<MODE_GATED, 2, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
+                 : g.w_dt == FT_NVFP4 ? launch_pipe<MODE_GATED, 3, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h)
                                       : launch_pipe<MODE_GATED, 0, __bf16>(grid, s, g, x, perm, tiles, n_tiles, nn, h);
     if (e != hipSuccess) return set_error(FT_ERR_HIP, "gemm1: %s", hipGetErrorString(e));
     return FT_OK;
@@ -937,6 +975,9 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
     else if (g.w_dt == FT_FP8)
         e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 2, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
                            : launch_pipe<MODE_LIST, 2, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
+    else if (g.w_dt == FT_NVFP4)
+        e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 3, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
+                           : launch_pipe<MODE_LIST, 3, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
     else
         e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 0, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
                            : launch_pipe<MODE_LIST, 0, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
