@@ -789,23 +789,39 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         __bf16* ts = reinterpret_cast<__bf16*>(smem);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS reads are done
         __builtin_amdgcn_s_barrier();        // ... and every other wave's
+        // Rows r, r + 1 of a lane's column c come from registers q, q + 1 (q
+        // even).  Lanes 2i and 2i + 1 swap one value (DPP quad_perm [1,0,3,2])
+        // so that the even lane holds row r, columns c, c + 1 and the odd lane
+        // row r + 1, columns c - 1, c: one packed conversion (round to nearest
+        // even) and one 32-bit LDS write per pair, half the writes of one bf16
+        // each.
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bool odd = lane & 1;
+        auto put = [&](int row, int col, float v0, float v1) __attribute__((always_inline)) {
+            const float send = odd ? v0 : v1;
+            const float recv = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, true));
+            const f32x2 pr = odd ? f32x2{recv, v1} : f32x2{v0, recv};
+            *reinterpret_cast<bf16x2*>(ts + (row + (odd ? 1 : 0)) * PITCH + (col & ~1)) =
+                __builtin_convertvector(pr, bf16x2);
+        };
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m >= mact) break;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
+            for (int q = 0; q < 16; q += 2) {
                 const int row = m * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
                 if constexpr (MODE == MODE_GATED) {
 #pragma unroll
                     for (int n = 0; n < NTL / 2; ++n)
-                        ts[row * PITCH + wn * (WN / 2) + n * 32 + l32] =
-                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(
-                                silu_mul_fast(acc[m][n][q] * bsc0, acc[m][n + NTL / 2][q] * bsc1)));
+                        put(row, wn * (WN / 2) + n * 32 + l32,
+                            silu_mul_fast(acc[m][n][q] * bsc0, acc[m][n + NTL / 2][q] * bsc1),
+                            silu_mul_fast(acc[m][n][q + 1] * bsc0, acc[m][n + NTL / 2][q + 1] * bsc1));
                 } else {
 #pragma unroll
                     for (int n = 0; n < NTL; ++n)
-                        ts[row * PITCH + wn * WN + n * 32 + l32] =
-                            __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(acc[m][n][q] * bsc0));
+                        put(row, wn * WN + n * 32 + l32, acc[m][n][q] * bsc0, acc[m][n][q + 1] * bsc0);
                 }
             }
         }
