@@ -137,6 +137,13 @@ SMALL = {
     "nvfp4": synth.LayerShape("gpu_small_nvfp4", H=512, E=16, k=4, I=384, n_shared=1,
                               wdtype="nvfp4"),
     "nvfp4_512": synth.LayerShape("gpu_small_nvfp4_512", H=512, E=16, k=6, I=512, wdtype="nvfp4"),
+    # the shortest rows: K = 128 (gate/up) and K = 64 (down) are two and one
+    # 64-wide stages of the MFMA tiles' copy rings
+    "short_bf16": synth.LayerShape("gpu_short_bf16", H=128, E=8, k=2, I=64, n_shared=1),
+    "short_mxfp4": synth.LayerShape("gpu_short_mx", H=128, E=8, k=3, I=64, wdtype="mxfp4"),
+    "short_fp8": synth.LayerShape("gpu_short_fp8", H=128, E=8, k=2, I=64, wdtype="fp8"),
+    "short_nvfp4": synth.LayerShape("gpu_short_nvfp4", H=128, E=8, k=2, I=64, n_shared=1,
+                                    wdtype="nvfp4"),
 }
 
 
