@@ -94,6 +94,48 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int n, int E,
         wave_scatter(ids, f0, f_hi, hist + w * E, perm, inv, lane);
 }
 
+// At most 64 slots (decode: T*k <= 64): one wavefront, no barriers.  Lane f
+// holds slot f; its position is the number of slots with a smaller expert
+// plus the number of earlier slots with the same expert (the stable counting
+// sort), and the counts and offsets of every expert are counted the same way,
+// with each slot's expert read as a scalar.  The same results as align_block.
+// EPL: experts per lane (E <= 64 EPL).
+template <int EPL>
+__device__ __forceinline__ void align_wave(const int32_t* ids, int n, int E,
+                                           int32_t* __restrict__ counts,
+                                           int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ perm,
+                                           int32_t* __restrict__ inv, int lane) {
+    const int v = lane < n ? ids[lane] : 0x7fffffff;
+    int cnt[EPL], off[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cnt[i] = off[i] = 0;
+    int pos = 0;
+    for (int f = 0; f < n; ++f) {
+        const int vf = __builtin_amdgcn_readlane(v, f);
+        pos += (vf < v) || (vf == v && f < lane);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            cnt[i] += vf == e;
+            off[i] += vf < e;
+        }
+    }
+    if (lane < n) {
+        perm[pos] = lane;
+        inv[lane] = pos;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            counts[e] = cnt[i];
+            offsets[e] = off[i];
+        }
+    }
+    if (lane == 0) offsets[E] = n;
+}
+
 __global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __restrict__ ids,
                                                               int n, int E,
                                                               int32_t* __restrict__ counts,
@@ -101,6 +143,16 @@ __global__ __launch_bounds__(SW * 64) void align_small_kernel(const int32_t* __r
                                                               int32_t* __restrict__ perm,
                                                               int32_t* __restrict__ inv) {
     extern __shared__ int lds[];
+    if (n <= 64) {  // block-uniform
+        if (threadIdx.x >= 64) return;
+        const int l = threadIdx.x;
+        if (E <= 64) align_wave<1>(ids, n, E, counts, offsets, perm, inv, l);
+        else if (E <= 128) align_wave<2>(ids, n, E, counts, offsets, perm, inv, l);
+        else if (E <= 256) align_wave<4>(ids, n, E, counts, offsets, perm, inv, l);
+        else if (E <= 512) align_wave<8>(ids, n, E, counts, offsets, perm, inv, l);
+        else align_wave<16>(ids, n, E, counts, offsets, perm, inv, l);
+        return;
+    }
     align_block(ids, n, E, counts, offsets, perm, inv, lds);
 }
 
@@ -123,6 +175,10 @@ __global__ __launch_bounds__(SW * 64) void topk_align_small_kernel(
         topk_token<NPL>(logits + (size_t)t * E, bias, E, k, ids + (size_t)t * k, w + (size_t)t * k,
                         ids_s + t * k, lane);
     __syncthreads();
+    if (n <= 64) {  // block-uniform
+        if (wave == 0) align_wave<NPL>(ids_s, n, E, counts, offsets, perm, inv, lane);
+        return;
+    }
     align_block(ids_s, n, E, counts, offsets, perm, inv, lds + ((n + 3) & ~3));
 }
 

@@ -80,8 +80,11 @@ def test_router_logits(name, T):
 # ---------------------------------------------------------------------------
 # alignment
 # ---------------------------------------------------------------------------
+# (up to 64 slots take the one-wavefront path: (8, 8, 128) is exactly 64,
+# (7, 8, 1024) the largest expert count, (4, 6, 257) a count past a power of 2)
 ALIGN_CASES = [(1, 8, 128), (64, 2, 8), (512, 8, 128), (513, 8, 128), (16384, 8, 256),
-               (1000, 6, 1024), (4096, 8, 128), (3, 1, 1), (700, 16, 1024)]
+               (1000, 6, 1024), (4096, 8, 128), (3, 1, 1), (700, 16, 1024), (8, 8, 128),
+               (7, 8, 1024), (4, 6, 257), (2, 4, 64), (9, 8, 16)]
 
 
 @pytest.mark.parametrize("T,k,E", ALIGN_CASES)
