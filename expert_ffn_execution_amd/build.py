@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libftmoe.so")
 SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip",
-           "ffn_stream.hip", "combine.hip", "step.cpp"]
+           "ffn_stream.hip", "combine.hip", "step.cpp", "host_ffn.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -26,8 +26,19 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           f"-I{os.path.join(ROOT, 'include')}"]
 
 
+# host-only C++ (no device code): the host compiler
+HOST_SOURCES = {"host_ffn.cpp"}
+HOST_CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-pthread", f"-I{os.path.join(ROOT, 'include')}"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+    if src in HOST_SOURCES:
+        cmd = ["g++", *HOST_CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"g++ failed for {src}:\n{r.stderr}")
+        return obj
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +56,7 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -31,7 +31,7 @@ EXPORTS = [
     "ft_set_profile_events", "ft_moe_combine", "ft_slot_cache_create", "ft_slot_cache_destroy",
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
-    "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy",
+    "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
 ]
 
 
@@ -111,6 +111,7 @@ def load() -> C.CDLL:
         "ft_slot_cache_evict": [P, I32, I32],
         "ft_slot_cache_stats": [P, C.POINTER(CacheStats)],
         "ft_slot_cache_lookup": [P, I32, I32],
+        "ft_host_expert_ffn": [I32, I32, I32, P, P, I32, I32, P, I32],
         "ft_slot_cache_resize": [P, I32, P, P],
         "ft_moe_step_run": [C.POINTER(MoeStep), P],
         "ft_moe_graph_create": [C.POINTER(MoeStep), P, C.POINTER(P)],
@@ -264,6 +265,21 @@ def ffn(wts: MoeWeights, x: torch.Tensor, k: int, perm: torch.Tensor, offsets: t
     _check(load().ft_moe_ffn(C.byref(wts), _p(x), _dt(x), T, k, _p(perm), _p(offsets),
                              _p(slot_of_expert), _p(y), _dt(y), _p(ws), ws.numel(),
                              _stream(stream)))
+    return y
+
+
+def host_expert_ffn(slot: torch.Tensor, x: torch.Tensor, H: int, I: int, n_threads: int = 8,
+                    y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ft_host_expert_ffn: one bf16 expert's FFN on host cores.  slot: host
+    uint8 view of the expert's slot; x [T, H] bf16 host.  Returns y [T, H] fp32."""
+    if slot.is_cuda or x.is_cuda:
+        raise FtError(ERR_INVALID_ARG, "host_expert_ffn takes host tensors")
+    x = x.contiguous()
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32)
+    _check(load().ft_host_expert_ffn(BF16, H, I, slot.data_ptr(), x.data_ptr(), BF16, T,
+                                     y.data_ptr(), n_threads))
     return y
 
 

@@ -14,16 +14,50 @@ the map of layer l+1.  For prefill every expert of the next layer is
 prefetched: a prefill batch routes to nearly all experts, so the whole next
 layer streams in while the current one computes (FreeToken hub article,
 paragraph on prefill overlap).
+
+Hybrid decode (``hybrid=True``): the pages' bandwidth-adaptive split of cache
+misses.  Of the m experts of layer l+1 that are neither resident nor in
+flight, n = split_misses(m, Bp, Bh) are copied to the GPU as before and the
+rest are computed on host cores straight from the pinned pool
+(ft_host_expert_ffn), in a background thread that overlaps the GPU's work on
+layer l; their rows are written into layer l+1's y_perm before its combine.
+Bp (pinned host-to-device GB/s) and Bh (host FFN GB/s of expert weights) come
+from ``calibrate()`` (chenxutan.com article, "瓶颈为什么是带宽而不是容量", the
+q* strategy; freelamp.com article, section 2.1).
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+import threading
+import time
 from typing import List, Optional
 
 import torch
 
 from . import ftmoe as ft
 from . import synth
+
+
+def split_misses(m: int, bp: float, bh: float) -> int:
+    """How many of m missed experts to copy to the GPU; the rest run on the CPU.
+
+    Copying n experts takes n*W/bp and computing m - n on the CPU (m - n)*W/bh;
+    the two overlap, so the step waits for the slower one.  The balance point
+    is n* = m*bp/(bp + bh) (the pages print the ratio garbled; balancing the
+    two sides gives this form): take whichever neighbouring integer finishes
+    sooner."""
+    if m <= 0:
+        return 0
+    if bh <= 0:
+        return m
+    if bp <= 0:
+        return 0
+    q = m * bp / (bp + bh)
+    lo = min(m, max(0, int(q)))
+    hi = min(m, lo + 1)
+    cost = lambda n: max(n / bp, (m - n) / bh)
+    return lo if cost(lo) <= cost(hi) else hi
 
 
 @dataclasses.dataclass
@@ -35,6 +69,7 @@ class StackStats:
     misses: int = 0
     bytes_h2d: int = 0
     prefetch_warnings: int = 0
+    cpu_experts: int = 0       # hybrid decode: missed experts computed on the host
 
     @property
     def hit_rate(self) -> float:
@@ -75,6 +110,8 @@ class SlotStack:
                        for _ in range(n_layers)]
         self.copy_stream = torch.cuda.Stream(device=dev)
         self.stats = StackStats()
+        self.bp = self.bh = 0.0   # GB/s, from calibrate()
+        self.host_threads = max(1, min(16, len(os.sched_getaffinity(0))))
 
     # ------------------------------------------------------------------
     def _route(self, l: int, x: torch.Tensor, logits: Optional[torch.Tensor] = None):
@@ -88,9 +125,12 @@ class SlotStack:
         counts, offsets, perm, inv = ft.align(ids, sh.E)
         counts_h = torch.empty(sh.E, dtype=torch.int32, pin_memory=True)
         counts_h.copy_(counts, non_blocking=True)
+        perm_h = torch.empty(perm.shape, dtype=torch.int32, pin_memory=True)
+        perm_h.copy_(perm, non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
-        return dict(ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, counts_h=counts_h, ev=ev)
+        return dict(ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, counts_h=counts_h,
+                    perm_h=perm_h, ev=ev)
 
     def _experts_of(self, r) -> List[int]:
         r["ev"].synchronize()
@@ -112,12 +152,70 @@ class SlotStack:
         if status == ft.WARN_OVERLAP_DISABLED:
             self.stats.prefetch_warnings += 1
 
+    # ---- hybrid decode: the CPU share of a layer's misses -----------------
+    def calibrate(self, reps: int = 5):
+        """Measure Bp (pinned host-to-device copy of one expert slot) and Bh
+        (host FFN of one expert at T = 1, bytes of weights per second), GB/s."""
+        sh = self.sh
+        src = self.host[0][0]
+        dst = torch.empty_like(src, device=self.dev)
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        self.bp = reps * self.expert_bytes / (time.perf_counter() - t) / 1e9
+        x = torch.zeros((1, sh.H), dtype=torch.bfloat16)
+        ft.host_expert_ffn(self.host[0][0], x, sh.H, sh.I, self.host_threads)
+        t = time.perf_counter()
+        for e in range(reps):
+            ft.host_expert_ffn(self.host[0][e % sh.E], x, sh.H, sh.I, self.host_threads)
+        self.bh = reps * self.expert_bytes / (time.perf_counter() - t) / 1e9
+        return self.bp, self.bh
+
+    def _cpu_share(self, l: int, need: List[int]) -> List[int]:
+        """Routed experts of layer l's demand to compute on the host: the
+        misses beyond split_misses(m, Bp, Bh)."""
+        miss = [e for e in need if e < self.sh.E and self.cache.lookup(l, e) < 0]
+        return miss[split_misses(len(miss), self.bp, self.bh):]
+
+    def _start_cpu(self, l: int, r: dict, experts: List[int], x: torch.Tensor):
+        """Host FFN of `experts` on their rows of layer l, in a background
+        thread; results are (y_perm positions, fp32 rows) pairs."""
+        sh = self.sh
+        cnt = r["counts_h"].tolist()
+        off = [0]
+        for c in cnt:
+            off.append(off[-1] + c)
+        perm = r["perm_h"]
+        xh = x.to("cpu")
+        jobs = []
+        for e in experts:
+            pos = list(range(off[e], off[e + 1]))
+            tok = perm[off[e]:off[e + 1]].long() // sh.k
+            jobs.append((e, pos, xh[tok].contiguous()))
+        out = []
+
+        def work():
+            for e, pos, xe in jobs:
+                out.append((pos, ft.host_expert_ffn(self.host[l][e], xe, sh.H, sh.I,
+                                                    self.host_threads)))
+
+        th = threading.Thread(target=work)
+        th.start()
+        self.stats.cpu_experts += len(experts)
+        return th, out
+
     def forward(self, xs: List[torch.Tensor], prefill: bool = False,
                 out_dtype=torch.bfloat16,
-                logits: Optional[List[torch.Tensor]] = None) -> List[torch.Tensor]:
+                logits: Optional[List[torch.Tensor]] = None,
+                hybrid: bool = False) -> List[torch.Tensor]:
         """One pass through all layers; xs[l] is layer l's input batch [T, H]
         (independent per layer).  `logits` optionally supplies each layer's
-        router logits instead of the router GEMM.  Returns the per-layer outputs."""
+        router logits instead of the router GEMM.  `hybrid` splits each layer's
+        misses between PCIe copies and host cores (decode; needs calibrate()).
+        Returns the per-layer outputs."""
         sh = self.sh
         lg = logits if logits is not None else [None] * self.L
         outs = []
@@ -129,6 +227,11 @@ class SlotStack:
                 self.wts.shared_slot = self.cache.lookup(l, sh.E)
             y = ft.ffn(self.wts, xs[l], sh.k, r["perm"], r["offsets"],
                        slot_of_expert=self.tables[l])
+            if "cpu" in r:  # the host's rows of this layer (its experts were skipped above)
+                th, res = r["cpu"]
+                th.join()
+                for pos, yc in res:
+                    y[torch.tensor(pos, device=self.dev)] = yc.to(self.dev, y.dtype)
             outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared,
                                    out_dtype=out_dtype))
             self.cache.release(l)
@@ -136,6 +239,11 @@ class SlotStack:
                 if prefill:
                     self._prefetch(l + 1, list(range(self.n_exp)))
                 need = self._experts_of(nxt)
+                if hybrid and not prefill:
+                    cpu = self._cpu_share(l + 1, need)
+                    if cpu:
+                        need = [e for e in need if e not in cpu]
+                        nxt["cpu"] = self._start_cpu(l + 1, nxt, cpu, xs[l + 1])
                 if not prefill:
                     self._prefetch(l + 1, need)
                 self._map(l + 1, need)

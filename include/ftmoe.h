@@ -374,6 +374,25 @@ ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
 /* Slot of (layer, expert), or -1 when not cached.  Host query, no device work. */
 int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert);
 
+/* --------------------------------------------------------------------------
+ * Host expert FFN: the CPU side of the bandwidth-adaptive split of cache
+ * misses.  The pages' hybrid backend sends part of a step's missed experts
+ * over PCIe to the GPU and computes the rest on the CPU straight from host
+ * memory, at the same time, in the ratio of the measured PCIe and host
+ * bandwidths so that both finish together (chenxutan.com article, "瓶颈为什么是
+ * 带宽而不是容量", the q* strategy and the MoE backend list; freelamp.com
+ * article, section 2.1).  This call is that CPU share for one expert; the
+ * split is the caller's (expert_ffn_execution_amd/stack.py).
+ *   y[r] = W_down (bf16(silu(W_gate x[r]) * (W_up x[r]))) for r < T, fp32 sums,
+ *   h rounded to bf16 as on the GPU.
+ *   slot: host pointer to one expert slot (ft_expert_layout; FT_BF16 only);
+ *   x [T][H] host, x_dt = FT_BF16; y [T][H] fp32 host; n_threads in [1, 256]
+ *   host threads (a persistent pool; the caller's thread is one of them).
+ * Synchronous; no device work.  Other weight or activation formats return
+ * FT_ERR_INVALID_ARG. */
+ft_status ft_host_expert_ffn(ft_dtype w_dt, int H, int I, const void* slot, const void* x,
+                             ft_dtype x_dt, int T, float* y, int n_threads);
+
 #ifdef __cplusplus
 }
 #endif

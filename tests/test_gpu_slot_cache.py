@@ -178,3 +178,38 @@ def test_resize_between_steps_matches_resident():
         assert st.cache.stats().held == 0
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("bp,bh", [(1.0, 1.0), (1.0, 1e6), (1e-6, 1.0)])
+def test_hybrid_decode_matches_oracle(bp, bh):
+    """Misses split between PCIe copies and host cores (bp:bh sets the share:
+    half, nearly all on the host, all on the host): every layer still matches
+    the oracle, the host rows being the CPU FFN's."""
+    _say("slot stack hybrid decode", bp, bh)
+    L = 3
+    st = SlotStack(SMALL, L, n_slots=12)
+    st.bp, st.bh = bp, bh
+    try:
+        experts = [[unpack_slot(st.host[l, e], SMALL) for e in range(SMALL.E)] for l in range(L)]
+        for step in range(4):
+            xs = _inputs(SMALL, L, 2, 40 + step)
+            lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
+            outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs], hybrid=True)
+            for l in range(L):
+                ids, w = orc.route(lgs[l], SMALL.k, st.biases[l].cpu().numpy())
+                ref = orc.moe_layer(xs[l].cpu(), ids, w, experts[l], "bf16", SMALL.I, out_fmt="f32")
+                check_close(outs[l], ref, "bf16", f"hybrid step {step} layer {l}")
+        assert st.stats.cpu_experts > 0
+        cs = st.cache.stats()
+        assert cs.held == 0
+    finally:
+        st.close()
+
+
+def test_calibrate_measures_both_bandwidths():
+    st = SlotStack(SMALL, 1, n_slots=8)
+    try:
+        bp, bh = st.calibrate()
+        assert bp > 0.1 and bh > 0.01, (bp, bh)
+    finally:
+        st.close()
