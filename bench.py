@@ -357,6 +357,34 @@ def run_slot_stack(args):
     t_dec = timed(st.forward, dec)
     d = {k: getattr(st.stats, k) - getattr(s0, k) for k in
          ("demand", "hits", "prefetch_hits", "misses", "bytes_h2d")}
+    # the same decode steps with each layer's misses split between PCIe copies
+    # and host cores (split_misses with the calibrated Bp, Bh)
+    bp, bh = st.calibrate()
+    log(f"calibration: Bp {bp:.1f} GB/s (pinned H2D of one expert), Bh {bh:.1f} GB/s (host FFN)")
+    hyb = [[synth.gen_x(sh, 1, step=30_000 + s, device=dev, layer=l) for l in range(L)]
+           for s in range(steps)]
+    timed(lambda xs: st.forward(xs, hybrid=True), warm)
+    s2 = dataclasses_replace(st.stats)
+    t_hyb = timed(lambda xs: st.forward(xs, hybrid=True), hyb)
+    t_off = timed(st.forward, [[synth.gen_x(sh, 1, step=40_000 + s, device=dev, layer=l)
+                                for l in range(L)] for s in range(steps)])
+    h = {k: getattr(st.stats, k) - getattr(s2, k) for k in
+         ("demand", "misses", "cpu_experts", "bytes_h2d")}
+    # a tight budget (128 slots for 8 layers of 128 experts): misses are the rule
+    st.resize(128)
+    tight = {}
+    for mode in ("offload", "hybrid"):
+        xs_t = [[synth.gen_x(sh, 1, step=50_000 + s, device=dev, layer=l) for l in range(L)]
+                for s in range(steps)]
+        fwd = (lambda xs: st.forward(xs, hybrid=True)) if mode == "hybrid" else st.forward
+        timed(fwd, warm)
+        s3 = dataclasses_replace(st.stats)
+        tt = timed(fwd, xs_t)
+        tight[mode] = {"ms_per_step": tt / steps * 1e3,
+                       "misses_per_step": (st.stats.misses - s3.misses) / steps,
+                       "host_experts_per_step": (st.stats.cpu_experts - s3.cpu_experts) / steps,
+                       "h2d_bytes_per_step": (st.stats.bytes_h2d - s3.bytes_h2d) / steps}
+    st.resize(L * synth.SLOT_STACK_SLOTS_PER_LAYER)
     pre = [synth.gen_x(sh, T_pre, step=20_000, device=dev, layer=l) for l in range(L)]
     t_res_pre = timed(resident_pass, [pre])
     s1 = dataclasses_replace(st.stats)
@@ -388,6 +416,15 @@ def run_slot_stack(args):
             "prefill_h2d_gbs": pre_bytes / t_pre / 1e9,
             "prefill_tokens_per_s": T_pre / t_pre,
             "prefetch_warnings": st.stats.prefetch_warnings,
+        },
+        "hybrid_decode": {
+            "bp_gbs": bp, "bh_gbs": bh,
+            "ms_per_step": t_hyb / steps * 1e3,
+            "offload_ms_per_step_same_state": t_off / steps * 1e3,
+            "host_experts_per_step": h["cpu_experts"] / steps,
+            "misses_per_step": h["misses"] / steps,
+            "h2d_bytes_per_step": h["bytes_h2d"] / steps,
+            "tight_budget_128_slots": tight,
         },
     }
     print(json.dumps(line), flush=True)

@@ -13,11 +13,16 @@
 //
 // Arithmetic as on the GPU: bf16 weights and activations, fp32 sums, h =
 // silu(g) * u rounded to bf16 before the down projection, fp32 output rows.
-// Rows are split over a small persistent thread pool (gate/up rows, then down
-// rows); each dot product keeps 16 separate fp32 partial sums so that the
-// compiler can vectorise it without reassociating, and the partial sums are
-// added in a fixed order (deterministic whatever the thread count: every row
-// is summed by one thread).
+// Weight rows are split over a small persistent thread pool (gate/up rows of
+// every expert of the job, then down rows); each dot product keeps 16
+// separate fp32 partial sums so that the compiler can vectorise it without
+// reassociating, and the partial sums are added in a fixed order
+// (deterministic whatever the thread count or the job's expert list: every
+// output element is one thread's one dot product).
+//
+// ft_host_moe_ffn_submit queues a whole layer's CPU share as one job for a
+// dispatcher thread, so the caller's thread only enqueues and later waits
+// (a decode step's CPU experts then overlap the GPU's copies and kernels).
 //
 // Plain host C++ (built with the host compiler, no device pass): only the C
 // header and the library's error helpers.
@@ -25,6 +30,8 @@
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
+#include <deque>
+#include <memory>
 #include <functional>
 #include <mutex>
 #include <thread>
@@ -44,13 +51,23 @@ void clear_error();
 
 namespace {
 
-// ---- a persistent pool: run(n, f) calls f(0..n-1) on n threads (the caller is 0)
+inline void cpu_relax() {
+#if defined(__x86_64__) || defined(__i386__)
+    __builtin_ia32_pause();
+#endif
+}
+
+// ---- a persistent pool: run(n, f) calls f(0..n-1) on n threads (the caller is 0).
+// Workers spin for a short while after each job before sleeping, so the
+// back-to-back phases of one job (and of the next layer's job) start without a
+// wake-up from the kernel.
 class Pool {
 public:
     ~Pool() {
         {
             std::lock_guard<std::mutex> g(mu_);
             stop_ = true;
+            agen_.store(~0u, std::memory_order_release);
         }
         cv_.notify_all();
         for (auto& t : th_) t.join();
@@ -62,17 +79,27 @@ public:
             std::lock_guard<std::mutex> g(mu_);
             job_ = &f;
             active_ = n - 1;
-            pending_ = n - 1;
+            pending_.store(n - 1, std::memory_order_relaxed);
             ++gen_;
+            agen_.store(gen_, std::memory_order_release);
         }
         cv_.notify_all();
         f(0);
-        std::unique_lock<std::mutex> g(mu_);
-        done_.wait(g, [&] { return pending_ == 0; });
+        for (int s = 0; pending_.load(std::memory_order_acquire) != 0; ++s) {
+            if (s < kSpin) {
+                cpu_relax();
+                continue;
+            }
+            std::unique_lock<std::mutex> g(mu_);
+            done_.wait(g, [&] { return pending_.load(std::memory_order_acquire) == 0; });
+            break;
+        }
+        std::lock_guard<std::mutex> g(mu_);
         job_ = nullptr;
     }
 
 private:
+    static constexpr int kSpin = 1 << 16;  // ~50-100 us of pause loops
     void grow(int want) {
         while ((int)th_.size() < want) {
             const int id = (int)th_.size() + 1;
@@ -82,6 +109,8 @@ private:
     void loop(int id) {
         unsigned seen = 0;
         for (;;) {
+            for (int s = 0; s < kSpin && agen_.load(std::memory_order_acquire) == seen; ++s)
+                cpu_relax();
             const std::function<void(int)>* f;
             {
                 std::unique_lock<std::mutex> g(mu_);
@@ -92,8 +121,10 @@ private:
                 f = job_;
             }
             (*f)(id);
-            std::lock_guard<std::mutex> g(mu_);
-            if (--pending_ == 0) done_.notify_all();
+            if (pending_.fetch_sub(1, std::memory_order_acq_rel) == 1) {
+                std::lock_guard<std::mutex> g(mu_);
+                done_.notify_all();
+            }
         }
     }
     std::vector<std::thread> th_;
@@ -101,7 +132,9 @@ private:
     std::condition_variable cv_, done_;
     const std::function<void(int)>* job_ = nullptr;
     unsigned gen_ = 0;
-    int active_ = 0, pending_ = 0;
+    std::atomic<unsigned> agen_{0};
+    std::atomic<int> pending_{0};
+    int active_ = 0;
     bool stop_ = false;
 };
 
@@ -147,6 +180,47 @@ DotFn pick_dot() {
     return (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) ? dot_avx2 : dot_generic;
 }
 
+// one expert's share of a job: its slot, its output rows [b, b + n) and the
+// first of its rows in the aligned order
+struct Span {
+    const uint16_t* w;
+    int b, n, lo;
+};
+
+// out[b + r] = FFN(xf[b + r]) for every span; xf [rows][H], hf [rows][I] scratch.
+// Gate/up weight rows of all spans are split over the threads in contiguous
+// ranges, then the down rows likewise.
+void ffn_spans(const std::vector<Span>& sp, int H, int I, const float* xf, float* hf, float* out,
+               int nt) {
+    static const DotFn dot = pick_dot();
+    const long n_sp = (long)sp.size();
+    pool().run(nt, [&](int t) {
+        const long u0 = n_sp * I * t / nt, u1 = n_sp * I * (t + 1) / nt;
+        for (long u = u0; u < u1; ++u) {
+            const Span& s = sp[u / I];
+            const int i = (int)(u % I);
+            const uint16_t* wg = s.w + (size_t)i * H;
+            const uint16_t* wu = s.w + (size_t)I * H + (size_t)i * H;
+            for (int r = 0; r < s.n; ++r) {
+                const float* a = xf + (size_t)(s.b + r) * H;
+                const float g = dot(wg, a, H);
+                const float v = dot(wu, a, H);
+                hf[(size_t)(s.b + r) * I + i] = round_bf16(g / (1.0f + std::exp(-g)) * v);
+            }
+        }
+    });
+    pool().run(nt, [&](int t) {
+        const long u0 = n_sp * H * t / nt, u1 = n_sp * H * (t + 1) / nt;
+        for (long u = u0; u < u1; ++u) {
+            const Span& s = sp[u / H];
+            const int d = (int)(u % H);
+            const uint16_t* wd = s.w + 2 * (size_t)I * H + (size_t)d * I;
+            for (int r = 0; r < s.n; ++r)
+                out[(size_t)(s.b + r) * H + d] = dot(wd, hf + (size_t)(s.b + r) * I, I);
+        }
+    });
+}
+
 }  // namespace
 
 extern "C" ft_status ft_host_expert_ffn(ft_dtype w_dt, int H, int I, const void* slot, const void* x,
@@ -157,28 +231,162 @@ extern "C" ft_status ft_host_expert_ffn(ft_dtype w_dt, int H, int I, const void*
     HOST_CHECK_ARG(T >= 0 && n_threads >= 1 && n_threads <= 256, "T >= 0 and n_threads in [1, 256]");
     HOST_CHECK_ARG(T == 0 || (slot && x && y), "null slot / x / y");
     if (T == 0) return FT_OK;
-    static const DotFn dot = pick_dot();
-    const uint16_t* wg = static_cast<const uint16_t*>(slot);
-    const uint16_t* wu = wg + (size_t)I * H;
-    const uint16_t* wd = wu + (size_t)I * H;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     std::vector<float> xf((size_t)T * H), hf((size_t)T * I);
     for (size_t i = 0; i < xf.size(); ++i) xf[i] = bf16_to_f32(xb[i]);
-    const int nt = n_threads;
-    // gate/up rows, then down rows, each split over the threads in contiguous ranges
-    pool().run(nt, [&](int t) {
-        const int i0 = (int)((long)I * t / nt), i1 = (int)((long)I * (t + 1) / nt);
-        for (int i = i0; i < i1; ++i)
-            for (int r = 0; r < T; ++r) {
-                const float g = dot(wg + (size_t)i * H, xf.data() + (size_t)r * H, H);
-                const float u = dot(wu + (size_t)i * H, xf.data() + (size_t)r * H, H);
-                hf[(size_t)r * I + i] = round_bf16(g / (1.0f + std::exp(-g)) * u);
-            }
-    });
-    pool().run(nt, [&](int t) {
-        const int d0 = (int)((long)H * t / nt), d1 = (int)((long)H * (t + 1) / nt);
-        for (int d = d0; d < d1; ++d)
-            for (int r = 0; r < T; ++r) y[(size_t)r * H + d] = dot(wd + (size_t)d * I, hf.data() + (size_t)r * I, I);
-    });
+    ffn_spans({Span{static_cast<const uint16_t*>(slot), 0, T, 0}}, H, I, xf.data(), hf.data(), y, n_threads);
     return FT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// asynchronous jobs: one dispatcher thread runs queued jobs in order
+struct ft_host_job_s {
+    ft_host_moe_job_desc d;
+    std::vector<Span> spans;
+    std::vector<int32_t> src;  // token of each output row
+    int n_rows = 0;
+    std::mutex mu;
+    std::condition_variable cv;
+    bool done = false;
+    ft_status st = FT_OK;
+};
+
+namespace {
+
+void run_job(ft_host_job* j) {
+    const ft_host_moe_job_desc& d = j->d;
+    const int H = d.H, I = d.I, n = j->n_rows;
+    const uint16_t* xb = static_cast<const uint16_t*>(d.x);
+    std::vector<float> xf((size_t)n * H), hf((size_t)n * I);
+    const int nt = d.n_threads;
+    pool().run(nt, [&](int t) {  // gather and widen the rows' inputs
+        for (long r = (long)n * t / nt; r < (long)n * (t + 1) / nt; ++r) {
+            const uint16_t* src = xb + (size_t)j->src[r] * H;
+            float* dst = xf.data() + (size_t)r * H;
+            for (int c = 0; c < H; ++c) dst[c] = bf16_to_f32(src[c]);
+        }
+    });
+    ffn_spans(j->spans, H, I, xf.data(), hf.data(), d.rows, nt);
+}
+
+class Dispatcher {
+public:
+    Dispatcher() {
+        pool();  // constructed first, so destroyed after this dispatcher
+        th_ = std::thread([this] { loop(); });
+    }
+    ~Dispatcher() {
+        {
+            std::lock_guard<std::mutex> g(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        th_.join();
+    }
+    void submit(ft_host_job* j) {
+        {
+            std::lock_guard<std::mutex> g(mu_);
+            q_.push_back(j);
+        }
+        cv_.notify_one();
+    }
+
+private:
+    void loop() {
+        for (;;) {
+            ft_host_job* j;
+            {
+                std::unique_lock<std::mutex> g(mu_);
+                cv_.wait(g, [&] { return stop_ || !q_.empty(); });
+                if (q_.empty()) return;  // stopping with nothing queued
+                j = q_.front();
+                q_.pop_front();
+            }
+            run_job(j);
+            {
+                std::lock_guard<std::mutex> g(j->mu);
+                j->done = true;
+            }
+            j->cv.notify_all();
+        }
+    }
+    std::thread th_;
+    std::mutex mu_;
+    std::condition_variable cv_;
+    std::deque<ft_host_job*> q_;
+    bool stop_ = false;
+};
+
+Dispatcher& dispatcher() {
+    static Dispatcher d;
+    return d;
+}
+
+}  // namespace
+
+extern "C" ft_status ft_host_moe_ffn_submit(const ft_host_moe_job_desc* d, ft_host_job** job, int* n_rows) {
+    ft::clear_error();
+    HOST_CHECK_ARG(d && job && n_rows, "null descriptor / job / n_rows");
+    *job = nullptr;
+    *n_rows = 0;
+    HOST_CHECK_ARG(d->w_dt == FT_BF16 && d->x_dt == FT_BF16, "host MoE FFN: bf16 weights and activations only");
+    HOST_CHECK_ARG(d->H > 0 && d->I > 0 && d->H % 64 == 0 && d->I % 64 == 0,
+                   "H and I must be positive multiples of 64");
+    HOST_CHECK_ARG(d->E > 0 && d->k > 0 && d->k <= d->E && d->T >= 0 && d->n_experts >= 0 &&
+                       d->n_experts <= d->E && d->max_rows >= 0,
+                   "need E > 0, 0 < k <= E, T >= 0, 0 <= n_experts <= E, max_rows >= 0");
+    HOST_CHECK_ARG(d->n_threads >= 1 && d->n_threads <= 256, "n_threads in [1, 256]");
+    HOST_CHECK_ARG(d->slot_stride >= (size_t)3 * d->H * d->I * 2, "slot_stride below one bf16 expert");
+    HOST_CHECK_ARG(d->n_experts == 0 || (d->experts && d->offsets && d->pool),
+                   "null experts / offsets / pool");
+    const long TK = (long)d->T * d->k;
+    auto j = std::make_unique<ft_host_job>();
+    j->d = *d;
+    std::vector<char> seen(d->E, 0);
+    int b = 0;
+    for (int q = 0; q < d->n_experts; ++q) {
+        const int e = d->experts[q];
+        HOST_CHECK_ARG(e >= 0 && e < d->E && !seen[e], "experts must be distinct and in [0, E)");
+        seen[e] = 1;
+        const int lo = d->offsets[e], hi = d->offsets[e + 1];
+        HOST_CHECK_ARG(0 <= lo && lo <= hi && hi <= TK, "offsets of expert %d out of [0, T*k]", e);
+        if (hi == lo) continue;
+        HOST_CHECK_ARG(d->perm && d->x, "null perm / x");
+        if ((long)b + (hi - lo) > d->max_rows)
+            return ft::set_error(FT_ERR_CAPACITY, "the experts hold more than max_rows = %d rows", d->max_rows);
+        for (int r = lo; r < hi; ++r) {
+            HOST_CHECK_ARG(d->perm[r] >= 0 && d->perm[r] < TK, "perm[%d] out of [0, T*k)", r);
+            j->src.push_back(d->perm[r] / d->k);
+        }
+        j->spans.push_back(Span{reinterpret_cast<const uint16_t*>(static_cast<const char*>(d->pool) +
+                                                                  (size_t)e * d->slot_stride),
+                                b, hi - lo, lo});
+        b += hi - lo;
+    }
+    HOST_CHECK_ARG(b == 0 || (d->rows && d->pos), "null rows / pos");
+    for (const Span& s : j->spans)
+        for (int r = 0; r < s.n; ++r) d->pos[s.b + r] = s.lo + r;
+    j->n_rows = b;
+    j->d.experts = nullptr;  // the list is not read after this call
+    *n_rows = b;
+    ft_host_job* h = j.release();
+    if (b == 0) {
+        h->done = true;  // nothing to compute
+    } else {
+        dispatcher().submit(h);
+    }
+    *job = h;
+    return FT_OK;
+}
+
+extern "C" ft_status ft_host_job_wait(ft_host_job* job) {
+    ft::clear_error();
+    HOST_CHECK_ARG(job, "null job");
+    {
+        std::unique_lock<std::mutex> g(job->mu);
+        job->cv.wait(g, [&] { return job->done; });
+    }
+    const ft_status st = job->st;
+    delete job;
+    return st;
 }

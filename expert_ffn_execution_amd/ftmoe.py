@@ -32,6 +32,7 @@ EXPORTS = [
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
+    "ft_host_moe_ffn_submit", "ft_host_job_wait",
 ]
 
 
@@ -78,6 +79,14 @@ class CacheStats(C.Structure):
                 ("in_flight", C.c_int), ("n_slots", C.c_int)]
 
 
+class HostMoeJobDesc(C.Structure):
+    _fields_ = [("w_dt", C.c_int), ("E", C.c_int), ("H", C.c_int), ("I", C.c_int), ("k", C.c_int),
+                ("pool", C.c_void_p), ("slot_stride", C.c_size_t), ("experts", C.c_void_p),
+                ("n_experts", C.c_int), ("offsets", C.c_void_p), ("perm", C.c_void_p),
+                ("x", C.c_void_p), ("x_dt", C.c_int), ("T", C.c_int), ("rows", C.c_void_p),
+                ("pos", C.c_void_p), ("max_rows", C.c_int), ("n_threads", C.c_int)]
+
+
 _lib = None
 
 
@@ -112,6 +121,8 @@ def load() -> C.CDLL:
         "ft_slot_cache_stats": [P, C.POINTER(CacheStats)],
         "ft_slot_cache_lookup": [P, I32, I32],
         "ft_host_expert_ffn": [I32, I32, I32, P, P, I32, I32, P, I32],
+        "ft_host_moe_ffn_submit": [C.POINTER(HostMoeJobDesc), C.POINTER(P), C.POINTER(C.c_int)],
+        "ft_host_job_wait": [P],
         "ft_slot_cache_resize": [P, I32, P, P],
         "ft_moe_step_run": [C.POINTER(MoeStep), P],
         "ft_moe_graph_create": [C.POINTER(MoeStep), P, C.POINTER(P)],
@@ -278,9 +289,55 @@ def host_expert_ffn(slot: torch.Tensor, x: torch.Tensor, H: int, I: int, n_threa
     T = x.shape[0]
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32)
+    if (y.is_cuda or y.dtype != torch.float32 or tuple(y.shape) != (T, H)
+            or not y.is_contiguous()):
+        raise FtError(ERR_INVALID_ARG, "y must be a contiguous host fp32 tensor [T, H]")
     _check(load().ft_host_expert_ffn(BF16, H, I, slot.data_ptr(), x.data_ptr(), BF16, T,
                                      y.data_ptr(), n_threads))
     return y
+
+
+class HostJob:
+    """A queued ft_host_moe_ffn_submit job: holds the buffers it reads and
+    writes until wait()."""
+
+    def __init__(self, handle, n_rows: int, keep):
+        self.handle, self.n_rows, self._keep = handle, n_rows, keep
+
+    def wait(self):
+        """ft_host_job_wait; idempotent on the Python side."""
+        if self.handle is not None:
+            h, self.handle = self.handle, None
+            _check(load().ft_host_job_wait(h))
+        return self.n_rows
+
+
+def host_moe_ffn_submit(pool: torch.Tensor, E: int, H: int, I: int, k: int,
+                        experts: Sequence[int], offsets: torch.Tensor, perm: torch.Tensor,
+                        x: torch.Tensor, rows: torch.Tensor, pos: torch.Tensor,
+                        n_threads: int = 8) -> HostJob:
+    """ft_host_moe_ffn_submit: the host FFN of `experts` on their rows of one
+    layer, queued on the library's host threads.  pool [E(+shared)][stride]
+    uint8 host (one layer's slots); offsets [E+1] / perm [T*k] int32 host as
+    ft_moe_align wrote them; x [T, H] bf16 host; rows [max_rows, H] fp32 and
+    pos [max_rows] int64 host outputs.  Returns the job (its n_rows is known
+    at once); call .wait() before reading rows / pos."""
+    for t in (pool, offsets, perm, x, rows, pos):
+        if t.is_cuda or not t.is_contiguous():
+            raise FtError(ERR_INVALID_ARG, "host_moe_ffn_submit takes contiguous host tensors")
+    if (offsets.dtype != torch.int32 or perm.dtype != torch.int32 or x.dtype != torch.bfloat16
+            or rows.dtype != torch.float32 or pos.dtype != torch.int64 or rows.dim() != 2
+            or rows.shape[1] != H or pos.shape[0] < rows.shape[0]):
+        raise FtError(ERR_INVALID_ARG, "host_moe_ffn_submit: tensor dtypes / shapes")
+    ex = (C.c_int32 * len(experts))(*experts)
+    d = HostMoeJobDesc(BF16, E, H, I, k, pool.data_ptr(), pool.stride(0) * pool.element_size(),
+                       C.cast(ex, C.c_void_p), len(experts), offsets.data_ptr(), perm.data_ptr(),
+                       x.data_ptr(), BF16, x.shape[0], rows.data_ptr(), pos.data_ptr(),
+                       rows.shape[0], n_threads)
+    h = C.c_void_p()
+    n = C.c_int()
+    _check(load().ft_host_moe_ffn_submit(C.byref(d), C.byref(h), C.byref(n)))
+    return HostJob(h, n.value, (pool, offsets, perm, x, rows, pos))
 
 
 def combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, w: torch.Tensor, n_shared: int = 0,

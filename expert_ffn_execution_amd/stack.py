@@ -18,9 +18,10 @@ paragraph on prefill overlap).
 Hybrid decode (``hybrid=True``): the pages' bandwidth-adaptive split of cache
 misses.  Of the m experts of layer l+1 that are neither resident nor in
 flight, n = split_misses(m, Bp, Bh) are copied to the GPU as before and the
-rest are computed on host cores straight from the pinned pool
-(ft_host_expert_ffn), in a background thread that overlaps the GPU's work on
-layer l; their rows are written into layer l+1's y_perm before its combine.
+rest are computed on host cores straight from the pinned pool, as one job
+queued on the library's host threads (ft_host_moe_ffn_submit) that overlaps
+the GPU's work on layer l and the copies of layer l+1; their rows are written
+into layer l+1's y_perm before its combine.
 Bp (pinned host-to-device GB/s) and Bh (host FFN GB/s of expert weights) come
 from ``calibrate()`` (chenxutan.com article, "瓶颈为什么是带宽而不是容量", the
 q* strategy; freelamp.com article, section 2.1).
@@ -29,7 +30,6 @@ from __future__ import annotations
 
 import dataclasses
 import os
-import threading
 import time
 from typing import List, Optional
 
@@ -98,6 +98,11 @@ class SlotStack:
                                shape.I, stage[e])
             self.host[l].copy_(stage)
         del stage
+        torch.cuda.synchronize()
+        # one CPU read per 4 KB page of the pool: the first CPU pass over pinned
+        # pages written by DMA ran at 6 GB/s, later passes at 85-95 GB/s (host
+        # FFN of cold experts), so hybrid decode would pay it on its first misses
+        int(self.host.view(-1)[::4096].sum())
         self.slots = torch.empty((n_slots, self.stride), dtype=torch.uint8, device=dev)
         self.cache = ft.SlotCache(n_layers, self.n_exp, self.expert_bytes, self.host,
                                   self.slots, scope)
@@ -110,11 +115,18 @@ class SlotStack:
                        for _ in range(n_layers)]
         self.copy_stream = torch.cuda.Stream(device=dev)
         self.stats = StackStats()
+        self._hbufs = [dict() for _ in range(n_layers)]
+        # host FFN outputs, two sets used by alternate layers: a set is refilled
+        # only after the copy that read it two layers earlier has finished
+        self._rows = [None, None]
+        self._rows_ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.bp = self.bh = 0.0   # GB/s, from calibrate()
-        self.host_threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        # host FFN threads: 8 measured fastest on a 16-core share (84-96 GB/s)
+        self.host_threads = max(1, min(8, len(os.sched_getaffinity(0))))
 
     # ------------------------------------------------------------------
-    def _route(self, l: int, x: torch.Tensor, logits: Optional[torch.Tensor] = None):
+    def _route(self, l: int, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+               want_x: bool = False):
         sh = self.sh
         T = x.shape[0]
         if logits is None:
@@ -123,14 +135,31 @@ class SlotStack:
         else:
             ids, w, _ = ft.route(T, sh.E, sh.k, logits=logits, bias=self.biases[l])
         counts, offsets, perm, inv = ft.align(ids, sh.E)
-        counts_h = torch.empty(sh.E, dtype=torch.int32, pin_memory=True)
-        counts_h.copy_(counts, non_blocking=True)
-        perm_h = torch.empty(perm.shape, dtype=torch.int32, pin_memory=True)
-        perm_h.copy_(perm, non_blocking=True)
-        ev = torch.cuda.Event()
+        hb = self._host_bufs(l, T)
+        hb["counts"].copy_(counts, non_blocking=True)
+        if want_x:  # the host FFN's inputs, ready with the routing (no wait on later work)
+            hb["offsets"].copy_(offsets, non_blocking=True)
+            hb["perm"].copy_(perm, non_blocking=True)
+            hb["x"].copy_(x, non_blocking=True)
+        ev = hb["ev"]
         ev.record()
-        return dict(ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, counts_h=counts_h,
-                    perm_h=perm_h, ev=ev)
+        return dict(ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, counts_h=hb["counts"],
+                    hb=hb, ev=ev)
+
+    def _host_bufs(self, l: int, T: int) -> dict:
+        """Layer l's pinned read-back buffers for a batch of T tokens, reused
+        from step to step (each is read on the host before the next step
+        writes it again)."""
+        hb = self._hbufs[l]
+        if hb.get("T") != T:
+            sh = self.sh
+            pin = dict(pin_memory=True)
+            hb.update(T=T, counts=torch.empty(sh.E, dtype=torch.int32, **pin),
+                      offsets=torch.empty(sh.E + 1, dtype=torch.int32, **pin),
+                      perm=torch.empty(T * sh.k, dtype=torch.int32, **pin),
+                      x=torch.empty((T, sh.H), dtype=torch.bfloat16, **pin),
+                      ev=torch.cuda.Event())
+        return hb
 
     def _experts_of(self, r) -> List[int]:
         r["ev"].synchronize()
@@ -168,10 +197,11 @@ class SlotStack:
         self.bp = reps * self.expert_bytes / (time.perf_counter() - t) / 1e9
         x = torch.zeros((1, sh.H), dtype=torch.bfloat16)
         ft.host_expert_ffn(self.host[0][0], x, sh.H, sh.I, self.host_threads)
+        n = min(4 * reps, sh.E - 1)  # distinct experts: weights come from DRAM, not cache
         t = time.perf_counter()
-        for e in range(reps):
-            ft.host_expert_ffn(self.host[0][e % sh.E], x, sh.H, sh.I, self.host_threads)
-        self.bh = reps * self.expert_bytes / (time.perf_counter() - t) / 1e9
+        for e in range(1, n + 1):
+            ft.host_expert_ffn(self.host[self.L - 1][e], x, sh.H, sh.I, self.host_threads)
+        self.bh = n * self.expert_bytes / (time.perf_counter() - t) / 1e9
         return self.bp, self.bh
 
     def _cpu_share(self, l: int, need: List[int]) -> List[int]:
@@ -180,32 +210,26 @@ class SlotStack:
         miss = [e for e in need if e < self.sh.E and self.cache.lookup(l, e) < 0]
         return miss[split_misses(len(miss), self.bp, self.bh):]
 
-    def _start_cpu(self, l: int, r: dict, experts: List[int], x: torch.Tensor):
-        """Host FFN of `experts` on their rows of layer l, in a background
-        thread; results are (y_perm positions, fp32 rows) pairs."""
-        sh = self.sh
-        cnt = r["counts_h"].tolist()
-        off = [0]
-        for c in cnt:
-            off.append(off[-1] + c)
-        perm = r["perm_h"]
-        xh = x.to("cpu")
-        jobs = []
-        for e in experts:
-            pos = list(range(off[e], off[e + 1]))
-            tok = perm[off[e]:off[e + 1]].long() // sh.k
-            jobs.append((e, pos, xh[tok].contiguous()))
-        out = []
-
-        def work():
-            for e, pos, xe in jobs:
-                out.append((pos, ft.host_expert_ffn(self.host[l][e], xe, sh.H, sh.I,
-                                                    self.host_threads)))
-
-        th = threading.Thread(target=work)
-        th.start()
+    def _start_cpu(self, l: int, r: dict, experts: List[int]):
+        """Queue the host FFN of `experts` on their rows of layer l
+        (ft_host_moe_ffn_submit: the library's host threads run it while this
+        thread goes on enqueueing GPU work).  r must come from _route with
+        want_x (its event already waited on).  Returns (job, set) where
+        set = (rows [n, H] fp32, pos [n] int64, event) pinned buffers."""
+        sh, hb = self.sh, r["hb"]
+        p = l & 1
+        need = hb["T"] * sh.k
+        if self._rows[p] is None or self._rows[p][0].shape[0] < need:
+            self._rows[p] = (torch.empty((need, sh.H), dtype=torch.float32, pin_memory=True),
+                             torch.empty(need, dtype=torch.int64, pin_memory=True))
+        else:
+            self._rows_ev[p].synchronize()  # the copy out of this set two layers ago
+        rows, pos = self._rows[p]
+        job = ft.host_moe_ffn_submit(self.host[l], sh.E, sh.H, sh.I, sh.k, experts,
+                                     hb["offsets"], hb["perm"], hb["x"], rows, pos,
+                                     self.host_threads)
         self.stats.cpu_experts += len(experts)
-        return th, out
+        return job, (rows, pos, self._rows_ev[p])
 
     def forward(self, xs: List[torch.Tensor], prefill: bool = False,
                 out_dtype=torch.bfloat16,
@@ -219,19 +243,22 @@ class SlotStack:
         sh = self.sh
         lg = logits if logits is not None else [None] * self.L
         outs = []
+        want_x = hybrid and not prefill
         r = self._route(0, xs[0], lg[0])
         self._map(0, self._experts_of(r))
         for l in range(self.L):
-            nxt = self._route(l + 1, xs[l + 1], lg[l + 1]) if l + 1 < self.L else None
+            nxt = (self._route(l + 1, xs[l + 1], lg[l + 1], want_x=want_x)
+                   if l + 1 < self.L else None)
             if sh.n_shared:
                 self.wts.shared_slot = self.cache.lookup(l, sh.E)
             y = ft.ffn(self.wts, xs[l], sh.k, r["perm"], r["offsets"],
                        slot_of_expert=self.tables[l])
             if "cpu" in r:  # the host's rows of this layer (its experts were skipped above)
-                th, res = r["cpu"]
-                th.join()
-                for pos, yc in res:
-                    y[torch.tensor(pos, device=self.dev)] = yc.to(self.dev, y.dtype)
+                job, (rows, pos, ev) = r["cpu"]
+                n = job.wait()
+                y.index_copy_(0, pos[:n].to(self.dev, non_blocking=True),
+                              rows[:n].to(self.dev, non_blocking=True).to(y.dtype))
+                ev.record()
             outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared,
                                    out_dtype=out_dtype))
             self.cache.release(l)
@@ -239,11 +266,11 @@ class SlotStack:
                 if prefill:
                     self._prefetch(l + 1, list(range(self.n_exp)))
                 need = self._experts_of(nxt)
-                if hybrid and not prefill:
+                if want_x:
                     cpu = self._cpu_share(l + 1, need)
                     if cpu:
                         need = [e for e in need if e not in cpu]
-                        nxt["cpu"] = self._start_cpu(l + 1, nxt, cpu, xs[l + 1])
+                        nxt["cpu"] = self._start_cpu(l + 1, nxt, cpu)
                 if not prefill:
                     self._prefetch(l + 1, need)
                 self._map(l + 1, need)

@@ -393,6 +393,55 @@ int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert);
 ft_status ft_host_expert_ffn(ft_dtype w_dt, int H, int I, const void* slot, const void* x,
                              ft_dtype x_dt, int T, float* y, int n_threads);
 
+/* --------------------------------------------------------------------------
+ * Host MoE FFN over a list of experts, asynchronous: the whole CPU share of
+ * one layer's missed experts in one job, run on the library's host threads
+ * while the caller goes on enqueueing GPU work (the same passages as
+ * ft_host_expert_ffn: the CPU and the PCIe copies work at the same time).
+ * For the listed experts in list order, and for each row j in
+ * [offsets[e], offsets[e+1]) of expert e in the aligned order (token
+ * t = perm[j] / k), with b counting the output rows up from 0:
+ *   rows[b] = W_down_e bf16(silu(W_gate_e x[t]) * (W_up_e x[t])),  pos[b] = j,
+ * the same arithmetic, and the same bits, as ft_host_expert_ffn.  The caller
+ * moves rows[b] to row pos[b] of the layer's y_perm.
+ * Descriptor (all pointers are host memory):
+ *   w_dt = FT_BF16, x_dt = FT_BF16; E experts, H, I multiples of 64, top-k k;
+ *   pool: expert e's slot at pool + e * slot_stride (ft_expert_layout);
+ *   experts [n_experts] distinct, in [0, E);
+ *   offsets [E+1] and perm [T*k] as ft_moe_align writes them;
+ *   x [T][H]; rows [max_rows][H] fp32 and pos [max_rows] int64, written;
+ *   n_threads in [1, 256].
+ * ft_host_moe_ffn_submit checks the descriptor (FT_ERR_INVALID_ARG; offsets
+ * and perm are read here, so they must be final; FT_ERR_CAPACITY when the
+ * experts hold more than max_rows rows), copies it and the expert list,
+ * queues the job and returns with *job set and *n_rows = the number of output
+ * rows.  Jobs run one at a time, in submission order.  Every buffer the
+ * descriptor names must stay as it is (rows, pos: unread) until
+ * ft_host_job_wait(job) returns: it waits for the job, returns its status and
+ * frees the handle; wait for every job exactly once.  No device work. */
+typedef struct {
+    ft_dtype w_dt;
+    int E, H, I, k;
+    const void* pool;
+    size_t slot_stride;
+    const int32_t* experts;
+    int n_experts;
+    const int32_t* offsets;
+    const int32_t* perm;
+    const void* x;
+    ft_dtype x_dt;
+    int T;
+    float* rows;
+    int64_t* pos;
+    int max_rows;
+    int n_threads;
+} ft_host_moe_job_desc;
+
+typedef struct ft_host_job_s ft_host_job;
+
+ft_status ft_host_moe_ffn_submit(const ft_host_moe_job_desc* d, ft_host_job** job, int* n_rows);
+ft_status ft_host_job_wait(ft_host_job* job);
+
 #ifdef __cplusplus
 }
 #endif

@@ -158,7 +158,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     the C compiler gives them."""
     structs = {"ft_moe_weights": ft.MoeWeights, "ft_moe_step": ft.MoeStep,
                "ft_slot_cache_desc": ft.SlotCacheDesc, "ft_map_stats": ft.MapStats,
-               "ft_cache_stats": ft.CacheStats}
+               "ft_cache_stats": ft.CacheStats, "ft_host_moe_job_desc": ft.HostMoeJobDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ftmoe.h"', 'int main(void) {']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
