@@ -191,8 +191,8 @@ def test_hybrid_decode_matches_oracle(bp, bh):
     st.bp, st.bh = bp, bh
     try:
         experts = [[unpack_slot(st.host[l, e], SMALL) for e in range(SMALL.E)] for l in range(L)]
-        for step in range(4):
-            xs = _inputs(SMALL, L, 2, 40 + step)
+        for step, T in enumerate((2, 5, 1, 3)):  # T changes: read-back buffers are re-sized
+            xs = _inputs(SMALL, L, T, 40 + step)
             lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
             outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs], hybrid=True)
             for l in range(L):
@@ -202,6 +202,32 @@ def test_hybrid_decode_matches_oracle(bp, bh):
         assert st.stats.cpu_experts > 0
         cs = st.cache.stats()
         assert cs.held == 0
+    finally:
+        st.close()
+
+
+def test_full_size_hybrid_decode_matches_oracle():
+    """Two layers of the 35B-A3B layer shape behind 24 slots, with the
+    calibrated bandwidths: misses go both ways, and each layer's output of a
+    few 4-token decode steps matches the oracle."""
+    sh = synth.SLOT_STACK
+    L = 2
+    _say("full-size hybrid decode")
+    st = SlotStack(sh, L, n_slots=24)
+    try:
+        bp, bh = st.calibrate()
+        _say("  calibrated Bp", bp, "Bh", bh)
+        experts = [[unpack_slot(st.host[l, e], sh) for e in range(sh.E)] for l in range(L)]
+        for step in range(3):
+            xs = _inputs(sh, L, 4, 300 + step)
+            lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
+            outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs], hybrid=True)
+            for l in range(L):
+                ids, w = orc.route(lgs[l], sh.k, st.biases[l].cpu().numpy())
+                ref = orc.moe_layer(xs[l].cpu(), ids, w, experts[l], "bf16", sh.I, out_fmt="f32")
+                check_close(outs[l], ref, "bf16", f"full-size hybrid step {step} layer {l}")
+        _say("  host experts", st.stats.cpu_experts, "misses", st.stats.misses)
+        assert st.stats.cpu_experts > 0 and st.stats.bytes_h2d > 0
     finally:
         st.close()
 
