@@ -183,102 +183,113 @@ __global__ __launch_bounds__(SW * 64) void topk_align_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large problems: units of UNIT consecutive slots, one wave each.
+// Large problems: units of UB = 256 consecutive slots, one block of 4 waves each.
 //   1) per-unit histograms hist[u][e]
-//   2) per-expert exclusive scan over units, counts[e]
-//   3) per-unit scatter from offsets[e] + hist[u][e]
+//   2) per-expert exclusive scan over units (in place), counts[e]
+//   3) per-unit scatter: wave w of unit u starts expert e at
+//      offsets[e] + hist[u][e] + (slots of e in the unit's earlier waves)
+// hist is read along units by consecutive experts (coalesced) in step 2.
 // ---------------------------------------------------------------------------
-constexpr int UNIT = 64;
+constexpr int UB = 256;
 
 __global__ __launch_bounds__(256) void unit_hist_kernel(const int32_t* __restrict__ ids, int n,
-                                                        int E, int U, int* __restrict__ hist) {
-    extern __shared__ int lds[];  // [4][E]
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int u = blockIdx.x * 4 + w;
-    int* h = lds + w * E;
-    for (int e = lane; e < E; e += 64) h[e] = 0;
+                                                        int E, int* __restrict__ hist) {
+    extern __shared__ int h[];  // [E]
+    const int u = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) h[e] = 0;
     __syncthreads();
-    if (u < U) {
-        const int f_lo = u * UNIT, f_hi = min(n, f_lo + UNIT);
-        for (int f = f_lo + lane; f < f_hi; f += 64) atomicAdd(&h[ids[f]], 1);
-    }
+    const int f = u * UB + tid;
+    if (f < n) atomicAdd(&h[ids[f]], 1);
     __syncthreads();
-    if (u < U)
-        for (int e = lane; e < E; e += 64) hist[(size_t)u * E + e] = h[e];
+    for (int e = tid; e < E; e += 256) hist[(size_t)u * E + e] = h[e];
 }
 
-__global__ __launch_bounds__(256) void unit_scan_kernel(int* __restrict__ hist, int E, int U,
-                                                        int32_t* __restrict__ counts) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    int carry = 0;
-    for (int u0 = 0; u0 < U; u0 += 64) {
-        const int u = u0 + lane;
-        int v = u < U ? hist[(size_t)u * E + e] : 0;
-        int incl = v;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
-        }
-        if (u < U) hist[(size_t)u * E + e] = carry + incl - v;
-        carry += __shfl(incl, 63, 64);
+// 64 experts per block, one per lane; wave w sums units [U w / 16, U (w + 1) / 16)
+constexpr int SCAN_W = 16;
+__global__ __launch_bounds__(SCAN_W * 64) void unit_scan_kernel(int* __restrict__ hist, int E, int U,
+                                                                int32_t* __restrict__ counts) {
+    __shared__ int part[SCAN_W][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
+    const int u0 = (int)((long)U * w / SCAN_W), u1 = (int)((long)U * (w + 1) / SCAN_W);
+    int s = 0;
+    if (e < E) {
+#pragma unroll 8
+        for (int u = u0; u < u1; ++u) s += hist[(size_t)u * E + e];
     }
-    if (lane == 0) counts[e] = carry;
+    part[w][lane] = s;
+    __syncthreads();
+    int carry = 0;
+    for (int q = 0; q < w; ++q) carry += part[q][lane];
+    if (e < E) {
+        for (int u = u0; u < u1; ++u) {
+            const int v = hist[(size_t)u * E + e];
+            hist[(size_t)u * E + e] = carry;
+            carry += v;
+        }
+        if (w == SCAN_W - 1) counts[e] = carry;
+    }
 }
 
 __global__ __launch_bounds__(256) void unit_scatter_kernel(const int32_t* __restrict__ ids,
-                                                           int n, int E, int U,
+                                                           int n, int E,
                                                            const int* __restrict__ hist,
                                                            const int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv) {
-    extern __shared__ int lds[];  // off[E], run[4][E]
+    extern __shared__ int lds[];  // off[E], sub[4][E], tot[4]
     int* off = lds;
-    int* run = lds + E;
+    int* sub = lds + E;
+    int* tot = lds + 5 * E;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // exclusive scan of counts: each wave scans a quarter, then combine
+    const int u = blockIdx.x;
+    for (int i = tid; i < 4 * E; i += 256) sub[i] = 0;
+    // exclusive scan of counts: each wave scans a quarter, then the quarters combine
     const int per = (E + 3) / 4;
     {
         int carry = 0;
         const int e_lo = w * per, e_hi = min(E, e_lo + per);
         for (int e0 = e_lo; e0 < e_hi; e0 += 64) {
-            int e = e0 + lane;
-            int v = e < e_hi ? counts[e] : 0;
+            const int e = e0 + lane;
+            const int v = e < e_hi ? counts[e] : 0;
             int incl = v;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
-                int t = __shfl_up(incl, o, 64);
+                const int t = __shfl_up(incl, o, 64);
                 if (lane >= o) incl += t;
             }
             if (e < e_hi) off[e] = carry + incl - v;
             carry += __shfl(incl, 63, 64);
         }
-        if (lane == 0) run[w] = carry;  // quarter totals (run[] reused below)
+        if (lane == 0) tot[w] = carry;
     }
     __syncthreads();
+    const int f = u * UB + tid;
+    if (f < n) atomicAdd(&sub[w * E + ids[f]], 1);  // the four waves' sub-histograms
     int add = 0;
-    for (int q = 0; q < w; ++q) add += run[q];
-    const int grand = run[0] + run[1] + run[2] + run[3];
-    __syncthreads();
+    for (int q = 0; q < w; ++q) add += tot[q];
     {
         const int e_lo = w * per, e_hi = min(E, e_lo + per);
         for (int e = e_lo + lane; e < e_hi; e += 64) off[e] += add;
     }
     __syncthreads();
-    if (blockIdx.x == 0) {
+    if (u == 0) {
         for (int e = tid; e < E; e += 256) offsets[e] = off[e];
-        if (tid == 0) offsets[E] = grand;
+        if (tid == 0) offsets[E] = tot[0] + tot[1] + tot[2] + tot[3];
     }
-    const int u = blockIdx.x * 4 + w;
-    if (u >= U) return;
-    int* r = run + w * E;
-    for (int e = lane; e < E; e += 64) r[e] = off[e] + hist[(size_t)u * E + e];
-    // wave-private from here on: no block barrier needed
-    const int f_lo = u * UNIT, f_hi = min(n, f_lo + UNIT);
-    for (int f0 = f_lo; f0 < f_hi; f0 += 64) wave_scatter(ids, f0, f_hi, r, perm, inv, lane);
+    // running bases of the four waves
+    for (int e = tid; e < E; e += 256) {
+        int b = off[e] + hist[(size_t)u * E + e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = sub[q * E + e];
+            sub[q * E + e] = b;
+            b += c;
+        }
+    }
+    __syncthreads();
+    wave_scatter(ids, u * UB + 64 * w, n, sub + w * E, perm, inv, lane);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, long n, int32_t v) {
@@ -302,7 +313,7 @@ constexpr long ALIGN_SMALL_MAX = 4096;
 size_t align_workspace(int T, int k, int E) {
     long n = (long)T * k;
     if (n <= ALIGN_SMALL_MAX) return 0;
-    long U = (n + UNIT - 1) / UNIT;
+    long U = (n + UB - 1) / UB;
     return (size_t)(U * E) * sizeof(int);
 }
 
@@ -316,14 +327,14 @@ ft_status launch_align(const int32_t* ids, int T, int k, int E, int32_t* counts,
         FT_LAUNCHED("align_small");
         return FT_OK;
     }
-    const int U = (int)((n + UNIT - 1) / UNIT);
+    const int U = (int)((n + UB - 1) / UB);
     int* hist = (int*)ws;
-    unit_hist_kernel<<<cdiv(U, 4), 256, 4 * E * sizeof(int), s>>>(ids, (int)n, E, U, hist);
+    unit_hist_kernel<<<U, 256, E * sizeof(int), s>>>(ids, (int)n, E, hist);
     FT_LAUNCHED("align_hist");
-    unit_scan_kernel<<<cdiv(E, 4), 256, 0, s>>>(hist, E, U, counts);
+    unit_scan_kernel<<<cdiv(E, 64), SCAN_W * 64, 0, s>>>(hist, E, U, counts);
     FT_LAUNCHED("align_scan");
-    unit_scatter_kernel<<<cdiv(U, 4), 256, 5 * E * sizeof(int), s>>>(ids, (int)n, E, U, hist,
-                                                                       counts, offsets, perm, inv);
+    unit_scatter_kernel<<<U, 256, (5 * E + 4) * sizeof(int), s>>>(ids, (int)n, E, hist, counts,
+                                                                   offsets, perm, inv);
     FT_LAUNCHED("align_scatter");
     return FT_OK;
 }

@@ -51,6 +51,10 @@ void prof_begin(int which, hipStream_t s) {
 void prof_end(int which, hipStream_t s) {
     if (g_prof[which][1] && !g_capturing) (void)hipEventRecord(g_prof[which][1], s);
 }
+StageEvents prof_stage(int which) {
+    if (g_capturing || !g_prof[which][0] || !g_prof[which][1]) return StageEvents{nullptr, nullptr};
+    return StageEvents{g_prof[which][0], g_prof[which][1]};
+}
 
 static std::atomic<int> g_ffn_path{0};
 
@@ -285,17 +289,11 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
         int* n_tiles = (int*)(wsb + p.count_off);
         r = launch_build_tiles(g, offsets, slot_of_expert, w->shared_slot, tiles, n_tiles,
                                p.max_tiles, s);
-        if (r == FT_OK) {
-            prof_begin(PROF_FFN_GEMM1, s);
+        if (r == FT_OK)
             r = launch_gemm1_mfma(g, (const __bf16*)x, perm, tiles, n_tiles, p.max_tiles,
                                   (__bf16*)h, s);
-            prof_end(PROF_FFN_GEMM1, s);
-        }
-        if (r == FT_OK) {
-            prof_begin(PROF_FFN_GEMM2, s);
+        if (r == FT_OK)
             r = launch_gemm2_mfma(g, (const __bf16*)h, tiles, n_tiles, p.max_tiles, y_perm, y_dt, s);
-            prof_end(PROF_FFN_GEMM2, s);
-        }
     }
     prof_end(PROF_FFN, s);
     return r;

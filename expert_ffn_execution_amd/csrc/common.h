@@ -2,6 +2,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <tuple>
+#include <utility>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -43,6 +46,36 @@ enum { PROF_FFN_GEMM1 = 0, PROF_FFN_GEMM2 = 1, PROF_FFN = 2, PROF_ROUTE = 3,
        PROF_ALIGN = 4, PROF_COMBINE = 5, PROF_N = 6 };
 void prof_begin(int which, hipStream_t s);
 void prof_end(int which, hipStream_t s);
+// The gate/up and down stages are one kernel each: their events ride on that
+// kernel's dispatch (hipExtLaunchKernel), which timestamps the kernel itself
+// and adds no marker packet (a marker between two kernels left the GPU idle
+// for 5-9 us).  Null events when the stage is not profiled or the thread
+// captures a graph.
+struct StageEvents {
+    hipEvent_t start, stop;
+};
+StageEvents prof_stage(int which);
+
+template <typename Tup, size_t... I>
+inline void kernel_argv(Tup& t, void** argv, std::index_sequence<I...>) {
+    ((argv[I] = (void*)&std::get<I>(t)), ...);
+}
+// kern<<<grid, block, lds, s>>>(args...), with stage `which`'s events when set
+template <typename... P, typename... A>
+inline hipError_t launch_timed(int which, void (*kern)(P...), dim3 grid, dim3 block, size_t lds,
+                               hipStream_t s, A... args) {
+    const StageEvents ev = prof_stage(which);
+    if (!ev.start) {
+        kern<<<grid, block, lds, s>>>(args...);
+        return hipGetLastError();
+    }
+    std::tuple<P...> t(args...);
+    void* argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    kernel_argv(t, argv, std::index_sequence_for<P...>{});
+    const hipError_t e = hipExtLaunchKernel((const void*)kern, grid, block, argv, lds, s, ev.start,
+                                            ev.stop, 0);
+    return e != hipSuccess ? e : hipGetLastError();
+}
 
 }  // namespace ft
 

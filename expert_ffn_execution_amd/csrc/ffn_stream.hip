@@ -832,7 +832,8 @@ ft_status launch_one(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) 
     if (lds > 65536)
         FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
-    kern<<<dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s>>>(a);
+    FT_HIP(ft::launch_timed(NM == 2 ? ft::PROF_FFN_GEMM1 : ft::PROF_FFN_GEMM2, kern,
+                        dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s, a));
     FT_LAUNCHED("ffn_stream");
     return FT_OK;
 }
@@ -910,7 +911,8 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     if (lds > 65536)
         FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
-    kern<<<dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s>>>(a);
+    FT_HIP(ft::launch_timed(NM == 2 ? ft::PROF_FFN_GEMM1 : ft::PROF_FFN_GEMM2, kern,
+                        dim3((unsigned)(groups * a.NB)), dim3(64 * NWAVE), lds, s, a));
     FT_LAUNCHED("ffn_stream_mx");
     return FT_OK;
 }
@@ -950,7 +952,6 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a1.dst = h;
     const int cap = (g.w_dt != FT_F32 && big) ? 4 : 8;
     ft_status r;
-    prof_begin(PROF_FFN_GEMM1, s);
     if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_FP8) {
@@ -964,7 +965,6 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     } else {
         r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     }
-    prof_end(PROF_FFN_GEMM1, s);
     if (r != FT_OK) return r;
 
     // down: rows H of length I
@@ -977,7 +977,6 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a2.K = g.I;
     a2.src = h;
     a2.dst = y;
-    prof_begin(PROF_FFN_GEMM2, s);
     if (g.w_dt == FT_F32) r = launch_rows<0, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) {
         if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
@@ -1005,7 +1004,6 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
         if (y_dt == FT_F32) r = launch_rows<2, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
         else r = launch_rows<2, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
     }
-    prof_end(PROF_FFN_GEMM2, s);
     return r;
 }
 

@@ -852,7 +852,6 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
         }
     }
 }
-#undef FT_LDS
 
 template <int MODE, int BT, typename OutT>
 hipError_t launch_pipe(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const __bf16* A,
@@ -867,8 +866,9 @@ hipError_t launch_pipe(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    kern<<<grid, pipe::NT, lds, s>>>(g, A, perm, tiles, n_tiles, n_ntiles, out);
-    return hipGetLastError();
+    return ft::launch_timed(MODE == MODE_GATED ? ft::PROF_FFN_GEMM1 : ft::PROF_FFN_GEMM2, kern,
+                            dim3(grid), dim3(pipe::NT), lds, s, g, A, perm, tiles, n_tiles,
+                            n_ntiles, out);
 }
 
 // Launch one instantiation (raising its dynamic LDS limit once).
@@ -942,6 +942,100 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (e == 0) *n_tiles = min(total + ns, max_tiles);
 }
 
+// ---------------------------------------------------------------------------
+// Router logits for many tokens: out[m][e] = sum_k x[m][k] W_r[e][k], fp32
+// accumulation of bf16 products.  The contraction has few columns (E), so
+// there are few output tiles, and a tile loop that loads one K slice ahead
+// waits one memory round trip per slice (the plain tile kernel took 26 us for
+// 4096 tokens x 128 experts x 2048).  Here a block takes 32 rows x 64 experts
+// and walks K in stages of 64 through an LDS ring of RD stages, filled by
+// direct global->LDS copies issued RD - 1 stages ahead (three 1 KB copies per
+// wave and stage), so that many round trips are in flight at once; two blocks
+// share a CU.  Wave w computes rows 16 (w & 1) .. + 15 and experts
+// 32 (w >> 1) .. + 31 with v_mfma_f32_16x16x32_bf16.  Rows past M and
+// experts past N re-read the last row and are not stored.
+// LDS stage: A rows 0..31 then B rows 0..63, 128 bytes each, chunk c of row r
+// at position c ^ ((r >> 1) & 7).
+namespace rpipe {
+constexpr int BM = 32, BN = 64, KS = 64, RD = 6, NT = 256;
+constexpr int A_BYTES = BM * KS * 2, STAGE = (BM + BN) * KS * 2;
+constexpr int CPW = STAGE / 1024 / (NT / 64);  // copies per wave and stage
+static_assert(CPW == 3, "one A copy and two B copies per wave");
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+}  // namespace rpipe
+
+__global__ __launch_bounds__(rpipe::NT, 2) void router_pipe_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ wr, int M, int N, int K,
+    float* __restrict__ out, int n_ntiles) {
+    using namespace rpipe;
+    __shared__ __attribute__((aligned(16))) unsigned char ring[RD * STAGE];
+    const int m0 = (blockIdx.x / n_ntiles) * BM, n0 = (blockIdx.x % n_ntiles) * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t rowb = (size_t)K * 2;
+    // this lane's copy sources: LDS position lane % 8 of row lane / 8 of the
+    // wave's 1 KB piece takes the global chunk (lane % 8) ^ swz(row)
+    const int ra = 8 * wave + (lane >> 3);
+    const unsigned char* asrc = reinterpret_cast<const unsigned char*>(x) +
+                                (size_t)min(m0 + ra, M - 1) * rowb + ((lane & 7) ^ swz(ra)) * 16;
+    const unsigned char* bsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rb = 16 * wave + 8 * i + (lane >> 3);
+        bsrc[i] = reinterpret_cast<const unsigned char*>(wr) + (size_t)min(n0 + rb, N - 1) * rowb +
+                  ((lane & 7) ^ swz(rb)) * 16;
+    }
+    const int nst = K / KS;
+    // blocks start at different K stages (and wrap around), so that the rows
+    // they read at one moment sit at different offsets
+    const int rot = (int)(blockIdx.x % (unsigned)nst);
+    auto issue = [&](int st) __attribute__((always_inline)) {
+        unsigned char* dst = ring + (st % RD) * STAGE;
+        const int kst = st + rot < nst ? st + rot : st + rot - nst;
+        __builtin_amdgcn_global_load_lds(asrc + (size_t)kst * KS * 2, FT_LDS(dst + wave * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(bsrc[i] + (size_t)kst * KS * 2,
+                                             FT_LDS(dst + A_BYTES + (2 * wave + i) * 1024), 16, 0, 0);
+    };
+    for (int st = 0; st < RD - 1 && st < nst; ++st) issue(st);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int ar = 16 * wm + (lane & 15);
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    for (int st = 0; st < nst; ++st) {
+        // stages st+1 .. min(st + RD - 2, nst - 1) may still be in flight; st must
+        // have landed (copies complete in issue order), then every wave's has
+        wait_vm_lgkm_upto<CPW * (RD - 2)>(CPW * (min(st + RD - 2, nst - 1) - st));
+        __syncthreads();
+        // the slot of stage st - 1, which every wave has finished reading
+        if (st + RD - 1 < nst) issue(st + RD - 1);
+        const unsigned char* sb = ring + (st % RD) * STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 4 * ks + (lane >> 4);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sb + ar * 128 + ((c ^ swz(ar)) * 16));
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int br = 32 * wn + 16 * n + (lane & 15);
+                const bf16x8_t b =
+                    *reinterpret_cast<const bf16x8_t*>(sb + A_BYTES + br * 128 + ((c ^ swz(br)) * 16));
+                acc[n] = mfma16(a, b, acc[n]);
+            }
+        }
+    }
+    // lane holds column lane & 15 and rows 4 (lane >> 4) + j of each 16 x 16 tile
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int col = n0 + 32 * wn + 16 * n + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = m0 + 16 * wm + 4 * (lane >> 4) + j;
+            if (row < M && col < N) out[(size_t)row * N + col] = acc[n][j];
+        }
+    }
+}
+
+#undef FT_LDS
+
 }  // namespace
 
 namespace ft {
@@ -1003,6 +1097,13 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
 
 ft_status launch_dense_gemm_f32out(const void* A, const void* B, int M, int N, int K,
                                    float* out, hipStream_t s) {
+    if (K % rpipe::KS == 0) {
+        const int n_ntiles = cdiv(N, rpipe::BN);
+        router_pipe_kernel<<<(unsigned)(cdiv(M, rpipe::BM) * n_ntiles), rpipe::NT, 0, s>>>(
+            (const __bf16*)A, (const __bf16*)B, M, N, K, out, n_ntiles);
+        FT_LAUNCHED("router logits");
+        return FT_OK;
+    }
     FfnGeom g{};
     const int n_ntiles = cdiv(N, RouterTile::BN);
     hipError_t e = launch_tile<RouterTile, MODE_DENSE, 0, float>(

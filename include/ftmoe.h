@@ -189,12 +189,16 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
  * counts).  Process-wide; a tuning and test knob.  Returns the previous value. */
 int ft_moe_ffn_set_path(int path);
 
-/* Profiling hook: HIP events (hipEvent_t as void*) recorded on the launch
- * stream right before / after the kernels of one stage, so that a caller can
- * time them with hipEventElapsedTime.  which: 0 = the FFN's gate/up GEMM
- * (+SwiGLU), 1 = its down GEMM, 2 = the whole ft_moe_ffn, 3 = ft_moe_route,
- * 4 = ft_moe_align, 5 = ft_moe_combine.  NULL events switch a stage off.
- * Process-wide setting, not synchronised between threads. */
+/* Profiling hook: HIP events (hipEvent_t as void*) that time one stage, so
+ * that a caller can read them with hipEventElapsedTime.  which: 0 = the FFN's
+ * gate/up kernel (+SwiGLU), 1 = its down kernel, 2 = the whole ft_moe_ffn,
+ * 3 = ft_moe_route, 4 = ft_moe_align, 5 = ft_moe_combine.  Stages 0 and 1 are
+ * one kernel each and their events are attached to that kernel's dispatch
+ * (hipExtLaunchKernel): they time the kernel itself and add no packet to the
+ * stream.  The others are recorded on the launch stream right before / after
+ * the stage's kernels (each such record can leave the GPU idle for a few
+ * microseconds).  NULL events switch a stage off.  Process-wide setting, not
+ * synchronised between threads; not applied while a graph is captured. */
 ft_status ft_set_profile_events(int which, void* start, void* stop);
 
 /* --------------------------------------------------------------------------

@@ -63,8 +63,9 @@ def test_route_tie_heavy_bitexact(T, E, k):
 
 
 @pytest.mark.parametrize("name,T", [("35b_a3b_bf16", 1), ("35b_a3b_bf16", 16),
-                                    ("35b_a3b_bf16", 300), ("tiny_f32", 64),
-                                    ("753b_a40b_bf16", 130)])
+                                    ("35b_a3b_bf16", 65), ("35b_a3b_bf16", 300),
+                                    ("35b_a3b_bf16", 4096), ("tiny_f32", 64),
+                                    ("753b_a40b_bf16", 130), ("753b_a40b_bf16", 1000)])
 def test_router_logits(name, T):
     _say("router logits", name, T)
     sh = synth.SHAPES[name]
