@@ -78,12 +78,30 @@ def test_router_logits(name, T):
     assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("H,E,T", [(64, 1000, 130), (128, 8, 65), (192, 100, 333),
+                                   (1024, 64, 97)])
+def test_router_logits_edge_shapes(H, E, T):
+    """The router's MFMA tiles (T > 64) at edge shapes: one or few K stages
+    (fewer than the copy ring holds), expert counts below or not a multiple of
+    the 64-expert tile, ragged row tails."""
+    _say("router logits edge", H, E, T)
+    sh = synth.LayerShape(f"router_edge_{H}_{E}", H=H, E=E, k=min(4, E), I=64)
+    x = synth.gen_x(sh, T)
+    wr = synth.gen_router(sh)
+    _, _, lg = ft.route(T, E, sh.k, x=x.to(DEV), w_router=wr.to(DEV))
+    ref = orc.router_logits(x, wr)
+    got = lg.cpu().numpy()
+    assert rel_l2(got, ref) <= 1e-5
+    assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
+
+
 # ---------------------------------------------------------------------------
 # alignment
 # ---------------------------------------------------------------------------
 # (up to 64 slots take the one-wavefront path: (8, 8, 128) is exactly 64,
 # (7, 8, 1024) the largest expert count, (4, 6, 257) a count past a power of 2)
 ALIGN_CASES = [(1, 8, 128), (64, 2, 8), (512, 8, 128), (513, 8, 128), (16384, 8, 256),
+               (4097, 1, 3), (1100, 4, 1024), (32768, 4, 64),
                (1000, 6, 1024), (4096, 8, 128), (3, 1, 1), (700, 16, 1024), (8, 8, 128),
                (7, 8, 1024), (4, 6, 257), (2, 4, 64), (9, 8, 16)]
 
