@@ -241,6 +241,8 @@ class SlotStack:
         misses between PCIe copies and host cores (decode; needs calibrate()).
         Returns the per-layer outputs."""
         sh = self.sh
+        if hybrid and sh.wdtype != "bf16":
+            raise ValueError("hybrid decode computes missed experts on the host in bf16 only")
         lg = logits if logits is not None else [None] * self.L
         outs = []
         want_x = hybrid and not prefill

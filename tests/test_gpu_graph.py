@@ -114,3 +114,37 @@ def test_step_and_graph(name, T, permuted):
                 assert torch.equal(a, b), f"replay {r}: {what} differs from the eager step"
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("T", [4, 600])
+def test_profile_events_time_the_expert_kernels(T):
+    """ft_set_profile_events on the gate/up and down stages: the events ride on
+    the kernels' own dispatch; both read a positive time that fits inside the
+    whole call, on the streaming (T = 4) and the MFMA (T = 600) path."""
+    sh = synth.SHAPES["35b_a3b_bf16"]
+    x = synth.gen_x(sh, T, device=DEV)
+    pool = torch.empty((sh.E, ft.slot_stride(sh.wdtype, sh.H, sh.I)), dtype=torch.uint8, device=DEV)
+    for e in range(sh.E):
+        ft.pack_expert(synth.gen_expert(sh, e, device=DEV), sh.wdtype,
+                       sh.H, sh.I, pool[e])
+    wts = ft.make_weights(sh.wdtype, sh.E, sh.H, sh.I, pool)
+    ids, w, _ = ft.route(T, sh.E, sh.k, x=x, w_router=synth.gen_router(sh, device=DEV))
+    _, off, perm, _ = ft.align(ids, sh.E)
+    ev = ft.HipEvents()
+    pairs = {which: (ev.create(), ev.create()) for which in (ft.PROF_GEMM1, ft.PROF_GEMM2)}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        for which, (e0, e1) in pairs.items():
+            ft.set_profile_events(which, e0, e1)
+        a.record()
+        ft.ffn(wts, x, sh.k, perm, off)
+        b.record()
+        torch.cuda.synchronize()
+    finally:
+        for which in pairs:
+            ft.set_profile_events(which, None, None)
+    total = a.elapsed_time(b)
+    t1 = ev.elapsed_ms(*pairs[ft.PROF_GEMM1])
+    t2 = ev.elapsed_ms(*pairs[ft.PROF_GEMM2])
+    ev.close()
+    assert 0 < t1 and 0 < t2 and t1 + t2 <= total * 1.05 + 0.01, (t1, t2, total)
