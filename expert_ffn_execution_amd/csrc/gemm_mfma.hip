@@ -1003,9 +1003,13 @@ __global__ __launch_bounds__(rpipe::NT, 2) void router_pipe_kernel(
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     for (int st = 0; st < nst; ++st) {
         // stages st+1 .. min(st + RD - 2, nst - 1) may still be in flight; st must
-        // have landed (copies complete in issue order), then every wave's has
+        // have landed (copies complete in issue order, and this wave's LDS
+        // reads of st - 1 are done), then every wave's has.  A plain barrier:
+        // __syncthreads() would also wait for the copies in flight (its fence
+        // covers them), which emptied the ring at every stage (17 vs 11.7 us
+        // for 4096 x 128 x 2048 in isolation)
         wait_vm_lgkm_upto<CPW * (RD - 2)>(CPW * (min(st + RD - 2, nst - 1) - st));
-        __syncthreads();
+        __builtin_amdgcn_s_barrier();
         // the slot of stage st - 1, which every wave has finished reading
         if (st + RD - 1 < nst) issue(st + RD - 1);
         const unsigned char* sb = ring + (st % RD) * STAGE;
