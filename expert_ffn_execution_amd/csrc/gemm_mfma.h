@@ -14,9 +14,9 @@ struct TileDesc {
     int slot;
 };
 
-constexpr int GEMM_BM = 128;   // rows per tile
-constexpr int GEMM_BN = 128;   // output columns per tile (gated: 64 gate + 64 up)
-constexpr int GEMM_BK = 64;    // contraction step
+// rows per M-tile assumed when the workspace's tile list is sized: no more
+// than the kernels' tile height (256), so the list always fits
+constexpr int GEMM_BM = 128;
 
 // Everything the FFN GEMM kernels need about the weights and the permutation.
 struct FfnGeom {

@@ -1,23 +1,23 @@
-// gemm_mfma.hip -- MFMA tile kernels of the grouped expert GEMMs (gfx950).
+// gemm_mfma.hip -- MFMA kernels for many tokens (gfx950): the grouped expert
+// GEMMs and the router logits.
 //
 // The expert FFN over many tokens is a set of dense contractions, one per
 // expert, over the rows routed to it (claypier.com article,
 // "从 MoE「用不到的权重」入手的推理引擎": only the experts a token needs are
-// computed).  Each 128-row M-tile of an expert's segment of the permutation is
-// one entry of a tile list; a block computes a 128 x 128 output tile with
-// v_mfma_f32_16x16x32_bf16 and fp32 accumulation, staging 64-wide K slices of
-// both operands through LDS (double-buffered: the global loads of slice k+1
-// are in flight while slice k feeds the MFMAs).
+// computed).  build_tiles_kernel lists each expert's segment of the
+// permutation as M-tiles of at most 256 rows; gemm_pipe_kernel computes a
+// 256 x 256 output tile of one M-tile with v_mfma_f32_32x32x16_bf16, its K
+// stages copied global -> LDS by the load units into two rings (activations,
+// weights), several stages ahead.
 //
-// GEMM1 fuses SwiGLU: the B tile holds 64 gate rows and the same 64 up rows,
-// each wavefront owns matching gate/up accumulators, and the epilogue writes
-// h = silu(g) * u in bf16.  GEMM2 multiplies h by the down projection.
-// MXFP4 weights are decoded exactly to bf16 (e2m1 value times the e8m0 block
-// scale) on their way into LDS, so the MFMA loop is the same for both formats.
+// GEMM1 fuses SwiGLU: the B tile holds 128 gate rows and the same 128 up
+// rows, each wavefront owns matching gate/up accumulators, and the epilogue
+// writes h = silu(g) * u in bf16.  GEMM2 multiplies h by the down projection.
+// Narrow weights (MXFP4, FP8, NVFP4) stay packed in LDS and are decoded
+// exactly to bf16 when a fragment is read.
 //
-// LDS layout of a 128 x 64 bf16 slice: row r is 128 bytes = 8 chunks of 16
-// bytes; chunk c is stored at position c ^ ((r >> 1) & 7) so that the 16 rows
-// a fragment read touches fall on distinct banks.
+// router_pipe_kernel computes the router logits of many tokens (x . W_r^T,
+// fp32) with the same kind of copy ring.
 #include "gemm_mfma.h"
 
 #include <type_traits>
@@ -25,29 +25,7 @@
 namespace {
 
 using ft::TileDesc;
-constexpr int BK = ft::GEMM_BK;
 
-__device__ __forceinline__ int lds_idx(int r, int c) {
-    return r * BK + ((c ^ ((r >> 1) & 7)) << 3);
-}
-
-// 32 e2m1 values (16 code bytes) times 2^(X-127) -> 4 chunks of 8 bf16.
-// Element 2j is the low nibble of byte j.
-__device__ __forceinline__ void decode_fp4x32(u32x4_t codes, uint32_t X, u32x4_t out[4]) {
-    const float sc = __uint_as_float(X << 23);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t w = codes[q];
-        out[q][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
-        out[q][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
-        out[q][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
-        out[q][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
-    }
-}
-
-__device__ __forceinline__ bf16x8_t frag(const __bf16* lds, int r, int c) {
-    return *reinterpret_cast<const bf16x8_t*>(lds + lds_idx(r, c));
-}
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -57,241 +35,8 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Tile shapes.  A block computes a BM x BN output tile with NW = (BM/WM) x
-// (BN/WN) wavefronts, each owning a WM x WN sub-tile of 16 x 16 MFMA tiles
-// (fp32 accumulators: WM*WN/64 registers per lane, held in AGPRs for the
-// large shape).  LDS holds two stages of BM x 64 (A) and BN x 64 (B) bf16.
-// ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_, int MINB_>
-struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MINB = MINB_;
-    static constexpr int WAVES_N = BN / WN, NW = (BM / WM) * (BN / WN), NT = NW * 64;
-    static constexpr int MT = WM / 16, NTL = WN / 16;
-    static constexpr int A_CH = BM * 8 / NT;   // 16-byte A chunks per thread per slice
-    static constexpr int B_CH = BN * 8 / NT;   // 16-byte bf16 B chunks per thread
-    static constexpr int B_MX = BN * 2 / NT;   // (row, half) MXFP4 units per thread
-    static constexpr size_t LDS = (size_t)2 * (BM + BN) * BK * 2;
-};
-// the router logits (N = E is small) use 64 x 64 tiles to spread over more CUs
-using RouterTile = TileCfg<64, 64, 32, 32, 4>;
-
-enum { MODE_GATED = 0, MODE_LIST = 1, MODE_DENSE = 2 };
-
-// B staging: 32-bit byte offsets from a block-uniform base (the slot), so
-// that the per-thread state is one VGPR per chunk.
-template <class C, int BT>
-struct BSlice {
-    static constexpr int NV = BT == 0 ? C::B_CH : C::B_MX;
-    u32x4_t v[NV];
-    uint32_t sc[BT == 0 ? 1 : NV];
-    const uint8_t* base;
-    uint32_t off[NV];
-    uint32_t scoff[BT == 0 ? 1 : NV];
-
-    // rowoff(r) = byte offset of B row r (codes for MXFP4), scoff(r) = its scales
-    template <typename RowF, typename ScF>
-    __device__ __forceinline__ void init(const uint8_t* b, int tid, RowF rowoff, ScF scrow) {
-        base = b;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if constexpr (BT == 0) {
-                off[i] = rowoff((tid >> 3) + (C::NT / 8) * i) + (tid & 7) * 16;
-            } else {
-                const int q = tid + C::NT * i;
-                off[i] = rowoff(q >> 1) + (q & 1) * 16;
-                scoff[i] = scrow(q >> 1) + (q & 1);
-            }
-        }
-    }
-    __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if constexpr (BT == 0) {
-                v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * BK * 2);
-            } else {
-                v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * (BK / 2));
-                sc[i] = base[scoff[i] + kt * (BK / 32)];
-            }
-        }
-    }
-    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if constexpr (BT == 0) {
-                *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + (C::NT / 8) * i, tid & 7)) = v[i];
-            } else {
-                u32x4_t d[4];
-                decode_fp4x32(v[i], sc[i], d);
-                const int q = tid + C::NT * i, r = q >> 1, h = (q & 1) * 4;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(lds + lds_idx(r, h + c)) = d[c];
-            }
-        }
-    }
-};
-
-// A staging: 32-bit element offsets of the (gathered) rows from the A base.
-template <class C>
-struct ASlice {
-    u32x4_t v[C::A_CH];
-    const __bf16* base;
-    uint32_t off[C::A_CH];
-    __device__ __forceinline__ void load(int kt) {
-#pragma unroll
-        for (int i = 0; i < C::A_CH; ++i)
-            v[i] = *reinterpret_cast<const u32x4_t*>(base + off[i] + kt * BK);
-    }
-    __device__ __forceinline__ void store(__bf16* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < C::A_CH; ++i)
-            *reinterpret_cast<u32x4_t*>(lds + lds_idx((tid >> 3) + (C::NT / 8) * i, tid & 7)) = v[i];
-    }
-};
-
-// One kernel for the three contractions:
-//   MODE_GATED: h[p][i] = bf16(silu(x_t . Wg_i) * (x_t . Wu_i)) (B tile = BN/2 gate rows
-//               followed by the same BN/2 up rows)
-//   MODE_LIST:  out[p][n] = A[p] . B_n over the tile list (down projection)
-//   MODE_DENSE: out[m][n] = A[m] . B_n for a dense M x N problem (router logits)
-template <class C, int MODE, int BT, typename OutT>
-__global__ __launch_bounds__(C::NT, C::MINB) void gemm_tile_kernel(
-    ft::FfnGeom g, const __bf16* __restrict__ A, const int32_t* __restrict__ perm,
-    const __bf16* __restrict__ Bdense, int M, int N, int K, const TileDesc* __restrict__ tiles,
-    const int* __restrict__ n_tiles, int n_ntiles, OutT* __restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) __bf16 smem[];
-    __bf16* const A0 = smem;
-    __bf16* const B0 = smem + 2 * C::BM * BK;
-    const int ti = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
-    TileDesc td;
-    if constexpr (MODE == MODE_DENSE) {
-        td = TileDesc{0, ti * C::BM, min(C::BM, M - ti * C::BM), 0};
-    } else {
-        if (ti >= *n_tiles) return;
-        td = tiles[ti];
-    }
-    const int tid = threadIdx.x;
-    const bool shared = MODE != MODE_DENSE && td.e == g.E;
-    // first output row of the tile (shared-expert rows follow the T*k routed rows)
-    const size_t obase = shared ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0;
-
-    ASlice<C> as;
-    as.base = A;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-        const int r = min((tid >> 3) + (C::NT / 8) * i, td.rows - 1);
-        uint32_t arow;
-        if constexpr (MODE == MODE_GATED) arow = shared ? (uint32_t)(td.p0 + r) : (uint32_t)(perm[td.p0 + r] / g.k);
-        else arow = (uint32_t)(obase + r);
-        as.off[i] = arow * (uint32_t)K + (tid & 7) * 8;
-    }
-    BSlice<C, BT> bs;
-    const uint8_t* slot = MODE == MODE_DENSE ? nullptr : g.pool + (size_t)td.slot * g.slot_stride;
-    const int i0 = nt * (C::BN / 2), n0 = nt * C::BN;
-    const uint32_t rowb = BT == 0 ? (uint32_t)K * 2 : (uint32_t)K / 2;  // bytes per B row
-    if constexpr (MODE == MODE_GATED) {
-        bs.init(slot, tid,
-                [&](int r) {
-                    const uint32_t row = i0 + (r % (C::BN / 2));
-                    return (uint32_t)(r < C::BN / 2 ? g.off[0] : g.off[1]) + row * rowb;
-                },
-                [&](int r) {
-                    const uint32_t row = i0 + (r % (C::BN / 2));
-                    return (uint32_t)(r < C::BN / 2 ? g.off[3] : g.off[4]) + row * (uint32_t)(K / 32);
-                });
-    } else if constexpr (MODE == MODE_LIST) {
-        // rows past N (N not a multiple of BN) re-read row N-1; their columns are not stored
-        bs.init(slot, tid,
-                [&](int r) { return (uint32_t)g.off[2] + (uint32_t)min(n0 + r, N - 1) * rowb; },
-                [&](int r) {
-                    return (uint32_t)g.off[5] + (uint32_t)min(n0 + r, N - 1) * (uint32_t)(K / 32);
-                });
-    } else {
-        bs.init(reinterpret_cast<const uint8_t*>(Bdense), tid,
-                [&](int r) { return (uint32_t)min(n0 + r, N - 1) * rowb; },
-                [&](int) { return 0u; });
-    }
-
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    f32x4_t acc[C::MT][C::NTL];
-#pragma unroll
-    for (int a = 0; a < C::MT; ++a)
-#pragma unroll
-        for (int b = 0; b < C::NTL; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / BK;
-    as.load(0);
-    bs.load(0);
-    as.store(A0, tid);
-    bs.store(B0, tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            as.load(kt + 1);
-            bs.load(kt + 1);
-        }
-        const __bf16* Ac = A0 + cur * (C::BM * BK);
-        const __bf16* Bc = B0 + cur * (C::BN * BK);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = ks * 4 + (lane >> 4);
-            bf16x8_t a[C::MT], b[C::NTL];
-#pragma unroll
-            for (int m = 0; m < C::MT; ++m) a[m] = frag(Ac, wm * C::WM + m * 16 + (lane & 15), ch);
-#pragma unroll
-            for (int n = 0; n < C::NTL; ++n) {
-                int brow;
-                if constexpr (MODE == MODE_GATED)  // first half of the wave's tiles: gate, second: up
-                    brow = (n < C::NTL / 2 ? 0 : C::BN / 2) + wn * (C::WN / 2) + (n % (C::NTL / 2)) * 16;
-                else
-                    brow = wn * C::WN + n * 16;
-                b[n] = frag(Bc, brow + (lane & 15), ch);
-            }
-#pragma unroll
-            for (int m = 0; m < C::MT; ++m)
-#pragma unroll
-                for (int n = 0; n < C::NTL; ++n) acc[m][n] = mfma16(a[m], b[n], acc[m][n]);
-        }
-        if (kt + 1 < nk) {
-            as.store(A0 + (cur ^ 1) * (C::BM * BK), tid);
-            bs.store(B0 + (cur ^ 1) * (C::BN * BK), tid);
-        }
-        __syncthreads();
-    }
-
-    // epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + j of each 16 x 16 tile
-#pragma unroll
-    for (int m = 0; m < C::MT; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wm * C::WM + m * 16 + 4 * (lane >> 4) + j;
-            if (row >= td.rows) continue;
-            if constexpr (MODE == MODE_GATED) {
-#pragma unroll
-                for (int n = 0; n < C::NTL / 2; ++n) {
-                    const int col = i0 + wn * (C::WN / 2) + n * 16 + (lane & 15);
-                    const float hv = silu_mul(acc[m][n][j], acc[m][n + C::NTL / 2][j]);
-                    reinterpret_cast<uint16_t*>(out)[(obase + row) * g.I + col] =
-                        (uint16_t)f32_to_bf16_bits(hv);
-                }
-            } else {
-#pragma unroll
-                for (int n = 0; n < C::NTL; ++n) {
-                    const int col = n0 + wn * C::WN + n * 16 + (lane & 15);
-                    if (col < N) {
-                        const float v = acc[m][n][j];
-                        if constexpr (sizeof(OutT) == 4)
-                            reinterpret_cast<float*>(out)[(obase + row) * N + col] = v;
-                        else
-                            reinterpret_cast<uint16_t*>(out)[(obase + row) * N + col] =
-                                (uint16_t)f32_to_bf16_bits(v);
-                    }
-                }
-            }
-        }
-}
+// MODE_GATED: gate/up + SwiGLU -> h; MODE_LIST: down projection -> y
+enum { MODE_GATED = 0, MODE_LIST = 1 };
 
 // ---------------------------------------------------------------------------
 // Pipelined tile kernel for the expert GEMMs.  256 x 256 output tile, 4
@@ -871,23 +616,6 @@ hipError_t launch_pipe(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const
                             n_ntiles, out);
 }
 
-// Launch one instantiation (raising its dynamic LDS limit once).
-template <class C, int MODE, int BT, typename OutT>
-hipError_t launch_tile(unsigned grid, hipStream_t s, const ft::FfnGeom& g, const __bf16* A,
-                       const int32_t* perm, const __bf16* Bd, int M, int N, int K,
-                       const TileDesc* tiles, const int* n_tiles, int n_ntiles, OutT* out) {
-    static bool attr_set = false;
-    auto kern = gemm_tile_kernel<C, MODE, BT, OutT>;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    kern<<<grid, C::NT, C::LDS, s>>>(g, A, perm, Bd, M, N, K, tiles, n_tiles, n_ntiles, out);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // tile list
 // ---------------------------------------------------------------------------
@@ -1101,19 +829,11 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
 
 ft_status launch_dense_gemm_f32out(const void* A, const void* B, int M, int N, int K,
                                    float* out, hipStream_t s) {
-    if (K % rpipe::KS == 0) {
-        const int n_ntiles = cdiv(N, rpipe::BN);
-        router_pipe_kernel<<<(unsigned)(cdiv(M, rpipe::BM) * n_ntiles), rpipe::NT, 0, s>>>(
-            (const __bf16*)A, (const __bf16*)B, M, N, K, out, n_ntiles);
-        FT_LAUNCHED("router logits");
-        return FT_OK;
-    }
-    FfnGeom g{};
-    const int n_ntiles = cdiv(N, RouterTile::BN);
-    hipError_t e = launch_tile<RouterTile, MODE_DENSE, 0, float>(
-        (unsigned)cdiv(M, RouterTile::BM) * n_ntiles, s, g, (const __bf16*)A, nullptr,
-        (const __bf16*)B, M, N, K, nullptr, nullptr, n_ntiles, out);
-    if (e != hipSuccess) return set_error(FT_ERR_HIP, "router gemm: %s", hipGetErrorString(e));
+    if (K % rpipe::KS != 0) return set_error(FT_ERR_INVALID_ARG, "router GEMM: K must be a multiple of 64");
+    const int n_ntiles = cdiv(N, rpipe::BN);
+    router_pipe_kernel<<<(unsigned)(cdiv(M, rpipe::BM) * n_ntiles), rpipe::NT, 0, s>>>(
+        (const __bf16*)A, (const __bf16*)B, M, N, K, out, n_ntiles);
+    FT_LAUNCHED("router logits");
     return FT_OK;
 }
 
