@@ -27,6 +27,7 @@
 // Plain host C++ (built with the host compiler, no device pass): only the C
 // header and the library's error helpers.
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
@@ -57,9 +58,23 @@ inline void cpu_relax() {
 #endif
 }
 
+// Spin until pred() holds or about kSpinUs microseconds have passed; true if it held.
+constexpr int kSpinUs = 100;
+template <class P>
+bool spin_until(P pred) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+        for (int i = 0; i < 64; ++i) {
+            if (pred()) return true;
+            cpu_relax();
+        }
+        if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(kSpinUs)) return pred();
+    }
+}
+
 // ---- a persistent pool: run(n, f) calls f(0..n-1) on n threads (the caller is 0).
-// Workers spin for a short while after each job before sleeping, so the
-// back-to-back phases of one job (and of the next layer's job) start without a
+// Workers spin for up to kSpinUs after each job before sleeping, so the
+// back-to-back phases of one job (and a next job soon after) start without a
 // wake-up from the kernel.
 class Pool {
 public:
@@ -85,21 +100,15 @@ public:
         }
         cv_.notify_all();
         f(0);
-        for (int s = 0; pending_.load(std::memory_order_acquire) != 0; ++s) {
-            if (s < kSpin) {
-                cpu_relax();
-                continue;
-            }
+        if (!spin_until([&] { return pending_.load(std::memory_order_acquire) == 0; })) {
             std::unique_lock<std::mutex> g(mu_);
             done_.wait(g, [&] { return pending_.load(std::memory_order_acquire) == 0; });
-            break;
         }
         std::lock_guard<std::mutex> g(mu_);
         job_ = nullptr;
     }
 
 private:
-    static constexpr int kSpin = 1 << 16;  // ~50-100 us of pause loops
     void grow(int want) {
         while ((int)th_.size() < want) {
             const int id = (int)th_.size() + 1;
@@ -109,8 +118,7 @@ private:
     void loop(int id) {
         unsigned seen = 0;
         for (;;) {
-            for (int s = 0; s < kSpin && agen_.load(std::memory_order_acquire) == seen; ++s)
-                cpu_relax();
+            spin_until([&] { return agen_.load(std::memory_order_acquire) != seen; });
             const std::function<void(int)>* f;
             {
                 std::unique_lock<std::mutex> g(mu_);
