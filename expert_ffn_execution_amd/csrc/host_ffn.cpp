@@ -59,7 +59,7 @@ inline void cpu_relax() {
 }
 
 // Spin until pred() holds or about kSpinUs microseconds have passed; true if it held.
-constexpr int kSpinUs = 100;
+constexpr int kSpinUs = 250;
 template <class P>
 bool spin_until(P pred) {
     const auto t0 = std::chrono::steady_clock::now();
@@ -73,7 +73,8 @@ bool spin_until(P pred) {
 }
 
 // ---- a persistent pool: run(n, f) calls f(0..n-1) on n threads (the caller is 0).
-// Workers spin for up to kSpinUs after each job before sleeping, so the
+// Workers spin for up to kSpinUs after each job before sleeping (a decode
+// step brings a layer's job about every 0.2 ms), so the
 // back-to-back phases of one job (and a next job soon after) start without a
 // wake-up from the kernel.
 class Pool {
