@@ -491,7 +491,7 @@ def run_graph_point(sh, banks, T, steps, warmup, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1"}))
         log("the MoE-layer path here is single-GPU; multi-GPU runs are not supported")
         sys.exit(2)
     import torch
