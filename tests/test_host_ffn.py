@@ -163,3 +163,33 @@ def test_moe_job_rejects_bad_descriptors():
     assert lib.ft_host_job_wait(None) == ft.ERR_INVALID_ARG
     job, _, _ = _job(sh, pool, offsets, perm, x, [])
     assert job.wait() == 0
+
+
+def test_moe_jobs_from_several_threads():
+    """Jobs submitted from four threads at once run one at a time and each
+    gives the same bits as the same job alone."""
+    import threading
+    sh, pool, _, offsets, perm, x = _layer(E=8, T=12, seed=9)
+    lists = [[0, 3], [7, 1], [2], [4, 5, 6]]
+    want = []
+    for ex in lists:
+        job, rows, pos = _job(sh, pool, offsets, perm, x, ex, n_threads=2)
+        n = job.wait()
+        want.append((rows[:n].clone(), pos[:n].clone()))
+    errors = []
+
+    def worker(i):
+        try:
+            for _ in range(5):
+                job, rows, pos = _job(sh, pool, offsets, perm, x, lists[i], n_threads=3)
+                n = job.wait()
+                assert torch.equal(rows[:n], want[i][0]) and torch.equal(pos[:n], want[i][1])
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    ths = [threading.Thread(target=worker, args=(i,)) for i in range(len(lists))]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    assert not errors, errors
