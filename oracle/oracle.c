@@ -6,7 +6,8 @@
  * Shares nothing with the HIP sources.  The operations and the readings they
  * follow are listed in oracle.h; each function below restates its definition.
  *
- * Build: gcc -O2 -fno-fast-math -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ * Build: gcc -O3 -fno-fast-math -fno-semantic-interposition -fopenmp -shared -fPIC
+ *        -std=c11 oracle.c -o liboracle.so -lm  (ISO C: no floating-point contraction)
  */
 #include "oracle.h"
 
@@ -76,8 +77,30 @@ double or_nvfp4_value(uint8_t code, uint8_t scale) {
     return or_mxfp4_value(code, 127) * or_fp8_value(scale);
 }
 
+/* Decode tables: the values of the functions above for every code, filled
+ * once when the library is loaded.  They only cache those exact fp64 values
+ * (the per-element ldexp calls made the narrow formats some ten times slower
+ * than bf16); a pin compares every entry with its function.
+ *   g_e2m1[c]  = or_mxfp4_value(c, 127)   (the e2m1 value, scale 2^0)
+ *   g_pow2[X]  = 2^(X - 127)              (the e8m0 scale; NaN for X = 255)
+ *   g_fp8[c]   = or_fp8_value(c) */
+static double g_e2m1[16], g_pow2[256], g_fp8[256];
+
+__attribute__((constructor)) static void or_fill_tables(void) {
+    for (int c = 0; c < 16; ++c) g_e2m1[c] = or_mxfp4_value((uint8_t)c, 127);
+    for (int X = 0; X < 256; ++X) g_pow2[X] = X == 255 ? NAN : ldexp(1.0, X - 127);
+    for (int c = 0; c < 256; ++c) g_fp8[c] = or_fp8_value((uint8_t)c);
+}
+
+/* the cached values, for the pins */
+double or_table_e2m1(uint8_t code) { return g_e2m1[code & 15]; }
+double or_table_pow2(uint8_t X) { return g_pow2[X]; }
+double or_table_fp8(uint8_t code) { return g_fp8[code]; }
+
 /* element (row, kk) of a [rows][K] matrix stored in fmt (ts: the tensor scale
- * of an NVFP4 matrix) */
+ * of an NVFP4 matrix).  MXFP4: e2m1 value times 2^(X-127); NVFP4: e2m1 value
+ * times the e4m3 block scale times the tensor scale; FP8: e4m3 value times the
+ * matrix scale.  Every product of table values here is exact in fp64. */
 static double w_at(const void* base, const uint8_t* sc, const uint8_t* ts, int fmt, int row, int K,
                    int kk) {
     size_t r = (size_t)row;
@@ -86,16 +109,16 @@ static double w_at(const void* base, const uint8_t* sc, const uint8_t* ts, int f
     if (fmt == OR_FP8) {  /* code times the matrix's fp32 scale (sc points at it) */
         float scale;
         memcpy(&scale, sc, 4);
-        return or_fp8_value(((const uint8_t*)base)[r * K + kk]) * (double)scale;
+        return g_fp8[((const uint8_t*)base)[r * K + kk]] * (double)scale;
     }
     uint8_t byte = ((const uint8_t*)base)[r * (K / 2) + kk / 2];
     uint8_t c = (kk & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
     if (fmt == OR_NVFP4) {
         float tensor;
         memcpy(&tensor, ts, 4);
-        return or_nvfp4_value(c, sc[r * (K / 16) + kk / 16]) * (double)tensor;
+        return g_e2m1[c] * g_fp8[sc[r * (K / 16) + kk / 16]] * (double)tensor;
     }
-    return or_mxfp4_value(c, sc[r * (K / 32) + kk / 32]);
+    return g_e2m1[c] * g_pow2[sc[r * (K / 32) + kk / 32]];
 }
 
 static double act_at(const void* x, int fmt, int t, int H, int h) {

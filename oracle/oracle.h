@@ -75,6 +75,12 @@ double or_fp8_value(uint8_t code);
 /* Exact value of one NVFP4 element before its tensor scale: the e2m1 code
  * times its block's e4m3 scale byte. */
 double or_nvfp4_value(uint8_t code, uint8_t scale);
+/* The cached decode values used per element (filled from the functions above
+ * when the library loads): e2m1 value of a code (scale 2^0), the e8m0 scale
+ * 2^(X-127) (NaN for 255), the e4m3 value of a code. */
+double or_table_e2m1(uint8_t code);
+double or_table_pow2(uint8_t X);
+double or_table_fp8(uint8_t code);
 /* bf16 bits -> double (exact) and double -> bf16 bits (round to nearest even). */
 double or_bf16_to_f64(uint16_t b);
 uint16_t or_f64_to_bf16(double v);

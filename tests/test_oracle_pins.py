@@ -228,6 +228,27 @@ def test_nvfp4_quantiser_round_trip():
     assert float(t[0]) == ts
 
 
+def test_decode_tables_equal_the_published_values():
+    # the oracle's per-element decode reads tables filled at load time: each
+    # entry must be the OCP e2m1 value, 2^(X-127) (NaN for X = 255) and torch's
+    # float8_e4m3fn decoding, signs of zeros included
+    tab = _e2m1_table()
+    for code in range(16):
+        v = orc.load().or_table_e2m1(code)
+        assert v == tab[code] and math.copysign(1.0, v) == math.copysign(1.0, tab[code]), code
+    for X in range(256):
+        v = orc.load().or_table_pow2(X)
+        assert math.isnan(v) if X == 255 else v == math.ldexp(1.0, X - 127), X
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).tolist()
+    for code in range(256):
+        v = orc.load().or_table_fp8(code)
+        if math.isnan(ref[code]):
+            assert math.isnan(v), code
+        else:
+            assert v == ref[code] and math.copysign(1.0, v) == math.copysign(1.0, ref[code]), code
+
+
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(2)
     vals = np.concatenate([
