@@ -7,13 +7,18 @@ combine (ft_moe_combine), on inputs already resident in HBM.  Layer weight
 banks rotate between steps so that the bytes touched between two uses of the
 same weights exceed four times the 256 MB Infinity Cache.
 
-Prints one JSON line: headline = prefill tokens/s of the workload, with the
-roofline of its dominant kernel (the gate/up grouped GEMM: HBM- or MFMA-bound
-by its arithmetic intensity against the ridge point), the
-decode points (HBM-bound FFN weight streaming) and the CPU oracle's rate on a
-bounded sample of the same workload.  A decode point's tokens/s comes from
-replays of the step captured as a HIP graph (ft_moe_graph_*); the same step
-enqueued call by call is reported beside it (eager_*).
+With no --workload the headline is the largest single-GPU workload, the
+753B-A40B-shaped layer (H 6144, 256 experts, top-8, I 2048, bf16 weights) at
+prefill T = 16384 with the per-expert N(0, 1) router bias that skews the load.
+The line carries the roofline of its dominant kernel (the gate/up grouped GEMM:
+HBM- or MFMA-bound by its arithmetic intensity against the ridge point), its
+decode points (T = 1, 32; HBM-bound weight streaming, rated as active-expert
+bytes over the gate/up + down kernel time), the CPU oracle's rate on a bounded
+sample of the same workload, and under "other_workloads" the same
+measurements for the 35B-A3B bf16, 284B-A13B MXFP4 and 753B-A40B MXFP4 layers
+and the 8-layer slot-cache stack.  A decode point's tokens/s comes from replays
+of the step captured as a HIP graph (ft_moe_graph_*); the same step enqueued
+call by call is reported beside it (eager_*).
 """
 from __future__ import annotations
 
@@ -32,8 +37,15 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 CAL_BYTES = 1 << 30            # calibration copy
 GEMM_SRC = os.path.join(ROOT, "expert_ffn_execution_amd", "csrc", "gemm_mfma.hip")
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm1_35b_a3b_prefill_traffic.json")
-GEMM1_KERNEL = "gemm_pipe_kernelILi0ELi0E"   # gate/up GEMM, bf16 weights
+DEFAULT_WORKLOAD = "753b_a40b_bf16"
+EXTRA_WORKLOADS = ("35b_a3b_bf16", "284b_a13b_mxfp4", "753b_a40b_mxfp4")
+# gate/up GEMM kernel (MODE_GATED) by weight format, as rocprofv3 names it
+GEMM1_KERNEL = {"bf16": "gemm_pipe_kernelILi0ELi0E", "mxfp4": "gemm_pipe_kernelILi0ELi1E",
+                "fp8": "gemm_pipe_kernelILi0ELi2E", "nvfp4": "gemm_pipe_kernelILi0ELi3E"}
+
+
+def traffic_json(workload, T):
+    return os.path.join(ROOT, "profiles", f"gemm1_traffic_{workload}_T{T}.json")
 
 
 def _sha(path):
@@ -42,11 +54,12 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per gate/up GEMM launch from the committed counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def stored_traffic(workload, T):
+    """HBM bytes per gate/up GEMM launch from the committed counter summary of
+    this workload and token count, or None when there is none or the kernel
+    source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_json(workload, T)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -55,10 +68,14 @@ def stored_traffic():
     return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
 
-def summarize_pmc(fetch_dir, write_dir):
-    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark -> the
-    committed traffic summary.  Counters are KiB per dispatch; each is scaled by
-    its reading for the 1 GiB calibration copy."""
+def summarize_pmc(fetch_dir, write_dir, workload, T):
+    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark (one
+    workload) -> the committed traffic summary of its gate/up GEMM.  Counters
+    are KiB per dispatch; each is scaled by its reading for the 1 GiB
+    calibration copy."""
+    from expert_ffn_execution_amd import synth
+    kname = GEMM1_KERNEL[synth.SHAPES[workload].wdtype]
+    T = int(T)
     import csv
     import glob
 
@@ -69,20 +86,20 @@ def summarize_pmc(fetch_dir, write_dir):
         cal = [float(r["Counter_Value"]) for r in rows
                if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
         cal = max(cal) if cal else float("nan")
-        g1 = [float(r["Counter_Value"]) for r in rows if GEMM1_KERNEL in r["Kernel_Name"]]
+        g1 = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
         return cal, (sum(g1) / len(g1) if g1 else float("nan")), len(g1)
 
     fc, fg, nf = read(fetch_dir, "FETCH_SIZE")
     wc, wg, nw = read(write_dir, "WRITE_SIZE")
     f_scale, w_scale = CAL_BYTES / (fc * 1024.0), CAL_BYTES / (wc * 1024.0)
-    out = {"source_sha256": _sha(GEMM_SRC), "kernel": GEMM1_KERNEL,
+    out = {"source_sha256": _sha(GEMM_SRC), "kernel": kname, "workload": workload, "T": T,
            "calibration_copy_bytes": CAL_BYTES,
            "fetch_kib_calibration": fc, "write_kib_calibration": wc,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "fetch_kib_per_launch": fg, "write_kib_per_launch": wg, "launches": [nf, nw],
            "fetch_bytes_per_launch": fg * 1024.0 * f_scale,
            "write_bytes_per_launch": wg * 1024.0 * w_scale}
-    with open(TRAFFIC_JSON, "w") as f:
+    with open(traffic_json(workload, T), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -113,14 +130,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="35b_a3b_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the chosen workload (no other_workloads section)")
     ap.add_argument("--tokens", type=int, default=0, help="prefill tokens (default: workload's)")
     ap.add_argument("--decode", default="", help="decode token counts, e.g. 1,16,64 "
                                                  "(default: workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the traffic summary from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "T"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs of one workload")
     return ap.parse_args()
 
 
@@ -311,9 +330,23 @@ def cpu_baseline(sh, bank, T, dev, seconds):
     if n2 > n:
         n, t = n2, run(n2)
     return {"value": n / t, "unit": "tokens/s", "cores": orc.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {n} tokens of the T={T} batch, layer 0 weights "
                       f"(router GEMM, top-k, align, per-token expert loops, combine), "
                       f"{t:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def h2d_peak_gbs(dev, nbytes=1 << 30):
@@ -337,7 +370,7 @@ def h2d_peak_gbs(dev, nbytes=1 << 30):
 def run_slot_stack(args):
     """8 layers of the 35B-A3B layer shape behind a 512-slot global LRU over a
     pinned host pool: decode T=1 steps, then one prefill, each timed against
-    the same layers fully resident in HBM."""
+    the same layers fully resident in HBM.  Returns the JSON line's dict."""
     import torch
     from expert_ffn_execution_amd import ftmoe as ft
     from expert_ffn_execution_amd import synth
@@ -453,7 +486,9 @@ def run_slot_stack(args):
             "tight_budget_128_slots": tight,
         },
     }
-    print(json.dumps(line), flush=True)
+    del resident, rwts
+    torch.cuda.empty_cache()
+    return line
 
 
 def dataclasses_replace(obj):
@@ -488,6 +523,74 @@ def run_graph_point(sh, banks, T, steps, warmup, dev):
     return ms
 
 
+def decode_entry(sh, r, g_ms, T):
+    """One decode point: graph-replayed step rate, and the FFN's weight
+    streaming rated as active-expert bytes (gate/up + down of every distinct
+    routed expert, plus the shared one) over the sum of the gate/up and down
+    kernel durations."""
+    ffn_s = r["ffn_ms"] * 1e-3
+    narrow = sh.wdtype in ("mxfp4", "fp8", "nvfp4") and T >= 2
+    return {
+        "T": T, "tokens_per_s": T / (g_ms / 1e3), "ms_per_step": g_ms,
+        "eager_tokens_per_s": r["tokens_per_s"], "eager_ms_per_step": r["ms_per_step"],
+        "ffn_us": r["ffn_ms"] * 1e3, "gate_up_us": r["gemm1_ms"] * 1e3,
+        "down_us": r["gemm2_ms"] * 1e3, "active_experts": r["active_experts"],
+        "gate_up_gbs": r["gemm1_gbs"], "down_gbs": r["gemm2_gbs"],
+        "roofline": {"bound": "hbm", "achieved": r["weight_bytes"] / ffn_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["weight_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": ("gate/up + down weight streaming on matrix cores (stream_mx_kernel)"
+                                if narrow else "gate/up + down weight streaming (stream_kernel)"),
+                     "bytes_per_step": r["weight_bytes"]}}
+
+
+def run_workload(name, args, dev, with_cpu):
+    """Prefill point, decode points and (optionally) the CPU oracle of one
+    workload; its weight banks are freed before returning."""
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+
+    sh = synth.SHAPES[name]
+    pts = synth.POINTS[sh.name]
+    T_pre = args.tokens or max(pts)
+    dec = [int(v) for v in args.decode.split(",")] if args.decode else [p for p in pts if p <= 64]
+    n_exp = synth.n_experts_total(sh)
+    bank_bytes = n_exp * ft.slot_stride(sh.wdtype, sh.H, sh.I)
+    n_banks = max(2, min(8, math.ceil(4 * MALL_BYTES * 4 / bank_bytes)))
+    log(f"workload {sh.name}: {n_banks} weight banks of {bank_bytes / 1e9:.2f} GB")
+    banks = [Bank(sh, l, dev) for l in range(n_banks)]
+    torch.cuda.synchronize()
+
+    head = run_point(sh, banks, T_pre, args.steps, args.warmup, dev, prefill=True)
+    log("prefill", sh.name, json.dumps(head))
+    decode = []
+    for T in dec:
+        r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
+        g_ms = run_graph_point(sh, banks, T, max(args.steps, 50), args.warmup, dev)
+        decode.append(decode_entry(sh, r, g_ms, T))
+        log("decode", sh.name, json.dumps(decode[-1]))
+    cpu = None
+    if with_cpu:
+        cpu = cpu_baseline(sh, banks[0], T_pre, dev, args.cpu_seconds)
+        log("cpu", json.dumps(cpu))
+    del banks
+    torch.cuda.empty_cache()
+    return {"sh": sh, "T": T_pre, "n_banks": n_banks, "head": head, "decode": decode, "cpu": cpu,
+            "roofline": dict(**gemm1_roofline(head), traffic=stored_traffic(sh.name, T_pre),
+                             kernel="gate/up grouped GEMM + SwiGLU (gemm1)")}
+
+
+def summary_of(w):
+    """The other_workloads entry of one workload."""
+    h = w["head"]
+    return {"prefill": {"T": w["T"], "tokens_per_s": h["tokens_per_s"], "ms_per_step": h["ms_per_step"],
+                        "gemm1_us": h["gemm1_ms"] * 1e3, "gemm2_us": h["gemm2_ms"] * 1e3,
+                        "gemm1_tflops": h["gemm1_tflops"], "gemm2_tflops": h["gemm2_tflops"],
+                        "ffn_tflops": h["ffn_tflops"], "roofline": w["roofline"]},
+            "decode": w["decode"], "weights": w["sh"].wdtype}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -513,61 +616,37 @@ def main():
     torch.empty_like(cal).copy_(cal)
     del cal
     if args.workload == synth.SLOT_STACK.name:
-        run_slot_stack(args)
+        print(json.dumps(run_slot_stack(args)), flush=True)
         return
-    sh = synth.SHAPES[args.workload]
-    pts = synth.POINTS[sh.name]
-    T_pre = args.tokens or max(pts)
-    dec = [int(v) for v in args.decode.split(",")] if args.decode else [p for p in pts if p <= 64]
-    n_exp = synth.n_experts_total(sh)
-    bank_bytes = n_exp * ft.slot_stride(sh.wdtype, sh.H, sh.I)
-    n_banks = max(2, min(8, math.ceil(4 * MALL_BYTES * 4 / bank_bytes)))
-    log(f"workload {sh.name}: {n_banks} weight banks of {bank_bytes / 1e9:.2f} GB")
-    banks = [Bank(sh, l, dev) for l in range(n_banks)]
-    torch.cuda.synchronize()
-
-    head = run_point(sh, banks, T_pre, args.steps, args.warmup, dev, prefill=True)
-    log("prefill", json.dumps(head))
-    decode = []
-    for T in dec:
-        r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
-        g_ms = run_graph_point(sh, banks, T, max(args.steps, 50), args.warmup, dev)
-        decode.append({
-            "T": T, "tokens_per_s": T / (g_ms / 1e3), "ms_per_step": g_ms,
-            "eager_tokens_per_s": r["tokens_per_s"], "eager_ms_per_step": r["ms_per_step"],
-            "ffn_us": r["ffn_ms"] * 1e3, "gate_up_us": r["gemm1_ms"] * 1e3,
-            "down_us": r["gemm2_ms"] * 1e3, "active_experts": r["active_experts"],
-            "down_gbs": r["gemm2_gbs"],
-            "roofline": {"bound": "hbm", "achieved": r["gemm1_gbs"], "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": r["gemm1_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": ("gate/up weight streaming on matrix cores (stream_mx_kernel, NM=2)"
-                                    if sh.wdtype in ("mxfp4", "fp8", "nvfp4") and T >= 2 else
-                                    "gate/up weight streaming (stream_kernel, NM=2)"),
-                         "bytes_per_launch": r["w13_bytes"]}})
-        log("decode", json.dumps(decode[-1]))
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sh, banks[0], T_pre, dev, args.cpu_seconds)
-        log("cpu", json.dumps(cpu))
-
+    w = run_workload(args.workload, args, dev, with_cpu=not args.no_cpu_baseline)
+    sh, head = w["sh"], w["head"]
+    others = {}
+    if not args.no_extras and args.workload == DEFAULT_WORKLOAD and not args.tokens and not args.decode:
+        for name in EXTRA_WORKLOADS:
+            others[name] = summary_of(run_workload(name, args, dev, with_cpu=False))
+        st = run_slot_stack(args)
+        others[synth.SLOT_STACK.name] = {k: st[k] for k in ("value", "unit", "ms_per_step", "config",
+                                                             "roofline", "slot_cache", "hybrid_decode")}
     line = {
         "metric": "MoE-layer tokens/s (prefill); decode HBM GB/s and prefill MFMA TFLOP/s vs peak",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if sh.wdtype == "f32" else "bf16", "data": "synthetic",
-        "config": {"workload": f"{sh.name} prefill T={T_pre}", "H": sh.H, "E": sh.E, "k": sh.k,
-                   "I": sh.I, "n_shared": sh.n_shared, "tokens": T_pre, "weights": sh.wdtype,
-                   "activations": "bf16", "weight_banks": n_banks},
-        "roofline": dict(**gemm1_roofline(head),
-                     traffic=stored_traffic() if sh.name == "35b_a3b_bf16" and T_pre == 4096
-                     else None,
-                     kernel="gate/up grouped GEMM + SwiGLU (gemm1)"),
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if sh.wdtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{sh.name} prefill T={w['T']}", "H": sh.H, "E": sh.E, "k": sh.k,
+                   "I": sh.I, "n_shared": sh.n_shared, "tokens": w["T"], "weights": sh.wdtype,
+                   "activations": "bf16", "router_bias": sh.bias if sh.bias == "none" else
+                   f"{sh.bias}({sh.bias_param})", "weight_banks": w["n_banks"]},
+        "roofline": w["roofline"],
         "prefill_detail": {"gemm1_us": head["gemm1_ms"] * 1e3, "gemm2_us": head["gemm2_ms"] * 1e3,
-                           "ffn_tflops": head["ffn_tflops"]},
-        "decode": decode,
-        "cpu_baseline": cpu,
+                           "gemm1_tflops": head["gemm1_tflops"], "gemm2_tflops": head["gemm2_tflops"],
+                           "ffn_tflops": head["ffn_tflops"],
+                           "ffn_mfma_frac": head["ffn_tflops"] / MFMA_BF16_PEAK_TFS},
+        "decode": w["decode"],
+        "cpu_baseline": w["cpu"],
     }
+    if others:
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 

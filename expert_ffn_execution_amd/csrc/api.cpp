@@ -253,6 +253,21 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
         FT_CHECK_ARG(act_dt == FT_BF16, "bf16/MXFP4/FP8/NVFP4 weights take bf16 activations");
         FT_CHECK_ARG(y_dt == FT_BF16 || y_dt == FT_F32, "y_dt must be FT_BF16 or FT_F32");
     }
+    {
+        // The kernels address an activation row (x for gate/up, h for down)
+        // with a 32-bit element offset and a weight row inside a slot with a
+        // 32-bit byte offset: refuse shapes past either range.
+        const uint64_t hrows = (uint64_t)T * k + (uint64_t)w->n_shared * T;
+        size_t offs[6];
+        const uint64_t slot_bytes = layout(w->w_dt, w->H, w->I, offs);
+        if ((uint64_t)T * w->H >= (1ull << 32) || hrows * w->I >= (1ull << 32) ||
+            slot_bytes >= (1ull << 32))
+            return set_error(FT_ERR_UNSUPPORTED,
+                             "shape beyond 32-bit offsets: T*H = %llu, (T*k + n_shared*T)*I = %llu, "
+                             "expert bytes = %llu (each must be < 2^32)",
+                             (unsigned long long)T * w->H, (unsigned long long)(hrows * w->I),
+                             (unsigned long long)slot_bytes);
+    }
     const FfnPlan p = plan_ffn(*w, T, k);
     FT_CHECK_ARG(ws && ws_bytes >= p.total && ((uintptr_t)ws & 255) == 0,
                  "workspace must be 256-byte aligned and >= %zu bytes", p.total);

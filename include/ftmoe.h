@@ -89,6 +89,13 @@ const char* ft_version(void);
  *     renormalised.
  * Logits must be finite (not checked on the device; the result is unspecified
  * otherwise).
+ * Computed logits are deterministic for a given batch, but their fp32
+ * summation order depends on the batch: up to 64 tokens take a dot-product
+ * kernel, more take matrix-core tiles whose blocks start their K loop at
+ * different stages.  A token's logits can thus differ in the last bits
+ * between batch sizes or positions (each within 1e-5 relative of the exact
+ * sum), and with them the picks at near-ties.  Routing from supplied logits
+ * is exact and position-independent.
  * ------------------------------------------------------------------------ */
 ft_status ft_moe_route(const void* x, ft_dtype x_dt, const void* w_router,
                        const float* logits_in, const float* bias, int T, int H, int E,
@@ -177,6 +184,10 @@ typedef struct {
  *   y_perm [T*k + n_shared*T][H] device, y_dt = FT_BF16 (bf16 weights/MXFP4)
  *     or FT_F32 (any weights);
  *   ws: device workspace of >= ft_moe_ffn_workspace(w, T, k) bytes.
+ * The kernels address activation rows with 32-bit element offsets and weight
+ * rows inside a slot with 32-bit byte offsets: T*H, (T*k + n_shared*T)*I and
+ * the expert's slot bytes (ft_expert_layout) must each be below 2^32, else
+ * FT_ERR_UNSUPPORTED and nothing is enqueued.
  * ------------------------------------------------------------------------ */
 size_t ft_moe_ffn_workspace(const ft_moe_weights* w, int T, int k);
 ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, int T, int k,

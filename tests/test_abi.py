@@ -111,6 +111,36 @@ def test_ffn_rejects_bad_arguments():
     assert lib.ft_moe_ffn_workspace(C.byref(w), 4, 2) > 4 * 2 * 128 * 2
 
 
+def test_ffn_refuses_shapes_past_32bit_offsets():
+    """The kernels address activation rows with 32-bit element offsets: T*k rows
+    of h at I = 2048 reach 2^32 elements at T*k = 2^21, so the boundary refuses
+    it (and anything larger) instead of wrapping; just below it is accepted up
+    to the workspace check."""
+    lib = ft.load()
+    p = C.c_void_p(4096)
+
+    def call(w, T, k, ws_bytes=1 << 62):
+        return lib.ft_moe_ffn(C.byref(w), p, ft.BF16, T, k, p, p, None, p, ft.BF16, p, ws_bytes, None)
+
+    w = _w(E=256, H=256, I=2048, slot_stride=ft.slot_stride("bf16", 256, 2048))
+    assert call(w, T=1 << 18, k=8) == ft.ERR_UNSUPPORTED          # (T*k)*I = 2^32
+    assert "32-bit" in ft.last_error()
+    # one token fewer passes this check and stops at the next one (a workspace
+    # too small), so no kernel is launched
+    assert call(w, T=(1 << 18) - 1, k=8, ws_bytes=16) == ft.ERR_INVALID_ARG
+    assert "workspace" in ft.last_error()
+    # one shared-expert row per token tips it over: (T*k + T)*I >= 2^32
+    ws = _w(E=256, H=256, I=2048, n_shared=1, slot_stride=ft.slot_stride("bf16", 256, 2048))
+    T = (1 << 32) // (9 * 2048) + 1
+    assert call(ws, T=T, k=8) == ft.ERR_UNSUPPORTED
+    # T*H at the gate/up input
+    wh = _w(E=8, H=1 << 16, I=64, slot_stride=ft.slot_stride("bf16", 1 << 16, 64))
+    assert call(wh, T=1 << 16, k=1) == ft.ERR_UNSUPPORTED
+    # an expert slot of 2^32 bytes or more
+    big = ft.slot_stride("bf16", 1 << 16, 1 << 14)
+    assert call(_w(E=8, H=1 << 16, I=1 << 14, slot_stride=big), T=1, k=1) == ft.ERR_UNSUPPORTED
+
+
 def test_combine_rejects_bad_arguments():
     lib = ft.load()
     p = C.c_void_p(4096)

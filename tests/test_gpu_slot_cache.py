@@ -114,7 +114,8 @@ def test_pageable_pool_is_refused():
 def test_full_size_slot_stack_sampled():
     """8 layers of the 35B-A3B layer shape, 64 slots per layer under one global
     LRU, Zipf(1.1)-biased routers: a few decode steps and one prefill, each
-    layer's output compared with the resident computation."""
+    layer's output compared with the resident computation; then decode steps
+    and a prefill with every layer compared with the oracle."""
     sh = synth.SLOT_STACK
     L = synth.SLOT_STACK_LAYERS
     _say("full-size slot stack")
@@ -133,6 +134,26 @@ def test_full_size_slot_stack_sampled():
             assert torch.equal(outs[l], ref)
         assert st.stats.prefetch_warnings == 0
         _say("  hit rate", st.stats.hit_rate, "demand", st.stats.demand)
+        # every layer against the oracle, routed from the oracle's logits on both
+        # sides: two decode steps (all tokens) and one prefill (64 seeded tokens
+        # of each layer)
+        experts = [[unpack_slot(st.host[l, e], sh) for e in range(sh.E)] for l in range(L)]
+        rng = np.random.default_rng(5)
+        for step, T in ((200, 1), (201, 1), (202, 2048)):
+            xs = _inputs(sh, L, T, step)
+            lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
+            outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs],
+                              prefill=T > 1)
+            tok = (np.arange(T, dtype=np.int32) if T <= 64
+                   else np.sort(rng.choice(T, size=64, replace=False)).astype(np.int32))
+            for l in range(L):
+                ids, w = orc.route(lgs[l], sh.k, st.biases[l].cpu().numpy())
+                ref = orc.moe_layer(xs[l].cpu(), ids, w, experts[l], "bf16", sh.I, out_fmt="f32",
+                                    tokens=tok)
+                got = outs[l].cpu()[torch.from_numpy(tok).long()]
+                e, m = check_close(got, ref, "bf16", f"full-size stack T{T} layer {l}")
+            _say(f"  oracle T={T}: {L} layers, last rel_l2 {e:.3e} max/amax {m:.3e}")
+        assert st.stats.prefetch_warnings == 0
     finally:
         st.close()
 
