@@ -32,8 +32,9 @@ EXPORTS = [
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
-    "ft_host_moe_ffn_submit", "ft_host_job_wait",
+    "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FT_NOALLOC_SCRATCH_BYTES
 
 
 class FtError(RuntimeError):
@@ -109,6 +110,7 @@ def load() -> C.CDLL:
         "ft_expert_layout": [I32, I32, I32, P],
         "ft_moe_ffn_workspace": [C.POINTER(MoeWeights), I32, I32],
         "ft_moe_ffn": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P, SZ, P],
+        "ft_moe_ffn_noalloc": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P],
         "ft_moe_ffn_set_path": [I32],
         "ft_set_profile_events": [I32, P, P],
         "ft_moe_combine": [P, I32, P, P, I32, I32, I32, I32, P, I32, P],
@@ -276,6 +278,21 @@ def ffn(wts: MoeWeights, x: torch.Tensor, k: int, perm: torch.Tensor, offsets: t
     _check(load().ft_moe_ffn(C.byref(wts), _p(x), _dt(x), T, k, _p(perm), _p(offsets),
                              _p(slot_of_expert), _p(y), _dt(y), _p(ws), ws.numel(),
                              _stream(stream)))
+    return y
+
+
+def ffn_noalloc(wts: MoeWeights, x: torch.Tensor, k: int, perm: torch.Tensor,
+                offsets: torch.Tensor, slot_of_expert: Optional[torch.Tensor] = None,
+                y_dtype=torch.bfloat16, y: Optional[torch.Tensor] = None, stream=None):
+    """ft_moe_ffn_noalloc (workspace in the library's static scratch array).
+    Returns y_perm [T*k + n_shared*T, H]; y is allocated here unless given."""
+    T = x.shape[0]
+    rows = T * k + wts.n_shared * T
+    if y is None:
+        y = torch.empty((rows, wts.H), dtype=y_dtype, device=x.device)
+    _dev(x, perm, offsets, slot_of_expert, y)
+    _check(load().ft_moe_ffn_noalloc(C.byref(wts), _p(x), _dt(x), T, k, _p(perm), _p(offsets),
+                                     _p(slot_of_expert), _p(y), _dt(y), _stream(stream)))
     return y
 
 

@@ -195,6 +195,33 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
                      const int32_t* slot_of_expert, void* y_perm, ft_dtype y_dt, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* --------------------------------------------------------------------------
+ * ft_moe_ffn_noalloc -- ft_moe_ffn without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc.
+ *
+ * The workspace is a static device array of FT_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library, which the HIP runtime places on every GPU the
+ * library runs on and keeps until the process ends; its device address is
+ * looked up once per device, on the first call with that device current.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   Arguments, results (bit for bit) and errors: those of ft_moe_ffn on the
+ *   same inputs, without ws / ws_bytes.  FT_ERR_CAPACITY (nothing enqueued)
+ *   when ft_moe_ffn_workspace(w, T, k) exceeds FT_NOALLOC_SCRATCH_BYTES;
+ *   FT_ERR_HIP when the array's address cannot be obtained.
+ *   Every call on one GPU uses that GPU's one array and leaves its last
+ *   contents there; nothing in it needs clearing (every byte a call reads was
+ *   written earlier in the same call).  Calls that can overlap on one GPU
+ *   (other streams, other threads, without ordering between them) race on the
+ *   array and give undefined results: order them on one stream.
+ * ------------------------------------------------------------------------ */
+#define FT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ft_status ft_moe_ffn_noalloc(const ft_moe_weights* w, const void* x, ft_dtype act_dt, int T,
+                             int k, const int32_t* perm, const int32_t* offsets,
+                             const int32_t* slot_of_expert, void* y_perm, ft_dtype y_dt,
+                             void* stream);
+
 /* Kernel family used by ft_moe_ffn: 0 = choose by size (default),
  * 1 = weight-streaming (small token counts), 2 = MFMA tiles (large token
  * counts).  Process-wide; a tuning and test knob.  Returns the previous value. */

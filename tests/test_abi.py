@@ -141,6 +141,23 @@ def test_ffn_refuses_shapes_past_32bit_offsets():
     assert call(_w(E=8, H=1 << 16, I=1 << 14, slot_stride=big), T=1, k=1) == ft.ERR_UNSUPPORTED
 
 
+def test_ffn_noalloc_refuses_what_its_scratch_cannot_hold():
+    """ft_moe_ffn_noalloc takes its workspace from a 64 MiB static array: a
+    call needing more returns FT_ERR_CAPACITY before any device work."""
+    lib = ft.load()
+    p = C.c_void_p(4096)
+    w = _w(E=128, H=2048, I=768, slot_stride=ft.slot_stride("bf16", 2048, 768))
+    T = 8192                                   # h alone: 8192 * 8 * 768 * 2 B = 96 MiB
+    assert lib.ft_moe_ffn_workspace(C.byref(w), T, 8) > ft.NOALLOC_SCRATCH_BYTES
+    assert lib.ft_moe_ffn_noalloc(C.byref(w), p, ft.BF16, T, 8, p, p, None, p, ft.BF16,
+                                  None) == ft.ERR_CAPACITY
+    assert "static scratch" in ft.last_error()
+    assert lib.ft_moe_ffn_noalloc(None, p, ft.BF16, 4, 2, p, p, None, p, ft.BF16,
+                                  None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_ffn_noalloc(C.byref(w), p, ft.BF16, 0, 8, p, p, None, p, ft.BF16,
+                                  None) == ft.OK          # empty batch: no-op
+
+
 def test_combine_rejects_bad_arguments():
     lib = ft.load()
     p = C.c_void_p(4096)
