@@ -83,6 +83,10 @@ def summarize_pmc(fetch_dir, write_dir, workload, T):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        for f in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+            rows += [{"Kernel_Name": n, "Counter_Value": v} for n, v in rocpd_rows(
+                f, "select kernel_name, value from counters_collection where counter_name = ?",
+                (counter,))]
         cal = [float(r["Counter_Value"]) for r in rows
                if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
         cal = max(cal) if cal else float("nan")
@@ -104,10 +108,31 @@ def summarize_pmc(fetch_dir, write_dir, workload, T):
     print(json.dumps(out))
 
 
-def summarize_stats(stats_csv, command, out_md, top=16):
-    """rocprofv3 --kernel-trace --stats kernel_stats.csv -> a short markdown table."""
+def rocpd_rows(db, query, params=()):
+    """Rows of a query on a rocprofv3 rocpd database (its SQLite output)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(query, params))
+    finally:
+        con.close()
+
+
+def summarize_stats(stats, command, out_md, top=16):
+    """rocprofv3 --kernel-trace --stats output (kernel_stats.csv, or the rocpd
+    database *_results.db) -> a short markdown table of kernel durations."""
     import csv
-    rows = list(csv.DictReader(open(stats_csv)))
+    if stats.endswith(".db"):
+        rows = []
+        q = ("select name, count(*), sum(duration), avg(duration), min(duration), max(duration) "
+             "from kernels group by name order by sum(duration) desc")
+        res = rocpd_rows(stats, q)
+        tot = sum(r[2] for r in res)
+        for name, n, sm, av, mn, mx in res:
+            rows.append({"Name": name, "Calls": n, "AverageNs": av, "MinNs": mn, "MaxNs": mx,
+                         "Percentage": 100.0 * sm / tot})
+    else:
+        rows = list(csv.DictReader(open(stats)))
     lines = [f"# {os.path.basename(out_md)[:-3]}", "", "Command (from the repository root):", "",
              "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
