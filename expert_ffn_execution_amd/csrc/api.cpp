@@ -25,6 +25,7 @@ ft_status launch_ffn_stream(const FfnGeom&, const void*, const int32_t*, const i
                             const int32_t*, int, void*, void*, ft_dtype, hipStream_t);
 ft_status launch_combine(const void*, ft_dtype, const int32_t*, const float*, int, int, int, int,
                          void*, ft_dtype, hipStream_t);
+ft_status launch_scatter_rows(const float*, const int64_t*, int, int, void*, ft_dtype, hipStream_t);
 bool topk_align_small_ok(int T, int k);
 ft_status launch_topk_align_small(const float*, const float*, int, int, int, int32_t*, float*,
                                   int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t);
@@ -330,6 +331,17 @@ ft_status ft_moe_combine(const void* y_perm, ft_dtype y_dt, const int32_t* inv_p
     ft_status r = launch_combine(y_perm, y_dt, inv_perm, topk_w, T, k, H, n_shared, out, out_dt, s);
     prof_end(PROF_COMBINE, s);
     return r;
+}
+
+ft_status ft_moe_scatter_rows(const float* rows, const int64_t* pos, int n, int H, void* y_perm,
+                              ft_dtype y_dt, void* stream) {
+    clear_error();
+    FT_CHECK_ARG(n >= 0 && H > 0 && H % 8 == 0, "bad n/H (H must be a multiple of 8)");
+    FT_CHECK_ARG(y_dt == FT_BF16 || y_dt == FT_F32, "y_dt must be FT_BF16 or FT_F32");
+    if (n == 0) return FT_OK;
+    FT_CHECK_ARG(rows && pos && y_perm, "null pointer");
+    FT_CHECK_ARG(aligned16(rows) && aligned16(y_perm), "rows / y_perm must be 16-byte aligned");
+    return launch_scatter_rows(rows, pos, n, H, y_perm, y_dt, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -53,9 +53,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     }
 }
 
+// y[pos[i]] = rows[i] rounded to the output format (fp32 -> bf16 to nearest
+// even, or copied), one block per row, 8 consecutive elements per thread.
+template <typename OT>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restrict__ rows,
+                                                           const int64_t* __restrict__ pos, int H,
+                                                           OT* __restrict__ y) {
+    const int i = blockIdx.x;
+    const int d = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (d >= H) return;
+    const float* src = rows + (size_t)i * H + d;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + 4);
+    OT* dst = y + (size_t)pos[i] * H + d;
+    if constexpr (sizeof(OT) == 2) {
+        *reinterpret_cast<u32x4_t*>(dst) =
+            u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                    pack_bf16x2(b[2], b[3])};
+    } else {
+        *reinterpret_cast<f32x4_t*>(dst) = a;
+        *reinterpret_cast<f32x4_t*>(dst + 4) = b;
+    }
+}
+
 }  // namespace
 
 namespace ft {
+
+ft_status launch_scatter_rows(const float* rows, const int64_t* pos, int n, int H, void* y,
+                              ft_dtype y_dt, hipStream_t s) {
+    dim3 grid((unsigned)n, (unsigned)cdiv(H, 256 * 8)), block(256);
+    if (y_dt == FT_BF16)
+        scatter_rows_kernel<__bf16><<<grid, block, 0, s>>>(rows, pos, H, (__bf16*)y);
+    else
+        scatter_rows_kernel<float><<<grid, block, 0, s>>>(rows, pos, H, (float*)y);
+    FT_LAUNCHED("scatter_rows");
+    return FT_OK;
+}
 
 ft_status launch_combine(const void* y, ft_dtype y_dt, const int32_t* inv, const float* w, int T,
                          int k, int H, int n_shared, void* out, ft_dtype out_dt, hipStream_t s) {

@@ -26,6 +26,7 @@
 //
 // Plain host C++ (built with the host compiler, no device pass): only the C
 // header and the library's error helpers.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -313,10 +314,12 @@ private:
             }
             run_job(j);
             {
+                // notify under the job's lock: once it is released the waiter
+                // may return and free the job (its condition variable too)
                 std::lock_guard<std::mutex> g(j->mu);
                 j->done = true;
+                j->cv.notify_all();
             }
-            j->cv.notify_all();
         }
     }
     std::thread th_;
@@ -398,4 +401,23 @@ extern "C" ft_status ft_host_job_wait(ft_host_job* job) {
     const ft_status st = job->st;
     delete job;
     return st;
+}
+
+// The split of a decode step's m missed experts (chenxutan.com article,
+// "瓶颈为什么是带宽而不是容量", the q* strategy; freelamp.com article, section
+// 2.1): n go over PCIe to the GPU (n W / Bp) while m - n are computed here
+// from host memory ((m - n) W / Bh), at the same time.  The printed formula is
+// garbled; balancing the two sides gives n* = m Bp / (Bp + Bh), and of the two
+// integers around it the one whose slower side finishes sooner is taken (the
+// lower one on a tie).
+extern "C" int ft_split_misses(int m, double bp, double bh) {
+    if (m <= 0) return 0;
+    if (!(bh > 0.0)) return m;   // no host side: everything to the GPU
+    if (!(bp > 0.0)) return 0;   // no link: everything on the host
+    const double q = (double)m * bp / (bp + bh);
+    int lo = (int)q;
+    lo = lo < 0 ? 0 : lo > m ? m : lo;
+    const int hi = lo + 1 > m ? m : lo + 1;
+    auto cost = [&](int n) { return std::max(n / bp, (m - n) / bh); };
+    return cost(lo) <= cost(hi) ? lo : hi;
 }

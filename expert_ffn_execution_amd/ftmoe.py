@@ -32,7 +32,8 @@ EXPORTS = [
     "ft_slot_cache_map", "ft_slot_cache_release", "ft_slot_cache_prefetch", "ft_slot_cache_evict",
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
-    "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc",
+    "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc", "ft_split_misses",
+    "ft_moe_scatter_rows",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # FT_NOALLOC_SCRATCH_BYTES
 
@@ -111,6 +112,7 @@ def load() -> C.CDLL:
         "ft_moe_ffn_workspace": [C.POINTER(MoeWeights), I32, I32],
         "ft_moe_ffn": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P, SZ, P],
         "ft_moe_ffn_noalloc": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P],
+        "ft_moe_scatter_rows": [P, P, I32, I32, P, I32, P],
         "ft_moe_ffn_set_path": [I32],
         "ft_set_profile_events": [I32, P, P],
         "ft_moe_combine": [P, I32, P, P, I32, I32, I32, I32, P, I32, P],
@@ -135,6 +137,8 @@ def load() -> C.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = C.c_int
+    lib.ft_split_misses.argtypes = [I32, C.c_double, C.c_double]
+    lib.ft_split_misses.restype = C.c_int
     lib.ft_moe_align_workspace.restype = C.c_size_t
     lib.ft_expert_layout.restype = C.c_size_t
     lib.ft_moe_ffn_workspace.restype = C.c_size_t
@@ -355,6 +359,28 @@ def host_moe_ffn_submit(pool: torch.Tensor, E: int, H: int, I: int, k: int,
     n = C.c_int()
     _check(load().ft_host_moe_ffn_submit(C.byref(d), C.byref(h), C.byref(n)))
     return HostJob(h, n.value, (pool, offsets, perm, x, rows, pos))
+
+
+def split_misses(m: int, bp: float, bh: float) -> int:
+    """ft_split_misses: how many of m missed experts to copy to the GPU (the
+    rest run on host cores), from the measured Bp and Bh in GB/s."""
+    return load().ft_split_misses(int(m), float(bp), float(bh))
+
+
+def scatter_rows(rows: torch.Tensor, pos: torch.Tensor, y_perm: torch.Tensor, n: Optional[int] = None,
+                 stream=None) -> torch.Tensor:
+    """ft_moe_scatter_rows: y_perm[pos[i]] = rows[i] (rounded to y_perm's dtype)
+    for the first n rows (all by default); rows [>=n, H] fp32, pos [>=n] int64,
+    both on y_perm's device."""
+    n = rows.shape[0] if n is None else n
+    H = y_perm.shape[1]
+    if (rows.dtype != torch.float32 or pos.dtype != torch.int64 or rows.shape[1] != H
+            or not rows.is_contiguous() or not pos.is_contiguous() or not y_perm.is_contiguous()):
+        raise FtError(ERR_INVALID_ARG, "scatter_rows: rows fp32 [n, H], pos int64 [n], contiguous")
+    _dev(rows, pos, y_perm)
+    _check(load().ft_moe_scatter_rows(_p(rows), _p(pos), n, H, _p(y_perm), _dt(y_perm),
+                                      _stream(stream)))
+    return y_perm
 
 
 def combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, w: torch.Tensor, n_shared: int = 0,

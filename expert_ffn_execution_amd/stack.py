@@ -17,11 +17,16 @@ paragraph on prefill overlap).
 
 Hybrid decode (``hybrid=True``): the pages' bandwidth-adaptive split of cache
 misses.  Of the m experts of layer l+1 that are neither resident nor in
-flight, n = split_misses(m, Bp, Bh) are copied to the GPU as before and the
+flight, n = ft_split_misses(m, Bp, Bh) are copied to the GPU as before and the
 rest are computed on host cores straight from the pinned pool, as one job
 queued on the library's host threads (ft_host_moe_ffn_submit) that overlaps
-the GPU's work on layer l and the copies of layer l+1; their rows are written
-into layer l+1's y_perm before its combine.
+the GPU's work on layer l and the copies of layer l+1; their rows are copied
+to the device and placed into layer l+1's y_perm by ft_moe_scatter_rows before
+its combine.
+
+Each layer's device buffers (logits, routing, alignment, workspaces, y_perm,
+output) are allocated once per batch size and reused from step to step: the
+outputs forward() returns stay valid until the next call.
 Bp (pinned host-to-device GB/s) and Bh (host FFN GB/s of expert weights) come
 from ``calibrate()`` (chenxutan.com article, "瓶颈为什么是带宽而不是容量", the
 q* strategy; freelamp.com article, section 2.1).
@@ -39,25 +44,9 @@ from . import ftmoe as ft
 from . import synth
 
 
-def split_misses(m: int, bp: float, bh: float) -> int:
-    """How many of m missed experts to copy to the GPU; the rest run on the CPU.
-
-    Copying n experts takes n*W/bp and computing m - n on the CPU (m - n)*W/bh;
-    the two overlap, so the step waits for the slower one.  The balance point
-    is n* = m*bp/(bp + bh) (the pages print the ratio garbled; balancing the
-    two sides gives this form): take whichever neighbouring integer finishes
-    sooner."""
-    if m <= 0:
-        return 0
-    if bh <= 0:
-        return m
-    if bp <= 0:
-        return 0
-    q = m * bp / (bp + bh)
-    lo = min(m, max(0, int(q)))
-    hi = min(m, lo + 1)
-    cost = lambda n: max(n / bp, (m - n) / bh)
-    return lo if cost(lo) <= cost(hi) else hi
+# How many of m missed experts to copy to the GPU (the rest run on host
+# cores): the library's ft_split_misses.
+split_misses = ft.split_misses
 
 
 @dataclasses.dataclass
@@ -116,25 +105,55 @@ class SlotStack:
         self.copy_stream = torch.cuda.Stream(device=dev)
         self.stats = StackStats()
         self._hbufs = [dict() for _ in range(n_layers)]
+        self._dbufs = [dict() for _ in range(n_layers)]
         # host FFN outputs, two sets used by alternate layers: a set is refilled
         # only after the copy that read it two layers earlier has finished
         self._rows = [None, None]
+        self._rows_dev = [None, None]
         self._rows_ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.bp = self.bh = 0.0   # GB/s, from calibrate()
         # host FFN threads: 8 measured fastest on a 16-core share (84-96 GB/s)
         self.host_threads = max(1, min(8, len(os.sched_getaffinity(0))))
 
     # ------------------------------------------------------------------
+    def _dev_bufs(self, l: int, T: int, out_dtype) -> dict:
+        """Layer l's device buffers for a batch of T tokens (allocated on the
+        first use of this T, then reused)."""
+        db = self._dbufs[l]
+        if db.get("T") != T:
+            sh, dev, k = self.sh, self.dev, self.sh.k
+            i32, f32 = torch.int32, torch.float32
+            db.clear()
+            db.update(T=T, logits=torch.empty((T, sh.E), dtype=f32, device=dev),
+                      ids=torch.empty((T, k), dtype=i32, device=dev),
+                      w=torch.empty((T, k), dtype=f32, device=dev),
+                      align=(torch.empty(sh.E, dtype=i32, device=dev),
+                             torch.empty(sh.E + 1, dtype=i32, device=dev),
+                             torch.empty(T * k, dtype=i32, device=dev),
+                             torch.empty(T * k, dtype=i32, device=dev)),
+                      aws=torch.empty(max(1, ft.align_workspace(T, k, sh.E)), dtype=torch.uint8,
+                                      device=dev),
+                      fws=torch.empty(max(256, ft.ffn_workspace(self.wts, T, k)),
+                                      dtype=torch.uint8, device=dev),
+                      y=torch.empty((T * k + sh.n_shared * T, sh.H), dtype=torch.bfloat16,
+                                    device=dev))
+        if db.get("out") is None or db["out"].dtype != out_dtype:
+            db["out"] = torch.empty((T, self.sh.H), dtype=out_dtype, device=self.dev)
+        return db
+
     def _route(self, l: int, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
-               want_x: bool = False):
+               want_x: bool = False, out_dtype=torch.bfloat16):
         sh = self.sh
         T = x.shape[0]
+        db = self._dev_bufs(l, T, out_dtype)
         if logits is None:
             ids, w, _ = ft.route(T, sh.E, sh.k, x=x, w_router=self.routers[l],
-                                 bias=self.biases[l])
+                                 bias=self.biases[l], logits_out=db["logits"], ids=db["ids"],
+                                 w=db["w"])
         else:
-            ids, w, _ = ft.route(T, sh.E, sh.k, logits=logits, bias=self.biases[l])
-        counts, offsets, perm, inv = ft.align(ids, sh.E)
+            ids, w, _ = ft.route(T, sh.E, sh.k, logits=logits, bias=self.biases[l],
+                                 ids=db["ids"], w=db["w"])
+        counts, offsets, perm, inv = ft.align(ids, sh.E, ws=db["aws"], out=db["align"])
         hb = self._host_bufs(l, T)
         hb["counts"].copy_(counts, non_blocking=True)
         if want_x:  # the host FFN's inputs, ready with the routing (no wait on later work)
@@ -144,7 +163,7 @@ class SlotStack:
         ev = hb["ev"]
         ev.record()
         return dict(ids=ids, w=w, offsets=offsets, perm=perm, inv=inv, counts_h=hb["counts"],
-                    hb=hb, ev=ev)
+                    hb=hb, ev=ev, db=db)
 
     def _host_bufs(self, l: int, T: int) -> dict:
         """Layer l's pinned read-back buffers for a batch of T tokens, reused
@@ -222,6 +241,8 @@ class SlotStack:
         if self._rows[p] is None or self._rows[p][0].shape[0] < need:
             self._rows[p] = (torch.empty((need, sh.H), dtype=torch.float32, pin_memory=True),
                              torch.empty(need, dtype=torch.int64, pin_memory=True))
+            self._rows_dev[p] = (torch.empty((need, sh.H), dtype=torch.float32, device=self.dev),
+                                 torch.empty(need, dtype=torch.int64, device=self.dev))
         else:
             self._rows_ev[p].synchronize()  # the copy out of this set two layers ago
         rows, pos = self._rows[p]
@@ -229,7 +250,7 @@ class SlotStack:
                                      hb["offsets"], hb["perm"], hb["x"], rows, pos,
                                      self.host_threads)
         self.stats.cpu_experts += len(experts)
-        return job, (rows, pos, self._rows_ev[p])
+        return job, (rows, pos, self._rows_dev[p], self._rows_ev[p])
 
     def forward(self, xs: List[torch.Tensor], prefill: bool = False,
                 out_dtype=torch.bfloat16,
@@ -246,23 +267,25 @@ class SlotStack:
         lg = logits if logits is not None else [None] * self.L
         outs = []
         want_x = hybrid and not prefill
-        r = self._route(0, xs[0], lg[0])
+        r = self._route(0, xs[0], lg[0], out_dtype=out_dtype)
         self._map(0, self._experts_of(r))
         for l in range(self.L):
-            nxt = (self._route(l + 1, xs[l + 1], lg[l + 1], want_x=want_x)
+            nxt = (self._route(l + 1, xs[l + 1], lg[l + 1], want_x=want_x, out_dtype=out_dtype)
                    if l + 1 < self.L else None)
             if sh.n_shared:
                 self.wts.shared_slot = self.cache.lookup(l, sh.E)
+            db = r["db"]
             y = ft.ffn(self.wts, xs[l], sh.k, r["perm"], r["offsets"],
-                       slot_of_expert=self.tables[l])
+                       slot_of_expert=self.tables[l], y=db["y"], ws=db["fws"])
             if "cpu" in r:  # the host's rows of this layer (its experts were skipped above)
-                job, (rows, pos, ev) = r["cpu"]
+                job, (rows, pos, (rows_d, pos_d), ev) = r["cpu"]
                 n = job.wait()
-                y.index_copy_(0, pos[:n].to(self.dev, non_blocking=True),
-                              rows[:n].to(self.dev, non_blocking=True).to(y.dtype))
+                if n:
+                    rows_d[:n].copy_(rows[:n], non_blocking=True)
+                    pos_d[:n].copy_(pos[:n], non_blocking=True)
+                    ft.scatter_rows(rows_d, pos_d, y, n)
                 ev.record()
-            outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared,
-                                   out_dtype=out_dtype))
+            outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared, out=db["out"]))
             self.cache.release(l)
             if nxt is not None:
                 if prefill:

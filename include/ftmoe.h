@@ -484,6 +484,31 @@ typedef struct ft_host_job_s ft_host_job;
 ft_status ft_host_moe_ffn_submit(const ft_host_moe_job_desc* d, ft_host_job** job, int* n_rows);
 ft_status ft_host_job_wait(ft_host_job* job);
 
+/* --------------------------------------------------------------------------
+ * ft_split_misses -- how many of a decode step's m missed experts to copy to
+ * the GPU; the other m - n are computed on host cores (ft_host_moe_ffn_submit)
+ * at the same time (chenxutan.com article, "瓶颈为什么是带宽而不是容量", the
+ * q* strategy; freelamp.com article, section 2.1).  Copying n experts takes
+ * n W / Bp and the host FFN of m - n takes (m - n) W / Bh; they overlap, so the
+ * step waits for the slower.  The printed formula is garbled; balancing the
+ * two sides gives n* = m Bp / (Bp + Bh), and of the integers on either side
+ * the one that finishes sooner is returned (the lower one on a tie).
+ *   bp: measured pinned host-to-device GB/s; bh: measured host FFN GB/s of
+ *   expert weights.  bh <= 0 returns m, bp <= 0 returns 0, m <= 0 returns 0.
+ * Host arithmetic only; never fails. */
+int ft_split_misses(int m, double bp, double bh);
+
+/* --------------------------------------------------------------------------
+ * ft_moe_scatter_rows -- place expert output rows computed elsewhere (the
+ * host's share of a hybrid decode step, ft_host_moe_ffn_submit) into y_perm:
+ *   y_perm[pos[i]] = rows[i] for i < n, rounded to y_dt (FT_BF16: to nearest
+ *   even; FT_F32: copied).
+ * rows [n][H] fp32, pos [n] int64 (distinct rows of y_perm), y_perm
+ * [..][H] in y_dt: all device memory; H % 8 == 0, rows and y_perm 16-byte
+ * aligned.  Asynchronous on `stream`; n == 0 is a no-op. */
+ft_status ft_moe_scatter_rows(const float* rows, const int64_t* pos, int n, int H, void* y_perm,
+                              ft_dtype y_dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -158,6 +158,16 @@ def test_ffn_noalloc_refuses_what_its_scratch_cannot_hold():
                                   None) == ft.OK          # empty batch: no-op
 
 
+def test_scatter_rows_rejects_bad_arguments():
+    lib = ft.load()
+    p = C.c_void_p(4096)
+    assert lib.ft_moe_scatter_rows(p, p, 4, 100, p, ft.BF16, None) == ft.ERR_INVALID_ARG  # H % 8
+    assert lib.ft_moe_scatter_rows(p, p, 4, 64, p, ft.MXFP4, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_scatter_rows(p, p, -1, 64, p, ft.BF16, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_scatter_rows(None, None, 0, 64, None, ft.BF16, None) == ft.OK  # empty
+    assert lib.ft_moe_scatter_rows(C.c_void_p(4100), p, 4, 64, p, ft.BF16, None) == ft.ERR_INVALID_ARG
+
+
 def test_combine_rejects_bad_arguments():
     lib = ft.load()
     p = C.c_void_p(4096)

@@ -281,6 +281,27 @@ def test_layer_a3b_prefill_all_rows():
     _check_heaviest_expert(L, x.to(DEV), r, "a3b prefill")
 
 
+@pytest.mark.parametrize("y_dtype", [torch.bfloat16, torch.float32])
+def test_scatter_rows(y_dtype):
+    """ft_moe_scatter_rows puts fp32 rows at the listed rows of y_perm, rounded
+    to y's dtype (torch's round-to-nearest-even conversion as the reference),
+    and leaves the other rows alone."""
+    _say("scatter rows", y_dtype)
+    rng = np.random.default_rng(17)
+    R, H, n = 300, 2048, 37
+    rows = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32) * 3.0)
+    rows[0, :8] = torch.tensor([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, 65504.0, 1e-40, -1e-30,
+                                3.0e38, 1.00390625])  # ties, signed zero, subnormal, large
+    pos = torch.from_numpy(rng.choice(R, size=n, replace=False).astype(np.int64))
+    y = torch.full((R, H), 5.0, dtype=y_dtype, device=DEV)
+    ft.scatter_rows(rows.to(DEV), pos.to(DEV), y)
+    ref = torch.full((R, H), 5.0, dtype=y_dtype)
+    ref[pos] = rows.to(y_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu().view(torch.int16 if y_dtype == torch.bfloat16 else torch.int32),
+                       ref.view(torch.int16 if y_dtype == torch.bfloat16 else torch.int32))
+
+
 # ---------------------------------------------------------------------------
 # invariants on the device
 # ---------------------------------------------------------------------------
