@@ -412,14 +412,35 @@ def run_slot_stack(args):
     resident = [st.host[l].to(dev) for l in range(L)]
     rwts = [ft.make_weights(sh.wdtype, sh.E, sh.H, sh.I, p) for p in resident]
 
+    rbufs = {}
+
+    def resident_bufs(l, T):
+        # per-layer buffers reused from step to step, as the stack does
+        if (l, T) not in rbufs:
+            i32, f32 = torch.int32, torch.float32
+            rbufs[(l, T)] = dict(
+                logits=torch.empty((T, sh.E), dtype=f32, device=dev),
+                ids=torch.empty((T, sh.k), dtype=i32, device=dev),
+                w=torch.empty((T, sh.k), dtype=f32, device=dev),
+                al=(torch.empty(sh.E, dtype=i32, device=dev), torch.empty(sh.E + 1, dtype=i32, device=dev),
+                    torch.empty(T * sh.k, dtype=i32, device=dev), torch.empty(T * sh.k, dtype=i32, device=dev)),
+                aws=torch.empty(max(1, ft.align_workspace(T, sh.k, sh.E)), dtype=torch.uint8, device=dev),
+                fws=torch.empty(max(256, ft.ffn_workspace(rwts[l], T, sh.k)), dtype=torch.uint8, device=dev),
+                y=torch.empty((T * sh.k, sh.H), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((T, sh.H), dtype=torch.bfloat16, device=dev))
+        return rbufs[(l, T)]
+
     def resident_pass(xs):
+        cs = torch.cuda.current_stream()
         outs = []
         for l in range(L):
-            ids, w, _ = ft.route(xs[l].shape[0], sh.E, sh.k, x=xs[l], w_router=st.routers[l],
-                                 bias=st.biases[l])
-            c, off, perm, inv = ft.align(ids, sh.E)
-            y = ft.ffn(rwts[l], xs[l], sh.k, perm, off)
-            outs.append(ft.combine(y, inv, w))
+            T = xs[l].shape[0]
+            b = resident_bufs(l, T)
+            ids, w, _ = ft.route(T, sh.E, sh.k, x=xs[l], w_router=st.routers[l], bias=st.biases[l],
+                                 logits_out=b["logits"], ids=b["ids"], w=b["w"], stream=cs)
+            c, off, perm, inv = ft.align(ids, sh.E, ws=b["aws"], out=b["al"], stream=cs)
+            y = ft.ffn(rwts[l], xs[l], sh.k, perm, off, y=b["y"], ws=b["fws"], stream=cs)
+            outs.append(ft.combine(y, inv, w, out=b["out"], stream=cs))
         return outs
 
     def timed(fn, batches):
@@ -511,7 +532,7 @@ def run_slot_stack(args):
             "tight_budget_128_slots": tight,
         },
     }
-    del resident, rwts
+    del resident, rwts, rbufs
     torch.cuda.empty_cache()
     return line
 

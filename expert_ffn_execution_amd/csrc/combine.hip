@@ -76,9 +76,61 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restri
     }
 }
 
+// dst[i] = src[i] for i < n: a few hundred int32 between device memory and
+// pinned host memory mapped for the device (one block; an in-stream copy of
+// this size costs more than the kernel)
+__global__ __launch_bounds__(256) void copy_i32_kernel(const int32_t* __restrict__ src,
+                                                       int32_t* __restrict__ dst, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+    __threadfence_system();
+}
+
+// copy_i32 and then *flag = epoch (pinned host memory mapped for the
+// device): the host polls the flag instead of an event
+__global__ __launch_bounds__(256) void copy_i32_flag_kernel(const int32_t* __restrict__ src,
+                                                            int32_t* __restrict__ dst, int n,
+                                                            int32_t* flag, int32_t epoch) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+    __threadfence_system();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+// a slot table of up to TABLE_MAX entries carried in the kernel's arguments
+struct TableArg {
+    int32_t v[ft::TABLE_MAX];
+};
+__global__ __launch_bounds__(256) void set_table_kernel(const TableArg t, int32_t* __restrict__ dst, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = t.v[i];
+}
+
 }  // namespace
 
 namespace ft {
+
+ft_status launch_copy_i32_flag(const int32_t* src, int32_t* dst, int n, int32_t* flag, int32_t epoch,
+                               hipStream_t s) {
+    copy_i32_flag_kernel<<<1, 256, 0, s>>>(src, dst, n, flag, epoch);
+    FT_LAUNCHED("copy_i32_flag");
+    return FT_OK;
+}
+
+ft_status launch_set_table(const int32_t* table, int n, int32_t* dst, hipStream_t s) {
+    if (n > TABLE_MAX) return set_error(FT_ERR_INVALID_ARG, "slot table of %d entries > %d", n, TABLE_MAX);
+    TableArg t;
+    for (int i = 0; i < n; ++i) t.v[i] = table[i];
+    set_table_kernel<<<1, 256, 0, s>>>(t, dst, n);
+    FT_LAUNCHED("set_table");
+    return FT_OK;
+}
+
+ft_status launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s) {
+    copy_i32_kernel<<<1, 256, 0, s>>>(src, dst, n);
+    FT_LAUNCHED("copy_i32");
+    return FT_OK;
+}
 
 ft_status launch_scatter_rows(const float* rows, const int64_t* pos, int n, int H, void* y,
                               ft_dtype y_dt, hipStream_t s) {

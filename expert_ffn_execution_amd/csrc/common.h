@@ -39,6 +39,9 @@ void clear_error();
     } while (0)
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// largest slot table uploaded through a kernel argument (ft_slot_cache_map)
+constexpr int TABLE_MAX = 512;
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // profiling hooks: events recorded around selected kernels (see ft_set_profile_events)

@@ -1,9 +1,12 @@
 // slot_cache.cpp -- HIP copy engine and C entry points of the expert-slot cache.
 //
 // Copies run as hipMemcpyAsync from the pinned host pool on the caller's copy
-// stream; each slot has a "filled" event (recorded after its copy) and a
-// "read" event (recorded on the compute stream when the layer that used it is
-// released).  A copy into a slot first waits for the slot's read event, and
+// stream; each slot has a "filled" event (recorded after its copy) and refers
+// to a "read" event recorded on the compute stream when the layer that used it
+// is released (one event per release, shared by that layer's slots, from a
+// small pool; a slot keeps the generation it saw, and once the pool has
+// recorded that event again the copy waits for the newer point, which comes
+// later on the same stream).  A copy into a slot first waits for that event, and
 // the compute stream waits for the filled events of the slots a layer maps:
 // the next layer's weights travel while the current layer computes, with no
 // host synchronisation (FreeToken hub article, paragraph on prefill overlap;
@@ -12,6 +15,7 @@
 // pool is refused (FreeToken hub article, install caveat on WSL).
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -19,16 +23,37 @@
 #include "common.h"
 #include "slot_policy.h"
 
+namespace ft {
+ft_status route_align(const ft_moe_step* st, hipStream_t s);
+ft_status launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
+ft_status launch_copy_i32_flag(const int32_t* src, int32_t* dst, int n, int32_t* flag, int32_t epoch,
+                               hipStream_t s);
+ft_status launch_set_table(const int32_t* table, int n, int32_t* dst, hipStream_t s);
+}
+
 struct ft_slot_cache {
     ft_slot_cache_desc d;
     ftp::Policy policy;
-    std::vector<hipEvent_t> filled, read;
-    std::vector<char> read_valid;
-    // pinned staging ring for slot-table uploads
+    std::vector<hipEvent_t> filled;
+    std::vector<int> read_ev;          // slot -> pool event of its last release (-1: none)
+    std::vector<long long> read_gen;   // slot -> that event's generation at the release
+    std::vector<hipEvent_t> rpool;     // release events
+    std::vector<long long> rgen;       // times each was recorded
+    int rpos = 0;
+    // pinned staging ring for slot-table uploads, and its device mapping (a
+    // one-block kernel uploads a table; null: hipMemcpyAsync)
     int32_t* stage = nullptr;
+    const int32_t* stage_dev = nullptr;
     std::vector<hipEvent_t> stage_ev;
     std::vector<char> stage_used;
     int ring = 0, ring_pos = 0;
+    // ft_slot_stack_forward: one event per layer marks its expert counts on the
+    // host, or (mapped buffers) a flag per layer that the copying kernel sets
+    // to the pass's epoch after the counts
+    std::vector<hipEvent_t> counts_ev;
+    int32_t* flags = nullptr;        // pinned [n_layers]
+    int32_t* flags_dev = nullptr;    // its device mapping, or null
+    int32_t epoch = 0;
 
     explicit ft_slot_cache(const ft_slot_cache_desc& dd)
         : d(dd), policy(dd.n_layers, dd.n_experts, dd.n_slots, dd.scope, dd.expert_bytes) {}
@@ -46,8 +71,21 @@ struct HipEngine final : ftp::Engine {
         if (e != hipSuccess && err == hipSuccess) err = e;
         return e == hipSuccess;
     }
+    int shared_ev = -1;  // this call's release event, once recorded
+    bool wait_read(int slot) {  // the copy stream waits for the slot's last reader
+        const int ev = c->read_ev[slot];
+        if (ev < 0) return true;
+        if (c->rgen[ev] != c->read_gen[slot]) {
+            // recorded again since: the slot's release is earlier on the compute
+            // stream than that newer point, so it is done once the newer one is
+            hipError_t q = hipEventQuery(c->rpool[ev]);
+            if (q == hipSuccess) return true;
+            if (q != hipErrorNotReady) return ok(q);
+        }
+        return ok(hipStreamWaitEvent(copy_s, c->rpool[ev], 0));
+    }
     bool copy(int slot, int layer, int expert) override {
-        if (c->read_valid[slot] && !ok(hipStreamWaitEvent(copy_s, c->read[slot], 0))) return false;
+        if (!wait_read(slot)) return false;
         const char* src = (const char*)c->d.host_pool +
                           ((size_t)layer * c->d.n_experts + expert) * c->d.host_stride;
         char* dst = (char*)c->d.dev_slots + (size_t)slot * c->d.slot_stride;
@@ -60,12 +98,19 @@ struct HipEngine final : ftp::Engine {
         if (e == hipErrorNotReady) return false;
         return ok(e);
     }
+    bool copy_wait(int slot) override { return ok(hipEventSynchronize(c->filled[slot])); }
     bool compute_wait(int slot) override {
         return ok(hipStreamWaitEvent(compute, c->filled[slot], 0));
     }
     bool record_read(int slot) override {
-        if (!ok(hipEventRecord(c->read[slot], compute))) return false;
-        c->read_valid[slot] = 1;
+        if (shared_ev < 0) {
+            shared_ev = c->rpos;
+            c->rpos = (c->rpos + 1) % (int)c->rpool.size();
+            if (!ok(hipEventRecord(c->rpool[shared_ev], compute))) return false;
+            ++c->rgen[shared_ev];
+        }
+        c->read_ev[slot] = shared_ev;
+        c->read_gen[slot] = c->rgen[shared_ev];
         return true;
     }
     bool move(int, int) override { return false; }  // only ResizeEngine moves slots
@@ -79,12 +124,11 @@ struct ResizeEngine final : ftp::Engine {
     hipStream_t copy_s;
     char* dst_base;
     std::vector<hipEvent_t>& filled_new;
-    std::vector<hipEvent_t>& read_new;
-    std::vector<char>& read_valid_new;
+    std::vector<int>& read_ev_new;
     hipError_t err = hipSuccess;
     ResizeEngine(ft_slot_cache* cc, hipStream_t cp, char* base, std::vector<hipEvent_t>& f,
-                 std::vector<hipEvent_t>& r, std::vector<char>& rv)
-        : c(cc), copy_s(cp), dst_base(base), filled_new(f), read_new(r), read_valid_new(rv) {}
+                 std::vector<int>& r)
+        : c(cc), copy_s(cp), dst_base(base), filled_new(f), read_ev_new(r) {}
     bool ok(hipError_t e) {
         if (e != hipSuccess && err == hipSuccess) err = e;
         return e == hipSuccess;
@@ -95,11 +139,15 @@ struct ResizeEngine final : ftp::Engine {
         if (e == hipErrorNotReady) return false;
         return ok(e);
     }
+    bool copy_wait(int) override { return false; }
     bool compute_wait(int) override { return false; }
     bool record_read(int) override { return false; }
     bool move(int src, int dst) override {
         if (!ok(hipStreamWaitEvent(copy_s, c->filled[src], 0))) return false;
-        if (read_valid_new[dst] && !ok(hipStreamWaitEvent(copy_s, read_new[dst], 0))) return false;
+        // (a reused pool event is a later point of the compute stream: waiting
+        // for it is conservative)
+        if (read_ev_new[dst] >= 0 && !ok(hipStreamWaitEvent(copy_s, c->rpool[read_ev_new[dst]], 0)))
+            return false;
         const char* from = (const char*)c->d.dev_slots + (size_t)src * c->d.slot_stride;
         char* to = dst_base + (size_t)dst * c->d.slot_stride;
         if (!ok(hipMemcpyAsync(to, from, c->d.expert_bytes, hipMemcpyDeviceToDevice, copy_s)))
@@ -155,22 +203,45 @@ ft_status ft_slot_cache_create(const ft_slot_cache_desc* desc, ft_slot_cache** o
     }
     ft_slot_cache* c = new (std::nothrow) ft_slot_cache(d);
     if (!c) return ft::set_error(FT_ERR_CAPACITY, "out of host memory");
-    c->filled.resize(d.n_slots);
-    c->read.resize(d.n_slots);
-    c->read_valid.assign(d.n_slots, 0);
+    c->filled.assign(d.n_slots, nullptr);
+    c->read_ev.assign(d.n_slots, -1);
+    c->read_gen.assign(d.n_slots, 0);
     for (int s = 0; s < d.n_slots; ++s) {
-        if (hipEventCreateWithFlags(&c->filled[s], hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&c->read[s], hipEventDisableTiming) != hipSuccess) {
+        if (make_event(&c->filled[s]) != hipSuccess) {
             ft_slot_cache_destroy(c);
             return ft::set_error(FT_ERR_HIP, "hipEventCreate failed");
         }
     }
+    // release events: enough that one is recorded again only long after its
+    // slots' copies were issued (4 per layer)
+    c->rpool.assign((size_t)4 * d.n_layers + 4, nullptr);
+    c->rgen.assign(c->rpool.size(), 0);
+    for (auto& e : c->rpool)
+        if (make_event(&e) != hipSuccess) {
+            ft_slot_cache_destroy(c);
+            return ft::set_error(FT_ERR_HIP, "hipEventCreate failed");
+        }
     c->ring = 8;
     if (hipHostMalloc((void**)&c->stage, sizeof(int32_t) * (size_t)d.n_experts * c->ring,
                       hipHostMallocDefault) != hipSuccess) {
         c->stage = nullptr;
         ft_slot_cache_destroy(c);
         return ft::set_error(FT_ERR_HIP, "hipHostMalloc of the slot-table staging ring failed");
+    }
+    {
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, c->stage, 0) == hipSuccess) c->stage_dev = (const int32_t*)dp;
+        else (void)hipGetLastError();
+        if (hipHostMalloc((void**)&c->flags, sizeof(int32_t) * (size_t)d.n_layers, hipHostMallocDefault) ==
+            hipSuccess) {
+            for (int l = 0; l < d.n_layers; ++l) c->flags[l] = 0;
+            dp = nullptr;
+            if (hipHostGetDevicePointer(&dp, c->flags, 0) == hipSuccess) c->flags_dev = (int32_t*)dp;
+            else (void)hipGetLastError();
+        } else {
+            c->flags = nullptr;
+            (void)hipGetLastError();
+        }
     }
     c->stage_ev.resize(c->ring);
     c->stage_used.assign(c->ring, 0);
@@ -187,11 +258,14 @@ ft_status ft_slot_cache_destroy(ft_slot_cache* c) {
     if (!c) return FT_OK;
     for (hipEvent_t e : c->filled)
         if (e) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
-    for (hipEvent_t e : c->read)
+    for (hipEvent_t e : c->rpool)
         if (e) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
     for (hipEvent_t e : c->stage_ev)
         if (e) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->counts_ev)
+        if (e) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
     if (c->stage) (void)hipHostFree(c->stage);
+    if (c->flags) (void)hipHostFree(c->flags);
     delete c;
     return FT_OK;
 }
@@ -205,15 +279,27 @@ ft_status ft_slot_cache_map(ft_slot_cache* c, int layer, const int32_t* experts_
     std::vector<int32_t> slot_of((size_t)(n > 0 ? n : 1));
     ft_status r = c->policy.map(eng, layer, experts_host, n, slot_of.data(), st);
     if (r != FT_OK) return hip_status(eng, r);
-    // slot table through the pinned staging ring
+    if (c->d.n_experts <= ft::TABLE_MAX) {  // the table rides in a kernel's arguments
+        int32_t tab[ft::TABLE_MAX];
+        for (int e = 0; e < c->d.n_experts; ++e) tab[e] = -1;
+        for (int q = 0; q < n; ++q) tab[experts_host[q]] = slot_of[q];
+        return ft::launch_set_table(tab, c->d.n_experts, slot_table_dev, (hipStream_t)compute);
+    }
+    // larger tables through the pinned staging ring
     const int i = c->ring_pos;
     c->ring_pos = (c->ring_pos + 1) % c->ring;
     if (c->stage_used[i]) FT_HIP(hipEventSynchronize(c->stage_ev[i]));
     int32_t* tab = c->stage + (size_t)i * c->d.n_experts;
     for (int e = 0; e < c->d.n_experts; ++e) tab[e] = -1;
     for (int q = 0; q < n; ++q) tab[experts_host[q]] = slot_of[q];
-    FT_HIP(hipMemcpyAsync(slot_table_dev, tab, sizeof(int32_t) * c->d.n_experts,
-                          hipMemcpyHostToDevice, (hipStream_t)compute));
+    if (c->stage_dev) {
+        ft_status r2 = ft::launch_copy_i32(c->stage_dev + (size_t)i * c->d.n_experts, slot_table_dev,
+                                           c->d.n_experts, (hipStream_t)compute);
+        if (r2 != FT_OK) return r2;
+    } else {
+        FT_HIP(hipMemcpyAsync(slot_table_dev, tab, sizeof(int32_t) * c->d.n_experts,
+                              hipMemcpyHostToDevice, (hipStream_t)compute));
+    }
     FT_HIP(hipEventRecord(c->stage_ev[i], (hipStream_t)compute));
     c->stage_used[i] = 1;
     return FT_OK;
@@ -254,37 +340,33 @@ ft_status ft_slot_cache_resize(ft_slot_cache* c, int n_slots, void* dev_slots, v
     const int old_n = c->d.n_slots;
     const bool moved = dev_slots && dev_slots != c->d.dev_slots;
     // the event set of the new size: slots below min(old, new) keep theirs
-    std::vector<hipEvent_t> filled(n_slots, nullptr), read(n_slots, nullptr);
-    std::vector<char> read_valid(n_slots, 0);
+    std::vector<hipEvent_t> filled(n_slots, nullptr);
+    std::vector<int> read_ev(n_slots, -1);
+    std::vector<long long> read_gen(n_slots, 0);
     for (int s = 0; s < n_slots; ++s) {
         if (s < old_n) {
             filled[s] = c->filled[s];
-            read[s] = c->read[s];
-            read_valid[s] = c->read_valid[s];
-        } else if (make_event(&filled[s]) != hipSuccess || make_event(&read[s]) != hipSuccess) {
-            for (int q = old_n; q <= s; ++q) {
-                if (filled[q]) (void)hipEventDestroy(filled[q]);
-                if (read[q]) (void)hipEventDestroy(read[q]);
-            }
+            read_ev[s] = c->read_ev[s];
+            read_gen[s] = c->read_gen[s];
+        } else if (make_event(&filled[s]) != hipSuccess) {
+            for (int q = old_n; q < s; ++q) (void)hipEventDestroy(filled[q]);
             return ft::set_error(FT_ERR_HIP, "hipEventCreate failed");
         }
     }
     char* base = (char*)(moved ? dev_slots : c->d.dev_slots);
-    ResizeEngine eng(c, (hipStream_t)copy_stream, base, filled, read, read_valid);
+    ResizeEngine eng(c, (hipStream_t)copy_stream, base, filled, read_ev);
     const ft_status r = c->policy.resize(eng, n_slots, moved);
     if (r != FT_OK && r != FT_ERR_HIP) {  // nothing changed
-        for (int s = old_n; s < n_slots; ++s) (void)hipEventDestroy(filled[s]), (void)hipEventDestroy(read[s]);
+        for (int s = old_n; s < n_slots; ++s) (void)hipEventDestroy(filled[s]);
         return hip_status(eng.err, r);
     }
-    // the policy now has n_slots slots: retire the events of dropped slots
-    // (after the work they mark) and switch to the new set and array
-    for (int s = n_slots; s < old_n; ++s) {
+    // the policy now has n_slots slots: retire the fill events of dropped
+    // slots (after the copies they mark) and switch to the new set and array
+    for (int s = n_slots; s < old_n; ++s)
         (void)hipEventSynchronize(c->filled[s]), (void)hipEventDestroy(c->filled[s]);
-        (void)hipEventSynchronize(c->read[s]), (void)hipEventDestroy(c->read[s]);
-    }
     c->filled.swap(filled);
-    c->read.swap(read);
-    c->read_valid.swap(read_valid);
+    c->read_ev.swap(read_ev);
+    c->read_gen.swap(read_gen);
     c->d.n_slots = n_slots;
     c->d.dev_slots = base;
     return hip_status(eng.err, r);
@@ -292,6 +374,156 @@ ft_status ft_slot_cache_resize(ft_slot_cache* c, int n_slots, void* dev_slots, v
 
 int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert) {
     return c ? c->policy.lookup(layer, expert) : -1;
+}
+
+// One pass through a stack of layers whose experts come through the cache:
+// per layer l, the routing of layer l + 2 is enqueued first (its inputs do
+// not depend on the layers before it here), then layer l's FFN and combine and its
+// release; once layer l + 1's expert counts are on the host its missing
+// experts are prefetched on the copy stream (the next layer's weights travel
+// while this layer computes: claypier.com article, "按带宽决定分工的思路";
+// FreeToken hub article, paragraph on prefill overlap) and mapped.
+ft_status ft_slot_stack_forward(ft_slot_cache* c, const ft_stack_pass* p, void* compute,
+                                void* copy_stream, ft_stack_stats* out) {
+    ft::clear_error();
+    FT_CHECK_ARG(c && p && p->layers && p->counts_host, "null cache / pass / layers / counts_host");
+    const int L = p->n_layers;
+    FT_CHECK_ARG(L >= 1 && L <= c->d.n_layers, "n_layers must be in [1, %d]", c->d.n_layers);
+    const ft_moe_step* S = p->layers;
+    const int E = S[0].weights.E, ns = S[0].weights.n_shared;
+    FT_CHECK_ARG(E + ns == c->d.n_experts, "E + n_shared must equal the cache's experts per layer");
+    for (int l = 0; l < L; ++l)
+        FT_CHECK_ARG(S[l].T >= 1 && S[l].weights.E == E && S[l].weights.n_shared == ns &&
+                         S[l].slot_of_expert && S[l].counts,
+                     "layer %d: T >= 1, the same E and n_shared, a slot table and counts", l);
+    hipStream_t cs = (hipStream_t)compute;
+    while ((int)c->counts_ev.size() < L) {
+        hipEvent_t e = nullptr;
+        FT_HIP(make_event(&e));
+        c->counts_ev.push_back(e);
+    }
+    // the counts go to the host through the buffer's device mapping when it
+    // has one (a one-block kernel), else by hipMemcpyAsync
+    int32_t* counts_dev_map = nullptr;
+    {
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, p->counts_host, 0) == hipSuccess) counts_dev_map = (int32_t*)dp;
+        else (void)hipGetLastError();
+    }
+    const bool use_flags = counts_dev_map && c->flags_dev;
+    const int32_t epoch = ++c->epoch;  // this pass's flag value
+    ft_stack_stats acc{};
+    const ft_cache_stats before = c->policy.stats();
+    std::vector<int32_t> need, all(E + ns);
+    for (int e = 0; e < E + ns; ++e) all[e] = e;
+
+    auto route = [&](int l) -> ft_status {
+        const ft_moe_step& st = S[l];
+        ft_status r;
+        const float* lin = p->logits_in ? p->logits_in[l] : nullptr;
+        if (lin) {
+            r = ft_moe_route(nullptr, st.act_dt, nullptr, lin, st.bias, st.T, st.weights.H, E, st.k,
+                             nullptr, st.topk_ids, st.topk_w, compute);
+            if (r == FT_OK)
+                r = ft_moe_align(st.topk_ids, st.T, st.k, E, st.counts, st.offsets, st.perm,
+                                 st.inv_perm, st.align_ws, st.align_ws_bytes, compute);
+        } else {
+            r = ft::route_align(&st, cs);
+        }
+        if (r != FT_OK) return r;
+        if (use_flags) {
+            return ft::launch_copy_i32_flag(st.counts, counts_dev_map + (size_t)l * E, E,
+                                            c->flags_dev + l, epoch, cs);
+        }
+        FT_HIP(hipMemcpyAsync(p->counts_host + (size_t)l * E, st.counts, sizeof(int32_t) * E,
+                              hipMemcpyDeviceToHost, cs));
+        FT_HIP(hipEventRecord(c->counts_ev[l], cs));
+        return FT_OK;
+    };
+    auto experts_of = [&](int l) -> ft_status {  // distinct experts with rows, ascending (+ shared)
+        if (use_flags) {
+            // the kernel sets the flag after the counts (system-scope release);
+            // the counts are usually there already (routing runs ahead).  A
+            // bounded wait: a stream that stopped (an earlier failure) gives
+            // an error rather than a hung host
+            const auto t0 = std::chrono::steady_clock::now();
+            while (__atomic_load_n(c->flags + l, __ATOMIC_ACQUIRE) != epoch) {
+                if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(20))
+                    return ft::set_error(FT_ERR_HIP, "layer %d's expert counts did not arrive", l);
+#if defined(__x86_64__)
+                __builtin_ia32_pause();
+#endif
+            }
+        } else {
+            // poll briefly before a blocking wait
+            hipError_t q = hipErrorNotReady;
+            for (int i = 0; i < 2000 && q == hipErrorNotReady; ++i) q = hipEventQuery(c->counts_ev[l]);
+            if (q == hipErrorNotReady) q = hipEventSynchronize(c->counts_ev[l]);
+            FT_HIP(q);
+        }
+        need.clear();
+        const int32_t* cnt = p->counts_host + (size_t)l * E;
+        for (int e = 0; e < E; ++e)
+            if (cnt[e] > 0) need.push_back(e);
+        if (ns) need.push_back(E);
+        return FT_OK;
+    };
+    auto map = [&](int l) -> ft_status {
+        ft_map_stats ms{};
+        // (the step's slot table is the map's output here; the descriptor holds
+        // it as the FFN's read-only input)
+        ft_status r = ft_slot_cache_map(c, l, need.data(), (int)need.size(),
+                                        const_cast<int32_t*>(S[l].slot_of_expert), compute,
+                                        copy_stream, &ms);
+        acc.demand += ms.n_demand;
+        acc.hits += ms.n_hit;
+        acc.prefetch_hits += ms.n_prefetch_hit;
+        acc.misses += ms.n_miss;
+        return r;
+    };
+    auto prefetch = [&](int l, const std::vector<int32_t>& ex) -> ft_status {
+        ft_status r = ft_slot_cache_prefetch(c, l, ex.data(), (int)ex.size(), copy_stream, nullptr);
+        if (r == FT_WARN_OVERLAP_DISABLED) {
+            ++acc.prefetch_warnings;
+            return FT_OK;
+        }
+        return r;
+    };
+#define FT_STACK_TRY(call)              \
+    do {                                \
+        const ft_status r_ = (call);    \
+        if (r_ != FT_OK) return r_;     \
+    } while (0)
+    // Routing runs two layers ahead of the FFN, so that while the host waits
+    // for layer l + 1's counts and maps its experts the GPU still has layer
+    // l + 2's routing and layer l's FFN queued.
+    FT_STACK_TRY(route(0));
+    if (L > 1) FT_STACK_TRY(route(1));
+    FT_STACK_TRY(experts_of(0));
+    FT_STACK_TRY(map(0));
+    for (int l = 0; l < L; ++l) {
+        if (l + 2 < L) FT_STACK_TRY(route(l + 2));
+        ft_moe_step st = S[l];
+        if (ns) st.weights.shared_slot = c->policy.lookup(l, E);
+        FT_STACK_TRY(ft_moe_ffn(&st.weights, st.x, st.act_dt, st.T, st.k, st.perm, st.offsets,
+                                st.slot_of_expert, st.y_perm, st.y_dt, st.ffn_ws, st.ffn_ws_bytes,
+                                compute));
+        FT_STACK_TRY(ft_moe_combine(st.y_perm, st.y_dt, st.inv_perm, st.topk_w, st.T, st.k,
+                                    st.weights.H, ns, st.out, st.out_dt, compute));
+        FT_STACK_TRY(ft_slot_cache_release(c, l, compute));
+        if (l + 1 < L) {
+            // layer l + 1's counts come after layer l - 1's map on the compute
+            // stream, so once they are here its copies have landed and its
+            // slots can take layer l + 1's experts
+            FT_STACK_TRY(experts_of(l + 1));
+            FT_STACK_TRY(prefetch(l + 1, p->prefill ? all : need));
+            FT_STACK_TRY(map(l + 1));
+        }
+    }
+#undef FT_STACK_TRY
+    acc.bytes_h2d = c->policy.stats().bytes_h2d - before.bytes_h2d;
+    if (out) *out = acc;
+    return FT_OK;
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/ftmoe.h"
@@ -32,6 +33,8 @@ struct Engine {
     virtual bool copy(int slot, int layer, int expert) = 0;
     // has the last copy into `slot` completed?
     virtual bool copy_done(int slot) = 0;
+    // block the host until the last copy into `slot` has completed
+    virtual bool copy_wait(int slot) = 0;
     // make the compute stream wait for the last copy into `slot`
     virtual bool compute_wait(int slot) = 0;
     // record: work enqueued on the compute stream so far is the last reader of `slot`
@@ -72,12 +75,30 @@ class Policy {
         ft_status v = check_list(layer, experts, n);
         if (v != FT_OK) return v;
         refresh(eng);
-        // capacity: the misses must fit in free slots plus evictable slots that hold
-        // none of the requested experts
+        // capacity: the misses must fit in free slots plus slots that are neither
+        // held nor hold a requested expert.  Those whose copy is still in flight
+        // become evictable when it lands: if the request needs them, the host
+        // waits for the least recently used ones (a request that fits is never
+        // refused for timing).
         int need = 0;
         for (int i = 0; i < n; ++i)
             if (lookup(layer, experts[i]) < 0) ++need;
-        if (need > obtainable(layer, experts, n)) return FT_ERR_CAPACITY;
+        const int have = obtainable(layer, experts, n);
+        if (need > have) {
+            std::vector<int> landing;
+            for (int s = lo(layer); s < hi(layer); ++s) {
+                const Entry& en = slots_[s];
+                if (en.layer >= 0 && !en.held && en.copying && !requested(en, layer, experts, n))
+                    landing.push_back(s);
+            }
+            if (need > have + (int)landing.size()) return FT_ERR_CAPACITY;
+            std::sort(landing.begin(), landing.end(),
+                      [&](int a, int b) { return slots_[a].last < slots_[b].last; });
+            for (int i = 0; i < need - have; ++i) {
+                if (!eng.copy_wait(landing[i])) return FT_ERR_HIP;
+                slots_[landing[i]].copying = false;
+            }
+        }
         ft_map_stats m{};
         m.n_demand = n;
         for (int i = 0; i < n; ++i) {

@@ -33,7 +33,7 @@ EXPORTS = [
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
     "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc", "ft_split_misses",
-    "ft_moe_scatter_rows",
+    "ft_moe_scatter_rows", "ft_slot_stack_forward",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # FT_NOALLOC_SCRATCH_BYTES
 
@@ -66,6 +66,16 @@ class SlotCacheDesc(C.Structure):
                 ("host_pool", C.c_void_p), ("host_stride", C.c_size_t),
                 ("dev_slots", C.c_void_p), ("slot_stride", C.c_size_t), ("n_slots", C.c_int),
                 ("scope", C.c_int)]
+
+
+class StackPass(C.Structure):
+    _fields_ = [("n_layers", C.c_int), ("layers", C.c_void_p), ("logits_in", C.c_void_p),
+                ("counts_host", C.c_void_p), ("prefill", C.c_int)]
+
+
+class StackStats(C.Structure):
+    _fields_ = [("demand", C.c_longlong), ("hits", C.c_longlong), ("prefetch_hits", C.c_longlong),
+                ("misses", C.c_longlong), ("bytes_h2d", C.c_longlong), ("prefetch_warnings", C.c_int)]
 
 
 class MapStats(C.Structure):
@@ -113,6 +123,7 @@ def load() -> C.CDLL:
         "ft_moe_ffn": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P, SZ, P],
         "ft_moe_ffn_noalloc": [C.POINTER(MoeWeights), P, I32, I32, I32, P, P, P, P, I32, P],
         "ft_moe_scatter_rows": [P, P, I32, I32, P, I32, P],
+        "ft_slot_stack_forward": [P, C.POINTER(StackPass), P, P, C.POINTER(StackStats)],
         "ft_moe_ffn_set_path": [I32],
         "ft_set_profile_events": [I32, P, P],
         "ft_moe_combine": [P, I32, P, P, I32, I32, I32, I32, P, I32, P],
@@ -275,9 +286,8 @@ def ffn(wts: MoeWeights, x: torch.Tensor, k: int, perm: torch.Tensor, offsets: t
     rows = T * k + wts.n_shared * T
     if y is None:
         y = torch.empty((rows, wts.H), dtype=y_dtype, device=dev)
-    need = ffn_workspace(wts, T, k)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = torch.empty(ffn_workspace(wts, T, k), dtype=torch.uint8, device=dev)
     _dev(x, perm, offsets, slot_of_expert, y, ws)
     _check(load().ft_moe_ffn(C.byref(wts), _p(x), _dt(x), T, k, _p(perm), _p(offsets),
                              _p(slot_of_expert), _p(y), _dt(y), _p(ws), ws.numel(),
@@ -558,6 +568,22 @@ class SlotCache:
                                                   C.byref(got)),
                     allow=(OK, WARN_OVERLAP_DISABLED))
         return st, got.value
+
+    def forward_stack(self, steps, n_layers: int, counts_host: torch.Tensor, logits_in=None,
+                      prefill: bool = False, compute=None, copy=None) -> StackStats:
+        """ft_slot_stack_forward over n_layers: steps is a ctypes array of
+        MoeStep (one per layer, with its buffers), counts_host a pinned int32
+        host tensor [n_layers, E], logits_in None or a ctypes array of
+        n_layers device pointers (None entries: router GEMM)."""
+        if counts_host.is_cuda or not counts_host.is_pinned() or counts_host.dtype != torch.int32:
+            raise FtError(ERR_INVALID_ARG, "counts_host must be pinned host int32")
+        p = StackPass(n_layers, C.cast(steps, C.c_void_p),
+                      None if logits_in is None else C.cast(logits_in, C.c_void_p),
+                      counts_host.data_ptr(), int(prefill))
+        st = StackStats()
+        _check(load().ft_slot_stack_forward(self.h, C.byref(p), _stream(compute), _stream(copy),
+                                            C.byref(st)))
+        return st
 
     def evict(self, layer: int, expert: int = -1):
         _check(load().ft_slot_cache_evict(self.h, layer, expert))

@@ -26,13 +26,16 @@ its combine.
 
 Each layer's device buffers (logits, routing, alignment, workspaces, y_perm,
 output) are allocated once per batch size and reused from step to step: the
-outputs forward() returns stay valid until the next call.
+outputs forward() returns stay valid until the next call.  Without hybrid
+decode the whole pass is one library call (ft_slot_stack_forward), which does
+the per-layer host work in C++; hybrid decode keeps the loop here.
 Bp (pinned host-to-device GB/s) and Bh (host FFN GB/s of expert weights) come
 from ``calibrate()`` (chenxutan.com article, "瓶颈为什么是带宽而不是容量", the
 q* strategy; freelamp.com article, section 2.1).
 """
 from __future__ import annotations
 
+import ctypes as C
 import dataclasses
 import os
 import time
@@ -112,6 +115,8 @@ class SlotStack:
         self._rows_dev = [None, None]
         self._rows_ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.bp = self.bh = 0.0   # GB/s, from calibrate()
+        self._steps = {}          # (T, out dtype) -> ctypes array of per-layer step descriptors
+        self._counts_host = torch.empty((n_layers, shape.E), dtype=torch.int32, pin_memory=True)
         # host FFN threads: 8 measured fastest on a 16-core share (84-96 GB/s)
         self.host_threads = max(1, min(8, len(os.sched_getaffinity(0))))
 
@@ -123,6 +128,7 @@ class SlotStack:
         if db.get("T") != T:
             sh, dev, k = self.sh, self.dev, self.sh.k
             i32, f32 = torch.int32, torch.float32
+            self._steps.clear()  # descriptors name the buffers freed here
             db.clear()
             db.update(T=T, logits=torch.empty((T, sh.E), dtype=f32, device=dev),
                       ids=torch.empty((T, k), dtype=i32, device=dev),
@@ -138,22 +144,24 @@ class SlotStack:
                       y=torch.empty((T * k + sh.n_shared * T, sh.H), dtype=torch.bfloat16,
                                     device=dev))
         if db.get("out") is None or db["out"].dtype != out_dtype:
+            self._steps.clear()
             db["out"] = torch.empty((T, self.sh.H), dtype=out_dtype, device=self.dev)
         return db
 
     def _route(self, l: int, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
-               want_x: bool = False, out_dtype=torch.bfloat16):
+               want_x: bool = False, out_dtype=torch.bfloat16, stream=None):
         sh = self.sh
         T = x.shape[0]
         db = self._dev_bufs(l, T, out_dtype)
         if logits is None:
             ids, w, _ = ft.route(T, sh.E, sh.k, x=x, w_router=self.routers[l],
                                  bias=self.biases[l], logits_out=db["logits"], ids=db["ids"],
-                                 w=db["w"])
+                                 w=db["w"], stream=stream)
         else:
             ids, w, _ = ft.route(T, sh.E, sh.k, logits=logits, bias=self.biases[l],
-                                 ids=db["ids"], w=db["w"])
-        counts, offsets, perm, inv = ft.align(ids, sh.E, ws=db["aws"], out=db["align"])
+                                 ids=db["ids"], w=db["w"], stream=stream)
+        counts, offsets, perm, inv = ft.align(ids, sh.E, ws=db["aws"], out=db["align"],
+                                              stream=stream)
         hb = self._host_bufs(l, T)
         hb["counts"].copy_(counts, non_blocking=True)
         if want_x:  # the host FFN's inputs, ready with the routing (no wait on later work)
@@ -185,8 +193,8 @@ class SlotStack:
         need = torch.nonzero(r["counts_h"]).flatten().tolist()
         return need + ([self.sh.E] if self.sh.n_shared else [])  # the shared expert rides along
 
-    def _map(self, l: int, experts: List[int]):
-        st = self.cache.map(l, experts, self.tables[l], copy=self.copy_stream)
+    def _map(self, l: int, experts: List[int], stream=None):
+        st = self.cache.map(l, experts, self.tables[l], compute=stream, copy=self.copy_stream)
         self.stats.demand += st.n_demand
         self.stats.hits += st.n_hit
         self.stats.prefetch_hits += st.n_prefetch_hit
@@ -252,6 +260,49 @@ class SlotStack:
         self.stats.cpu_experts += len(experts)
         return job, (rows, pos, self._rows_dev[p], self._rows_ev[p])
 
+    def _native_steps(self, T: int, out_dtype):
+        """The per-layer ft_moe_step descriptors of the native pass for T tokens
+        (buffers from _dev_bufs; x is set per call)."""
+        key = (T, out_dtype)
+        if key not in self._steps:
+            sh = self.sh
+            arr = (ft.MoeStep * self.L)()
+            for l in range(self.L):
+                db = self._dev_bufs(l, T, out_dtype)
+                c, off, perm, inv = db["align"]
+                b = self.biases[l]
+                arr[l] = ft.MoeStep(self.wts, 0, ft.BF16, self.routers[l].data_ptr(),
+                                    None if b is None else b.data_ptr(), T, sh.k,
+                                    self.tables[l].data_ptr(), db["logits"].data_ptr(),
+                                    db["ids"].data_ptr(), db["w"].data_ptr(), c.data_ptr(),
+                                    off.data_ptr(), perm.data_ptr(), inv.data_ptr(),
+                                    db["aws"].data_ptr(), db["aws"].numel(), db["y"].data_ptr(),
+                                    ft.BF16, db["fws"].data_ptr(), db["fws"].numel(),
+                                    db["out"].data_ptr(), ft._dt(db["out"]))
+            self._steps[key] = arr
+        return self._steps[key]
+
+    def _forward_native(self, xs, prefill, out_dtype, logits):
+        T = xs[0].shape[0]
+        arr = self._native_steps(T, out_dtype)
+        for l in range(self.L):
+            if xs[l].shape[0] != T or not xs[l].is_cuda or not xs[l].is_contiguous():
+                raise ValueError("every layer's input must be a contiguous device [T, H] tensor")
+            arr[l].x = xs[l].data_ptr()
+        lin = None
+        if logits is not None:
+            lin = (C.c_void_p * self.L)(*[None if a is None else a.data_ptr() for a in logits])
+        st = self.cache.forward_stack(arr, self.L, self._counts_host, lin, prefill,
+                                      compute=torch.cuda.current_stream(), copy=self.copy_stream)
+        self.stats.demand += st.demand
+        self.stats.hits += st.hits
+        self.stats.prefetch_hits += st.prefetch_hits
+        self.stats.misses += st.misses
+        self.stats.bytes_h2d += st.bytes_h2d
+        self.stats.prefetch_warnings += st.prefetch_warnings
+        self.stats.steps += 1
+        return [self._dbufs[l]["out"] for l in range(self.L)]
+
     def forward(self, xs: List[torch.Tensor], prefill: bool = False,
                 out_dtype=torch.bfloat16,
                 logits: Optional[List[torch.Tensor]] = None,
@@ -264,29 +315,34 @@ class SlotStack:
         sh = self.sh
         if hybrid and sh.wdtype != "bf16":
             raise ValueError("hybrid decode computes missed experts on the host in bf16 only")
+        if not (hybrid and not prefill):
+            return self._forward_native(xs, prefill, out_dtype, logits)
         lg = logits if logits is not None else [None] * self.L
         outs = []
         want_x = hybrid and not prefill
-        r = self._route(0, xs[0], lg[0], out_dtype=out_dtype)
-        self._map(0, self._experts_of(r))
+        cs = torch.cuda.current_stream()  # the compute stream (looked up once)
+        r = self._route(0, xs[0], lg[0], out_dtype=out_dtype, stream=cs)
+        self._map(0, self._experts_of(r), cs)
         for l in range(self.L):
-            nxt = (self._route(l + 1, xs[l + 1], lg[l + 1], want_x=want_x, out_dtype=out_dtype)
+            nxt = (self._route(l + 1, xs[l + 1], lg[l + 1], want_x=want_x, out_dtype=out_dtype,
+                               stream=cs)
                    if l + 1 < self.L else None)
             if sh.n_shared:
                 self.wts.shared_slot = self.cache.lookup(l, sh.E)
             db = r["db"]
             y = ft.ffn(self.wts, xs[l], sh.k, r["perm"], r["offsets"],
-                       slot_of_expert=self.tables[l], y=db["y"], ws=db["fws"])
+                       slot_of_expert=self.tables[l], y=db["y"], ws=db["fws"], stream=cs)
             if "cpu" in r:  # the host's rows of this layer (its experts were skipped above)
                 job, (rows, pos, (rows_d, pos_d), ev) = r["cpu"]
                 n = job.wait()
                 if n:
                     rows_d[:n].copy_(rows[:n], non_blocking=True)
                     pos_d[:n].copy_(pos[:n], non_blocking=True)
-                    ft.scatter_rows(rows_d, pos_d, y, n)
+                    ft.scatter_rows(rows_d, pos_d, y, n, stream=cs)
                 ev.record()
-            outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared, out=db["out"]))
-            self.cache.release(l)
+            outs.append(ft.combine(y, r["inv"], r["w"], n_shared=sh.n_shared, out=db["out"],
+                                   stream=cs))
+            self.cache.release(l, compute=cs)
             if nxt is not None:
                 if prefill:
                     self._prefetch(l + 1, list(range(self.n_exp)))
@@ -298,7 +354,7 @@ class SlotStack:
                         nxt["cpu"] = self._start_cpu(l + 1, nxt, cpu)
                 if not prefill:
                     self._prefetch(l + 1, need)
-                self._map(l + 1, need)
+                self._map(l + 1, need, cs)
                 r = nxt
         self.stats.steps += 1
         return outs
@@ -317,6 +373,7 @@ class SlotStack:
             self.slots = dev_slots
             self.wts = ft.make_weights(self.sh.wdtype, self.sh.E, self.sh.H, self.sh.I,
                                        self.slots, n_shared=self.sh.n_shared, shared_slot=0)
+            self._steps.clear()  # their weights name the old array
 
     def close(self):
         self.cache.close()

@@ -413,6 +413,49 @@ ft_status ft_slot_cache_resize(ft_slot_cache* c, int n_slots, void* dev_slots, v
 /* Counters since creation. */
 ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
 
+/* --------------------------------------------------------------------------
+ * ft_slot_stack_forward -- one pass through a stack of MoE layers whose
+ * experts come through the cache, as one call (the per-layer host work runs
+ * here rather than in the caller).  For each layer l in order: the routing
+ * and alignment of layer l + 2 are enqueued first (a layer's input must not
+ * depend on the outputs of the layers before it), then layer l's FFN, combine and
+ * ft_slot_cache_release; then, once layer l + 1's expert counts have reached
+ * the host, its missing experts are prefetched on `copy_stream` (every expert
+ * of the layer when `prefill`) while layer l computes, and mapped into its
+ * slot table.  The pages describe this double-buffered streaming of the next
+ * layer's experts (claypier.com article, "按带宽决定分工的思路"; FreeToken hub
+ * article, paragraph on prefill overlap).
+ *   layers [n_layers]: one ft_moe_step per layer with its buffers; its
+ *     weights.pool is the cache's device slot array, slot_of_expert that
+ *     layer's device slot table (E + n_shared entries, written by the map),
+ *     counts its device expert histogram; T >= 1; E and n_shared equal for all
+ *     layers, E + n_shared == the cache's experts per layer; weights.shared_slot
+ *     is ignored (looked up per layer).
+ *   logits_in: NULL, or [n_layers] device fp32 logits per layer (NULL entries
+ *     compute the router GEMM from x and w_router).
+ *   counts_host: pinned host [n_layers][E] int32, written (the expert lists).
+ * The host waits (hipEventSynchronize) for each layer's counts; everything
+ * else is asynchronous on `compute` / `copy_stream`.  Stops at the first
+ * failing call and returns its status (earlier layers stay enqueued).
+ * FT_WARN_OVERLAP_DISABLED from a prefetch is counted, not returned.
+ * stats (may be NULL): demand, hits, prefetch hits and misses of the maps,
+ * H2D bytes enqueued, prefetch warnings. */
+typedef struct {
+    int n_layers;
+    const ft_moe_step* layers;
+    const float* const* logits_in;
+    int32_t* counts_host;
+    int prefill;
+} ft_stack_pass;
+
+typedef struct {
+    long long demand, hits, prefetch_hits, misses, bytes_h2d;
+    int prefetch_warnings;
+} ft_stack_stats;
+
+ft_status ft_slot_stack_forward(ft_slot_cache* c, const ft_stack_pass* p, void* compute,
+                                void* copy_stream, ft_stack_stats* stats);
+
 /* Slot of (layer, expert), or -1 when not cached.  Host query, no device work. */
 int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert);
 

@@ -11,7 +11,7 @@ namespace {
 
 struct Mock final : ftp::Engine {
     explicit Mock(int n_slots) : pending(n_slots, 0) {}
-    std::vector<int> log;  // (kind, slot, layer, expert): kind 0 copy, 1 wait, 2 read
+    std::vector<int> log;  // (kind, slot, layer, expert): kind 0 copy, 1 wait, 2 read, 3 move, 4 host wait
     std::vector<char> pending;
     bool auto_complete = true, fail_next = false;
 
@@ -31,6 +31,11 @@ struct Mock final : ftp::Engine {
         return true;
     }
     bool copy_done(int slot) override { return !pending[slot]; }
+    bool copy_wait(int slot) override {  // the copy completes while the host waits
+        rec(4, slot, -1, -1);
+        pending[slot] = 0;
+        return true;
+    }
     bool compute_wait(int slot) override {
         rec(1, slot, -1, -1);
         return true;

@@ -215,7 +215,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     the C compiler gives them."""
     structs = {"ft_moe_weights": ft.MoeWeights, "ft_moe_step": ft.MoeStep,
                "ft_slot_cache_desc": ft.SlotCacheDesc, "ft_map_stats": ft.MapStats,
-               "ft_cache_stats": ft.CacheStats, "ft_host_moe_job_desc": ft.HostMoeJobDesc}
+               "ft_cache_stats": ft.CacheStats, "ft_host_moe_job_desc": ft.HostMoeJobDesc,
+               "ft_stack_pass": ft.StackPass, "ft_stack_stats": ft.StackStats}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ftmoe.h"', 'int main(void) {']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -236,6 +237,14 @@ def test_struct_layouts_match_the_header(tmp_path):
         for f in py._fields_:
             want.append(f"{cname} {f[0]} {getattr(py, f[0]).offset}")
     assert [l for l in got if l] == want
+
+
+def test_stack_forward_rejects_bad_arguments():
+    lib = ft.load()
+    p = ft.StackPass(0, None, None, None, 0)
+    assert lib.ft_slot_stack_forward(None, C.byref(p), None, None, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_slot_stack_forward(C.c_void_p(4096), None, None, None, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_slot_stack_forward(C.c_void_p(4096), C.byref(p), None, None, None) == ft.ERR_INVALID_ARG
 
 
 def test_slot_cache_resize_rejects_bad_arguments():

@@ -276,6 +276,29 @@ def test_map_waits_for_in_flight_copies(lib):
     assert (1, slots[0], -1, -1) in c.log()          # compute waits on the fill
 
 
+def test_map_waits_for_landing_copies_it_must_evict(lib):
+    """A request that fits once in-flight copies land is served: the host
+    waits for the least recently used of them (engine call 4) and evicts it,
+    as the textbook LRU (which has no copies in flight) would; a request that
+    does not fit even then is refused and changes nothing."""
+    c = Cache(lib, 2, 8, 4)
+    lib.pol_set_auto_complete(c.h, 0)
+    assert c.prefetch(1, [0, 1, 2, 3]) == (OK, 4)            # four copies in flight
+    c.log()
+    r, slots, st = c.map(0, [5, 6])
+    assert r == OK and st == [2, 0, 0, 2]
+    waits = [e for e in c.log() if e[0] == 4]
+    assert len(waits) == 2 and {w[1] for w in waits} == {0, 1}  # the two oldest: (1, 0), (1, 1)
+    assert c.lookup(1, 0) == -1 and c.lookup(1, 1) == -1 and c.lookup(1, 2) >= 0
+    c.release(0)
+    lib.pol_set_auto_complete(c.h, 1)
+    assert c.map(0, [5])[0] == OK                             # held: 1, room: 3
+    before = [c.lookup(l, e) for l in range(2) for e in range(8)]
+    c.log()
+    assert c.map(0, [1, 2, 3, 4, 5])[0] == CAPACITY           # 4 misses > 3 other slots
+    assert [c.lookup(l, e) for l in range(2) for e in range(8)] == before and c.log() == []
+
+
 def test_release_records_last_reader_and_copy_failure_retries(lib):
     c = Cache(lib, 1, 8, 4)
     assert c.map(0, [1, 2])[0] == OK
