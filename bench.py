@@ -108,6 +108,52 @@ def summarize_pmc(fetch_dir, write_dir, workload, T):
     print(json.dumps(out))
 
 
+def summarize_counters(pmc_dir, workload):
+    """rocprofv3 --pmc run (rocpd database) of this benchmark -> the mean per
+    dispatch of every collected counter, for the workload's two expert GEMMs.
+    A counter's value is summed over its hardware instances first."""
+    import glob
+    from expert_ffn_execution_amd import synth
+    k1 = GEMM1_KERNEL[synth.SHAPES[workload].wdtype]
+    kernels = {"gemm1": k1, "gemm2": k1.replace("ILi0E", "ILi1E", 1)}
+    per = {}
+    for db in glob.glob(os.path.join(pmc_dir, "**", "*_results.db"), recursive=True):
+        for name, counter, value, disp in rocpd_rows(
+                db, "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+            for tag, key in kernels.items():
+                if key in name:
+                    d = per.setdefault(tag, {}).setdefault(counter, {})
+                    d[disp] = d.get(disp, 0.0) + value
+        # with --kernel-trace in the same run: the mean duration of the same dispatches
+        try:
+            for tag, key in kernels.items():
+                r = rocpd_rows(db, "select avg(duration), count(*) from kernels where name like ?",
+                               (f"%{key}%",))
+                if r and r[0][1]:
+                    per.setdefault("duration_ns", {})[tag] = {"mean": r[0][0], "n": r[0][1]}
+        except Exception:  # counters-only run: no kernels view
+            pass
+    dur = per.pop("duration_ns", {})
+    out = {tag: {c: sum(v.values()) / len(v) for c, v in cs.items()} for tag, cs in per.items()}
+    out["dispatches"] = {tag: len(next(iter(cs.values()))) for tag, cs in per.items()}
+    out["kernels"] = kernels
+    if dur:
+        out["duration_ns"] = dur
+    print(json.dumps(out))
+    return out
+
+
+def run_mfma_rate():
+    """The stand-alone issue-rate probe (built next to the library), run as a
+    child process; its JSON lines pass through."""
+    import subprocess
+    exe = os.path.join(ROOT, "expert_ffn_execution_amd", "mfma_rate")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is not built: run python -m expert_ffn_execution_amd.build")
+    r = subprocess.run([exe], timeout=300)
+    return r.returncode
+
+
 def rocpd_rows(db, query, params=()):
     """Rows of a query on a rocprofv3 rocpd database (its SQLite output)."""
     import sqlite3
@@ -165,6 +211,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "T"),
                     help="write the traffic summary from two rocprofv3 --pmc runs of one workload")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="run the matrix-core issue-rate probe (bf16 vs block-scaled fp8 x fp4 and "
+                         "fp4 x fp4; burst and sustained) and print its JSON lines")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "WORKLOAD"),
+                    help="mean per dispatch of each counter of a rocprofv3 --pmc run, for the "
+                         "workload's two expert GEMMs")
     return ap.parse_args()
 
 
@@ -643,6 +695,8 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1"}))
         log("the MoE-layer path here is single-GPU; multi-GPU runs are not supported")
         sys.exit(2)
+    if args.mfma_rate:
+        sys.exit(run_mfma_rate())
     import torch
     from expert_ffn_execution_amd import ftmoe as ft
     from expert_ffn_execution_amd import synth
@@ -652,6 +706,9 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     ft.load()
     dev = "cuda:0"

@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libftmoe.so")
+# stand-alone matrix-core issue-rate probe (not part of the library)
+PROBE_SRC = "mfma_rate.hip"
+PROBE = os.path.join(PKG, "mfma_rate")
 SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip",
            "ffn_stream.hip", "combine.hip", "step.cpp", "host_ffn.cpp", "noalloc.hip"]
 ARCH = "gfx950"
@@ -61,9 +64,20 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
+
+
+def build_probe() -> str:
+    cmd = [HIPCC, *[f for f in CFLAGS if f != "-fPIC"], "-x", "hip", os.path.join(CSRC, PROBE_SRC),
+           "-o", PROBE + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":
