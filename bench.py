@@ -514,6 +514,22 @@ def run_slot_stack(args):
     t_dec = timed(st.forward, dec)
     d = {k: getattr(st.stats, k) - getattr(s0, k) for k in
          ("demand", "hits", "prefetch_hits", "misses", "bytes_h2d")}
+    # the same decode without host waits (device-table passes): experts not in
+    # a slot are read from the pinned pool over the host link, and the LRU
+    # takes each pass's routing afterwards; the final flush is timed too
+    dtx = [[synth.gen_x(sh, 1, step=60_000 + s, device=dev, layer=l) for l in range(L)]
+           for s in range(steps)]
+
+    def dt_run(batches):
+        for xs in batches:
+            st.forward(xs, device_table=True)
+        st.flush()
+
+    timed(dt_run, [warm])
+    s4 = dataclasses_replace(st.stats)
+    t_dt = timed(dt_run, [dtx])
+    dt = {k: getattr(st.stats, k) - getattr(s4, k) for k in
+          ("demand", "hits", "prefetch_hits", "misses", "bytes_h2d")}
     # the same decode steps with each layer's misses split between PCIe copies
     # and host cores (split_misses with the calibrated Bp, Bh)
     bp, bh = st.calibrate()
@@ -573,6 +589,12 @@ def run_slot_stack(args):
             "prefill_h2d_gbs": pre_bytes / t_pre / 1e9,
             "prefill_tokens_per_s": T_pre / t_pre,
             "prefetch_warnings": st.stats.prefetch_warnings,
+            "device_table_decode": {
+                "ms_per_step": t_dt / steps * 1e3,
+                "vs_resident": t_dt / t_res,
+                "hit_rate": dt["hits"] / max(1, dt["demand"]),
+                "misses": dt["misses"], "h2d_bytes": dt["bytes_h2d"],
+            },
         },
         "hybrid_decode": {
             "bp_gbs": bp, "bh_gbs": bh,

@@ -142,6 +142,10 @@ ft_status check_weights(const ft_moe_weights* w) {
     FT_CHECK_ARG(need > 0 && w->slot_stride >= need && w->slot_stride % 256 == 0,
                  "slot_stride %zu must be a multiple of 256 and >= %zu", w->slot_stride, need);
     FT_CHECK_ARG(w->pool && ((uintptr_t)w->pool & 255) == 0, "pool must be 256-byte aligned");
+    FT_CHECK_ARG(!w->host_pool || (((uintptr_t)w->host_pool & 255) == 0 && w->host_stride >= need &&
+                                   w->host_stride % 256 == 0),
+                 "host_pool must be 256-byte aligned with host_stride a multiple of 256 and >= %zu",
+                 need);
     FT_CHECK_ARG(!w->n_shared || w->shared_slot >= 0, "bad shared_slot");
     return FT_OK;
 }
@@ -152,6 +156,19 @@ extern "C" {
 
 const char* ft_last_error(void) { return g_err; }
 const char* ft_version(void) { return "ftmoe 0.1 gfx950"; }
+
+ft_status ft_host_device_pointer(const void* host, void** dev) {
+    clear_error();
+    FT_CHECK_ARG(host && dev, "null host / dev");
+    *dev = nullptr;
+    // (the runtime only reads the host address; its signature is not const)
+    if (hipHostGetDevicePointer(dev, const_cast<void*>(host), 0) != hipSuccess || !*dev) {
+        (void)hipGetLastError();
+        *dev = nullptr;
+        return set_error(FT_ERR_UNSUPPORTED, "host address %p is not mapped for the current device", host);
+    }
+    return FT_OK;
+}
 
 int ft_moe_ffn_set_path(int path) { return g_ffn_path.exchange(path); }
 
@@ -284,6 +301,8 @@ ft_status ft_moe_ffn(const ft_moe_weights* w, const void* x, ft_dtype act_dt, in
     g.w_dt = w->w_dt;
     g.pool = (const uint8_t*)w->pool;
     g.slot_stride = w->slot_stride;
+    g.host_pool = (const uint8_t*)w->host_pool;
+    g.host_stride = w->host_stride;
     layout(w->w_dt, w->H, w->I, g.off);
     for (int m = 0; m < 3; ++m)  // NVFP4 tensor scales follow the down block scales
         g.toff[m] = g.off[5] + (size_t)w->H * w->I / 16 + 4 * (size_t)m;

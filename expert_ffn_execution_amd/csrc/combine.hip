@@ -98,6 +98,23 @@ __global__ __launch_bounds__(256) void copy_i32_flag_kernel(const int32_t* __res
     }
 }
 
+// the expert counts of up to STACK_MAX_LAYERS layers, gathered into one
+// host-visible array [n_layers][n], then a flag (as copy_i32_flag_kernel)
+struct CountsArg {
+    const int32_t* src[ft::STACK_MAX_LAYERS];
+};
+__global__ __launch_bounds__(256) void copy_counts_flag_kernel(const CountsArg a, int n_layers, int n,
+                                                               int32_t* __restrict__ dst, int32_t* flag,
+                                                               int32_t epoch) {
+    for (int l = 0; l < n_layers; ++l)
+        for (int i = threadIdx.x; i < n; i += blockDim.x) dst[(size_t)l * n + i] = a.src[l][i];
+    __threadfence_system();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
 // a slot table of up to TABLE_MAX entries carried in the kernel's arguments
 struct TableArg {
     int32_t v[ft::TABLE_MAX];
@@ -114,6 +131,17 @@ ft_status launch_copy_i32_flag(const int32_t* src, int32_t* dst, int n, int32_t*
                                hipStream_t s) {
     copy_i32_flag_kernel<<<1, 256, 0, s>>>(src, dst, n, flag, epoch);
     FT_LAUNCHED("copy_i32_flag");
+    return FT_OK;
+}
+
+ft_status launch_copy_counts_flag(const int32_t* const* src, int n_layers, int n, int32_t* dst,
+                                  int32_t* flag, int32_t epoch, hipStream_t s) {
+    if (n_layers < 1 || n_layers > STACK_MAX_LAYERS)
+        return set_error(FT_ERR_INVALID_ARG, "%d layers: 1 to %d", n_layers, STACK_MAX_LAYERS);
+    CountsArg a{};
+    for (int l = 0; l < n_layers; ++l) a.src[l] = src[l];
+    copy_counts_flag_kernel<<<1, 256, 0, s>>>(a, n_layers, n, dst, flag, epoch);
+    FT_LAUNCHED("copy_counts_flag");
     return FT_OK;
 }
 

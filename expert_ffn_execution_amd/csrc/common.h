@@ -42,6 +42,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // largest slot table uploaded through a kernel argument (ft_slot_cache_map)
 constexpr int TABLE_MAX = 512;
+// layers of one device-table stack pass (their counts travel in one kernel's arguments)
+constexpr int STACK_MAX_LAYERS = 64;
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // profiling hooks: events recorded around selected kernels (see ft_set_profile_events)

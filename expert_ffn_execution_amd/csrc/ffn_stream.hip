@@ -66,6 +66,8 @@ struct Walk {
 struct StreamArgs {
     const uint8_t* pool;
     size_t slot_stride;
+    const uint8_t* host_pool;  // slot-table entries -2 - j: expert j of this pool
+    size_t host_stride;
     size_t moff[2], soff[2];  // matrix / scale byte offsets inside a slot
     size_t toff[2];           // NVFP4: the matrices' fp32 tensor scales
     const int32_t* offsets;
@@ -99,7 +101,7 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // registers, so the block's first weight address needs no further load.
 struct Group { int e, c, lo, hi, slot; };
 __device__ bool find_group(const int32_t* __restrict__ offsets, const int32_t* __restrict__ slot_of,
-                           int E, int RCAP, int j, int lane, Group& g) {
+                           const void* host_pool, int E, int RCAP, int j, int lane, Group& g) {
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += 256) {
         int nc[4], lo[4], hi[4], sl[4];
@@ -113,7 +115,7 @@ __device__ bool find_group(const int32_t* __restrict__ offsets, const int32_t* _
                 hi[i] = offsets[e + 1];
                 if (slot_of) sl[i] = slot_of[e];
             }
-            nc[i] = hi[i] > lo[i] && sl[i] >= 0 ? (hi[i] - lo[i] + RCAP - 1) / RCAP : 0;
+            nc[i] = hi[i] > lo[i] && ft::slot_has_weights(sl[i], host_pool) ? (hi[i] - lo[i] + RCAP - 1) / RCAP : 0;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -146,7 +148,7 @@ struct GroupRows {
 __device__ __forceinline__ bool resolve_group(const StreamArgs& a, int j, int lane, GroupRows& gr) {
     if (j < a.n_routed_groups) {
         Group g;
-        if (!find_group(a.offsets, a.slot_of, a.E, a.RCAP, j, lane, g)) return false;
+        if (!find_group(a.offsets, a.slot_of, a.host_pool, a.E, a.RCAP, j, lane, g)) return false;
         const int c = __builtin_amdgcn_readfirstlane(g.c);
         gr.slot = __builtin_amdgcn_readfirstlane(g.slot);
         const int lo = __builtin_amdgcn_readfirstlane(g.lo);
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
     bool shared;
     if (j < a.n_routed_groups) {
         Group g;
-        if (!find_group(a.offsets, a.slot_of, a.E, a.RCAP, j, lane, g)) return;
+        if (!find_group(a.offsets, a.slot_of, a.host_pool, a.E, a.RCAP, j, lane, g)) return;
         const int c = __builtin_amdgcn_readfirstlane(g.c);
         slot = __builtin_amdgcn_readfirstlane(g.slot);
         const int lo = __builtin_amdgcn_readfirstlane(g.lo);
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
         shared = true;
     }
     if (R <= 0) return;
-    const uint8_t* sl = a.pool + (size_t)slot * a.slot_stride;
+    const uint8_t* sl = ft::slot_weights(a.pool, a.slot_stride, a.host_pool, a.host_stride, slot);
     const u32x4_t* mat[NM];
     const uint8_t* scl[NM];
     float msc[NM];  // FP8: the matrix scales (applied to the reduced sums); else 1
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     const int rgw = nrg > wave ? (nrg - wave + NWAVE - 1) / NWAVE : 0;    // ... of this wave
     const int U = rgw * nks;                                              // (group, step) pairs
     const int ln = lane & 15, q = lane >> 4;
-    const uint8_t* sl = a.pool + (size_t)gr.slot * a.slot_stride;
+    const uint8_t* sl = ft::slot_weights(a.pool, a.slot_stride, a.host_pool, a.host_stride, gr.slot);
     const size_t rowb = WT == 3 ? (size_t)K : (size_t)K / 2, srowb = (size_t)K / (WT == 4 ? 16 : 32);
     float msc[NM];  // FP8 matrix / NVFP4 tensor scales (applied to the finished sums)
 #pragma unroll
@@ -930,6 +932,8 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     StreamArgs a{};
     a.pool = g.pool;
     a.slot_stride = g.slot_stride;
+    a.host_pool = g.host_pool;
+    a.host_stride = g.host_stride;
     a.offsets = offsets;
     a.slot_of = slot_of;
     a.E = g.E;

@@ -24,9 +24,23 @@ struct FfnGeom {
     ft_dtype w_dt;
     const uint8_t* pool;
     size_t slot_stride;
+    const uint8_t* host_pool;  // device-visible host experts (slot -2 - j), or null
+    size_t host_stride;
     size_t off[6];  // gate, up, down, gate_sc, up_sc, down_sc (bytes within a slot)
     size_t toff[3];  // NVFP4: the fp32 tensor scales of gate, up, down
 };
+
+// A slot-table entry names where an expert's weights are: slot s >= 0 of the
+// device pool, or (entry -2 - j, with a host pool) expert j of the host pool,
+// read over the host link; -1 (or -2 - j without a host pool) skips the expert.
+__host__ __device__ __forceinline__ bool slot_has_weights(int slot, const void* host_pool) {
+    return slot >= 0 || (slot <= -2 && host_pool != nullptr);
+}
+__device__ __forceinline__ const uint8_t* slot_weights(const uint8_t* pool, size_t stride,
+                                                       const uint8_t* host_pool, size_t host_stride,
+                                                       int slot) {
+    return slot >= 0 ? pool + (size_t)slot * stride : host_pool + (size_t)(-2 - slot) * host_stride;
+}
 
 // Build the M-tile list from offsets (one block).  tiles[0..max_tiles),
 // *n_tiles receives the count.

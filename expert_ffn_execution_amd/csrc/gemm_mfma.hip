@@ -257,7 +257,7 @@ __global__ __launch_bounds__(pipe::NT, 1) void gemm_pipe_kernel(
     const int NOUT = MODE == MODE_GATED ? g.I : g.H;   // output columns (h or y)
     const bool shared = td.e == g.E;
     const size_t obase = shared ? (size_t)g.T * g.k + td.p0 : (size_t)td.p0;
-    const uint8_t* slot = g.pool + (size_t)td.slot * g.slot_stride;
+    const uint8_t* slot = ft::slot_weights(g.pool, g.slot_stride, g.host_pool, g.host_stride, td.slot);
     // gated: B rows [0, 128) = gate rows c0.., [128, 256) = up rows c0..; plain: rows c0..
     const int c0 = nt * (MODE == MODE_GATED ? BN / 2 : BN);
 
@@ -634,6 +634,7 @@ __device__ __forceinline__ void tile_span(int c, int n, int m, int& start, int& 
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ slot_of,
+                                                           const void* host_pool,
                                                            int E, int T, int n_shared,
                                                            int shared_slot, int BMr,
                                                            TileDesc* tiles, int* n_tiles,
@@ -645,7 +646,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
         off = offsets[e];
         c = offsets[e + 1] - off;
         slot = slot_of ? slot_of[e] : e;
-        if (slot >= 0 && c > 0) cnt = (c + BMr - 1) / BMr;
+        if (ft::slot_has_weights(slot, host_pool) && c > 0) cnt = (c + BMr - 1) / BMr;
     }
     scan[e] = cnt;
     __syncthreads();
@@ -784,8 +785,9 @@ int tile_rows(const FfnGeom&) { return pipe::BM; }
 ft_status launch_build_tiles(const FfnGeom& g, const int32_t* offsets,
                              const int32_t* slot_of_expert, int shared_slot, TileDesc* tiles,
                              int* n_tiles, int max_tiles, hipStream_t s) {
-    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, slot_of_expert, g.E, g.T, g.n_shared,
-                                          shared_slot, tile_rows(g), tiles, n_tiles, max_tiles);
+    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, slot_of_expert, g.host_pool, g.E, g.T,
+                                          g.n_shared, shared_slot, tile_rows(g), tiles, n_tiles,
+                                          max_tiles);
     FT_LAUNCHED("build_tiles");
     return FT_OK;
 }

@@ -9,9 +9,15 @@
 // chains per wave (8) and operands held in registers, so only the instruction
 // differs.  Each point runs twice: a burst of a few milliseconds, and a
 // sustained run of about 400 ms, long enough for the chip's power management
-// to settle.  Wave 0 of every block reads the shader-clock counter (s_memtime)
-// and the 100 MHz constant clock (s_memrealtime) at its start and end; their
-// ratio is the average shader clock the block saw.
+// to settle.  The operands are either small integers that every MFMA reuses
+// (few bits change) or two sets of random bits (finite bf16 values in
+// [2^-7, 2), any fp8 / fp4 codes) that consecutive MFMAs alternate between,
+// since the matrix cores' power, and with it the clock the chip can hold,
+// depends on how many bits change.  Both sets are made before the loop, so
+// the loop holds MFMAs only.  Wave 0 of
+// every block reads the shader-clock counter (s_memtime) and the 100 MHz
+// constant clock (s_memrealtime) at its start and end; their ratio is the
+// average shader clock the block saw.
 //
 // Output: one JSON object per line.  Exit status 0 when every launch succeeded.
 #include <hip/hip_runtime.h>
@@ -25,6 +31,9 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned lcg(unsigned v) { return v * 1664525u + 1013904223u; }
 
 constexpr int CHAINS = 8;
 constexpr int THREADS = 256;
@@ -33,7 +42,7 @@ enum Kind { BF16 = 0, FP8_FP4 = 1, FP4_FP4 = 2 };
 
 double flop_per_instruction(int kind) { return kind == BF16 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64; }
 
-template <int KIND>
+template <int KIND, bool RAND>
 __global__ __launch_bounds__(THREADS) void issue_kernel(float* sink, unsigned long long* clocks, int iters,
                                                         int seed) {
     unsigned long long t0 = 0, r0 = 0;
@@ -54,10 +63,26 @@ __global__ __launch_bounds__(THREADS) void issue_kernel(float* sink, unsigned lo
             a[q] = (__bf16)(float)((t + q) & 3);
             b[q] = (__bf16)(float)((3 * t + q) & 3);
         }
+        bf16x8 a2 = a, b2 = b;
+        if constexpr (RAND) {
+            u32x4 r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r[0][q] = lcg(lcg(2u * t + q));
+                r[1][q] = lcg(lcg(7u * t + q + 1u));
+                r[2][q] = lcg(r[0][q] ^ 0x9e3779b9u);
+                r[3][q] = lcg(r[1][q] ^ 0x7f4a7c15u);
+            }
+            // sign and mantissa random, exponent 0x78..0x7f: finite, in [2^-7, 2)
+            a = __builtin_bit_cast(bf16x8, (r[0] & 0x83FF83FFu) | 0x3C003C00u);
+            b = __builtin_bit_cast(bf16x8, (r[1] & 0x83FF83FFu) | 0x3C003C00u);
+            a2 = __builtin_bit_cast(bf16x8, (r[2] & 0x83FF83FFu) | 0x3C003C00u);
+            b2 = __builtin_bit_cast(bf16x8, (r[3] & 0x83FF83FFu) | 0x3C003C00u);
+        }
         for (int i = 0; i < iters; ++i)
 #pragma unroll
             for (int c = 0; c < CHAINS; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c & 1 ? a2 : a, c & 1 ? b2 : b, acc[c], 0, 0, 0);
     } else {
         // operand formats of the scaled MFMA: 0 = fp8 e4m3, 4 = fp4 e2m1; scale
         // bytes 127 = 2^0
@@ -68,10 +93,21 @@ __global__ __launch_bounds__(THREADS) void issue_kernel(float* sink, unsigned lo
             a[q] = (7 * t + q) & 0x3f3f3f3f;
             b[q] = (5 * t + q) & 0x33333333;
         }
+        i32x8 a2 = a, b2 = b;
+        if constexpr (RAND) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                a[q] = (int)lcg(lcg(2u * t + q));
+                b[q] = (int)lcg(lcg(7u * t + q + 1u));
+                a2[q] = (int)lcg((unsigned)a[q] ^ 0x9e3779b9u);
+                b2[q] = (int)lcg((unsigned)b[q] ^ 0x7f4a7c15u);
+            }
+        }
         for (int i = 0; i < iters; ++i)
 #pragma unroll
             for (int c = 0; c < CHAINS; ++c)
-                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], FA, FB, 0, 127, 0, 127);
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(c & 1 ? a2 : a, c & 1 ? b2 : b, acc[c],
+                                                                         FA, FB, 0, 127, 0, 127);
     }
     float s = 0.f;
 #pragma unroll
@@ -100,13 +136,13 @@ struct Point {
         }                                                                                  \
     } while (0)
 
-template <int KIND>
+template <int KIND, bool RAND>
 Point run(int blocks, int iters, float* sink, unsigned long long* clocks_dev) {
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
     CHECK(hipEventRecord(e0));
-    issue_kernel<KIND><<<blocks, THREADS>>>(sink, clocks_dev, iters, 1);
+    issue_kernel<KIND, RAND><<<blocks, THREADS>>>(sink, clocks_dev, iters, 1);
     CHECK(hipGetLastError());
     CHECK(hipEventRecord(e1));
     CHECK(hipEventSynchronize(e1));
@@ -126,20 +162,20 @@ Point run(int blocks, int iters, float* sink, unsigned long long* clocks_dev) {
     return {ms, flops / (ms * 1e-3) / 1e12, ref > 0 ? cyc / ref * 0.1 : 0.0};
 }
 
-template <int KIND>
+template <int KIND, bool RAND>
 void sweep(const char* name, int ncu, float* sink, unsigned long long* clocks_dev) {
     for (int wps = 1; wps <= 2; ++wps) {
         const int blocks = ncu * wps;  // 256-thread blocks, one per CU per slot: wps waves per SIMD
-        run<KIND>(blocks, 64, sink, clocks_dev);                       // warm-up
-        const Point probe = run<KIND>(blocks, 2000, sink, clocks_dev);  // sizes the runs below
+        run<KIND, RAND>(blocks, 64, sink, clocks_dev);                       // warm-up
+        const Point probe = run<KIND, RAND>(blocks, 2000, sink, clocks_dev);  // sizes the runs below
         const double per_iter_ms = probe.ms / 2000.0;
         for (double target_ms : {5.0, 400.0}) {
             const long long it = (long long)(target_ms / per_iter_ms);
             const int iters = (int)(it < 1 ? 1 : (it > 200000000 ? 200000000 : it));
-            const Point p = run<KIND>(blocks, iters, sink, clocks_dev);
-            printf("{\"mfma\": \"%s\", \"waves_per_simd\": %d, \"chains\": %d, \"ms\": %.3f, "
-                   "\"tflops\": %.1f, \"shader_clock_ghz\": %.3f}\n",
-                   name, wps, CHAINS, p.ms, p.tflops, p.clock_ghz);
+            const Point p = run<KIND, RAND>(blocks, iters, sink, clocks_dev);
+            printf("{\"mfma\": \"%s\", \"operands\": \"%s\", \"waves_per_simd\": %d, \"chains\": %d, "
+                   "\"ms\": %.3f, \"tflops\": %.1f, \"shader_clock_ghz\": %.3f}\n",
+                   name, RAND ? "random" : "fixed", wps, CHAINS, p.ms, p.tflops, p.clock_ghz);
             fflush(stdout);
         }
     }
@@ -160,9 +196,11 @@ int main() {
     CHECK(hipMalloc(&sink, (size_t)max_blocks * THREADS * sizeof(float)));
     CHECK(hipMalloc(&clocks_dev, (size_t)max_blocks * 2 * sizeof(unsigned long long)));
     printf("{\"compute_units\": %d, \"bf16_flop_per_cycle_per_cu\": %d}\n", ncu, 4 * 1024);
-    sweep<BF16>("bf16 32x32x16", ncu, sink, clocks_dev);
-    sweep<FP8_FP4>("scaled fp8 x fp4 32x32x64", ncu, sink, clocks_dev);
-    sweep<FP4_FP4>("scaled fp4 x fp4 32x32x64", ncu, sink, clocks_dev);
+    sweep<BF16, false>("bf16 32x32x16", ncu, sink, clocks_dev);
+    sweep<FP8_FP4, false>("scaled fp8 x fp4 32x32x64", ncu, sink, clocks_dev);
+    sweep<FP4_FP4, false>("scaled fp4 x fp4 32x32x64", ncu, sink, clocks_dev);
+    sweep<BF16, true>("bf16 32x32x16", ncu, sink, clocks_dev);
+    sweep<FP8_FP4, true>("scaled fp8 x fp4 32x32x64", ncu, sink, clocks_dev);
     CHECK(hipFree(sink));
     CHECK(hipFree(clocks_dev));
     return 0;

@@ -13,6 +13,16 @@
 // claypier.com article, "按带宽决定分工的思路": whole-layer double-buffered
 // streaming).  Asynchronous copies need page-locked host memory, so a pageable
 // pool is refused (FreeToken hub article, install caveat on WSL).
+//
+// Device-table passes (FT_STACK_DEVICE_TABLE) turn the order around for
+// decode: the FFN reads a device slot table that maps each expert either to
+// its slot (once the copy into it has landed) or to the pinned host pool, so a
+// whole pass is enqueued without the host waiting for any layer's routing.  A
+// kernel then brings every layer's counts to a pinned ring and sets a flag;
+// later calls take each finished pass through the same LRU map and release,
+// whose copies fill slots for the passes after.  A pass records one read
+// event for all the slots its table maps, which is what a copy into one of
+// them waits for.
 #include <hip/hip_runtime.h>
 
 #include <chrono>
@@ -29,6 +39,8 @@ ft_status launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s
 ft_status launch_copy_i32_flag(const int32_t* src, int32_t* dst, int n, int32_t* flag, int32_t epoch,
                                hipStream_t s);
 ft_status launch_set_table(const int32_t* table, int n, int32_t* dst, hipStream_t s);
+ft_status launch_copy_counts_flag(const int32_t* const* src, int n_layers, int n, int32_t* dst,
+                                  int32_t* flag, int32_t epoch, hipStream_t s);
 }
 
 struct ft_slot_cache {
@@ -54,6 +66,17 @@ struct ft_slot_cache {
     int32_t* flags = nullptr;        // pinned [n_layers]
     int32_t* flags_dev = nullptr;    // its device mapping, or null
     int32_t epoch = 0;
+    // device-table passes (FT_STACK_DEVICE_TABLE), set up on first use
+    static constexpr int DT_RING = 4;      // passes routed but not yet taken through the LRU, at most
+    int32_t* dtab = nullptr;               // device [n_layers][n_experts]: slot, or -2 - host index
+    std::vector<int32_t> htab;             // what dtab holds
+    const uint8_t* host_dev = nullptr;     // device address of the host pool
+    int32_t* dt_counts = nullptr;          // pinned [DT_RING][n_layers][n_experts]
+    int32_t* dt_counts_dev = nullptr;
+    int32_t* dt_flags = nullptr;           // pinned [DT_RING]: the pass number whose counts are there
+    int32_t* dt_flags_dev = nullptr;
+    long long dt_enq = 0, dt_done = 0;     // passes enqueued / taken through the LRU
+    int dt_layers[DT_RING] = {};
 
     explicit ft_slot_cache(const ft_slot_cache_desc& dd)
         : d(dd), policy(dd.n_layers, dd.n_experts, dd.n_slots, dd.scope, dd.expert_bytes) {}
@@ -99,10 +122,17 @@ struct HipEngine final : ftp::Engine {
         return ok(e);
     }
     bool copy_wait(int slot) override { return ok(hipEventSynchronize(c->filled[slot])); }
+    // device-table bookkeeping: kernels find slots through the device table,
+    // which maps a slot only once its copy has landed, and each pass records
+    // one read event for every slot the table maps; so the compute stream
+    // neither waits for copies nor records reads here
+    bool dt = false;
     bool compute_wait(int slot) override {
+        if (dt) return true;
         return ok(hipStreamWaitEvent(compute, c->filled[slot], 0));
     }
     bool record_read(int slot) override {
+        if (dt) return true;
         if (shared_ev < 0) {
             shared_ev = c->rpos;
             c->rpos = (c->rpos + 1) % (int)c->rpool.size();
@@ -176,6 +206,111 @@ ft_status hip_status(hipError_t err, ft_status st) {
 ft_status hip_status(const HipEngine& eng, ft_status st) { return hip_status(eng.err, st); }
 
 hipError_t make_event(hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); }
+
+// ---- device-table passes ---------------------------------------------------
+
+ft_status dt_setup(ft_slot_cache* c) {
+    if (c->dtab) return FT_OK;
+    const ft_slot_cache_desc& d = c->d;
+    if (d.n_experts > ft::TABLE_MAX)
+        return ft::set_error(FT_ERR_UNSUPPORTED, "device-table passes: %d experts per layer > %d",
+                             d.n_experts, ft::TABLE_MAX);
+    void* hp = nullptr;
+    // (the runtime only reads the host address; its signature is not const)
+    if (hipHostGetDevicePointer(&hp, const_cast<void*>(d.host_pool), 0) != hipSuccess || !hp) {
+        (void)hipGetLastError();
+        return ft::set_error(FT_ERR_UNSUPPORTED, "device-table passes: the host pool has no device mapping");
+    }
+    if (((uintptr_t)hp & 255) || d.host_stride % 256)
+        return ft::set_error(FT_ERR_UNSUPPORTED,
+                             "device-table passes: the host pool must be 256-byte aligned with a "
+                             "stride that is a multiple of 256");
+    const size_t n = (size_t)d.n_layers * d.n_experts;
+    FT_HIP(hipMalloc((void**)&c->dtab, sizeof(int32_t) * n));
+    FT_HIP(hipHostMalloc((void**)&c->dt_counts, sizeof(int32_t) * n * ft_slot_cache::DT_RING,
+                         hipHostMallocDefault));
+    FT_HIP(hipHostMalloc((void**)&c->dt_flags, sizeof(int32_t) * ft_slot_cache::DT_RING,
+                         hipHostMallocDefault));
+    for (int i = 0; i < ft_slot_cache::DT_RING; ++i) c->dt_flags[i] = 0;
+    void* dp = nullptr;
+    FT_HIP(hipHostGetDevicePointer(&dp, c->dt_counts, 0));
+    c->dt_counts_dev = (int32_t*)dp;
+    FT_HIP(hipHostGetDevicePointer(&dp, c->dt_flags, 0));
+    c->dt_flags_dev = (int32_t*)dp;
+    c->htab.assign(n, INT32_MIN);  // nothing uploaded yet: every row differs
+    c->host_dev = (const uint8_t*)hp;
+    return FT_OK;
+}
+
+// Take the oldest pass not yet counted through the LRU: map and release each
+// of its layers' experts (ascending layer), as the per-layer path would have.
+// Returns FT_OK with *done = false when its counts are not there and !block.
+ft_status dt_account_one(ft_slot_cache* c, HipEngine& eng, bool block, bool* done, ft_stack_stats* acc) {
+    *done = false;
+    if (c->dt_done >= c->dt_enq) return FT_OK;
+    const int ring = (int)(c->dt_done % ft_slot_cache::DT_RING);
+    const int32_t want = (int32_t)(c->dt_done + 1);
+    if (__atomic_load_n(c->dt_flags + ring, __ATOMIC_ACQUIRE) != want) {
+        if (!block) return FT_OK;
+        // bounded: a stream that stopped (an earlier failure) gives an error
+        // rather than a hung host
+        const auto t0 = std::chrono::steady_clock::now();
+        while (__atomic_load_n(c->dt_flags + ring, __ATOMIC_ACQUIRE) != want) {
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(20))
+                return ft::set_error(FT_ERR_HIP, "the expert counts of pass %lld did not arrive",
+                                     c->dt_done + 1);
+#if defined(__x86_64__)
+            __builtin_ia32_pause();
+#endif
+        }
+    }
+    const int E = c->d.n_experts, L = c->dt_layers[ring];
+    const int32_t* cnt = c->dt_counts + (size_t)ring * c->d.n_layers * E;
+    std::vector<int32_t> need, slots((size_t)E);
+    for (int l = 0; l < L; ++l) {
+        need.clear();
+        for (int e = 0; e < E; ++e)
+            if (cnt[(size_t)l * E + e] > 0) need.push_back(e);
+        ft_map_stats ms{};
+        ft_status r = c->policy.map(eng, l, need.data(), (int)need.size(), slots.data(), &ms);
+        if (r == FT_OK) r = c->policy.release(eng, l);
+        if (r != FT_OK) return hip_status(eng, r);
+        acc->demand += ms.n_demand;
+        acc->hits += ms.n_hit;
+        acc->prefetch_hits += ms.n_prefetch_hit;
+        acc->misses += ms.n_miss;
+    }
+    ++c->dt_done;
+    *done = true;
+    return FT_OK;
+}
+
+// Bring the device table to the cache's state: an expert maps to its slot
+// once the copy into it has landed, else to the host pool.  Rows that change
+// are written on the compute stream, ahead of the pass that reads them.
+ft_status dt_sync(ft_slot_cache* c, hipStream_t cs) {
+    const int E = c->d.n_experts;
+    std::vector<int32_t> row((size_t)E);
+    for (int l = 0; l < c->d.n_layers; ++l) {
+        for (int e = 0; e < E; ++e) {
+            const int sl = c->policy.lookup(l, e);
+            bool landed = sl >= 0;
+            if (landed && c->policy.entry(sl).copying) {
+                const hipError_t q = hipEventQuery(c->filled[sl]);
+                if (q != hipSuccess && q != hipErrorNotReady) FT_HIP(q);
+                landed = q == hipSuccess;
+            }
+            row[e] = landed ? sl : -2 - (l * E + e);
+        }
+        int32_t* have = c->htab.data() + (size_t)l * E;
+        if (std::memcmp(row.data(), have, sizeof(int32_t) * E) != 0) {
+            const ft_status r = ft::launch_set_table(row.data(), E, c->dtab + (size_t)l * E, cs);
+            if (r != FT_OK) return r;
+            std::memcpy(have, row.data(), sizeof(int32_t) * E);
+        }
+    }
+    return FT_OK;
+}
 
 }  // namespace
 
@@ -266,6 +401,9 @@ ft_status ft_slot_cache_destroy(ft_slot_cache* c) {
         if (e) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
     if (c->stage) (void)hipHostFree(c->stage);
     if (c->flags) (void)hipHostFree(c->flags);
+    if (c->dtab) (void)hipFree(c->dtab);  // after the read events above: no pass still reads it
+    if (c->dt_counts) (void)hipHostFree(c->dt_counts);
+    if (c->dt_flags) (void)hipHostFree(c->dt_flags);
     delete c;
     return FT_OK;
 }
@@ -383,10 +521,117 @@ int ft_slot_cache_lookup(const ft_slot_cache* c, int layer, int expert) {
 // experts are prefetched on the copy stream (the next layer's weights travel
 // while this layer computes: claypier.com article, "按带宽决定分工的思路";
 // FreeToken hub article, paragraph on prefill overlap) and mapped.
+namespace {
+
+// One FT_STACK_DEVICE_TABLE pass (or, with n_layers == 0, a flush).
+ft_status dt_forward(ft_slot_cache* c, const ft_stack_pass* p, hipStream_t cs, hipStream_t copy_s,
+                     ft_stack_stats* out) {
+    const int L = p->n_layers, E = c->d.n_experts;
+    FT_CHECK_ARG(L >= 0 && L <= c->d.n_layers, "n_layers must be in [0, %d]", c->d.n_layers);
+    if (L > ft::STACK_MAX_LAYERS)
+        return ft::set_error(FT_ERR_UNSUPPORTED, "device-table passes: %d layers > %d", L,
+                             ft::STACK_MAX_LAYERS);
+    const ft_moe_step* S = p->layers;
+    FT_CHECK_ARG(L == 0 || S, "null layers");
+    for (int l = 0; l < L; ++l) {
+        if (S[l].weights.n_shared)
+            return ft::set_error(FT_ERR_UNSUPPORTED, "device-table passes: no shared expert");
+        FT_CHECK_ARG(S[l].T >= 1 && S[l].weights.E == E && S[l].counts,
+                     "layer %d: T >= 1, E == the cache's experts per layer, counts", l);
+        FT_CHECK_ARG(S[l].weights.pool == c->d.dev_slots && S[l].weights.slot_stride == c->d.slot_stride,
+                     "layer %d: weights.pool / slot_stride must be the cache's slot array", l);
+    }
+    if (L == 0 && !c->dtab) {  // a flush before any device-table pass
+        if (out) *out = ft_stack_stats{};
+        return FT_OK;
+    }
+    ft_status r = dt_setup(c);
+    if (r != FT_OK) return r;
+    HipEngine eng(c, cs, copy_s);
+    eng.dt = true;
+    ft_stack_stats acc{};
+    const long long h2d0 = c->policy.stats().bytes_h2d;
+    // passes whose counts are back, then (blocking) room in the ring for this
+    // one; a flush takes every pending pass
+    bool done = true;
+    while (done) {
+        r = dt_account_one(c, eng, false, &done, &acc);
+        if (r != FT_OK) return r;
+    }
+    const long long keep = L > 0 ? ft_slot_cache::DT_RING - 1 : 0;
+    while (c->dt_enq - c->dt_done > keep) {
+        r = dt_account_one(c, eng, true, &done, &acc);
+        if (r != FT_OK) return r;
+    }
+    if (L > 0) {
+        r = dt_sync(c, cs);
+        if (r != FT_OK) return r;
+        const int32_t* cnts[ft::STACK_MAX_LAYERS];
+        for (int l = 0; l < L; ++l) {
+            const ft_moe_step& st = S[l];
+            const float* lin = p->logits_in ? p->logits_in[l] : nullptr;
+            if (lin) {
+                r = ft_moe_route(nullptr, st.act_dt, nullptr, lin, st.bias, st.T, st.weights.H, E, st.k,
+                                 nullptr, st.topk_ids, st.topk_w, cs);
+                if (r == FT_OK)
+                    r = ft_moe_align(st.topk_ids, st.T, st.k, E, st.counts, st.offsets, st.perm,
+                                     st.inv_perm, st.align_ws, st.align_ws_bytes, cs);
+            } else {
+                r = ft::route_align(&st, cs);
+            }
+            ft_moe_weights w = st.weights;
+            w.host_pool = c->host_dev;
+            w.host_stride = c->d.host_stride;
+            if (r == FT_OK)
+                r = ft_moe_ffn(&w, st.x, st.act_dt, st.T, st.k, st.perm, st.offsets, c->dtab + (size_t)l * E,
+                               st.y_perm, st.y_dt, st.ffn_ws, st.ffn_ws_bytes, cs);
+            if (r == FT_OK)
+                r = ft_moe_combine(st.y_perm, st.y_dt, st.inv_perm, st.topk_w, st.T, st.k, w.H, 0,
+                                   st.out, st.out_dt, cs);
+            if (r != FT_OK) return r;
+            cnts[l] = st.counts;
+        }
+        const int ring = (int)(c->dt_enq % ft_slot_cache::DT_RING);
+        r = ft::launch_copy_counts_flag(cnts, L, E, c->dt_counts_dev + (size_t)ring * c->d.n_layers * E, c->dt_flags_dev + ring,
+                                        (int32_t)(c->dt_enq + 1), cs);
+        if (r != FT_OK) return r;
+        // one read point, after the pass, for every slot the table maps: a
+        // copy into such a slot waits for it
+        const int ev = c->rpos;
+        c->rpos = (c->rpos + 1) % (int)c->rpool.size();
+        FT_HIP(hipEventRecord(c->rpool[ev], cs));
+        ++c->rgen[ev];
+        for (int32_t v : c->htab)
+            if (v >= 0) {
+                c->read_ev[v] = ev;
+                c->read_gen[v] = c->rgen[ev];
+            }
+        c->dt_layers[ring] = L;
+        ++c->dt_enq;
+    }
+    acc.bytes_h2d = c->policy.stats().bytes_h2d - h2d0;
+    if (out) *out = acc;
+    return hip_status(eng, FT_OK);
+}
+
+}  // namespace
+
 ft_status ft_slot_stack_forward(ft_slot_cache* c, const ft_stack_pass* p, void* compute,
                                 void* copy_stream, ft_stack_stats* out) {
     ft::clear_error();
-    FT_CHECK_ARG(c && p && p->layers && p->counts_host, "null cache / pass / layers / counts_host");
+    FT_CHECK_ARG(c && p, "null cache / pass");
+    FT_CHECK_ARG((p->flags & ~FT_STACK_DEVICE_TABLE) == 0, "unknown flags 0x%x", p->flags);
+    ft_stack_stats flushed{};
+    if (p->flags & FT_STACK_DEVICE_TABLE) {
+        if (!p->prefill) return dt_forward(c, p, (hipStream_t)compute, (hipStream_t)copy_stream, out);
+        if (c->dt_enq > c->dt_done) {  // a prefill: count the pending passes first
+            ft_stack_pass flush{};
+            flush.flags = FT_STACK_DEVICE_TABLE;
+            const ft_status r = dt_forward(c, &flush, (hipStream_t)compute, (hipStream_t)copy_stream, &flushed);
+            if (r != FT_OK) return r;
+        }
+    }
+    FT_CHECK_ARG(p->layers && p->counts_host, "null layers / counts_host");
     const int L = p->n_layers;
     FT_CHECK_ARG(L >= 1 && L <= c->d.n_layers, "n_layers must be in [1, %d]", c->d.n_layers);
     const ft_moe_step* S = p->layers;
@@ -412,7 +657,7 @@ ft_status ft_slot_stack_forward(ft_slot_cache* c, const ft_stack_pass* p, void* 
     }
     const bool use_flags = counts_dev_map && c->flags_dev;
     const int32_t epoch = ++c->epoch;  // this pass's flag value
-    ft_stack_stats acc{};
+    ft_stack_stats acc = flushed;
     const ft_cache_stats before = c->policy.stats();
     std::vector<int32_t> need, all(E + ns);
     for (int e = 0; e < E + ns; ++e) all[e] = e;
@@ -521,7 +766,7 @@ ft_status ft_slot_stack_forward(ft_slot_cache* c, const ft_stack_pass* p, void* 
         }
     }
 #undef FT_STACK_TRY
-    acc.bytes_h2d = c->policy.stats().bytes_h2d - before.bytes_h2d;
+    acc.bytes_h2d = flushed.bytes_h2d + c->policy.stats().bytes_h2d - before.bytes_h2d;
     if (out) *out = acc;
     return FT_OK;
 }

@@ -33,8 +33,9 @@ EXPORTS = [
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
     "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc", "ft_split_misses",
-    "ft_moe_scatter_rows", "ft_slot_stack_forward",
+    "ft_moe_scatter_rows", "ft_slot_stack_forward", "ft_host_device_pointer",
 ]
+STACK_DEVICE_TABLE = 1   # FT_STACK_DEVICE_TABLE
 NOALLOC_SCRATCH_BYTES = 64 << 20   # FT_NOALLOC_SCRATCH_BYTES
 
 
@@ -47,7 +48,7 @@ class FtError(RuntimeError):
 class MoeWeights(C.Structure):
     _fields_ = [("w_dt", C.c_int), ("E", C.c_int), ("H", C.c_int), ("I", C.c_int),
                 ("n_shared", C.c_int), ("pool", C.c_void_p), ("slot_stride", C.c_size_t),
-                ("shared_slot", C.c_int)]
+                ("shared_slot", C.c_int), ("host_pool", C.c_void_p), ("host_stride", C.c_size_t)]
 
 
 class MoeStep(C.Structure):
@@ -70,7 +71,7 @@ class SlotCacheDesc(C.Structure):
 
 class StackPass(C.Structure):
     _fields_ = [("n_layers", C.c_int), ("layers", C.c_void_p), ("logits_in", C.c_void_p),
-                ("counts_host", C.c_void_p), ("prefill", C.c_int)]
+                ("counts_host", C.c_void_p), ("prefill", C.c_int), ("flags", C.c_int)]
 
 
 class StackStats(C.Structure):
@@ -143,6 +144,7 @@ def load() -> C.CDLL:
         "ft_moe_graph_create": [C.POINTER(MoeStep), P, C.POINTER(P)],
         "ft_moe_graph_launch": [P, P],
         "ft_moe_graph_destroy": [P],
+        "ft_host_device_pointer": [P, C.POINTER(P)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -262,11 +264,26 @@ def pack_expert(ex: dict, wdtype: str, H: int, I: int, out: torch.Tensor):
         out[off:off + b.numel()].copy_(b)
 
 
+def host_device_pointer(t: torch.Tensor) -> int:
+    """ft_host_device_pointer: the device-visible address of a pinned host tensor."""
+    if t.is_cuda or not t.is_pinned():
+        raise FtError(ERR_INVALID_ARG, "host_device_pointer needs a pinned host tensor")
+    out = C.c_void_p()
+    _check(load().ft_host_device_pointer(C.c_void_p(t.data_ptr()), C.byref(out)))
+    return out.value
+
+
 def make_weights(wdtype: str, E: int, H: int, I: int, pool: torch.Tensor, n_shared: int = 0,
-                 shared_slot: int = 0) -> MoeWeights:
-    """Describe a device slot array pool [n_slots, slot_stride] (uint8)."""
+                 shared_slot: int = 0, host_pool: Optional[torch.Tensor] = None) -> MoeWeights:
+    """Describe a device slot array pool [n_slots, slot_stride] (uint8), and
+    optionally a pinned host array host_pool [n, stride] (uint8) whose expert
+    j a slot-table entry -2 - j reads over the host link."""
     _dev(pool)
-    return MoeWeights(DT[wdtype], E, H, I, n_shared, pool.data_ptr(), pool.shape[1], shared_slot)
+    hp, hs = None, 0
+    if host_pool is not None:
+        hp, hs = host_device_pointer(host_pool), host_pool.shape[-1]
+    return MoeWeights(DT[wdtype], E, H, I, n_shared, pool.data_ptr(), pool.shape[1], shared_slot,
+                      hp, hs)
 
 
 def ffn_workspace(wts: MoeWeights, T: int, k: int) -> int:
@@ -569,17 +586,22 @@ class SlotCache:
                     allow=(OK, WARN_OVERLAP_DISABLED))
         return st, got.value
 
-    def forward_stack(self, steps, n_layers: int, counts_host: torch.Tensor, logits_in=None,
-                      prefill: bool = False, compute=None, copy=None) -> StackStats:
+    def forward_stack(self, steps, n_layers: int, counts_host: Optional[torch.Tensor], logits_in=None,
+                      prefill: bool = False, compute=None, copy=None,
+                      device_table: bool = False) -> StackStats:
         """ft_slot_stack_forward over n_layers: steps is a ctypes array of
         MoeStep (one per layer, with its buffers), counts_host a pinned int32
-        host tensor [n_layers, E], logits_in None or a ctypes array of
-        n_layers device pointers (None entries: router GEMM)."""
-        if counts_host.is_cuda or not counts_host.is_pinned() or counts_host.dtype != torch.int32:
+        host tensor [n_layers, E] (unused by device-table decode passes),
+        logits_in None or a ctypes array of n_layers device pointers (None
+        entries: router GEMM).  device_table: FT_STACK_DEVICE_TABLE (with
+        n_layers == 0: flush the pending passes)."""
+        if counts_host is not None and (counts_host.is_cuda or not counts_host.is_pinned()
+                                        or counts_host.dtype != torch.int32):
             raise FtError(ERR_INVALID_ARG, "counts_host must be pinned host int32")
-        p = StackPass(n_layers, C.cast(steps, C.c_void_p),
+        p = StackPass(n_layers, None if steps is None else C.cast(steps, C.c_void_p),
                       None if logits_in is None else C.cast(logits_in, C.c_void_p),
-                      counts_host.data_ptr(), int(prefill))
+                      None if counts_host is None else counts_host.data_ptr(), int(prefill),
+                      STACK_DEVICE_TABLE if device_table else 0)
         st = StackStats()
         _check(load().ft_slot_stack_forward(self.h, C.byref(p), _stream(compute), _stream(copy),
                                             C.byref(st)))

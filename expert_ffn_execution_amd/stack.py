@@ -24,6 +24,13 @@ the GPU's work on layer l and the copies of layer l+1; their rows are copied
 to the device and placed into layer l+1's y_perm by ft_moe_scatter_rows before
 its combine.
 
+Device-table decode (``device_table=True``): the pass runs without the host
+waiting for any layer's histogram.  The library keeps a device slot table that
+sends each expert either to its slot (once its copy has landed) or to the
+pinned pool, read over the host link; the histograms come back in one copy
+after the pass and the LRU takes them up to two passes later (``flush()``
+settles the rest), copying missed experts into slots for the passes after.
+
 Each layer's device buffers (logits, routing, alignment, workspaces, y_perm,
 output) are allocated once per batch size and reused from step to step: the
 outputs forward() returns stay valid until the next call.  Without hybrid
@@ -282,7 +289,22 @@ class SlotStack:
             self._steps[key] = arr
         return self._steps[key]
 
-    def _forward_native(self, xs, prefill, out_dtype, logits):
+    def _add_stats(self, st):
+        self.stats.demand += st.demand
+        self.stats.hits += st.hits
+        self.stats.prefetch_hits += st.prefetch_hits
+        self.stats.misses += st.misses
+        self.stats.bytes_h2d += st.bytes_h2d
+        self.stats.prefetch_warnings += st.prefetch_warnings
+
+    def flush(self):
+        """Take every pending device-table pass through the LRU (its stats
+        are then in self.stats)."""
+        st = self.cache.forward_stack(None, 0, None, device_table=True,
+                                      compute=torch.cuda.current_stream(), copy=self.copy_stream)
+        self._add_stats(st)
+
+    def _forward_native(self, xs, prefill, out_dtype, logits, device_table=False):
         T = xs[0].shape[0]
         arr = self._native_steps(T, out_dtype)
         for l in range(self.L):
@@ -293,30 +315,31 @@ class SlotStack:
         if logits is not None:
             lin = (C.c_void_p * self.L)(*[None if a is None else a.data_ptr() for a in logits])
         st = self.cache.forward_stack(arr, self.L, self._counts_host, lin, prefill,
-                                      compute=torch.cuda.current_stream(), copy=self.copy_stream)
-        self.stats.demand += st.demand
-        self.stats.hits += st.hits
-        self.stats.prefetch_hits += st.prefetch_hits
-        self.stats.misses += st.misses
-        self.stats.bytes_h2d += st.bytes_h2d
-        self.stats.prefetch_warnings += st.prefetch_warnings
+                                      compute=torch.cuda.current_stream(), copy=self.copy_stream,
+                                      device_table=device_table)
+        self._add_stats(st)
         self.stats.steps += 1
         return [self._dbufs[l]["out"] for l in range(self.L)]
 
     def forward(self, xs: List[torch.Tensor], prefill: bool = False,
                 out_dtype=torch.bfloat16,
                 logits: Optional[List[torch.Tensor]] = None,
-                hybrid: bool = False) -> List[torch.Tensor]:
+                hybrid: bool = False, device_table: bool = False) -> List[torch.Tensor]:
         """One pass through all layers; xs[l] is layer l's input batch [T, H]
         (independent per layer).  `logits` optionally supplies each layer's
         router logits instead of the router GEMM.  `hybrid` splits each layer's
         misses between PCIe copies and host cores (decode; needs calibrate()).
+        `device_table` runs a decode pass without host waits: experts not in
+        a slot are read from the pinned pool over the host link, and the LRU
+        takes the pass's routing up to two passes later (flush() settles it).
         Returns the per-layer outputs."""
         sh = self.sh
         if hybrid and sh.wdtype != "bf16":
             raise ValueError("hybrid decode computes missed experts on the host in bf16 only")
+        if hybrid and device_table:
+            raise ValueError("hybrid and device_table decode are separate modes")
         if not (hybrid and not prefill):
-            return self._forward_native(xs, prefill, out_dtype, logits)
+            return self._forward_native(xs, prefill, out_dtype, logits, device_table)
         lg = logits if logits is not None else [None] * self.L
         outs = []
         want_x = hybrid and not prefill

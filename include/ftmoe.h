@@ -68,6 +68,10 @@ typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_FP8 = 3, FT_NVFP4 = 4 }
 const char* ft_last_error(void);
 /* Library version string. */
 const char* ft_version(void);
+/* Device-visible address of page-locked host memory (hipHostGetDevicePointer),
+ * e.g. for ft_moe_weights.host_pool.  FT_ERR_INVALID_ARG for a null argument,
+ * FT_ERR_UNSUPPORTED when `host` is not mapped for the current device. */
+ft_status ft_host_device_pointer(const void* host, void** dev);
 
 /* --------------------------------------------------------------------------
  * ft_moe_route -- router top-k gating.
@@ -161,6 +165,13 @@ typedef struct {
     const void* pool;     /* device base of the slot array */
     size_t slot_stride;   /* bytes between slots (>= ft_expert_layout(), multiple of 256) */
     int shared_slot;      /* slot index of the shared expert (n_shared == 1) */
+    /* Optional host tier: the device-visible address of a page-locked host
+     * array of experts in the same slot layout (NULL: none).  A slot table
+     * entry -2 - j then reads expert j's weights from host_pool + j *
+     * host_stride over the host link (zero-copy) instead of a device slot.
+     * 256-byte aligned; host_stride >= ft_expert_layout(), a multiple of 256. */
+    const void* host_pool;
+    size_t host_stride;
 } ft_moe_weights;
 
 /* --------------------------------------------------------------------------
@@ -180,7 +191,8 @@ typedef struct {
  *   perm, offsets: ft_moe_align's outputs for the same ids;
  *   slot_of_expert [E] int32 device, or NULL for slot e = expert e: the slot
  *     in `pool` holding expert e; -1 skips expert e (its rows of y_perm are
- *     not written);
+ *     not written); -2 - j reads expert e's weights from expert j of
+ *     w->host_pool (skips it when there is no host pool);
  *   y_perm [T*k + n_shared*T][H] device, y_dt = FT_BF16 (bf16 weights/MXFP4)
  *     or FT_F32 (any weights);
  *   ws: device workspace of >= ft_moe_ffn_workspace(w, T, k) bytes.
@@ -434,18 +446,39 @@ ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
  *   logits_in: NULL, or [n_layers] device fp32 logits per layer (NULL entries
  *     compute the router GEMM from x and w_router).
  *   counts_host: pinned host [n_layers][E] int32, written (the expert lists).
- * The host waits (hipEventSynchronize) for each layer's counts; everything
- * else is asynchronous on `compute` / `copy_stream`.  Stops at the first
- * failing call and returns its status (earlier layers stay enqueued).
- * FT_WARN_OVERLAP_DISABLED from a prefetch is counted, not returned.
+ * The host waits for each layer's counts: it polls a flag that the kernel
+ * copying them sets (when counts_host has a device mapping), else
+ * hipEventSynchronize; everything else is asynchronous on `compute` /
+ * `copy_stream`.  Stops at the first failing call and returns its status
+ * (earlier layers stay enqueued).  FT_WARN_OVERLAP_DISABLED from a prefetch
+ * is counted, not returned.
  * stats (may be NULL): demand, hits, prefetch hits and misses of the maps,
- * H2D bytes enqueued, prefetch warnings. */
+ * H2D bytes enqueued, prefetch warnings.
+ *
+ * flags & FT_STACK_DEVICE_TABLE (decode; ignored with `prefill`, which runs
+ * as above): the pass does not wait for the host.  The cache keeps a device
+ * slot table [layers][E] that the FFN reads directly: an expert resident in a
+ * slot (its copy landed) is read there, any other one straight from the
+ * pinned host pool over the host link (ft_moe_weights.host_pool, table entry
+ * -2 - (l * E + e)), so the pass's kernels are enqueued back to back and give
+ * the same bits either way.  The LRU learns the pass's routing afterwards: a
+ * small kernel copies every layer's counts into a ring of pinned buffers in
+ * the cache and sets a flag, and a later call (or a flush) takes each
+ * finished pass's experts through map and release in order, which copies
+ * missed experts into slots on `copy_stream` (after the slot's last reader);
+ * the table maps them once their copies have landed.  Stats of a call count
+ * the passes it took through the LRU (up to two passes behind); a call with
+ * n_layers == 0 only flushes (waits for and counts every pending pass).
+ * Needs n_shared == 0, E <= 512, n_layers <= 64 and a device mapping of the
+ * host pool; otherwise FT_ERR_UNSUPPORTED.  counts_host is not used. */
+#define FT_STACK_DEVICE_TABLE 1
 typedef struct {
     int n_layers;
     const ft_moe_step* layers;
     const float* const* logits_in;
     int32_t* counts_host;
     int prefill;
+    int flags;  /* FT_STACK_DEVICE_TABLE or 0 */
 } ft_stack_pass;
 
 typedef struct {

@@ -83,10 +83,11 @@ def test_align_rejects_bad_arguments():
 
 def _w(**kw):
     a = dict(w_dt=ft.BF16, E=8, H=256, I=128, n_shared=0, pool=4096,
-             slot_stride=ft.slot_stride("bf16", 256, 128), shared_slot=0)
+             slot_stride=ft.slot_stride("bf16", 256, 128), shared_slot=0, host_pool=None,
+             host_stride=0)
     a.update(kw)
     return ft.MoeWeights(a["w_dt"], a["E"], a["H"], a["I"], a["n_shared"], a["pool"],
-                         a["slot_stride"], a["shared_slot"])
+                         a["slot_stride"], a["shared_slot"], a["host_pool"], a["host_stride"])
 
 
 def test_ffn_rejects_bad_arguments():
@@ -239,8 +240,30 @@ def test_struct_layouts_match_the_header(tmp_path):
     assert [l for l in got if l] == want
 
 
+def test_ffn_rejects_a_bad_host_pool():
+    """The host tier of ft_moe_weights is checked before any device work:
+    256-byte aligned, stride a multiple of 256 covering one expert."""
+    lib = ft.load()
+    p = C.c_void_p(4096)
+    st = ft.slot_stride("bf16", 256, 128)
+
+    def call(w):
+        return lib.ft_moe_ffn(C.byref(w), p, ft.BF16, 4, 2, p, p, None, p, ft.BF16, p, 1 << 30, None)
+
+    assert call(_w(host_pool=4096 + 64, host_stride=st)) == ft.ERR_INVALID_ARG   # misaligned
+    assert call(_w(host_pool=8192, host_stride=st + 16)) == ft.ERR_INVALID_ARG   # stride % 256
+    assert call(_w(host_pool=8192, host_stride=256)) == ft.ERR_INVALID_ARG       # below one expert
+    assert "host_pool" in ft.last_error()
+    assert lib.ft_host_device_pointer(None, C.byref(C.c_void_p())) == ft.ERR_INVALID_ARG
+    assert lib.ft_host_device_pointer(p, None) == ft.ERR_INVALID_ARG
+
+
 def test_stack_forward_rejects_bad_arguments():
     lib = ft.load()
+    # unknown flags are refused before the cache is looked at
+    bad = ft.StackPass(0, None, None, None, 0, 2)
+    assert lib.ft_slot_stack_forward(C.c_void_p(4096), C.byref(bad), None, None, None) == ft.ERR_INVALID_ARG
+    assert "flags" in ft.last_error()
     p = ft.StackPass(0, None, None, None, 0)
     assert lib.ft_slot_stack_forward(None, C.byref(p), None, None, None) == ft.ERR_INVALID_ARG
     assert lib.ft_slot_stack_forward(C.c_void_p(4096), None, None, None, None) == ft.ERR_INVALID_ARG

@@ -260,3 +260,107 @@ def test_calibrate_measures_both_bandwidths():
         assert bp > 0.1 and bh > 0.01, (bp, bh)
     finally:
         st.close()
+
+
+# ---------------------------------------------------------------------------
+# device-table decode passes (FT_STACK_DEVICE_TABLE)
+
+@pytest.mark.parametrize("n_slots", [12, 40])
+def test_device_table_decode_matches_resident(n_slots):
+    """Passes enqueued without host waits: experts in slots are read there,
+    the others from the pinned pool; every layer bitwise equal to the
+    all-resident layer, and after a flush the LRU has counted every pass."""
+    _say("device-table decode, slots", n_slots)
+    L = 4
+    st = SlotStack(SMALL, L, n_slots=n_slots)
+    try:
+        for step in range(10):
+            xs = _inputs(SMALL, L, 2, 500 + step)
+            outs = st.forward(xs, device_table=True)
+            for l in range(L):
+                ref, _, _ = _resident_layer(st, l, xs[l])
+                assert torch.equal(outs[l], ref), (n_slots, step, l)
+        st.flush()
+        s = st.stats
+        assert s.demand > 0 and s.misses > 0
+        # 12 slots are fewer than one pass's distinct experts (about 20 over
+        # the 4 layers), so the LRU thrashes; 40 hold them
+        if n_slots >= 40:
+            assert s.hits > 0
+        assert s.hits + s.prefetch_hits + s.misses == s.demand
+        cs = st.cache.stats()
+        assert cs.held == 0 and 0 < cs.resident <= n_slots
+        # after the flush every copy it issued lands, and the slots hold their experts
+        assert _slots_hold_their_experts(st) == cs.resident
+    finally:
+        st.close()
+
+
+def test_device_table_decode_between_other_modes():
+    """Device-table passes, a prefill through the per-layer path (which first
+    settles the pending passes), per-layer decode, a resize, and device-table
+    passes again: every layer of every pass bitwise equal to the resident one."""
+    _say("device-table decode between other modes")
+    L = 3
+    st = SlotStack(SMALL, L, n_slots=2 * SMALL.E)
+    try:
+        def check(outs, xs, what):
+            for l in range(L):
+                ref, _, _ = _resident_layer(st, l, xs[l])
+                assert torch.equal(outs[l], ref), (what, l)
+
+        for step in range(3):
+            xs = _inputs(SMALL, L, 1, 600 + step)
+            check(st.forward(xs, device_table=True), xs, f"dt {step}")
+        xs = _inputs(SMALL, L, 300, 610)
+        check(st.forward(xs, prefill=True, device_table=True), xs, "prefill")
+        assert st.stats.prefetch_warnings == 0
+        for step in range(2):
+            xs = _inputs(SMALL, L, 2, 620 + step)
+            check(st.forward(xs), xs, f"per-layer {step}")
+        st.resize(20, new_array=True)
+        for step in range(4):
+            xs = _inputs(SMALL, L, 3, 630 + step)
+            check(st.forward(xs, device_table=True), xs, f"dt after resize {step}")
+        st.flush()
+        s = st.stats
+        assert s.hits + s.prefetch_hits + s.misses == s.demand
+        cs = st.cache.stats()
+        assert cs.held == 0 and cs.resident <= 20
+        assert _slots_hold_their_experts(st) == cs.resident
+    finally:
+        st.close()
+
+
+def test_full_size_device_table_decode_matches_oracle():
+    """8 layers of the 35B-A3B layer shape, 512 slots under one global LRU,
+    Zipf(1.1)-biased routers: device-table decode steps, each layer compared
+    with the resident computation, the last two with the oracle."""
+    sh = synth.SLOT_STACK
+    L = synth.SLOT_STACK_LAYERS
+    _say("full-size device-table decode")
+    st = SlotStack(sh, L, n_slots=L * synth.SLOT_STACK_SLOTS_PER_LAYER)
+    try:
+        for step in range(6):
+            xs = _inputs(sh, L, 1, 700 + step)
+            outs = st.forward(xs, device_table=True)
+            for l in range(L):
+                ref, _, _ = _resident_layer(st, l, xs[l])
+                assert torch.equal(outs[l], ref), (step, l)
+        experts = [[unpack_slot(st.host[l, e], sh) for e in range(sh.E)] for l in range(L)]
+        for step in (710, 711):
+            xs = _inputs(sh, L, 1, step)
+            lgs = [orc.router_logits(xs[l].cpu(), st.routers[l].cpu()) for l in range(L)]
+            outs = st.forward(xs, logits=[torch.from_numpy(a).to(DEV) for a in lgs],
+                              device_table=True)
+            for l in range(L):
+                ids, w = orc.route(lgs[l], sh.k, st.biases[l].cpu().numpy())
+                ref = orc.moe_layer(xs[l].cpu(), ids, w, experts[l], "bf16", sh.I, out_fmt="f32")
+                check_close(outs[l], ref, "bf16", f"device-table step {step} layer {l}")
+        st.flush()
+        s = st.stats
+        _say("  demand", s.demand, "hits", s.hits, "misses", s.misses)
+        assert s.hits + s.prefetch_hits + s.misses == s.demand and s.misses > 0
+        assert st.cache.stats().held == 0
+    finally:
+        st.close()
