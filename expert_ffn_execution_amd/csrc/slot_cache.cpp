@@ -273,7 +273,18 @@ ft_status dt_account_one(ft_slot_cache* c, HipEngine& eng, bool block, bool* don
             if (cnt[(size_t)l * E + e] > 0) need.push_back(e);
         ft_map_stats ms{};
         ft_status r = c->policy.map(eng, l, need.data(), (int)need.size(), slots.data(), &ms);
-        if (r == FT_OK) r = c->policy.release(eng, l);
+        if (r == FT_ERR_CAPACITY) {
+            // more distinct experts than the layer's slots can take (the map
+            // checks this before changing anything): the pass already read
+            // them from the host pool; count the non-resident ones as misses
+            ms = ft_map_stats{};
+            ms.n_demand = (int)need.size();
+            for (int32_t e : need)
+                if (c->policy.lookup(l, e) >= 0) ++ms.n_hit; else ++ms.n_miss;
+            r = FT_OK;
+        } else if (r == FT_OK) {
+            r = c->policy.release(eng, l);
+        }
         if (r != FT_OK) return hip_status(eng, r);
         acc->demand += ms.n_demand;
         acc->hits += ms.n_hit;

@@ -364,3 +364,25 @@ def test_full_size_device_table_decode_matches_oracle():
         assert st.cache.stats().held == 0
     finally:
         st.close()
+
+
+def test_device_table_decode_beyond_layer_capacity():
+    """Per-layer scope with 3 slots per layer and up to 16 distinct experts per
+    layer: the LRU cannot take a layer's experts (the bookkeeping counts them
+    and moves on), and every pass still matches the resident layers."""
+    _say("device-table decode beyond a layer's slots")
+    L = 2
+    st = SlotStack(SMALL, L, n_slots=3 * L, scope=ft.SCOPE_PER_LAYER)
+    try:
+        for step in range(4):
+            xs = _inputs(SMALL, L, 4, 800 + step)
+            outs = st.forward(xs, device_table=True)
+            for l in range(L):
+                ref, _, _ = _resident_layer(st, l, xs[l])
+                assert torch.equal(outs[l], ref), (step, l)
+        st.flush()
+        s = st.stats
+        assert s.demand > 0 and s.hits + s.prefetch_hits + s.misses == s.demand
+        assert st.cache.stats().held == 0
+    finally:
+        st.close()
