@@ -574,6 +574,21 @@ ft_status dt_forward(ft_slot_cache* c, const ft_stack_pass* p, hipStream_t cs, h
         r = dt_account_one(c, eng, true, &done, &acc);
         if (r != FT_OK) return r;
     }
+    // one read point after the pass's kernels (also after a partly enqueued
+    // pass that failed) for every slot the table maps: a copy into such a
+    // slot waits for it
+    auto mark_reads = [&]() -> ft_status {
+        const int ev = c->rpos;
+        c->rpos = (c->rpos + 1) % (int)c->rpool.size();
+        FT_HIP(hipEventRecord(c->rpool[ev], cs));
+        ++c->rgen[ev];
+        for (int32_t v : c->htab)
+            if (v >= 0) {
+                c->read_ev[v] = ev;
+                c->read_gen[v] = c->rgen[ev];
+            }
+        return FT_OK;
+    };
     if (L > 0) {
         r = dt_sync(c, cs);
         if (r != FT_OK) return r;
@@ -599,24 +614,18 @@ ft_status dt_forward(ft_slot_cache* c, const ft_stack_pass* p, hipStream_t cs, h
             if (r == FT_OK)
                 r = ft_moe_combine(st.y_perm, st.y_dt, st.inv_perm, st.topk_w, st.T, st.k, w.H, 0,
                                    st.out, st.out_dt, cs);
-            if (r != FT_OK) return r;
+            if (r != FT_OK) {
+                (void)mark_reads();
+                return r;
+            }
             cnts[l] = st.counts;
         }
         const int ring = (int)(c->dt_enq % ft_slot_cache::DT_RING);
-        r = ft::launch_copy_counts_flag(cnts, L, E, c->dt_counts_dev + (size_t)ring * c->d.n_layers * E, c->dt_flags_dev + ring,
-                                        (int32_t)(c->dt_enq + 1), cs);
+        r = ft::launch_copy_counts_flag(cnts, L, E, c->dt_counts_dev + (size_t)ring * c->d.n_layers * E,
+                                        c->dt_flags_dev + ring, (int32_t)(c->dt_enq + 1), cs);
+        const ft_status rm = mark_reads();
         if (r != FT_OK) return r;
-        // one read point, after the pass, for every slot the table maps: a
-        // copy into such a slot waits for it
-        const int ev = c->rpos;
-        c->rpos = (c->rpos + 1) % (int)c->rpool.size();
-        FT_HIP(hipEventRecord(c->rpool[ev], cs));
-        ++c->rgen[ev];
-        for (int32_t v : c->htab)
-            if (v >= 0) {
-                c->read_ev[v] = ev;
-                c->read_gen[v] = c->rgen[ev];
-            }
+        if (rm != FT_OK) return rm;
         c->dt_layers[ring] = L;
         ++c->dt_enq;
     }
