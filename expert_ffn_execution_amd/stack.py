@@ -28,7 +28,7 @@ Device-table decode (``device_table=True``): the pass runs without the host
 waiting for any layer's histogram.  The library keeps a device slot table that
 sends each expert either to its slot (once its copy has landed) or to the
 pinned pool, read over the host link; the histograms come back in one copy
-after the pass and the LRU takes them up to two passes later (``flush()``
+after the pass and the LRU takes them one or two passes later (``flush()``
 settles the rest), copying missed experts into slots for the passes after.
 
 Each layer's device buffers (logits, routing, alignment, workspaces, y_perm,
@@ -331,7 +331,7 @@ class SlotStack:
         misses between PCIe copies and host cores (decode; needs calibrate()).
         `device_table` runs a decode pass without host waits: experts not in
         a slot are read from the pinned pool over the host link, and the LRU
-        takes the pass's routing up to two passes later (flush() settles it).
+        takes the pass's routing one or two passes later (flush() settles it).
         Returns the per-layer outputs."""
         sh = self.sh
         if hybrid and sh.wdtype != "bf16":

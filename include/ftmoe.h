@@ -467,7 +467,8 @@ ft_status ft_slot_cache_stats(const ft_slot_cache* c, ft_cache_stats* out);
  * finished pass's experts through map and release in order, which copies
  * missed experts into slots on `copy_stream` (after the slot's last reader);
  * the table maps them once their copies have landed.  Stats of a call count
- * the passes it took through the LRU (up to two passes behind); a call with
+ * the passes it took through the LRU (the host runs at most one pass ahead of
+ * that, FTMOE_DT_LAG = 0..3 in the environment changes it); a call with
  * n_layers == 0 only flushes (waits for and counts every pending pass).
  * Needs n_shared == 0, E <= 512, n_layers <= 64 and a device mapping of the
  * host pool; otherwise FT_ERR_UNSUPPORTED.  counts_host is not used. */
