@@ -414,16 +414,25 @@ def cpu_baseline(sh, bank, T, dev, seconds):
 
 
 def cpu_model():
-    """The host CPU's model name (from /proc/cpuinfo)."""
+    """The host CPU's model name, with its family / model numbers (from
+    /proc/cpuinfo; a virtual machine may report only the brand)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                k, _, v = line.partition(":")
+                info.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    import platform
-    return platform.processor() or "unknown"
+    name = info.get("model name")
+    if not name:
+        import platform
+        return platform.processor() or "unknown"
+    if "cpu family" in info and "model" in info:
+        name += f" (family {info['cpu family']}, model {info['model']})"
+    return name
 
 
 def h2d_peak_gbs(dev, nbytes=1 << 30):
