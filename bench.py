@@ -154,6 +154,48 @@ def run_mfma_rate():
     return r.returncode
 
 
+# A helper process started before this one touches the GPU runs amd-smi when
+# asked and answers with the GFX (per-XCD) clocks in MHz: a process that has
+# initialised the GPU starts no other program itself.
+_CLOCK_HELPER = r"""
+import json, re, subprocess, sys
+for line in sys.stdin:
+    if line.strip() != "go":
+        break
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock"], capture_output=True, text=True, timeout=30)
+        mhz = [int(v) for v in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+    except Exception:
+        mhz = []
+    print(json.dumps(mhz), flush=True)
+"""
+
+
+class ClockSampler:
+    """GPU clocks read by amd-smi on request (see _CLOCK_HELPER)."""
+
+    def __init__(self):
+        import subprocess
+        self.p = subprocess.Popen([sys.executable, "-c", _CLOCK_HELPER], stdin=subprocess.PIPE,
+                                  stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+
+    def sample(self):
+        try:
+            self.p.stdin.write("go\n")
+            self.p.stdin.flush()
+            return json.loads(self.p.stdout.readline() or "[]")
+        except (OSError, ValueError):
+            return []
+
+    def close(self):
+        try:
+            self.p.stdin.write("quit\n")
+            self.p.stdin.flush()
+            self.p.wait(timeout=10)
+        except Exception:
+            self.p.kill()
+
+
 def rocpd_rows(db, query, params=()):
     """Rows of a query on a rocprofv3 rocpd database (its SQLite output)."""
     import sqlite3
@@ -244,8 +286,10 @@ class Bank:
         self.expert_bytes = ft.expert_layout(sh.wdtype, sh.H, sh.I)[0]
 
 
-def run_point(sh, banks, T, steps, warmup, dev, prefill):
-    """Time `steps` full steps at T tokens; returns a dict of measurements."""
+def run_point(sh, banks, T, steps, warmup, dev, prefill, clock=None):
+    """Time `steps` full steps at T tokens; returns a dict of measurements.
+    With a ClockSampler, the GPU clocks are then sampled while about three
+    seconds of the same steps run (untimed)."""
     import torch
     from expert_ffn_execution_amd import ftmoe as ft
     from expert_ffn_execution_amd import synth
@@ -292,6 +336,18 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     for which in prof:
         ft.set_profile_events(which, None, None)
     ms = t0.elapsed_time(t1) / steps
+    clock_mhz = None
+    if clock is not None:
+        # enqueue ~3 s of steps, then ask for the clocks while they run
+        import threading
+        got = []
+        for i in range(max(1, int(3000 / ms))):
+            step(warmup + steps + i)
+        th = threading.Thread(target=lambda: got.append(clock.sample()))
+        th.start()
+        th.join(timeout=60)
+        torch.cuda.synchronize()
+        clock_mhz = got[0] if got else []
     # the two expert kernels carry their events on their own dispatch: these are
     # kernel durations; the FFN's time is their sum (its tile-list kernel aside)
     dur = {which: sum(hev.elapsed_ms(a, b) for a, b in lst) / steps
@@ -320,7 +376,7 @@ def run_point(sh, banks, T, steps, warmup, dev, prefill):
     fl1 = 2.0 * rows * 2 * sh.I * sh.H
     fl2 = 2.0 * rows * sh.I * sh.H
     res = {
-        "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3),
+        "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "gpu_clock_mhz": clock_mhz,
         "ffn_ms": dur[ft.PROF_FFN], "gemm1_ms": dur[ft.PROF_GEMM1], "gemm2_ms": dur[ft.PROF_GEMM2],
         "active_experts": n_act, "weight_bytes": ffn_bytes,
         "ffn_gbs": ffn_bytes / (dur[ft.PROF_FFN] * 1e-3) / 1e9,
@@ -656,7 +712,7 @@ def decode_entry(sh, r, g_ms, T):
     """One decode point: graph-replayed step rate, and the FFN's weight
     streaming rated as active-expert bytes (gate/up + down of every distinct
     routed expert, plus the shared one) over the sum of the gate/up and down
-    kernel durations."""
+    kernel durations (and, second, over the whole replayed step)."""
     ffn_s = r["ffn_ms"] * 1e-3
     narrow = sh.wdtype in ("mxfp4", "fp8", "nvfp4") and T >= 2
     return {
@@ -665,6 +721,7 @@ def decode_entry(sh, r, g_ms, T):
         "ffn_us": r["ffn_ms"] * 1e3, "gate_up_us": r["gemm1_ms"] * 1e3,
         "down_us": r["gemm2_ms"] * 1e3, "active_experts": r["active_experts"],
         "gate_up_gbs": r["gemm1_gbs"], "down_gbs": r["gemm2_gbs"],
+        "step_gbs": r["weight_bytes"] / (g_ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": r["weight_bytes"] / ffn_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["weight_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
@@ -673,7 +730,7 @@ def decode_entry(sh, r, g_ms, T):
                      "bytes_per_step": r["weight_bytes"]}}
 
 
-def run_workload(name, args, dev, with_cpu):
+def run_workload(name, args, dev, with_cpu, clock=None):
     """Prefill point, decode points and (optionally) the CPU oracle of one
     workload; its weight banks are freed before returning."""
     import torch
@@ -691,7 +748,7 @@ def run_workload(name, args, dev, with_cpu):
     banks = [Bank(sh, l, dev) for l in range(n_banks)]
     torch.cuda.synchronize()
 
-    head = run_point(sh, banks, T_pre, args.steps, args.warmup, dev, prefill=True)
+    head = run_point(sh, banks, T_pre, args.steps, args.warmup, dev, prefill=True, clock=clock)
     log("prefill", sh.name, json.dumps(head))
     decode = []
     for T in dec:
@@ -741,6 +798,12 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
+    # started before anything here touches the GPU; not under a profiler (its
+    # preloaded library initialises the GPU in every process it starts) and
+    # not in the single-workload runs the profiles use
+    under_profiler = any(k.startswith("ROCPROF") for k in os.environ)
+    clock = (ClockSampler() if args.workload == DEFAULT_WORKLOAD and not args.no_extras
+             and not under_profiler else None)
     ft.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -752,7 +815,9 @@ def main():
     if args.workload == synth.SLOT_STACK.name:
         print(json.dumps(run_slot_stack(args)), flush=True)
         return
-    w = run_workload(args.workload, args, dev, with_cpu=not args.no_cpu_baseline)
+    w = run_workload(args.workload, args, dev, with_cpu=not args.no_cpu_baseline, clock=clock)
+    if clock is not None:
+        clock.close()
     sh, head = w["sh"], w["head"]
     others = {}
     if not args.no_extras and args.workload == DEFAULT_WORKLOAD and not args.tokens and not args.decode:
@@ -772,6 +837,9 @@ def main():
                    "activations": "bf16", "router_bias": sh.bias if sh.bias == "none" else
                    f"{sh.bias}({sh.bias_param})", "weight_banks": w["n_banks"]},
         "roofline": w["roofline"],
+        # per-XCD GFX clocks that amd-smi read while the same prefill steps ran
+        # right after the timed ones (the peaks above assume 2.4 GHz)
+        "gpu_clock_mhz": head["gpu_clock_mhz"],
         "prefill_detail": {"gemm1_us": head["gemm1_ms"] * 1e3, "gemm2_us": head["gemm2_ms"] * 1e3,
                            "gemm1_tflops": head["gemm1_tflops"], "gemm2_tflops": head["gemm2_tflops"],
                            "ffn_tflops": head["ffn_tflops"],
