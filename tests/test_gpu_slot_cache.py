@@ -386,3 +386,53 @@ def test_device_table_decode_beyond_layer_capacity():
         assert st.cache.stats().held == 0
     finally:
         st.close()
+
+
+def test_mixed_operations_random_walk():
+    """A seeded random walk over the cache's operations: device-table and
+    per-layer decode passes, prefills, explicit evictions of one expert or a
+    whole layer, and resizes (in place and into a new array).  After every
+    pass each layer equals the resident layer bitwise; at the end the LRU's
+    counts add up and every resident slot holds its expert.  The per-layer
+    passes map a layer's experts before it runs, so they run only where the
+    slots can take them (a prefill routes to all 32 experts, T = 4 decode to
+    up to 16); device-table passes run at any budget."""
+    _say("slot cache random walk")
+    L = 3
+    n_slots = 24
+    st = SlotStack(SMALL, L, n_slots=n_slots)
+    rng = np.random.default_rng(2034)  # a walk that visits every kind of operation
+    try:
+        step = 0
+        for it in range(32):
+            op = rng.choice(["dt", "dt", "dt", "layer", "prefill", "evict", "resize"])
+            if op == "prefill" and n_slots < SMALL.E:
+                op = "dt"
+            if op in ("dt", "layer", "prefill"):
+                T = 300 if op == "prefill" else int(rng.integers(1, 5))
+                if op == "layer":
+                    T = min(T, n_slots // SMALL.k)
+                xs = _inputs(SMALL, L, T, 900 + step)
+                step += 1
+                outs = st.forward(xs, prefill=op == "prefill", device_table=op != "layer")
+                for l in range(L):
+                    ref, _, _ = _resident_layer(st, l, xs[l])
+                    assert torch.equal(outs[l], ref), (it, op, l)
+            elif op == "evict":
+                st.flush()  # nothing of this cache may be held or in flight for an eviction
+                torch.cuda.synchronize()
+                st.copy_stream.synchronize()
+                l = int(rng.integers(0, L))
+                st.cache.evict(l, int(rng.integers(-1, SMALL.E)))
+            else:
+                st.flush()
+                n_slots = int(rng.choice([8, 20, 2 * SMALL.E]))
+                st.resize(n_slots, new_array=bool(rng.integers(0, 2)))
+        st.flush()
+        s = st.stats
+        assert s.demand > 0 and s.hits + s.prefetch_hits + s.misses == s.demand
+        cs = st.cache.stats()
+        assert cs.held == 0
+        assert _slots_hold_their_experts(st) == cs.resident
+    finally:
+        st.close()
