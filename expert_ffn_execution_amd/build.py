@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libftmoe.so")
 # stand-alone matrix-core issue-rate probe (not part of the library)
 PROBE_SRC = "mfma_rate.hip"
 PROBE = os.path.join(PKG, "mfma_rate")
-SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip",
+SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip", "router_mfma.hip",
            "ffn_stream.hip", "combine.hip", "step.cpp", "host_ffn.cpp", "noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

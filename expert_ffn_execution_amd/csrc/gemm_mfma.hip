@@ -1,5 +1,5 @@
 // gemm_mfma.hip -- MFMA kernels for many tokens (gfx950): the grouped expert
-// GEMMs and the router logits.
+// GEMMs.
 //
 // The expert FFN over many tokens is a set of dense contractions, one per
 // expert, over the rows routed to it (claypier.com article,
@@ -15,10 +15,8 @@
 // writes h = silu(g) * u in bf16.  GEMM2 multiplies h by the down projection.
 // Narrow weights (MXFP4, FP8, NVFP4) stay packed in LDS and are decoded
 // exactly to bf16 when a fragment is read.
-//
-// router_pipe_kernel computes the router logits of many tokens (x . W_r^T,
-// fp32) with the same kind of copy ring.
 #include "gemm_mfma.h"
+#include "lds_ring.h"
 
 #include <type_traits>
 
@@ -26,9 +24,6 @@ namespace {
 
 using ft::TileDesc;
 
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 // v_mfma_f32_32x32x16_bf16 sustains about twice the rate of the 16x16x32 form
 // on gfx950 (measured), so the expert GEMMs use it
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -139,25 +134,8 @@ static_assert(steady_in_flight<0, LA>() == 8 && steady_in_flight<1, LA>() == 12 
               "issue order");
 }  // namespace pipe
 
-#define FT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-// the same with a run-time count (capped at N)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm_upto(int n) {
-    if constexpr (N <= 0) {
-        wait_vm_lgkm<0>();
-    } else {
-        if (n >= N) wait_vm_lgkm<N>();
-        else wait_vm_lgkm_upto<N - 1>(n);
-    }
-}
+using ft::wait_vm_lgkm;
+using ft::wait_vm_lgkm_upto;
 
 // 8 e4m3 codes (bytes of w0, then w1) -> 8 bf16, exact
 __device__ __forceinline__ bf16x8_t fp8_frag(uint32_t w0, uint32_t w1) {
@@ -671,104 +649,6 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (e == 0) *n_tiles = min(total + ns, max_tiles);
 }
 
-// ---------------------------------------------------------------------------
-// Router logits for many tokens: out[m][e] = sum_k x[m][k] W_r[e][k], fp32
-// accumulation of bf16 products.  The contraction has few columns (E), so
-// there are few output tiles, and a tile loop that loads one K slice ahead
-// waits one memory round trip per slice (the plain tile kernel took 26 us for
-// 4096 tokens x 128 experts x 2048).  Here a block takes 32 rows x 64 experts
-// and walks K in stages of 64 through an LDS ring of RD stages, filled by
-// direct global->LDS copies issued RD - 1 stages ahead (three 1 KB copies per
-// wave and stage), so that many round trips are in flight at once; two blocks
-// share a CU.  Wave w computes rows 16 (w & 1) .. + 15 and experts
-// 32 (w >> 1) .. + 31 with v_mfma_f32_16x16x32_bf16.  Rows past M and
-// experts past N re-read the last row and are not stored.
-// LDS stage: A rows 0..31 then B rows 0..63, 128 bytes each, chunk c of row r
-// at position c ^ ((r >> 1) & 7).
-namespace rpipe {
-constexpr int BM = 32, BN = 64, KS = 64, RD = 6, NT = 256;
-constexpr int A_BYTES = BM * KS * 2, STAGE = (BM + BN) * KS * 2;
-constexpr int CPW = STAGE / 1024 / (NT / 64);  // copies per wave and stage
-static_assert(CPW == 3, "one A copy and two B copies per wave");
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-}  // namespace rpipe
-
-__global__ __launch_bounds__(rpipe::NT, 2) void router_pipe_kernel(
-    const __bf16* __restrict__ x, const __bf16* __restrict__ wr, int M, int N, int K,
-    float* __restrict__ out, int n_ntiles) {
-    using namespace rpipe;
-    __shared__ __attribute__((aligned(16))) unsigned char ring[RD * STAGE];
-    const int m0 = (blockIdx.x / n_ntiles) * BM, n0 = (blockIdx.x % n_ntiles) * BN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const size_t rowb = (size_t)K * 2;
-    // this lane's copy sources: LDS position lane % 8 of row lane / 8 of the
-    // wave's 1 KB piece takes the global chunk (lane % 8) ^ swz(row)
-    const int ra = 8 * wave + (lane >> 3);
-    const unsigned char* asrc = reinterpret_cast<const unsigned char*>(x) +
-                                (size_t)min(m0 + ra, M - 1) * rowb + ((lane & 7) ^ swz(ra)) * 16;
-    const unsigned char* bsrc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int rb = 16 * wave + 8 * i + (lane >> 3);
-        bsrc[i] = reinterpret_cast<const unsigned char*>(wr) + (size_t)min(n0 + rb, N - 1) * rowb +
-                  ((lane & 7) ^ swz(rb)) * 16;
-    }
-    const int nst = K / KS;
-    // blocks start at different K stages (and wrap around), so that the rows
-    // they read at one moment sit at different offsets
-    const int rot = (int)(blockIdx.x % (unsigned)nst);
-    auto issue = [&](int st) __attribute__((always_inline)) {
-        unsigned char* dst = ring + (st % RD) * STAGE;
-        const int kst = st + rot < nst ? st + rot : st + rot - nst;
-        __builtin_amdgcn_global_load_lds(asrc + (size_t)kst * KS * 2, FT_LDS(dst + wave * 1024), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_global_load_lds(bsrc[i] + (size_t)kst * KS * 2,
-                                             FT_LDS(dst + A_BYTES + (2 * wave + i) * 1024), 16, 0, 0);
-    };
-    for (int st = 0; st < RD - 1 && st < nst; ++st) issue(st);
-    const int wm = wave & 1, wn = wave >> 1;
-    const int ar = 16 * wm + (lane & 15);
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    for (int st = 0; st < nst; ++st) {
-        // stages st+1 .. min(st + RD - 2, nst - 1) may still be in flight; st must
-        // have landed (copies complete in issue order, and this wave's LDS
-        // reads of st - 1 are done), then every wave's has.  A plain barrier:
-        // __syncthreads() would also wait for the copies in flight (its fence
-        // covers them), which emptied the ring at every stage (17 vs 11.7 us
-        // for 4096 x 128 x 2048 in isolation)
-        wait_vm_lgkm_upto<CPW * (RD - 2)>(CPW * (min(st + RD - 2, nst - 1) - st));
-        __builtin_amdgcn_s_barrier();
-        // the slot of stage st - 1, which every wave has finished reading
-        if (st + RD - 1 < nst) issue(st + RD - 1);
-        const unsigned char* sb = ring + (st % RD) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int c = 4 * ks + (lane >> 4);
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sb + ar * 128 + ((c ^ swz(ar)) * 16));
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int br = 32 * wn + 16 * n + (lane & 15);
-                const bf16x8_t b =
-                    *reinterpret_cast<const bf16x8_t*>(sb + A_BYTES + br * 128 + ((c ^ swz(br)) * 16));
-                acc[n] = mfma16(a, b, acc[n]);
-            }
-        }
-    }
-    // lane holds column lane & 15 and rows 4 (lane >> 4) + j of each 16 x 16 tile
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int col = n0 + 32 * wn + 16 * n + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = m0 + 16 * wm + 4 * (lane >> 4) + j;
-            if (row < M && col < N) out[(size_t)row * N + col] = acc[n][j];
-        }
-    }
-}
-
-#undef FT_LDS
-
 }  // namespace
 
 namespace ft {
@@ -826,16 +706,6 @@ ft_status launch_gemm2_mfma(const FfnGeom& g, const __bf16* h, const TileDesc* t
         e = y_dt == FT_F32 ? launch_pipe<MODE_LIST, 0, float>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (float*)y)
                            : launch_pipe<MODE_LIST, 0, __bf16>(grid, s, g, h, nullptr, tiles, n_tiles, nn, (__bf16*)y);
     if (e != hipSuccess) return set_error(FT_ERR_HIP, "gemm2: %s", hipGetErrorString(e));
-    return FT_OK;
-}
-
-ft_status launch_dense_gemm_f32out(const void* A, const void* B, int M, int N, int K,
-                                   float* out, hipStream_t s) {
-    if (K % rpipe::KS != 0) return set_error(FT_ERR_INVALID_ARG, "router GEMM: K must be a multiple of 64");
-    const int n_ntiles = cdiv(N, rpipe::BN);
-    router_pipe_kernel<<<(unsigned)(cdiv(M, rpipe::BM) * n_ntiles), rpipe::NT, 0, s>>>(
-        (const __bf16*)A, (const __bf16*)B, M, N, K, out, n_ntiles);
-    FT_LAUNCHED("router logits");
     return FT_OK;
 }
 

@@ -109,11 +109,14 @@ def test_router_logits_batch_dependence():
 
 
 @pytest.mark.parametrize("H,E,T", [(64, 1000, 130), (128, 8, 65), (192, 100, 333),
-                                   (1024, 64, 97)])
+                                   (1024, 64, 97), (64, 1000, 2000), (192, 300, 8200),
+                                   (128, 256, 8192)])
 def test_router_logits_edge_shapes(H, E, T):
     """The router's MFMA tiles (T > 64) at edge shapes: one or few K stages
     (fewer than the copy ring holds), expert counts below or not a multiple of
-    the 64-expert tile, ragged row tails."""
+    the 64- or 128-expert tile, ragged row tails.  The last three take the
+    64 x 128 tiles (at least 256 of them): 256 and 256 blocks (a grid that is a
+    multiple of 8, whose blocks are reordered per XCD) and 387 (one that is not)."""
     _say("router logits edge", H, E, T)
     sh = synth.LayerShape(f"router_edge_{H}_{E}", H=H, E=E, k=min(4, E), I=64)
     x = synth.gen_x(sh, T)
