@@ -708,7 +708,48 @@ def run_graph_point(sh, banks, T, steps, warmup, dev):
     return ms
 
 
-def decode_entry(sh, r, g_ms, T):
+def run_fused_point(sh, banks, T, steps, warmup, dev):
+    """The same decode step as one fused kernel (ft_moe_step_fused), called
+    eagerly and replayed as one-node graphs, rotating over the weight banks
+    like the other decode timings; None where the fused step does not take the
+    shape (it returns FT_ERR_UNSUPPORTED)."""
+    import torch
+    from expert_ffn_execution_amd import ftmoe as ft
+    from expert_ffn_execution_amd import synth
+
+    steps_ = []
+    for i, b in enumerate(banks):
+        x = synth.gen_x(sh, T, step=i, device=dev).contiguous()
+        steps_.append(ft.LayerStep(b.wts, x, sh.k, b.wr, bias=b.bias))
+    try:
+        steps_[0].run_fused()
+    except ft.FtError as e:
+        if e.status == ft.ERR_UNSUPPORTED:
+            return None
+        raise
+    out = {}
+    graphs = [st.capture_fused() for st in steps_]
+    try:
+        for label, calls in (("fused_ms_per_step", [st.run_fused for st in steps_]),
+                             ("fused_graph_ms_per_step", [g.launch for g in graphs])):
+            for i in range(warmup):
+                calls[i % len(calls)]()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(steps):
+                calls[(warmup + i) % len(calls)]()
+            t1.record()
+            torch.cuda.synchronize()
+            out[label] = t0.elapsed_time(t1) / steps
+    finally:
+        for g in graphs:
+            g.close()
+    out["fused_timeouts"] = ft.fused_timeouts()
+    return out
+
+
+def decode_entry(sh, r, g_ms, T, fused=None):
     """One decode point: graph-replayed step rate, and the FFN's weight
     streaming rated as active-expert bytes (gate/up + down of every distinct
     routed expert, plus the shared one) over the sum of the gate/up and down
@@ -727,7 +768,8 @@ def decode_entry(sh, r, g_ms, T):
                      "frac": r["weight_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "kernel": ("gate/up + down weight streaming on matrix cores (stream_mx_kernel)"
                                 if narrow else "gate/up + down weight streaming (stream_kernel)"),
-                     "bytes_per_step": r["weight_bytes"]}}
+                     "bytes_per_step": r["weight_bytes"]},
+        **({"fused": fused} if fused else {})}
 
 
 def run_workload(name, args, dev, with_cpu, clock=None):
@@ -754,7 +796,8 @@ def run_workload(name, args, dev, with_cpu, clock=None):
     for T in dec:
         r = run_point(sh, banks, T, max(args.steps, 50), args.warmup, dev, prefill=False)
         g_ms = run_graph_point(sh, banks, T, max(args.steps, 50), args.warmup, dev)
-        decode.append(decode_entry(sh, r, g_ms, T))
+        fused = run_fused_point(sh, banks, T, max(args.steps, 50), args.warmup, dev)
+        decode.append(decode_entry(sh, r, g_ms, T, fused))
         log("decode", sh.name, json.dumps(decode[-1]))
     cpu = None
     if with_cpu:

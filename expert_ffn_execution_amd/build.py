@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libftmoe.so")
 PROBE_SRC = "mfma_rate.hip"
 PROBE = os.path.join(PKG, "mfma_rate")
 SOURCES = ["api.cpp", "slot_cache.cpp", "route.hip", "align.hip", "gemm_mfma.hip", "router_mfma.hip",
-           "ffn_stream.hip", "combine.hip", "step.cpp", "host_ffn.cpp", "noalloc.hip"]
+           "ffn_stream.hip", "combine.hip", "step.cpp", "host_ffn.cpp", "noalloc.hip", "fused_decode.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -29,6 +29,8 @@ ft_status launch_scatter_rows(const float*, const int64_t*, int, int, void*, ft_
 bool topk_align_small_ok(int T, int k);
 ft_status launch_topk_align_small(const float*, const float*, int, int, int, int32_t*, float*,
                                   int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t);
+bool fused_shape_ok(int T, int k, int E, int H, int I, int n_shared);
+ft_status launch_fused_decode(const ft_moe_step* st, const size_t offs[3], hipStream_t s);
 
 static thread_local char g_err[512] = "";
 
@@ -395,6 +397,32 @@ ft_status route_align(const ft_moe_step* st, hipStream_t s) {
                                     st->counts, st->offsets, st->perm, st->inv_perm, s);
     prof_end(PROF_ROUTE, s);
     return r;
+}
+
+// Checks of the fused decode step (ft_moe_step_fused), then its launch.
+ft_status fused_step(const ft_moe_step* st, hipStream_t s) {
+    clear_error();
+    FT_CHECK_ARG(st, "null step");
+    const ft_moe_weights& w = st->weights;
+    ft_status v = check_weights(&w);
+    if (v != FT_OK) return v;
+    FT_CHECK_ARG(st->T >= 0, "T must be >= 0");
+    FT_CHECK_ARG(st->k >= 1 && st->k <= w.E, "k must be in [1, E]");
+    if (w.w_dt != FT_BF16 || st->act_dt != FT_BF16)
+        return set_error(FT_ERR_UNSUPPORTED, "the fused step takes bf16 weights and activations");
+    if (!fused_shape_ok(st->T > 0 ? st->T : 1, st->k, w.E, w.H, w.I, w.n_shared))
+        return set_error(FT_ERR_UNSUPPORTED,
+                         "the fused step takes T <= 4, E <= 512, T*k + n_shared*T <= 64, T*H and "
+                         "(T*k + n_shared*T)*I bf16 values within 128 KiB (T=%d k=%d E=%d H=%d I=%d)",
+                         st->T, st->k, w.E, w.H, w.I);
+    if (st->T == 0) return FT_OK;
+    FT_CHECK_ARG(st->x && st->w_router && st->logits && st->topk_ids && st->topk_w && st->out,
+                 "x, w_router, logits, topk_ids, topk_w and out are required");
+    FT_CHECK_ARG(aligned16(st->x) && aligned16(st->w_router), "x / w_router must be 16-byte aligned");
+    FT_CHECK_ARG(st->out_dt == FT_BF16 || st->out_dt == FT_F32, "out_dt must be FT_BF16 or FT_F32");
+    size_t offs[6];
+    layout(w.w_dt, w.H, w.I, offs);
+    return launch_fused_decode(st, offs, s);
 }
 
 }  // namespace ft

@@ -16,6 +16,8 @@
 namespace ft {
 void set_capturing(bool on);
 ft_status route_align(const ft_moe_step* st, hipStream_t s);
+ft_status fused_step(const ft_moe_step* st, hipStream_t s);
+ft_status fused_timeouts(int* count);
 }
 
 using namespace ft;
@@ -38,23 +40,14 @@ ft_status run_step(const ft_moe_step* st, void* stream) {
                           st->weights.H, st->weights.n_shared, st->out, st->out_dt, stream);
 }
 
-}  // namespace
+ft_status run_fused(const ft_moe_step* st, void* stream) { return fused_step(st, (hipStream_t)stream); }
 
-extern "C" {
-
-ft_status ft_moe_step_run(const ft_moe_step* st, void* stream) {
-    clear_error();
-    FT_CHECK_ARG(st, "null step");
-    return run_step(st, stream);
-}
-
-ft_status ft_moe_graph_create(const ft_moe_step* st, void* stream, ft_moe_graph** out) {
-    clear_error();
-    FT_CHECK_ARG(st && out, "null step / out");
+// Runs `run` once eagerly on `stream` (every argument check, first-use set-up
+// outside the capture), waits, then captures it on a private stream.
+ft_status create_graph(const ft_moe_step* st, void* stream, ft_moe_graph** out,
+                       ft_status (*run)(const ft_moe_step*, void*)) {
     *out = nullptr;
-    // one eager step first: every argument check runs, and per-kernel
-    // attributes (dynamic LDS limits) are set outside the capture
-    ft_status r = run_step(st, stream);
+    ft_status r = run(st, stream);
     if (r != FT_OK) return r;
     FT_HIP(hipStreamSynchronize((hipStream_t)stream));
 
@@ -64,7 +57,7 @@ ft_status ft_moe_graph_create(const ft_moe_step* st, void* stream, ft_moe_graph*
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
         set_capturing(true);  // profile events stay out of the graph
-        r = run_step(st, cap);
+        r = run(st, cap);
         set_capturing(false);
         e = hipStreamEndCapture(cap, &g->graph);
     }
@@ -79,6 +72,39 @@ ft_status ft_moe_graph_create(const ft_moe_step* st, void* stream, ft_moe_graph*
     }
     *out = g;
     return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ft_status ft_moe_step_run(const ft_moe_step* st, void* stream) {
+    clear_error();
+    FT_CHECK_ARG(st, "null step");
+    return run_step(st, stream);
+}
+
+ft_status ft_moe_graph_create(const ft_moe_step* st, void* stream, ft_moe_graph** out) {
+    clear_error();
+    FT_CHECK_ARG(st && out, "null step / out");
+    return create_graph(st, stream, out, run_step);
+}
+
+ft_status ft_moe_step_fused(const ft_moe_step* st, void* stream) {
+    return fused_step(st, (hipStream_t)stream);
+}
+
+ft_status ft_moe_graph_create_fused(const ft_moe_step* st, void* stream, ft_moe_graph** out) {
+    clear_error();
+    FT_CHECK_ARG(st && out, "null step / out");
+    return create_graph(st, stream, out, run_fused);
+}
+
+ft_status ft_moe_fused_timeouts(int* count) {
+    clear_error();
+    FT_CHECK_ARG(count, "null count");
+    *count = 0;
+    return fused_timeouts(count);
 }
 
 ft_status ft_moe_graph_launch(ft_moe_graph* g, void* stream) {

@@ -33,7 +33,8 @@ EXPORTS = [
     "ft_slot_cache_stats", "ft_slot_cache_lookup", "ft_slot_cache_resize", "ft_moe_step_run",
     "ft_moe_graph_create", "ft_moe_graph_launch", "ft_moe_graph_destroy", "ft_host_expert_ffn",
     "ft_host_moe_ffn_submit", "ft_host_job_wait", "ft_moe_ffn_noalloc", "ft_split_misses",
-    "ft_moe_scatter_rows", "ft_slot_stack_forward", "ft_host_device_pointer",
+    "ft_moe_scatter_rows", "ft_slot_stack_forward", "ft_host_device_pointer", "ft_moe_step_fused",
+    "ft_moe_graph_create_fused", "ft_moe_fused_timeouts",
 ]
 STACK_DEVICE_TABLE = 1   # FT_STACK_DEVICE_TABLE
 NOALLOC_SCRATCH_BYTES = 64 << 20   # FT_NOALLOC_SCRATCH_BYTES
@@ -145,6 +146,9 @@ def load() -> C.CDLL:
         "ft_moe_graph_launch": [P, P],
         "ft_moe_graph_destroy": [P],
         "ft_host_device_pointer": [P, C.POINTER(P)],
+        "ft_moe_step_fused": [C.POINTER(MoeStep), P],
+        "ft_moe_graph_create_fused": [C.POINTER(MoeStep), P, C.POINTER(P)],
+        "ft_moe_fused_timeouts": [C.POINTER(C.c_int)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -469,14 +473,24 @@ class LayerStep:
         """ft_moe_graph_create (runs the step once, then captures it)."""
         return Graph(self, stream)
 
+    def run_fused(self, stream=None) -> torch.Tensor:
+        """ft_moe_step_fused: the step as one kernel; writes logits, ids, w and out."""
+        _check(load().ft_moe_step_fused(C.byref(self.desc), _stream(stream)))
+        return self.out
+
+    def capture_fused(self, stream=None) -> "Graph":
+        """ft_moe_graph_create_fused (one fused step, then its one-node graph)."""
+        return Graph(self, stream, fused=True)
+
 
 class Graph:
     """A captured LayerStep (ft_moe_graph_*); keeps the step's buffers alive."""
 
-    def __init__(self, step: LayerStep, stream=None):
+    def __init__(self, step: LayerStep, stream=None, fused: bool = False):
         self.step = step
         h = C.c_void_p()
-        _check(load().ft_moe_graph_create(C.byref(step.desc), _stream(stream), C.byref(h)))
+        create = load().ft_moe_graph_create_fused if fused else load().ft_moe_graph_create
+        _check(create(C.byref(step.desc), _stream(stream), C.byref(h)))
         self.h = h
 
     def launch(self, stream=None) -> torch.Tensor:
@@ -493,6 +507,13 @@ class Graph:
             self.close()
         except Exception:
             pass
+
+
+def fused_timeouts() -> int:
+    """ft_moe_fused_timeouts: fused-step waits that gave up since the last call."""
+    n = C.c_int(0)
+    _check(load().ft_moe_fused_timeouts(C.byref(n)))
+    return n.value
 
 
 def set_profile_events(which: int, start, stop):

@@ -11,6 +11,7 @@
  *   ft_moe_combine  gate-weighted sum back to token order
  *   ft_moe_step_run / ft_moe_graph_*  the four as one step, eager or as a
  *                   captured HIP graph
+ *   ft_moe_step_fused  a decode step (up to 4 tokens) as one kernel launch
  *   ft_slot_cache_* LRU expert-slot cache over a pinned host expert pool, with
  *                   the next layer's missing experts copied while this layer
  *                   computes
@@ -32,7 +33,8 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Work is enqueued asynchronously; no entry point synchronises the stream
  *     unless stated.  The caller owns every buffer; the library never
- *     allocates device memory in these calls (workspace is passed in).
+ *     allocates device memory in these calls (workspace is passed in), except
+ *     the fused step's exchange buffer, made once per device on its first call.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failed check returns FT_ERR_INVALID_ARG / FT_ERR_UNSUPPORTED and
  *     enqueues nothing.  A HIP launch error returns FT_ERR_HIP.  The message
@@ -315,6 +317,53 @@ ft_status ft_moe_step_run(const ft_moe_step* step, void* stream);
 ft_status ft_moe_graph_create(const ft_moe_step* step, void* stream, ft_moe_graph** out);
 ft_status ft_moe_graph_launch(ft_moe_graph* graph, void* stream);
 ft_status ft_moe_graph_destroy(ft_moe_graph* graph);
+
+/* --------------------------------------------------------------------------
+ * Fused decode step: the whole layer in one kernel launch.
+ *
+ * ft_moe_step_fused enqueues the step of `step` as one kernel: router logits,
+ * top-k gating (the rule of ft_moe_route), gate/up + SwiGLU, down projection
+ * and the gated combine, with one grid-wide exchange after the logits and one
+ * after h; the down weights are loaded while the exchange of h is pending.
+ * The pages list graph-compatible execution among the runtime's features
+ * (refft.com guide, "深度解析", the runtime feature list); the launch gaps
+ * between the separate kernels are what this removes.
+ *   Writes logits [T][E], topk_ids, topk_w (each token's picks and gates by
+ *   the same rule as ft_moe_route, from these logits) and out [T][H]
+ *   (out_dt FT_BF16 or FT_F32).  counts, offsets, perm, inv_perm, y_perm and
+ *   the workspaces are neither read nor written (they may be NULL).
+ *   out[t] = sum over the picks j (and the shared expert, gate 1) of
+ *   topk_w[t][j] * (W_down h), each expert's down-projection row sum taken in
+ *   fp32 and never rounded to y_dt; h is rounded to bf16 as in ft_moe_ffn.
+ *   The sums run in another fixed order than the separate kernels', so the
+ *   logits and out agree with ft_moe_step_run to rounding, not bit for bit;
+ *   each is deterministic from run to run.
+ *   slot_of_expert as in ft_moe_ffn; an expert whose entry is -1 (or -2 - j
+ *   without a host pool) adds nothing to out.
+ * Supported: bf16 weights and activations, 1 <= T <= 4, E <= 512,
+ * T*k + n_shared*T <= 64, T*H and (T*k + n_shared*T)*I bf16 values of at
+ * most 128 KiB each; other steps return FT_ERR_UNSUPPORTED before anything
+ * is enqueued (T == 0 returns FT_OK and enqueues nothing).
+ * The grid is one block per CU and every block waits for the others twice:
+ * the device must have all its CUs free for the launch (another kernel that
+ * never ends on the same device would hold blocks back; each wait gives up
+ * after 0.1 s and is counted, see ft_moe_fused_timeouts).  The blocks
+ * exchange data through a buffer of about 150 KiB per device, allocated
+ * uncached on the first call on that device and held until the process ends;
+ * that first call synchronises the device and must not be captured.  Fused
+ * steps on one device must not overlap (they share that buffer); use one
+ * stream, or order them.
+ *
+ * ft_moe_graph_create_fused is ft_moe_graph_create for the fused step: one
+ * eager fused step, then the step captured as a graph of one kernel node,
+ * replayed with ft_moe_graph_launch and freed with ft_moe_graph_destroy.
+ *
+ * ft_moe_fused_timeouts waits for the current device, returns in *count the
+ * number of fused-step waits that gave up since the last call, and resets it.
+ * ------------------------------------------------------------------------ */
+ft_status ft_moe_step_fused(const ft_moe_step* step, void* stream);
+ft_status ft_moe_graph_create_fused(const ft_moe_step* step, void* stream, ft_moe_graph** out);
+ft_status ft_moe_fused_timeouts(int* count);
 
 /* --------------------------------------------------------------------------
  * Expert slot cache.

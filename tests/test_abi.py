@@ -211,6 +211,34 @@ def test_step_and_graph_reject_bad_arguments():
     assert lib.ft_moe_step_run(C.byref(_step(k=9)), None) == ft.ERR_INVALID_ARG
 
 
+def test_fused_step_refuses_what_it_cannot_take():
+    """The fused step's checks run on the host before any device call: bad
+    arguments and shapes past its limits come back without a GPU."""
+    lib = ft.load()
+    h = C.c_void_p()
+    assert lib.ft_moe_step_fused(None, None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_graph_create_fused(None, None, C.byref(h)) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_fused_timeouts(None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_step_fused(C.byref(_step(k=0)), None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_step_fused(C.byref(_step(k=9)), None) == ft.ERR_INVALID_ARG
+    assert lib.ft_moe_step_fused(C.byref(_step(T=0)), None) == ft.OK        # nothing enqueued
+
+    def step(w_dt=ft.BF16, act=ft.BF16, E=8, H=128, I=128, n_shared=0, T=4, k=2):
+        w = ft.MoeWeights(w_dt, E, H, I, n_shared, 4096,
+                          ft.slot_stride({ft.BF16: "bf16", ft.F32: "f32", ft.MXFP4: "mxfp4"}[w_dt], H, I), 0)
+        p = 4096
+        return ft.MoeStep(w, p, act, p, None, T, k, None, p, p, p, p, p, p, p, p, 1 << 20, p,
+                          ft.BF16, p, 1 << 20, p, ft.BF16)
+
+    for bad in (step(T=5), step(w_dt=ft.F32, act=ft.F32), step(w_dt=ft.MXFP4), step(E=600),
+                step(H=32768, T=3), step(I=4096, T=4, k=8, E=64),
+                step(T=4, k=16, n_shared=1, E=64)):
+        assert lib.ft_moe_step_fused(C.byref(bad), None) == ft.ERR_UNSUPPORTED
+        assert lib.ft_moe_graph_create_fused(C.byref(bad), None, C.byref(h)) == ft.ERR_UNSUPPORTED
+        assert not h.value
+    assert "fused step" in ft.last_error()
+
+
 def test_struct_layouts_match_the_header(tmp_path):
     """ctypes mirrors of the header's structs: same size and field offsets as
     the C compiler gives them."""
