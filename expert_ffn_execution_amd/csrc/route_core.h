@@ -7,9 +7,8 @@
 // logits l' = fl32(l + b), equal values ordered by increasing expert id,
 // -0.0 equal to +0.0; gates = softmax over the k picks.  Each lane holds
 // E/64 keys; a key packs the order-preserving integer image of l' above the
-// complemented expert id, so a single 64-bit max picks the largest value and,
-// among equal values, the lowest id.  k rounds of a wave max pick the experts
-// in order.
+// complemented expert id, so the larger key is the larger value and, among
+// equal values, the lower id.  k rounds pick the experts in order.
 #pragma once
 
 #include "common.h"
@@ -27,12 +26,12 @@ __device__ __forceinline__ float key_value(uint64_t key) {
     uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
     return __uint_as_float(u);
 }
-// Wave-wide max and sum, returned uniform.  DPP exchanges inside each row of
+// Wave-wide sum and max, returned uniform.  DPP exchanges inside each row of
 // 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
 // row_mirror: each pairs lanes across the next larger group), then the four
 // row results read as scalars.  (The xor-shuffle form goes through LDS
-// permutes, a round trip each: 12 per 64-bit max, and the top-k's k maxima
-// are a dependent chain.)
+// permutes, a round trip each, and the top-k's k maxima are a dependent
+// chain.)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
@@ -41,18 +40,10 @@ template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
     return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
 }
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
     return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = max_u64(v, dpp_u64<0xB1>(v));
-    v = max_u64(v, dpp_u64<0x4E>(v));
-    v = max_u64(v, dpp_u64<0x141>(v));
-    v = max_u64(v, dpp_u64<0x140>(v));
-    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 __device__ __forceinline__ double dpp_add_f64(double v, uint64_t o) { return v + __builtin_bit_cast(double, o); }
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -69,9 +60,23 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
            (__builtin_bit_cast(double, lane_u64(b, 32)) + __builtin_bit_cast(double, lane_u64(b, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
 // Token t's picks and gates: row = its E logits, ids_out / w_out = its k
 // slots; ids_copy (may be null) receives the picks too.  NPL = keys per lane
-// (E <= 64 * NPL).
+// (E <= 64 * NPL).  Each lane first sorts its NPL keys, so a pick compares
+// only the lanes' heads: the largest value by one 32-bit wave max, then the
+// lowest id among the lanes holding it (the largest complemented id) by
+// another; the winning lane drops its head.  (One 64-bit wave max over all
+// keys per pick took about 880 cycles a pick on one wavefront.)
 template <int NPL>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, const float* __restrict__ bias,
                                            int E, int k, int32_t* __restrict__ ids_out,
@@ -87,29 +92,39 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, const 
             key[i] = make_key(v, e);
         }
     }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+#pragma unroll
+        for (int j = i + 1; j < NPL; ++j) {
+            const uint64_t hi = key[i] > key[j] ? key[i] : key[j];
+            const uint64_t lo = key[i] > key[j] ? key[j] : key[i];
+            key[i] = hi;
+            key[j] = lo;
+        }
+    uint32_t hv = (uint32_t)(key[0] >> 32), lv = (uint32_t)key[0];
     float pick_v[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) pick_v[i] = 0.0f;
     float v0 = 0.0f;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        int e = (int)(~(uint32_t)best);
-        float v = key_value(best);
+        const uint32_t mh = wave_max_u32(hv);
+        const uint32_t ml = wave_max_u32(hv == mh ? lv : 0u);
+        const int e = (int)(~ml);
+        const float v = key_value(((uint64_t)mh << 32) | ml);
         if (j == 0) v0 = v;
-        if (lane == (e & 63)) {
-#pragma unroll
-            for (int i = 0; i < NPL; ++i)
-                if (i == (e >> 6)) key[i] = 0;
-        }
         if (lane == (j & 63)) {
 #pragma unroll
             for (int i = 0; i < NPL; ++i)
                 if (i == (j >> 6)) pick_v[i] = v;
             ids_out[j] = e;
             if (ids_copy) ids_copy[j] = e;
+        }
+        if (hv == mh && lv == ml) {  // the winning lane drops its head
+#pragma unroll
+            for (int i = 0; i + 1 < NPL; ++i) key[i] = key[i + 1];
+            key[NPL - 1] = 0;
+            hv = (uint32_t)(key[0] >> 32);
+            lv = (uint32_t)key[0];
         }
     }
     // gates in fp64: w_j = exp(v_j - v_0) / sum_i exp(v_i - v_0)
