@@ -614,10 +614,11 @@ __device__ __forceinline__ bf16x8_t nvfp4x8_bf16(uint32_t codes, float bs) {
     return __builtin_bit_cast(bf16x8_t, d);
 }
 
-// Per-step shape of the matrix-core kernel (WT: 2 = MXFP4, 3 = FP8, 4 = NVFP4).
+// Per-step shape of the matrix-core kernel (WT: 1 = bf16, 2 = MXFP4, 3 = FP8,
+// 4 = NVFP4).  bf16 rows need no decode: each 16-byte load is one fragment.
 template <int WT> struct MxShape {
     static constexpr int LPS = 2;                                // 16-byte code loads per lane, step, matrix
-    static constexpr int EPL = WT == 3 ? 16 : 32;                // weights per 16-byte load
+    static constexpr int EPL = WT == 1 ? 8 : WT == 3 ? 16 : 32;  // weights per 16-byte load
     static constexpr int LE = LPS * EPL;                         // weights per lane and step
     static constexpr int KS = 4 * LE;                            // K per step (128 code bytes of a row)
     static constexpr int NF = LE / 8;                            // 8-wide B fragments per lane, step
@@ -627,7 +628,7 @@ template <int WT> struct MxShape {
 
 template <int WT, int NM, typename OT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
-    static_assert(WT == 2 || WT == 3 || WT == 4, "narrow weights only");
+    static_assert(WT >= 1 && WT <= 4, "bf16 or narrow weights");
     using S = MxShape<WT>;
     constexpr int D = MX_D, LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
     static_assert(D % SPW == 0, "a scale word's steps share one register round");
@@ -646,7 +647,8 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     const int U = rgw * nks;                                              // (group, step) pairs
     const int ln = lane & 15, q = lane >> 4;
     const uint8_t* sl = ft::slot_weights(a.pool, a.slot_stride, a.host_pool, a.host_stride, gr.slot);
-    const size_t rowb = WT == 3 ? (size_t)K : (size_t)K / 2, srowb = (size_t)K / (WT == 4 ? 16 : 32);
+    const size_t rowb = WT == 1 ? (size_t)K * 2 : WT == 3 ? (size_t)K : (size_t)K / 2;
+    const size_t srowb = (size_t)K / (WT == 4 ? 16 : 32);
     float msc[NM];  // FP8 matrix / NVFP4 tensor scales (applied to the finished sums)
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -726,7 +728,9 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
 #pragma unroll
                     for (int f = 0; f < NF; ++f) {
                         bf16x8_t bw;
-                        if constexpr (WT == 2) {
+                        if constexpr (WT == 1) {
+                            bw = __builtin_bit_cast(bf16x8_t, cb[b][m][f]);
+                        } else if constexpr (WT == 2) {
                             // scale byte of this lane's 32-block: byte SPW-step s, group q, load h
                             const int h = f / 4, by = (v % SPW) * 4 * LPS + LPS * q + h;
                             const uint32_t word = sv[t][m][by >> 2];
@@ -865,6 +869,23 @@ bool mx_eligible(int WT, int K, int T) {
     if (WT == 4) return K % 256 == 0;
     return WT == 3 && K % 128 == 0;
 }
+// bf16 rows on matrix cores (more than one token, K a multiple of 64).  The
+// down rows always: 35B-A3B layer at 2 / 4 / 16 / 64 tokens 18.8 / 31.9 /
+// 69.4 / 98.0 us on the dot-product kernel, 14.8 / 21.1 / 52.5 / 76.8 us here;
+// 753B-A40B at 32 tokens 570 -> 515 us.  The gate/up rows only at up to 4
+// tokens with rows of at most 2048 (35B-A3B: 38.2 -> 25.9 us at 2 tokens,
+// 50.7 -> 46.9 at 4; but 88 -> 112 at 16, and the 753B-A40B layer's 6144-long
+// rows 128 -> 140 at 2 tokens).  FTMOE_BF16_MX forces 0 neither, 1 the down
+// rows only, 2 both.
+bool bf16_mx_eligible(int NM, int K, int T) {
+    static const int mode = [] {
+        const char* e = getenv("FTMOE_BF16_MX");
+        return e ? atoi(e) : -1;
+    }();
+    if (T < 2 || K % 64 != 0) return false;
+    if (mode >= 0) return mode >= 2 || (mode == 1 && NM == 1);
+    return NM == 1 || (T <= 4 && K <= 2048);
+}
 template <int WT, int NM, typename OT>
 ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     // Token rows per group: up to 8, within 64 KB of LDS (two blocks or more
@@ -891,7 +912,9 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
     // Rows per block.  A wavefront's start-up (group lookup, activation
     // staging, the first loads' latency) is fixed, so each wavefront streams
-    // at least wave_bytes of weights (64 KB FP8, 32 KB MXFP4: measured best);
+    // at least wave_bytes of weights (64 KB FP8, 32 KB MXFP4 and bf16: measured
+    // best; bf16 35B-A3B down rows at 16 / 64 tokens 49.4 / 73.7 us with 32 KB,
+    // 52.7 / 76.8 with 64 KB, 61.1 / 79.8 with 128 KB);
     // then the grid is held to at most target_blocks() and, while the rows can
     // still halve, to at least 512 blocks.  FP8 35B-A3B down rows (768 B) at
     // 4 / 16 / 64 tokens: 29 / 66 / 60 us with one row group per wavefront,
@@ -901,7 +924,8 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
         return e ? atoi(e) : 0;
     }();
     const size_t wave_bytes = (size_t)(wave_kb > 0 ? wave_kb : WT == 3 ? 64 : 32) * 1024;
-    const size_t row_w = (WT == 3 ? (size_t)a.K : (size_t)a.K / 2 + a.K / (WT == 4 ? 16 : 32)) * NM;  // weight bytes per row
+    const size_t row_w = (WT == 1 ? (size_t)a.K * 2 : WT == 3 ? (size_t)a.K
+                                                  : (size_t)a.K / 2 + a.K / (WT == 4 ? 16 : 32)) * NM;  // weight bytes per row
     auto nblk = [&](int rpb) { return groups * ((a.N + rpb - 1) / rpb); };
     int rpb = 16 * NWAVE;
     while (rpb < a.N && (size_t)(rpb / NWAVE) * row_w < wave_bytes) rpb *= 2;
@@ -957,7 +981,10 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     const int cap = (g.w_dt != FT_F32 && big) ? 4 : 8;
     ft_status r;
     if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
-    else if (g.w_dt == FT_BF16) r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    else if (g.w_dt == FT_BF16) {
+        if (bf16_mx_eligible(2, a1.K, a1.T)) r = launch_mx<1, 2, float>(a1, g.n_shared, max_lds, s);
+        else r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+    }
     else if (g.w_dt == FT_FP8) {
         if (mx_eligible(3, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
         else r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
@@ -983,8 +1010,13 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a2.dst = y;
     if (g.w_dt == FT_F32) r = launch_rows<0, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) {
-        if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
-        else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+        if (bf16_mx_eligible(1, a2.K, a2.T)) {
+            if (y_dt == FT_F32) r = launch_mx<1, 1, float>(a2, g.n_shared, max_lds, s);
+            else r = launch_mx<1, 1, __bf16>(a2, g.n_shared, max_lds, s);
+        } else {
+            if (y_dt == FT_F32) r = launch_rows<1, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
+            else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
+        }
     } else if (g.w_dt == FT_FP8) {
         if (mx_eligible(3, a2.K, a2.T)) {
             if (y_dt == FT_F32) r = launch_mx<3, 1, float>(a2, g.n_shared, max_lds, s);
