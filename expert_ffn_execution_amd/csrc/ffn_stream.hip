@@ -310,7 +310,7 @@ __device__ __forceinline__ void with_rows(int R, F&& f) {
 // NM = 2: gate and up rows -> h = silu(gate) * up (row length H, N = I).
 // NM = 1: down rows -> y (row length I, N = H).
 template <int WT, int NM, int QMAX, int RMAX, typename OT>
-__global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
+__device__ __forceinline__ void stream_body(const StreamArgs& a) {
     using AT = typename std::conditional<WT == 0, float, __bf16>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     AT* xs = reinterpret_cast<AT*>(smem);
@@ -538,6 +538,16 @@ __global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
         }
     };
     with_rows<RMAX>(R, stream);
+}
+
+template <int WT, int NM, int QMAX, int RMAX, typename OT>
+__global__ __launch_bounds__(256) void stream_kernel(const StreamArgs a) {
+    stream_body<WT, NM, QMAX, RMAX, OT>(a);
+}
+// The same held to 168 VGPRs, so that three wavefronts fit a SIMD
+template <int WT, int NM, int QMAX, int RMAX, typename OT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void stream_kernel_w3(const StreamArgs a) {
+    stream_body<WT, NM, QMAX, RMAX, OT>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -834,7 +844,11 @@ ft_status launch_one(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) 
     a.wk = make_walk(a.K, W<WT>::EPC, QMAX);
     a.RPB = pick_rpb(groups, a.N, 64 / a.wk.LPR, target_blocks(RMAX));
     a.NB = (a.N + a.RPB - 1) / a.RPB;
+    // bf16 gate/up rows at up to 4 token rows fit 168 VGPRs: three wavefronts
+    // per SIMD instead of two (35B-A3B at 8 / 16 tokens 64.3 / 87.9 -> 57.5 /
+    // 84.5 us; 753B-A40B at 2 tokens 127.5 -> 122.2 us)
     auto kern = stream_kernel<WT, NM, QMAX, RMAX, OT>;
+    if constexpr (WT == 1 && NM == 2 && RMAX == 4) kern = stream_kernel_w3<WT, NM, QMAX, RMAX, OT>;
     if (lds > 65536)
         FT_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
@@ -858,13 +872,16 @@ ft_status launch_rows(const StreamArgs& a, int n_shared, int cap, size_t max_lds
 // multiple of 128.  Only with more than one token: at one token the lean
 // one-row dot-product kernel is as fast for MXFP4 and faster for FP8
 // (35B-A3B gate/up 12.8 vs 17.5 us).
-bool mx_eligible(int WT, int K, int T) {
-    static const bool off = getenv("FTMOE_MX_DOT") != nullptr;  // keep the dot-product kernel
+int mx_min_t() {
     static const int min_t = [] {
         const char* e = getenv("FTMOE_MX_MIN_T");
         return e ? atoi(e) : 2;
     }();
-    if (off || T < min_t) return false;
+    return min_t;
+}
+bool mx_eligible(int WT, int K, int T) {
+    static const bool off = getenv("FTMOE_MX_DOT") != nullptr;  // keep the dot-product kernel
+    if (off || T < mx_min_t()) return false;
     if (WT == 2) return K % 512 == 0;
     if (WT == 4) return K % 256 == 0;
     return WT == 3 && K % 128 == 0;
@@ -882,7 +899,7 @@ bool bf16_mx_eligible(int NM, int K, int T) {
         const char* e = getenv("FTMOE_BF16_MX");
         return e ? atoi(e) : -1;
     }();
-    if (T < 2 || K % 64 != 0) return false;
+    if (T < mx_min_t() || K % 64 != 0) return false;
     if (mode >= 0) return mode >= 2 || (mode == 1 && NM == 1);
     return NM == 1 || (T <= 4 && K <= 2048);
 }
@@ -979,11 +996,16 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a1.src = x;
     a1.dst = h;
     const int cap = (g.w_dt != FT_F32 && big) ? 4 : 8;
+    // bf16 gate/up groups of at most 4 token rows (the three-wavefront kernel)
+    // while routed rows average at most 2 per expert; beyond that more experts
+    // would be split into groups that re-read their weights (35B-A3B at 64
+    // tokens: 138 us with 8 rows a group, 172 with 4)
+    const int cap1 = g.w_dt == FT_BF16 && (long)g.T * g.k <= 2L * g.E ? 4 : cap;
     ft_status r;
     if (g.w_dt == FT_F32) r = launch_rows<0, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     else if (g.w_dt == FT_BF16) {
         if (bf16_mx_eligible(2, a1.K, a1.T)) r = launch_mx<1, 2, float>(a1, g.n_shared, max_lds, s);
-        else r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
+        else r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap1, max_lds, s);
     }
     else if (g.w_dt == FT_FP8) {
         if (mx_eligible(3, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
