@@ -251,7 +251,9 @@ def test_layer_tiny_f32():
     check_close(r["out"], ref, "f32", "tiny")
 
 
-@pytest.mark.parametrize("T", [1, 16, 64, 300])
+# T = 3: gate/up and down rows on the matrix-core streaming kernel; 16: gate/up
+# on the three-wavefront dot-product kernel; 64: groups of up to 8 token rows
+@pytest.mark.parametrize("T", [1, 3, 16, 64, 300])
 def test_layer_a3b_bf16(T):
     sh = synth.A3B_BF16
     _say("layer 35b-a3b bf16 T", T)
