@@ -756,6 +756,16 @@ def decode_entry(sh, r, g_ms, T, fused=None):
     kernel durations (and, second, over the whole replayed step)."""
     ffn_s = r["ffn_ms"] * 1e-3
     narrow = sh.wdtype in ("mxfp4", "fp8", "nvfp4") and T >= 2
+    # bf16: down rows on matrix cores from 2 tokens, gate/up rows too at 2-4
+    # tokens on rows of at most 2048 (the library's dispatch rule)
+    if sh.wdtype == "bf16" and T >= 2:
+        kern = ("gate/up + down weight streaming on matrix cores (stream_mx_kernel)"
+                if T <= 4 and sh.H <= 2048 else
+                "gate/up weight streaming (stream_kernel) + down on matrix cores (stream_mx_kernel)")
+    elif narrow:
+        kern = "gate/up + down weight streaming on matrix cores (stream_mx_kernel)"
+    else:
+        kern = "gate/up + down weight streaming (stream_kernel)"
     return {
         "T": T, "tokens_per_s": T / (g_ms / 1e3), "ms_per_step": g_ms,
         "eager_tokens_per_s": r["tokens_per_s"], "eager_ms_per_step": r["ms_per_step"],
@@ -766,8 +776,7 @@ def decode_entry(sh, r, g_ms, T, fused=None):
         "roofline": {"bound": "hbm", "achieved": r["weight_bytes"] / ffn_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["weight_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": ("gate/up + down weight streaming on matrix cores (stream_mx_kernel)"
-                                if narrow else "gate/up + down weight streaming (stream_kernel)"),
+                     "kernel": kern,
                      "bytes_per_step": r["weight_bytes"]},
         **({"fused": fused} if fused else {})}
 
