@@ -584,7 +584,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 // Against the kernel above: gate/up 33 vs 56 us at 2 tokens and 353 vs 418
 // us at 64; down 195 vs 223 us at 64 tokens.
 // ---------------------------------------------------------------------------
-constexpr int MX_D = 4;  // steps in flight per wavefront (a multiple of 2)
+// Steps in flight per wavefront (a multiple of 2): 4 for bf16 rows, 2 for the
+// narrow formats, whose registers then leave room for more wavefronts.
+// Narrow rows with 2 against 4 (us): 284B-A13B MXFP4 gate/up 89.0 vs 94.0 at 8
+// tokens and 346 vs 352 at 64; 753B-A40B MXFP4 298 vs 305 at 32; 35B-A3B FP8
+// 49.0 vs 52.3 at 16 and 79.0 vs 81.8 at 64.  bf16 down rows at 64 tokens
+// were 2% slower with 2 (74.8 vs 73.5), 6 and 8 slower for every format.
+template <int WT> constexpr int mx_d() { return WT == 1 ? 4 : 2; }
 
 __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t codes, float sc) {
     u32x4_t d;
@@ -633,14 +639,14 @@ template <int WT> struct MxShape {
     static constexpr int KS = 4 * LE;                            // K per step (128 code bytes of a row)
     static constexpr int NF = LE / 8;                            // 8-wide B fragments per lane, step
     static constexpr int SPW = WT == 2 ? 16 / (4 * LPS) : 1;     // MXFP4: steps per 16-byte scale word
-    static constexpr int NSV = WT == 2 ? 2 * MX_D / SPW : 1;     // MXFP4: scale-word slots
+    static constexpr int NSV = WT == 2 ? 2 * mx_d<WT>() / SPW : 1;  // MXFP4: scale-word slots
 };
 
 template <int WT, int NM, typename OT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     static_assert(WT >= 1 && WT <= 4, "bf16 or narrow weights");
     using S = MxShape<WT>;
-    constexpr int D = MX_D, LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
+    constexpr int D = mx_d<WT>(), LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
     static_assert(D % SPW == 0, "a scale word's steps share one register round");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16* xs = reinterpret_cast<__bf16*>(smem);
