@@ -935,9 +935,10 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
     // Rows per block.  A wavefront's start-up (group lookup, activation
     // staging, the first loads' latency) is fixed, so each wavefront streams
-    // at least wave_bytes of weights (64 KB FP8, 32 KB MXFP4 and bf16: measured
-    // best; bf16 35B-A3B down rows at 16 / 64 tokens 49.4 / 73.7 us with 32 KB,
-    // 52.7 / 76.8 with 64 KB, 61.1 / 79.8 with 128 KB);
+    // at least wave_bytes of weights (32 KB: measured best; bf16 35B-A3B down
+    // rows at 16 / 64 tokens 49.4 / 73.7 us with 32 KB, 52.7 / 76.8 with 64 KB,
+    // 61.1 / 79.8 with 128 KB; FP8 down rows, two steps in flight, 28.8 / 43.7
+    // with 32 KB, 35.1 / 45.7 with 64 KB);
     // then the grid is held to at most target_blocks() and, while the rows can
     // still halve, to at least 512 blocks.  FP8 35B-A3B down rows (768 B) at
     // 4 / 16 / 64 tokens: 29 / 66 / 60 us with one row group per wavefront,
@@ -946,7 +947,7 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
         const char* e = getenv("FTMOE_MX_WAVE_KB");
         return e ? atoi(e) : 0;
     }();
-    const size_t wave_bytes = (size_t)(wave_kb > 0 ? wave_kb : WT == 3 ? 64 : 32) * 1024;
+    const size_t wave_bytes = (size_t)(wave_kb > 0 ? wave_kb : 32) * 1024;
     const size_t row_w = (WT == 1 ? (size_t)a.K * 2 : WT == 3 ? (size_t)a.K
                                                   : (size_t)a.K / 2 + a.K / (WT == 4 ? 16 : 32)) * NM;  // weight bytes per row
     auto nblk = [&](int rpb) { return groups * ((a.N + rpb - 1) / rpb); };
