@@ -584,13 +584,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 // Against the kernel above: gate/up 33 vs 56 us at 2 tokens and 353 vs 418
 // us at 64; down 195 vs 223 us at 64 tokens.
 // ---------------------------------------------------------------------------
-// Steps in flight per wavefront (a multiple of 2): 4 for bf16 rows, 2 for the
-// narrow formats, whose registers then leave room for more wavefronts.
+// Steps in flight per wavefront (a multiple of 2): 4 for bf16 down rows, 2 for
+// bf16 gate/up rows and the narrow formats, whose registers then leave room
+// for more wavefronts (bf16 gate/up at 4 tokens 43.1 vs 45.5 us).
 // Narrow rows with 2 against 4 (us): 284B-A13B MXFP4 gate/up 89.0 vs 94.0 at 8
 // tokens and 346 vs 352 at 64; 753B-A40B MXFP4 298 vs 305 at 32; 35B-A3B FP8
 // 49.0 vs 52.3 at 16 and 79.0 vs 81.8 at 64.  bf16 down rows at 64 tokens
 // were 2% slower with 2 (74.8 vs 73.5), 6 and 8 slower for every format.
-template <int WT> constexpr int mx_d() { return WT == 1 ? 4 : 2; }
+template <int WT, int NM = 1> constexpr int mx_d() { return WT == 1 && NM == 1 ? 4 : 2; }
 
 __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t codes, float sc) {
     u32x4_t d;
@@ -639,15 +640,16 @@ template <int WT> struct MxShape {
     static constexpr int KS = 4 * LE;                            // K per step (128 code bytes of a row)
     static constexpr int NF = LE / 8;                            // 8-wide B fragments per lane, step
     static constexpr int SPW = WT == 2 ? 16 / (4 * LPS) : 1;     // MXFP4: steps per 16-byte scale word
-    static constexpr int NSV = WT == 2 ? 2 * mx_d<WT>() / SPW : 1;  // MXFP4: scale-word slots
+    static constexpr int NSV = WT == 2 ? 2 * mx_d<WT>() / SPW : 1;  // MXFP4: scale-word slots (D = 2 for both NM)
 };
 
 template <int WT, int NM, typename OT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(const StreamArgs a) {
     static_assert(WT >= 1 && WT <= 4, "bf16 or narrow weights");
     using S = MxShape<WT>;
-    constexpr int D = mx_d<WT>(), LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
+    constexpr int D = mx_d<WT, NM>(), LPS = S::LPS, KS = S::KS, NF = S::NF, SPW = S::SPW, NSV = S::NSV;
     static_assert(D % SPW == 0, "a scale word's steps share one register round");
+    static_assert(WT != 2 || NSV == 2 * D / SPW, "scale-word slots for D steps in flight");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16* xs = reinterpret_cast<__bf16*>(smem);
     const int j = blockIdx.x / a.NB, nb = blockIdx.x % a.NB;
