@@ -887,9 +887,19 @@ int mx_min_t() {
     }();
     return min_t;
 }
-bool mx_eligible(int WT, int K, int T) {
+// At one token (FTMOE_MX_MIN_T unset) only where measured faster: MXFP4 down
+// rows (284B-A13B 12.2 -> 10.9 us, 753B-A40B 16.5 -> 14.5), MXFP4 gate/up rows
+// of at most 4096 (284B-A13B 21.0 -> 19.1; 753B-A40B's 6144-long rows 27.5 vs
+// 28.1) and NVFP4 down rows (35B-A3B 7.8 -> 7.0); FP8 and NVFP4 gate/up rows
+// stay on the dot-product kernel (11.5 vs 15.8 us).
+bool mx_eligible(int WT, int NM, int K, int T) {
     static const bool off = getenv("FTMOE_MX_DOT") != nullptr;  // keep the dot-product kernel
-    if (off || T < mx_min_t()) return false;
+    static const bool forced = getenv("FTMOE_MX_MIN_T") != nullptr;
+    if (off || T < 1 || T < mx_min_t()) {
+        const bool one = !off && !forced && T == 1 &&
+                         ((WT == 2 && (NM == 1 || K <= 4096)) || (WT == 4 && NM == 1));
+        if (!one) return false;
+    }
     if (WT == 2) return K % 512 == 0;
     if (WT == 4) return K % 256 == 0;
     return WT == 3 && K % 128 == 0;
@@ -1017,12 +1027,12 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
         else r = launch_rows<1, 2, 4, float>(a1, g.n_shared, cap1, max_lds, s);
     }
     else if (g.w_dt == FT_FP8) {
-        if (mx_eligible(3, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
+        if (mx_eligible(3, 2, a1.K, a1.T)) r = launch_mx<3, 2, float>(a1, g.n_shared, max_lds, s);
         else r = launch_rows<3, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
     } else if (g.w_dt == FT_NVFP4) {
-        if (mx_eligible(4, a1.K, a1.T)) r = launch_mx<4, 2, float>(a1, g.n_shared, max_lds, s);
+        if (mx_eligible(4, 2, a1.K, a1.T)) r = launch_mx<4, 2, float>(a1, g.n_shared, max_lds, s);
         else r = launch_rows<4, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
-    } else if (mx_eligible(2, a1.K, a1.T)) {
+    } else if (mx_eligible(2, 2, a1.K, a1.T)) {
         r = launch_mx<2, 2, float>(a1, g.n_shared, max_lds, s);
     } else {
         r = launch_rows<2, 2, 4, float>(a1, g.n_shared, cap, max_lds, s);
@@ -1049,7 +1059,7 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
             else r = launch_rows<1, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
         }
     } else if (g.w_dt == FT_FP8) {
-        if (mx_eligible(3, a2.K, a2.T)) {
+        if (mx_eligible(3, 1, a2.K, a2.T)) {
             if (y_dt == FT_F32) r = launch_mx<3, 1, float>(a2, g.n_shared, max_lds, s);
             else r = launch_mx<3, 1, __bf16>(a2, g.n_shared, max_lds, s);
         } else {
@@ -1057,14 +1067,14 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
             else r = launch_rows<3, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
         }
     } else if (g.w_dt == FT_NVFP4) {
-        if (mx_eligible(4, a2.K, a2.T)) {
+        if (mx_eligible(4, 1, a2.K, a2.T)) {
             if (y_dt == FT_F32) r = launch_mx<4, 1, float>(a2, g.n_shared, max_lds, s);
             else r = launch_mx<4, 1, __bf16>(a2, g.n_shared, max_lds, s);
         } else {
             if (y_dt == FT_F32) r = launch_rows<4, 1, 8, float>(a2, g.n_shared, cap, max_lds, s);
             else r = launch_rows<4, 1, 8, __bf16>(a2, g.n_shared, cap, max_lds, s);
         }
-    } else if (mx_eligible(2, a2.K, a2.T)) {
+    } else if (mx_eligible(2, 1, a2.K, a2.T)) {
         if (y_dt == FT_F32) r = launch_mx<2, 1, float>(a2, g.n_shared, max_lds, s);
         else r = launch_mx<2, 1, __bf16>(a2, g.n_shared, max_lds, s);
     } else {
