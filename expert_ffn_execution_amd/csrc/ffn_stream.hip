@@ -77,6 +77,7 @@ struct StreamArgs {
     int N, K;  // weight rows, row length in elements
     Walk wk;
     int RPB, NB, RCAP;
+    int target;  // grid target in blocks (0: the default for the token rows)
     const void* src;  // x (gate/up) or h (down)
     void* dst;        // h (gate/up) or y (down)
 };
@@ -819,12 +820,14 @@ Walk make_walk(int K, int epc, int QMAX) {
 // blocks.  With one token per group the whole layer is a few items per wave
 // and a grid that stays resident at once is fastest; with more tokens per
 // group a finer grid balances groups of unequal size.
-int target_blocks(int rmax) {
+// `hint` (StreamArgs::target) overrides the default for one launch.
+int target_blocks(int rmax, int hint = 0) {
     static const int forced = [] {
         const char* s = getenv("FTMOE_STREAM_BLOCKS");
         return s ? atoi(s) : 0;
     }();
     if (forced > 0) return forced;
+    if (hint > 0) return hint;
     return rmax == 1 ? 1024 : 4096;
 }
 int pick_rpb(long groups, int N, int rows_per_item, int target) {
@@ -850,7 +853,7 @@ ft_status launch_one(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) 
     a.n_routed_groups = (int)((tk + act * (rcap - 1)) / rcap);
     const long groups = a.n_routed_groups + (n_shared ? (a.T + rcap - 1) / rcap : 0);
     a.wk = make_walk(a.K, W<WT>::EPC, QMAX);
-    a.RPB = pick_rpb(groups, a.N, 64 / a.wk.LPR, target_blocks(RMAX));
+    a.RPB = pick_rpb(groups, a.N, 64 / a.wk.LPR, target_blocks(RMAX, a.target));
     a.NB = (a.N + a.RPB - 1) / a.RPB;
     // bf16 gate/up rows at up to 4 token rows fit 168 VGPRs: three wavefronts
     // per SIMD instead of two (35B-A3B at 8 / 16 tokens 64.3 / 87.9 -> 57.5 /
@@ -965,7 +968,7 @@ ft_status launch_mx(StreamArgs a, int n_shared, size_t max_lds, hipStream_t s) {
     auto nblk = [&](int rpb) { return groups * ((a.N + rpb - 1) / rpb); };
     int rpb = 16 * NWAVE;
     while (rpb < a.N && (size_t)(rpb / NWAVE) * row_w < wave_bytes) rpb *= 2;
-    while (rpb < a.N && nblk(rpb) > target_blocks(rcap)) rpb *= 2;
+    while (rpb < a.N && nblk(rpb) > target_blocks(rcap, a.target)) rpb *= 2;
     while (rpb > 16 * NWAVE && nblk(rpb) < 512) rpb /= 2;
     a.RPB = rpb;
     a.NB = (a.N + a.RPB - 1) / a.RPB;
@@ -1000,6 +1003,12 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
     a.T = g.T;
     a.k = g.k;
     a.shared_slot = shared_slot;
+    // bf16 weights of a layer with rows longer than 2048, from 8 tokens on: a
+    // finer grid (753B-A40B gate/up + down at 8 / 16 / 32 / 64 tokens: 586 /
+    // 934 / 1466 / 2152 us with 4096 blocks, 558 / 923 / 1430 / 2055 with
+    // 8192; at 2 tokens 8192 was slower, and on the 35B-A3B layer at every
+    // token count)
+    a.target = (g.w_dt == FT_BF16 && big && g.T >= 8) ? 8192 : 0;
 
     // gate/up + SwiGLU: rows I of length H
     StreamArgs a1 = a;
