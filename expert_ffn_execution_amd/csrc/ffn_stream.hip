@@ -1050,6 +1050,10 @@ ft_status launch_ffn_stream(const FfnGeom& g, const void* x, const int32_t* perm
 
     // down: rows H of length I
     StreamArgs a2 = a;
+    // MXFP4 down rows of a layer with rows longer than 2048 from 16 tokens on:
+    // the finer grid too (753B-A40B at 32 tokens 149 -> 138 us, 284B-A13B at
+    // 64 187 -> 178; their gate/up rows were as fast or slower with it)
+    if (g.w_dt == FT_MXFP4 && big && g.T >= 16) a2.target = 8192;
     a2.moff[0] = g.off[2];
     a2.soff[0] = g.off[5];
     a2.toff[0] = g.toff[2];
